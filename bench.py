@@ -1,0 +1,251 @@
+"""Decode-attention benchmark on one MI355X.
+
+A step is one decode_attn_run (split pass + combine pass) over one batch of
+the batched long-context workload: batch 32, 32 query / 8 KV heads (GQA 4),
+head_dim 128, fp16 q/K/V, per-sequence context uniform in [16384, 32768],
+1 % of keys x8, 16-token pages in a shuffled pool. Inputs are resident in HBM
+before timing starts. Prints one JSON line.
+
+value   = algorithmic KV bytes per step / step time (GB/s), where the
+          algorithmic bytes are every attended K and V row read once per KV
+          head: sum_b L_b * H_kv * D * 2 bytes * 2.
+roofline: the split kernel alone, timed with HIP events on the stream it is
+          launched on, against the 8 TB/s HBM peak.
+cpu_baseline: the f64 CPU oracle on a bounded sample of the same batch.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/step + achieved HBM GB/s (% of peak), Llama-8B shape"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_long_batch_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kv_04_amd", "csrc", f)
+                  for f in ("decode_split.hip", "kernels.h")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per split-kernel launch from the committed counter summary,
+    or None if there is none or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_on_stream(fn, iters, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters  # ms
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """Time the oracle on whole sequences of the batch until ~budget_s of CPU
+    work; GB/s of algorithmic KV bytes processed."""
+    import numpy as np
+
+    import oracle
+    from decode_attention_kv_04_amd import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    spec = w.spec
+    elt = workloads.ELT_BYTES[spec.kv_dtype]
+    done_bytes = 0
+    spent = 0.0
+    rows = []
+    for b in range(spec.batch):
+        a = workloads.to_numpy_inputs(w, [b])
+        t = time.perf_counter()
+        oracle.decode_attention(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"],
+                                a["page_size"], a["scale"], a["window"])
+        spent += time.perf_counter() - t
+        t0, t1 = w.attended()[b]
+        done_bytes += (t1 - t0) * spec.num_kv_heads * spec.head_dim * elt * 2
+        rows.append(b)
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {spec.batch} sequences (all {spec.num_q_heads} query heads, "
+                  f"{sum(e - s for s, e in (w.attended()[b] for b in rows))} keys), f64 numpy, "
+                  f"{spent:.1f} s; host has {os.cpu_count()} logical CPUs",
+        "seconds": round(spent, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_batch", help="one of: long_batch, llama8b_3060, wide_gqa, "
+                    "mixed_window, tiny")
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = the planner decides")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_attention_kv_04_amd import binding, workloads
+    if not os.path.exists(binding.library_path()):
+        from decode_attention_kv_04_amd import build as _build
+        _build.build_library()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = workloads.NAMED[args.workload]
+    print(f"[bench] generating {spec.name} on {dev}", file=sys.stderr, flush=True)
+    w = workloads.make_workload(spec, dev)
+    torch.cuda.synchronize()
+    kv_bytes = w.kv_bytes()
+
+    params = binding.params_for(w.q, w.k_pool, w.page_table, window=w.window, scale=w.scale,
+                                out_dtype=spec.out_dtype, num_splits=args.num_splits)
+    t = time.perf_counter()
+    plan = binding.decode_attn_plan(params, w.seq_lens_host, device=0)
+    plan_us = (time.perf_counter() - t) * 1e6
+    out = torch.empty(w.q.shape, dtype=workloads.DTYPES[spec.out_dtype], device=dev)
+    ws = binding.alloc_workspace(plan, dev)
+    stream = torch.cuda.current_stream()
+    lib = binding.load()
+    sptr = stream.cuda_stream
+    ptrs = [w.q.data_ptr(), w.k_pool.data_ptr(), w.v_pool.data_ptr(), w.page_table.data_ptr(),
+            w.seq_lens.data_ptr(), out.data_ptr(), ws.data_ptr() if ws is not None else None,
+            plan.workspace_bytes]
+
+    def step():
+        st = lib.decode_attn_run(plan.handle, *ptrs, sptr)
+        if st != 0:
+            raise binding.DecodeAttnError(st, "decode_attn_run")
+
+    def split_only():
+        st = lib.decode_attn_split(plan.handle, *ptrs, sptr)
+        if st != 0:
+            raise binding.DecodeAttnError(st, "decode_attn_split")
+
+    def combine_only():
+        st = lib.decode_attn_combine(plan.handle, ptrs[4], ptrs[5], ptrs[6], ptrs[7], sptr)
+        if st != 0:
+            raise binding.DecodeAttnError(st, "decode_attn_combine")
+
+    print(f"[bench] plan: pages/split {plan.pages_per_split}, max splits {plan.max_splits}, "
+          f"work-groups {plan.info.split_work_groups}; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps, synchronized on both sides.
+    torch.cuda.synchronize()
+    ms_per_step = time_on_stream(step, args.steps, stream)
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # The dominant kernel alone (split pass), then the combine pass alone.
+    split_ms = time_on_stream(split_only, args.steps, stream)
+    combine_ms = time_on_stream(combine_only, args.steps, stream) if plan.max_splits > 1 else 0.0
+
+    ceiling = None
+    if not args.no_ceiling:
+        probe = ctypes.CDLL(os.path.join(ROOT, "decode_attention_kv_04_amd", "libda_probe.so"))
+        probe.da_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        sink = torch.empty(probe.da_probe_blocks() * 256, dtype=torch.int32, device=dev)
+        rd = lambda: probe.da_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), sptr)
+        for _ in range(2):
+            rd()
+        read_ms = time_on_stream(rd, 10, stream)
+        ceiling = nbytes / (read_ms * 1e-3) / 1e9
+        del buf, sink
+
+    achieved = kv_bytes / (split_ms * 1e-3) / 1e9
+    traffic = recorded_traffic()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+
+    step_gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.kv_dtype,
+        "data": "synthetic (seeded torch generator on the GPU, shapes and distributions of the workload)",
+        "config": {
+            "workload": spec.name,
+            "batch": spec.batch, "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim, "page_size": spec.page_size, "window": spec.window,
+            "context": list(spec.lengths), "attended_keys": int(plan.info.attended_keys),
+            "kv_dtype": spec.kv_dtype, "out_dtype": spec.out_dtype,
+            "pages_per_split": plan.pages_per_split, "max_splits": plan.max_splits,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split pass (da::split_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "avg_launch_us": round(split_ms * 1e3, 2),
+        },
+        "combine_us": round(combine_ms * 1e3, 2),
+        "plan_host_us": round(plan_us, 1),
+        "hbm_read_ceiling_GBps": round(ceiling, 1) if ceiling else None,
+        "split_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+// C ABI of the decode-attention library: argument checks, device query,
+// workspace carving and the two launches. Errors are status codes only
+// (llm-web pull 8, pipeline-creation commit: failures surface to the caller,
+// which chooses the fallback; the library has none).
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <unordered_map>
+
+#include <hip/hip_runtime_api.h>
+
+#include "decode_attn.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+std::mutex g_cu_mutex;
+std::unordered_map<int, int> g_cu_count;
+
+da_status device_cus(int device, int32_t* cus) {
+  {
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    auto it = g_cu_count.find(device);
+    if (it != g_cu_count.end()) {
+      *cus = it->second;
+      return DA_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return DA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  g_cu_count[device] = n;
+  *cus = n;
+  return DA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Checks shared by run and split; fills the kernel arguments.
+da_status prepare(const da_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* page_table, const int32_t* seq_lens, void* out, void* workspace,
+                  size_t workspace_bytes, da::KernelArgs* a) {
+  if (!plan) return DA_ERR_INVALID;
+  const da_params& p = plan->p;
+  if (p.batch > 0) {
+    if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return DA_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16)) return DA_ERR_INVALID;
+    if (!aligned(page_table, 4) || !aligned(seq_lens, 4)) return DA_ERR_INVALID;
+  }
+  if (plan->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan->ws_bytes) return DA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DA_ERR_INVALID;
+  }
+  a->q = q;
+  a->k_pool = k_pool;
+  a->v_pool = v_pool;
+  a->page_table = page_table;
+  a->seq_lens = seq_lens;
+  a->out = out;
+  a->ws_o = static_cast<float*>(workspace);
+  a->ws_ml = plan->ws_bytes > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_ml_offset)
+                                : nullptr;
+  a->batch = p.batch;
+  a->num_q_heads = p.num_q_heads;
+  a->num_kv_heads = p.num_kv_heads;
+  a->group = plan->group;
+  a->page_size = p.page_size;
+  a->max_pages = p.max_pages_per_seq;
+  a->window = p.window;
+  a->pages_per_split = plan->pages_per_split;
+  a->max_splits = plan->max_splits;
+  a->q_dtype = p.q_dtype;
+  a->out_dtype = p.out_dtype;
+  a->scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
+  return DA_OK;
+}
+
+da_status enqueue(const da_plan* plan, const da::KernelArgs& a, bool split, bool combine, void* stream) {
+  if (plan->p.batch == 0) return DA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // start from a clean error state
+  if (split) {
+    if (da::launch_split(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st) != hipSuccess)
+      return DA_ERR_HIP;
+  }
+  if (combine && plan->max_splits > 1) {
+    if (da::launch_combine(a, plan->p.head_dim, st) != hipSuccess) return DA_ERR_HIP;
+  }
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status decode_attn_plan(const da_params* p, const int32_t* host_seq_lens, int device, da_plan_t* plan_out,
+                           size_t* workspace_bytes_out) {
+  if (!p || !plan_out) return DA_ERR_INVALID;
+  int32_t cus = 0;
+  da_status st = device_cus(device, &cus);
+  if (st != DA_OK) return st;
+  return decode_attn_plan_for_cus(p, host_seq_lens, cus, plan_out, workspace_bytes_out);
+}
+
+da_status decode_attn_plan_for_cus(const da_params* p, const int32_t* host_seq_lens, int32_t num_cus,
+                                   da_plan_t* plan_out, size_t* workspace_bytes_out) {
+  if (!plan_out) return DA_ERR_INVALID;
+  da_plan* plan = nullptr;
+  da_status st = da::make_plan(p, host_seq_lens, num_cus, &plan);
+  if (st != DA_OK) return st;
+  *plan_out = plan;
+  if (workspace_bytes_out) *workspace_bytes_out = plan->ws_bytes;
+  return DA_OK;
+}
+
+da_status decode_attn_plan_info(da_plan_t plan, da_plan_info* info) {
+  if (!plan || !info) return DA_ERR_INVALID;
+  info->pages_per_split = plan->pages_per_split;
+  info->max_splits = plan->max_splits;
+  info->num_cus = plan->num_cus;
+  info->split_work_groups = plan->max_splits * plan->p.num_kv_heads * plan->p.batch;
+  info->active_units = plan->active_units;
+  info->attended_keys = plan->attended_keys;
+  info->workspace_bytes = plan->ws_bytes;
+  return DA_OK;
+}
+
+int32_t decode_attn_plan_splits(da_plan_t plan, int32_t b) {
+  if (!plan || b < 0 || b >= plan->p.batch) return 0;
+  return plan->splits[b];
+}
+
+da_status decode_attn_run(da_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* page_table, const int32_t* seq_lens, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  da::KernelArgs a;
+  da_status st = prepare(plan, q, k_pool, v_pool, page_table, seq_lens, out, workspace, workspace_bytes, &a);
+  if (st != DA_OK) return st;
+  return enqueue(plan, a, true, true, stream);
+}
+
+da_status decode_attn_split(da_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, const int32_t* seq_lens, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  da::KernelArgs a;
+  da_status st = prepare(plan, q, k_pool, v_pool, page_table, seq_lens, out, workspace, workspace_bytes, &a);
+  if (st != DA_OK) return st;
+  return enqueue(plan, a, true, false, stream);
+}
+
+da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!plan) return DA_ERR_INVALID;
+  if (plan->p.batch > 0) {
+    if (!seq_lens || !out) return DA_ERR_INVALID;
+    if (!aligned(seq_lens, 4) || !aligned(out, 16)) return DA_ERR_INVALID;
+  }
+  if (plan->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan->ws_bytes) return DA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DA_ERR_INVALID;
+  }
+  if (plan->max_splits <= 1) return DA_OK;
+  da::KernelArgs a{};
+  const da_params& p = plan->p;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_ml_offset);
+  a.batch = p.batch;
+  a.num_q_heads = p.num_q_heads;
+  a.num_kv_heads = p.num_kv_heads;
+  a.group = plan->group;
+  a.page_size = p.page_size;
+  a.max_pages = p.max_pages_per_seq;
+  a.window = p.window;
+  a.pages_per_split = plan->pages_per_split;
+  a.max_splits = plan->max_splits;
+  a.q_dtype = p.q_dtype;
+  a.out_dtype = p.out_dtype;
+  return enqueue(plan, a, false, true, stream);
+}
+
+void decode_attn_plan_destroy(da_plan_t plan) { delete plan; }
+
+const char* decode_attn_status_str(da_status s) {
+  switch (s) {
+    case DA_OK: return "DA_OK: success";
+    case DA_ERR_INVALID: return "DA_ERR_INVALID: invalid parameter, pointer, alignment or length";
+    case DA_ERR_UNSUPPORTED: return "DA_ERR_UNSUPPORTED: no kernel is built for these parameters";
+    case DA_ERR_WORKSPACE: return "DA_ERR_WORKSPACE: workspace missing or too small";
+    case DA_ERR_HIP: return "DA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown da_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace da {
+
+// Arguments of both passes (plain pointers and sizes; passed by value).
+struct KernelArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* ws_o;   // [B][H_q][S_max][D]
+  float* ws_ml;  // [B][H_q][S_max][2]  (m in log2 units, l)
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;          // G (<= the compiled group width)
+  int32_t page_size;
+  int32_t max_pages;      // page-table row stride
+  int32_t window;
+  int32_t pages_per_split;
+  int32_t max_splits;
+  int32_t q_dtype;        // da_dtype
+  int32_t out_dtype;      // da_dtype
+  float scale_log2;       // scale * log2(e): scores are kept in base-2 units
+};
+
+// Enqueue the split pass on `stream`. Returns hipSuccess or the launch error;
+// hipErrorInvalidValue if no kernel is compiled for (head_dim, kv_dtype,
+// group_tile).
+hipError_t launch_split(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream);
+
+// Enqueue the combine pass on `stream`.
+hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace da

@@ -1,0 +1,167 @@
+// Host planner: validation, split choice and workspace size.
+//
+// The split choice follows the two passages that pick a path on the host: the
+// sharded nest is chosen from the page count and only above 256 tokens (TVM
+// pull 20426, commit message and PR description), and the split threshold is
+// a knob with a 256-token default (mlx-runner pull 3, GQA-shared split
+// attention commit). Here the host picks one split length c (in pages) for the
+// whole batch from the attended page count and the compute-unit count, so
+// that the split pass launches a few work-groups per compute unit; contexts
+// of at most one split run in a single pass and write their output directly.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <new>
+
+namespace da {
+
+namespace {
+
+// Splits per KV head are sized so the split pass has about this many
+// work-groups per compute unit in total.
+constexpr int64_t kTargetGroupsPerCu = 4;
+// A split never holds fewer attended tokens than this (the pages' 256-token
+// switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
+constexpr int64_t kDefaultMinSplitTokens = 256;
+
+int64_t min_split_tokens() {
+  const char* s = std::getenv("DECODE_ATTN_SPLIT_MIN");
+  if (s && *s) {
+    char* end = nullptr;
+    long v = std::strtol(s, &end, 10);
+    if (end && *end == '\0' && v >= 1) return v;
+  }
+  return kDefaultMinSplitTokens;
+}
+
+bool log_enabled() {
+  const char* s = std::getenv("DECODE_ATTN_LOG");
+  return s && s[0] == '1';
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_dtype(da_dtype t) { return t == DA_F32 || t == DA_F16 || t == DA_BF16; }
+
+}  // namespace
+
+SeqRange seq_range(int64_t L, int64_t window, int64_t P) {
+  SeqRange r;
+  r.t1 = L;
+  r.t0 = (window > 0 && L > window) ? L - window : 0;
+  if (L == 0) {
+    r.pf = r.pe = 0;
+  } else {
+    r.pf = r.t0 / P;
+    r.pe = ceil_div(L, P);
+  }
+  return r;
+}
+
+int32_t group_tile_for(int32_t G) {
+  if (G == 1) return 1;
+  if (G == 2) return 2;
+  if (G >= 3 && G <= 4) return 4;
+  if (G >= 5 && G <= 8) return 8;
+  return 0;
+}
+
+da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da_plan** out) {
+  if (!p || !out) return DA_ERR_INVALID;
+  if (p->batch < 0 || p->num_q_heads < 1 || p->num_kv_heads < 1) return DA_ERR_INVALID;
+  if (p->num_q_heads % p->num_kv_heads != 0) return DA_ERR_INVALID;
+  if (p->head_dim < 1 || p->page_size < 1) return DA_ERR_INVALID;
+  if (p->window < 0 || p->num_splits < 0) return DA_ERR_INVALID;
+  if (!std::isfinite(p->scale)) return DA_ERR_INVALID;
+  if (!valid_dtype(p->q_dtype) || !valid_dtype(p->kv_dtype) || !valid_dtype(p->out_dtype))
+    return DA_ERR_INVALID;
+  if (num_cus < 1) return DA_ERR_INVALID;
+  if (p->batch > 0 && (!lens || p->max_pages_per_seq < 1)) return DA_ERR_INVALID;
+
+  const int32_t G = p->num_q_heads / p->num_kv_heads;
+  const int32_t gt = group_tile_for(G);
+  if (gt == 0) return DA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return DA_ERR_UNSUPPORTED;
+  if (p->page_size % 8 != 0 || p->page_size > 1024) return DA_ERR_UNSUPPORTED;
+  if (p->batch > 65535 || p->num_kv_heads > 65535) return DA_ERR_UNSUPPORTED;
+
+  const int64_t P = p->page_size;
+  const int64_t cap = static_cast<int64_t>(p->max_pages_per_seq) * P;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    if (lens[b] < 0 || static_cast<int64_t>(lens[b]) > cap) return DA_ERR_INVALID;
+  }
+
+  da_plan* plan = new (std::nothrow) da_plan();
+  if (!plan) return DA_ERR_INVALID;
+  plan->p = *p;
+  plan->group = G;
+  plan->group_tile = gt;
+  plan->num_cus = num_cus;
+
+  // Attended pages per sequence.
+  std::vector<int64_t> npages(p->batch);
+  int64_t max_np = 0, total_np = 0;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    SeqRange r = seq_range(lens[b], p->window, P);
+    npages[b] = r.pe - r.pf;
+    max_np = std::max(max_np, npages[b]);
+    total_np += npages[b];
+    plan->attended_keys += r.t1 - r.t0;
+  }
+
+  int64_t c;
+  if (max_np == 0) {
+    c = 1;
+  } else if (p->num_splits > 0) {
+    c = ceil_div(max_np, p->num_splits);
+  } else {
+    const int64_t work = total_np * p->num_kv_heads;  // page-heads to stream
+    const int64_t target = static_cast<int64_t>(num_cus) * kTargetGroupsPerCu;
+    c = ceil_div(work, target);
+    c = std::max(c, ceil_div(min_split_tokens(), P));
+    c = std::min(c, max_np);
+  }
+  c = std::max<int64_t>(c, 1);
+  if (c > INT32_MAX) c = INT32_MAX;
+  plan->pages_per_split = static_cast<int32_t>(c);
+
+  plan->splits.resize(p->batch);
+  int64_t smax = 1;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    int64_t s = std::max<int64_t>(1, ceil_div(npages[b], c));
+    plan->splits[b] = static_cast<int32_t>(s);
+    smax = std::max(smax, s);
+    plan->active_units += s * p->num_kv_heads;
+  }
+  if (smax > 65535 * 16) {  // grid x limit with headroom; unreachable for sane sizes
+    delete plan;
+    return DA_ERR_UNSUPPORTED;
+  }
+  plan->max_splits = static_cast<int32_t>(smax);
+
+  if (smax > 1) {
+    const size_t rows = static_cast<size_t>(p->batch) * p->num_q_heads * smax;
+    plan->ws_o_bytes = round_up(rows * p->head_dim * sizeof(float), 256);
+    plan->ws_ml_offset = plan->ws_o_bytes;
+    plan->ws_bytes = plan->ws_ml_offset + round_up(rows * 2 * sizeof(float), 256);
+  }
+
+  if (log_enabled()) {
+    std::fprintf(stderr,
+                 "decode_attn plan: B=%d Hq=%d Hkv=%d D=%d P=%d W=%d cus=%d pages/split=%lld "
+                 "max_splits=%lld units=%lld keys=%lld ws=%zu\n",
+                 p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, p->page_size, p->window,
+                 num_cus, static_cast<long long>(c), static_cast<long long>(smax),
+                 static_cast<long long>(plan->active_units), static_cast<long long>(plan->attended_keys),
+                 plan->ws_bytes);
+  }
+  *out = plan;
+  return DA_OK;
+}
+
+}  // namespace da

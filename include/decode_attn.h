@@ -1,0 +1,176 @@
+/*
+ * decode_attn.h - paged single-query decode attention on MI355X (gfx950).
+ *
+ * One decode step: every sequence b has one query token with H_q heads and a
+ * KV cache of L_b keys stored in fixed-size pages. For every query head h the
+ * library computes
+ *
+ *     out[b,h,:] = softmax_t(scale * <q[b,h,:], K[b,j,t,:]>) V[b,j,t,:]
+ *
+ * over the attended keys t, where j = floor(h / G) is the KV head that the G =
+ * H_q / H_kv consecutive query heads of a GQA group share, and the attended
+ * keys are the last `window` keys (all L_b keys when window = 0 or window >=
+ * L_b). A sequence with no attended key gets a zero row.
+ *
+ * Passages this follows:
+ *   - TVM pull 20426 "webgpu-decode-attention", commit message of the sharded
+ *     nest: paged decode attention whose context is cut into shards, each
+ *     producing an online-softmax state that a merge step combines; the host
+ *     picks the path from the page count. Its PR description: a sequence-
+ *     sharded kernel selected above 256 tokens; sliding windows.
+ *   - mlx-runner pull 3, commit message "GQA-shared split attention" and PR
+ *     description "Changes": a split kernel in which each group covers all
+ *     query heads of its GQA group, so each K/V row is read once per group,
+ *     writing per-split partials that a combine kernel merges; the split
+ *     threshold is a knob (default 256 tokens).
+ *   - llm-web pull 8, commits on build-time constants and on pipeline
+ *     creation errors: head_dim / dtype / window fixed per pipeline before
+ *     launch; errors surface at creation and the caller picks a fallback.
+ *
+ * Conventions
+ *   - Pointers are device pointers unless their name starts with host_.
+ *   - Every device buffer is owned by the caller. The library never allocates
+ *     or frees device memory. A plan is a small host object owned by the
+ *     caller and released with decode_attn_plan_destroy.
+ *   - Tensors are dense and row-major:
+ *       q           [B][H_q][D]                      q_dtype
+ *       k_pool      [num_pages][H_kv][P][D]          kv_dtype
+ *       v_pool      [num_pages][H_kv][P][D]          kv_dtype
+ *       page_table  [B][max_pages_per_seq]           int32, logical -> physical page
+ *       seq_lens    [B]                              int32, keys in the cache
+ *       out         [B][H_q][D]                      out_dtype
+ *     Key t of sequence b, KV head j, is row t % P of block
+ *     (page_table[b][t / P], j) of the pools. Only the pages holding attended
+ *     keys are read; rows outside the attended range (the tail of the last
+ *     page, keys before the window) may hold anything, NaN included.
+ *   - q, k_pool, v_pool and out must be 16-byte aligned; page_table and
+ *     seq_lens 4-byte aligned; workspace 256-byte aligned.
+ *   - Status codes are the only error channel; nothing is printed unless the
+ *     environment sets DECODE_ATTN_LOG=1 (plan decisions go to stderr).
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DA_OK = 0,
+  DA_ERR_INVALID = 1,     /* a parameter, pointer, alignment or length is invalid       */
+  DA_ERR_UNSUPPORTED = 2, /* valid, but no kernel is built for it (head_dim, group...)  */
+  DA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the plan requires        */
+  DA_ERR_HIP = 4          /* the HIP runtime reported an error (device query or launch) */
+} da_status;
+
+typedef enum { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
+
+typedef struct {
+  int32_t batch;             /* B >= 0                                              */
+  int32_t num_q_heads;       /* H_q >= 1                                            */
+  int32_t num_kv_heads;      /* H_kv >= 1, divides H_q; G = H_q / H_kv in 1..8       */
+  int32_t head_dim;          /* D in {64, 128, 256}                                 */
+  int32_t page_size;         /* P: a multiple of 8, 8..1024                         */
+  int32_t max_pages_per_seq; /* row stride of page_table; >= ceil(L_b / P)          */
+  int32_t window;            /* 0 = none; else attend the last `window` keys        */
+  float scale;               /* score scale, e.g. 1/sqrt(D); finite                 */
+  da_dtype q_dtype, kv_dtype, out_dtype;
+  int32_t num_splits;        /* 0 = the planner decides; > 0 caps the splits of the
+                                longest sequence at this count (1 = no split)       */
+} da_params;
+
+typedef struct da_plan* da_plan_t;
+
+/* What a plan decided (for logging, tests and benchmarks). */
+typedef struct {
+  int32_t pages_per_split;   /* c: pages of attended context per split              */
+  int32_t max_splits;        /* S_max over the batch (1 = no combine pass)          */
+  int32_t num_cus;           /* compute units the plan was made for                 */
+  int32_t split_work_groups; /* work-groups the split kernel launches               */
+  int64_t active_units;      /* sum over b of splits(b) * H_kv                      */
+  int64_t attended_keys;     /* sum over b of attended keys                         */
+  size_t workspace_bytes;    /* bytes of device workspace `run` needs (0 if none)   */
+} da_plan_info;
+
+/*
+ * decode_attn_plan: validate `p` and the B host-side lengths, pick how the
+ * attended context is cut into splits (pages per split, from the context
+ * lengths and the device's compute-unit count), and size the workspace. Host
+ * only: no device work, no allocation on the device. `device` is a HIP device
+ * ordinal; its compute-unit count is read once and cached.
+ *   host_seq_lens  [B] int32 host array (may be NULL when B = 0); values in
+ *                  0 .. max_pages_per_seq * P.
+ *   plan_out       receives a new plan on DA_OK (unchanged otherwise).
+ *   workspace_bytes_out (may be NULL) receives the workspace size run needs.
+ * Returns DA_ERR_INVALID / DA_ERR_UNSUPPORTED for bad or unbuilt parameters,
+ * DA_ERR_HIP if the device cannot be queried.
+ */
+da_status decode_attn_plan(const da_params* p, const int32_t* host_seq_lens, int device,
+                           da_plan_t* plan_out, size_t* workspace_bytes_out);
+
+/*
+ * decode_attn_plan_for_cus: as decode_attn_plan, for an explicit compute-unit
+ * count instead of a device query (num_cus >= 1). Makes no HIP call, so it
+ * also works on a host without a GPU.
+ */
+da_status decode_attn_plan_for_cus(const da_params* p, const int32_t* host_seq_lens, int32_t num_cus,
+                                   da_plan_t* plan_out, size_t* workspace_bytes_out);
+
+/* decode_attn_plan_info: copy a plan's decisions into *info. */
+da_status decode_attn_plan_info(da_plan_t plan, da_plan_info* info);
+
+/* decode_attn_plan_splits: number of splits of sequence b (1 .. max_splits). */
+int32_t decode_attn_plan_splits(da_plan_t plan, int32_t b);
+
+/*
+ * decode_attn_run: enqueue one decode-attention step on `stream` (a
+ * hipStream_t; NULL = the null stream): the split pass, then, if the plan has
+ * more than one split, the combine pass. Returns after enqueueing; no host
+ * synchronisation and no allocation, so it can be captured in a HIP graph.
+ *   q, k_pool, v_pool, page_table, seq_lens   read-only inputs (layouts above).
+ *   seq_lens   must hold the same lengths the plan was made from.
+ *   out        [B][H_q][D] out_dtype, fully written.
+ *   workspace  >= the plan's workspace_bytes (may be NULL if that is 0);
+ *              scratch for per-split states, contents undefined afterwards.
+ * Contents of page_table and seq_lens are not checked on the device: entries
+ * that point outside the pools are undefined behaviour. A device fault shows
+ * up at the caller's next synchronisation.
+ * Calls that share a workspace must be ordered on one stream.
+ */
+da_status decode_attn_run(da_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* page_table, const int32_t* seq_lens, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_split: the first pass of decode_attn_run alone. Every split of
+ * every sequence writes its online-softmax state (running max m, sum l,
+ * unnormalised O) to the workspace; sequences with a single split write their
+ * final output rows directly. Same arguments and checks as decode_attn_run.
+ */
+da_status decode_attn_split(da_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* page_table, const int32_t* seq_lens, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_combine: the second pass alone. Merges the split states that a
+ * preceding decode_attn_split (same plan, same seq_lens, same workspace) left
+ * in the workspace into the output rows of sequences with more than one split.
+ * Enqueues nothing when the plan has a single split.
+ */
+da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* decode_attn_plan_destroy: free a plan (NULL is ignored). */
+void decode_attn_plan_destroy(da_plan_t plan);
+
+/* decode_attn_status_str: static text for a status code. */
+const char* decode_attn_status_str(da_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

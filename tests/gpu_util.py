@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU tests: run the library on a workload and compare
+with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from decode_attention_kv_04_amd import binding, workloads
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+KV_TOL = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None, page_table=None,
+            window=None, seq_lens=None, seq_lens_host=None, two_phase=False):
+    """One decode_attn_run (or split + combine) on the workload's tensors;
+    returns (out tensor, plan). The output starts as NaN so unwritten rows show."""
+    q = w.q if q is None else q
+    k_pool = w.k_pool if k_pool is None else k_pool
+    v_pool = w.v_pool if v_pool is None else v_pool
+    page_table = w.page_table if page_table is None else page_table
+    seq_lens = w.seq_lens if seq_lens is None else seq_lens
+    seq_lens_host = w.seq_lens_host if seq_lens_host is None else seq_lens_host
+    window = w.window if window is None else window
+    out_dtype = out_dtype or w.spec.out_dtype
+    params = binding.params_for(q, k_pool, page_table, window=window, scale=w.scale, out_dtype=out_dtype,
+                                num_splits=num_splits)
+    plan = binding.decode_attn_plan(params, seq_lens_host, device=q.device.index)
+    out = torch.full(q.shape, float("nan"), dtype=TORCH_DT[out_dtype], device=q.device)
+    ws = binding.alloc_workspace(plan, q.device)
+    if ws is not None:
+        ws.fill_(0xFF)  # NaN bit patterns: stale state would show
+    if two_phase:
+        binding.decode_attn_split(plan, q, k_pool, v_pool, page_table, seq_lens, out, ws)
+        binding.decode_attn_combine(plan, seq_lens, out, ws)
+    else:
+        binding.decode_attn_run(plan, q, k_pool, v_pool, page_table, seq_lens, out, ws)
+    torch.cuda.synchronize()
+    return out, plan
+
+
+def host64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def oracle_for(w, rows=None):
+    a = workloads.to_numpy_inputs(w, rows)
+    return oracle.decode_attention(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"],
+                                   a["page_size"], a["scale"], a["window"])
+
+
+def check(got, ref, kv_dtype, out_dtype, label=""):
+    """Relative L2 over the whole output and per sequence, within the bound
+    for the KV dtype (1e-5 fp32, 1e-3 fp16/bf16, fp32 accumulation); a bf16
+    output is compared with the bf16-rounded oracle."""
+    got = host64(got) if isinstance(got, torch.Tensor) else got
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    if out_dtype == "bf16":
+        ref = oracle.round_to(ref, "bf16")
+    tol = KV_TOL[kv_dtype]
+    if out_dtype == "f16" and kv_dtype == "f32":
+        tol = 1e-3  # fp16 output rounding alone is ~2e-4
+    err = oracle.relative_l2(got, ref)
+    rows = oracle.relative_l2_per_row(got, ref)
+    worst = max(rows) if rows else 0.0
+    assert err <= tol, f"{label}: relative L2 {err:.3e} > {tol:g}"
+    assert worst <= tol, f"{label}: worst per-sequence relative L2 {worst:.3e} > {tol:g}"
+    return err, worst

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 oracle on the
+same seeded inputs, within relative L2 1e-5 (fp32 KV) / 1e-3 (fp16, bf16 KV),
+over the whole output and per sequence."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_04_amd import workloads as wl
+
+from gpu_util import check, host64, oracle_for, run_lib, say
+
+pytestmark = pytest.mark.gpu
+
+
+def make(spec, gpu, **kw):
+    say(f"[workload] {spec.name} {kw or ''}")
+    return wl.make_workload(spec.replace(**kw) if kw else spec, gpu)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b_3060", "wide_gqa"])
+def test_small_named_workloads_full_output(gpu, name):
+    spec = wl.NAMED[name]
+    w = make(spec, gpu)
+    out, plan = run_lib(w)
+    err, worst = check(out, oracle_for(w), spec.kv_dtype, spec.out_dtype, name)
+    say(f"  {name}: rel L2 {err:.2e} worst row {worst:.2e} splits {plan.max_splits}")
+
+
+def sample_rows(w, k):
+    L = w.seq_lens_host.tolist()
+    order = sorted(range(len(L)), key=lambda b: L[b])
+    picks = [order[0], order[-1], order[len(order) // 2]]
+    g = torch.Generator().manual_seed(1234)
+    extra = torch.randperm(len(L), generator=g).tolist()
+    for b in extra:
+        if len(picks) >= k:
+            break
+        if b not in picks:
+            picks.append(b)
+    return picks[:k]
+
+
+def test_long_batch_full_size_sampled(gpu):
+    """Batch 32, 32/8 heads, D 128, fp16, 16k-32k tokens, spiky keys: the
+    whole batch on the GPU in the planner's launch configuration (the one the
+    benchmark times), checked on sampled sequences."""
+    w = make(wl.LONG_BATCH, gpu)
+    out, plan = run_lib(w)
+    rows = sample_rows(w, 4)
+    say(f"  plan: pages/split {plan.pages_per_split} max splits {plan.max_splits}; rows {rows}")
+    ref = oracle_for(w, rows)
+    got = out[torch.tensor(rows, device=gpu)]
+    err, worst = check(got, ref, "f16", "f16", "long_batch")
+    assert torch.isfinite(out.float()).all()
+    say(f"  long_batch: rel L2 {err:.2e} worst row {worst:.2e}")
+
+
+def test_mixed_window_full_size_sampled(gpu):
+    """Batch 64, window 4096, half short (1-256) and half long (32k-64k), bf16,
+    32-token pages; pre-window pages hold NaN."""
+    w = make(wl.MIXED_WINDOW, gpu)
+    out, plan = run_lib(w)
+    L = w.seq_lens_host.tolist()
+    short = [b for b in range(len(L)) if L[b] <= 256][:3]
+    long = [b for b in range(len(L)) if L[b] > 256][:3]
+    rows = short + long
+    say(f"  plan: pages/split {plan.pages_per_split} max splits {plan.max_splits}; rows {rows}")
+    ref = oracle_for(w, rows)
+    got = out[torch.tensor(rows, device=gpu)]
+    err, worst = check(got, ref, "bf16", "f32", "mixed_window")
+    assert torch.isfinite(out.float()).all()
+    say(f"  mixed_window: rel L2 {err:.2e} worst row {worst:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Sweeps at sizes the oracle finishes in seconds
+# ---------------------------------------------------------------------------
+
+def test_every_length_up_to_three_pages_and_3060(gpu):
+    P = 16
+    lens = list(range(0, 3 * P + 2)) + [3060]
+    spec = wl.LLAMA8B_3060.replace(batch=len(lens), lengths=("list", tuple(lens)))
+    w = make(spec, gpu)
+    for ns in (0, 1, 2, 7):
+        out, _ = run_lib(w, num_splits=ns)
+        check(out, oracle_for(w), "f16", "f16", f"lengths splits={ns}")
+
+
+@pytest.mark.parametrize("W", [1, 15, 16, 17, 199, 200, 201, 1000])
+def test_window_sweep(gpu, W):
+    lens = (200, 37, 1, 16, 17, 513)
+    spec = wl.MIXED_WINDOW.replace(batch=len(lens), lengths=("list", lens), window=W, page_size=16)
+    w = make(spec, gpu)
+    for ns in (0, 1, 3):
+        out, _ = run_lib(w, num_splits=ns)
+        check(out, oracle_for(w), "bf16", "f32", f"window {W} splits={ns}")
+
+
+GRID = [(G, D, kv) for G in (1, 2, 3, 4, 5, 6, 7, 8) for D in (64, 128, 256) for kv in ("f32", "f16", "bf16")]
+
+
+@pytest.mark.parametrize("G,D,kv", GRID, ids=[f"G{g}-D{d}-{k}" for g, d, k in GRID])
+def test_group_dim_dtype_grid(gpu, G, D, kv):
+    Hkv = 2
+    spec = wl.WorkloadSpec(f"grid_G{G}_D{D}_{kv}", 3, G * Hkv, Hkv, D, kv, kv, "f32", 16,
+                           ("list", (1, 300, 777)), seed=G * 1000 + D + len(kv), spike_frac=0.01)
+    w = make(spec, gpu)
+    for ns in (0, 3):
+        out, _ = run_lib(w, num_splits=ns)
+        check(out, oracle_for(w), kv, "f32", f"G{G} D{D} {kv} splits={ns}")
+
+
+@pytest.mark.parametrize("P", [8, 16, 24, 32, 64])
+def test_page_sizes(gpu, P):
+    lens = (1, P - 1, P, P + 1, 5 * P + 3, 700)
+    spec = wl.WIDE_GQA.replace(batch=len(lens), lengths=("list", lens), page_size=P, head_dim=128,
+                               seed=40 + P)
+    w = make(spec, gpu)
+    for ns in (0, 1, 4):
+        out, _ = run_lib(w, num_splits=ns)
+        check(out, oracle_for(w), "bf16", "f32", f"P={P} splits={ns}")
+
+
+@pytest.mark.parametrize("ns", [1, 2, 3, 7, 10_000])
+def test_forced_split_counts(gpu, ns):
+    spec = wl.LLAMA8B_3060.replace(batch=3, lengths=("list", (3060, 1000, 17)))
+    w = make(spec, gpu)
+    out, plan = run_lib(w, num_splits=ns)
+    assert plan.max_splits == min(ns, math.ceil(3060 / 16))
+    check(out, oracle_for(w), "f16", "f16", f"splits={ns}")
+
+
+@pytest.mark.parametrize("q_dt,kv_dt,out_dt", [
+    ("f32", "f16", "f32"), ("f32", "bf16", "f32"), ("f16", "f32", "f32"), ("bf16", "bf16", "bf16"),
+    ("f16", "f16", "f32"), ("f16", "f16", "bf16"), ("f32", "f32", "f16"),
+])
+def test_mixed_dtypes(gpu, q_dt, kv_dt, out_dt):
+    spec = wl.WorkloadSpec(f"dt_{q_dt}_{kv_dt}_{out_dt}", 2, 8, 2, 128, q_dt, kv_dt, out_dt, 16,
+                           ("list", (900, 33)), seed=77)
+    w = make(spec, gpu)
+    for ns in (0, 1):
+        out, _ = run_lib(w, num_splits=ns)
+        check(out, oracle_for(w), kv_dt, out_dt, f"{q_dt}/{kv_dt}/{out_dt}")
+
+
+def test_empty_and_ragged_batch(gpu):
+    lens = (0, 1, 0, 4096, 2, 0)
+    spec = wl.LLAMA8B_3060.replace(batch=len(lens), lengths=("list", lens))
+    w = make(spec, gpu)
+    for ns in (0, 1, 5):
+        out, _ = run_lib(w, num_splits=ns)
+        got = host64(out)
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.array_equal(got[b], np.zeros_like(got[b]))
+        check(out, oracle_for(w), "f16", "f16", f"ragged splits={ns}")
+
+
+def test_empty_batch_is_a_noop(gpu):
+    spec = wl.LLAMA8B_3060.replace(batch=0, lengths=("list", ()))
+    from decode_attention_kv_04_amd import binding
+    p = binding.make_params(0, 32, 8, 128, 16, 1)
+    plan = binding.decode_attn_plan(p, [])
+    q = torch.empty((0, 32, 128), dtype=torch.float16, device=gpu)
+    kp = torch.empty((1, 8, 16, 128), dtype=torch.float16, device=gpu)
+    pt = torch.empty((0, 1), dtype=torch.int32, device=gpu)
+    sl = torch.empty((0,), dtype=torch.int32, device=gpu)
+    binding.decode_attn_run(plan, q, kp, kp, pt, sl, q.clone(), None)
+    torch.cuda.synchronize()
+
+
+def test_two_phase_api_equals_run(gpu):
+    w = make(wl.LLAMA8B_3060, gpu)
+    a, _ = run_lib(w, num_splits=6)
+    b, _ = run_lib(w, num_splits=6, two_phase=True)
+    assert torch.equal(a, b)
+
+
+def test_long_context_single_sequence_max_table(gpu):
+    """One sequence filling a 4096-page table (65536 tokens, P 16) in fp32."""
+    spec = wl.WorkloadSpec("long_f32", 1, 8, 2, 64, "f32", "f32", "f32", 16, ("fixed", 65536), seed=9)
+    w = make(spec, gpu)
+    out, plan = run_lib(w)
+    check(out, oracle_for(w), "f32", "f32", "65536 fp32")
