@@ -66,6 +66,56 @@ def time_on_stream(fn, iters, stream):
     return start.elapsed_time(end) / iters  # ms
 
 
+CALIBRATION_BYTES = 1 << 30
+
+
+def _probe():
+    lib = ctypes.CDLL(os.path.join(ROOT, "decode_attention_kv_04_amd", "libda_probe.so"))
+    vp = ctypes.c_void_p
+    lib.da_probe_read_cfg.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.da_probe_read_blocks.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.da_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    return lib
+
+
+def measure_ceilings(dev, sptr, stream):
+    """HBM read ceilings measured on this GPU over a 4 GiB buffer:
+    'stream' = each work-group reads one contiguous chunk (nontemporal
+    16-byte loads); 'gather4k' = 4 KiB blocks in a random order, the access
+    pattern of a shuffled page pool."""
+    import torch
+    probe = _probe()
+    nbytes = 4 << 30
+    nblk = nbytes // 4096
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    perm = torch.randperm(nblk, generator=g, device=dev).to(torch.int32)
+    sink = torch.empty(nblk * 256, dtype=torch.int32, device=dev)
+    runs = {
+        "stream": lambda: probe.da_probe_read_cfg(buf.data_ptr(), nbytes, sink.data_ptr(), 1024, 1, sptr),
+        "gather4k": lambda: probe.da_probe_read_blocks(buf.data_ptr(), perm.data_ptr(), nblk, 128, 1,
+                                                       sink.data_ptr(), sptr),
+    }
+    out = {}
+    for name, fn in runs.items():
+        for _ in range(2):
+            fn()
+        ms = time_on_stream(fn, 5, stream)
+        out[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, sink, perm
+    return out
+
+
+def calibration_copy(dev, sptr):
+    import torch
+    probe = _probe()
+    src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    probe.da_probe_copy(dst.data_ptr(), src.data_ptr(), CALIBRATION_BYTES, sptr)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(w, budget_s=12.0):
     """Time the oracle on whole sequences of the batch until ~budget_s of CPU
     work; GB/s of algorithmic KV bytes processed."""
@@ -116,6 +166,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the planner decides")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after timing, copy a buffer of known size once (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -182,20 +234,11 @@ def main():
     split_ms = time_on_stream(split_only, args.steps, stream)
     combine_ms = time_on_stream(combine_only, args.steps, stream) if plan.max_splits > 1 else 0.0
 
-    ceiling = None
+    ceilings = {}
     if not args.no_ceiling:
-        probe = ctypes.CDLL(os.path.join(ROOT, "decode_attention_kv_04_amd", "libda_probe.so"))
-        probe.da_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
-                                        ctypes.c_void_p, ctypes.c_void_p]
-        nbytes = 4 << 30
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        sink = torch.empty(probe.da_probe_blocks() * 256, dtype=torch.int32, device=dev)
-        rd = lambda: probe.da_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), sptr)
-        for _ in range(2):
-            rd()
-        read_ms = time_on_stream(rd, 10, stream)
-        ceiling = nbytes / (read_ms * 1e-3) / 1e9
-        del buf, sink
+        ceilings = measure_ceilings(dev, sptr, stream)
+    if args.calibrate:
+        calibration_copy(dev, sptr)
 
     achieved = kv_bytes / (split_ms * 1e-3) / 1e9
     traffic = recorded_traffic()
@@ -239,8 +282,11 @@ def main():
         },
         "combine_us": round(combine_ms * 1e3, 2),
         "plan_host_us": round(plan_us, 1),
-        "hbm_read_ceiling_GBps": round(ceiling, 1) if ceiling else None,
-        "split_frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
+        "hbm_read_ceiling_GBps": ceilings.get("stream"),
+        "gather4k_read_ceiling_GBps": ceilings.get("gather4k"),
+        "split_frac_of_gather4k_ceiling": (round(achieved / ceilings["gather4k"], 4)
+                                           if ceilings.get("gather4k") else None),
+        "calibration_copy_bytes": CALIBRATION_BYTES if args.calibrate else None,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_hash(),
     }

@@ -17,13 +17,22 @@
 // a load instruction covers RPI = 64 / LPR consecutive rows, each lane group
 // reading one contiguous LPR*16-byte segment of its row, so every wave-wide
 // 1 KiB load touches whole 64-128 byte lines. q.k is a per-lane partial dot
-// product finished by a sum over the LPR lanes of the row with DPP (no LDS,
-// no barrier), which leaves the full score in every lane of the row (the
-// 8-lanes-per-key layout of llm-web pull 8 is the same idea for WebGPU).
-// Each lane then owns the rows of its row slot as a private online-softmax
-// shard: its m, l and O slice live in VGPRs and the slots are merged once, at
-// the end, first across the wave with lane shuffles and then across the four
-// waves through LDS. No barrier is executed inside the key loop.
+// product (v_dot2 on packed 16-bit pairs when q and K share a 16-bit type,
+// fp32 FMAs otherwise) finished by a sum over the LPR lanes of the row with
+// DPP (no LDS, no barrier), which leaves the full score in every lane of the
+// row (llm-web pull 8, decode-attention commit: one key's dot product shared
+// by adjacent lanes, reduced without barrier trees). Each lane then owns the
+// rows of its row slot as a private online-softmax shard: its m, l and O
+// slice live in VGPRs, and the slots are merged once, at the end, across the
+// wave with lane shuffles and across the four waves through LDS. No barrier
+// is executed inside the key loop.
+//
+// Streaming. Each wave walks its tiles (TR rows) with PD tiles of K and V
+// loads in flight in registers while it computes the oldest one. The page of
+// every load group is tracked with a cursor advanced by additions (no integer
+// division in the loop), and its physical page id is fetched with a scalar
+// load one tile before the vector loads that need it. Only pages holding
+// attended keys are read.
 //
 // Masking uses selects, never multiplication by zero, because rows outside
 // the attended range may hold NaN: a score outside [t_lo, t_hi) becomes -inf
@@ -35,11 +44,19 @@
 #include "decode_attn.h"
 #include "kernels.h"
 
+#ifndef DA_PREFETCH_TILES
+#define DA_PREFETCH_TILES 2
+#endif
+#ifndef DA_NT_LOADS
+#define DA_NT_LOADS 1
+#endif
+
 namespace da {
 namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kPD = DA_PREFETCH_TILES;  // tiles in flight per wave while one is computed
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -88,6 +105,19 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo*b.lo + a.hi*b.hi for packed 16-bit pairs, fp32 accumulation.
+template <int KVT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  if constexpr (KVT == DA_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a), __builtin_bit_cast(bf162_t, b), acc,
+                                           false);
+}
+
 // 16 bytes of KV elements -> E floats.
 template <int KVT>
 __device__ __forceinline__ void unpack(const uint4& u, float* f) {
@@ -110,11 +140,37 @@ __device__ __forceinline__ void unpack(const uint4& u, float* f) {
   }
 }
 
-__device__ __forceinline__ float load_elem(const void* base, int64_t idx, int dtype) {
-  if (dtype == DA_F32) return static_cast<const float*>(base)[idx];
-  const uint16_t bits = static_cast<const uint16_t*>(base)[idx];
-  if (dtype == DA_F16) return h2f(bits);
-  return __uint_as_float(static_cast<uint32_t>(bits) << 16);
+// N contiguous elements of dtype QT at p -> floats (vector loads).
+template <int QT, int N>
+__device__ __forceinline__ void load_row_f32(const void* p, float* f) {
+  if constexpr (QT == DA_F32) {
+    static_assert(N % 4 == 0, "");
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const float4 x = static_cast<const float4*>(p)[i];
+      f[4 * i] = x.x;
+      f[4 * i + 1] = x.y;
+      f[4 * i + 2] = x.z;
+      f[4 * i + 3] = x.w;
+    }
+  } else {
+    static_assert(N % 4 == 0, "");
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint2 x = static_cast<const uint2*>(p)[i];
+      const uint32_t w[2] = {x.x, x.y};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if constexpr (QT == DA_F16) {
+          f[4 * i + 2 * k] = h2f(w[k] & 0xffffu);
+          f[4 * i + 2 * k + 1] = h2f(w[k] >> 16);
+        } else {
+          f[4 * i + 2 * k] = __uint_as_float(w[k] << 16);
+          f[4 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+      }
+    }
+  }
 }
 
 __device__ __forceinline__ void store_elem(void* base, int64_t idx, int dtype, float x) {
@@ -127,6 +183,18 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, int dtype, f
     uint32_t r = (x != x) ? 0x7fc00000u : u + 0x7fffu + ((u >> 16) & 1u);  // round to nearest even
     static_cast<uint16_t*>(base)[idx] = static_cast<uint16_t>(r >> 16);
   }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte K/V load (streamed once: optionally with the nontemporal hint).
+__device__ __forceinline__ uint4 load16(const char* p) {
+#if DA_NT_LOADS
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
 }
 
 // Merge state (m2, l2, o2) into (m, l, o); m in base-2 units, -inf = empty.
@@ -142,11 +210,14 @@ __device__ __forceinline__ void merge_into(float& m, float& l, float* o, float m
   m = M;
 }
 
-template <int D, int KVT, int GT>
+// QPACK: q and K/V share a 16-bit dtype; q is kept as packed pairs and q.k
+// uses v_dot2 with fp32 accumulation. Otherwise q is fp32 and q.k uses FMAs.
+template <int D, int KVT, int GT, bool QPACK>
 __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
   using LY = Layout<D, KVT, GT>;
   constexpr int LPR = LY::LPR, DPL = LY::DPL, VPL = LY::VPL, RPI = LY::RPI, NS = LY::NS, TR = LY::TR,
-                E = LY::E, SEG = LY::SEG;
+                E = LY::E, SEG = LY::SEG, ELT = LY::ELT;
+  static_assert(!QPACK || KVT != DA_F32, "packed q needs a 16-bit KV type");
 
   const int s = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -157,38 +228,69 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
   const int c = lane % LPR;  // lane within the row
   const int r = lane / LPR;  // row slot within a load instruction
 
+  // Attended tokens of this split: [t_lo, t_hi). Token counts fit int32 (the
+  // planner bounds max_pages_per_seq * page_size).
   const int P = a.page_size;
-  const int64_t L = a.seq_lens[b];
-  const int64_t t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
-  const int64_t pf = L > 0 ? t0 / P : 0;
-  const int64_t pe = L > 0 ? (L + P - 1) / P : 0;
-  const int64_t c_pages = a.pages_per_split;
-  int64_t nsplit = (pe - pf + c_pages - 1) / c_pages;
-  if (nsplit < 1) nsplit = 1;
-  if (nsplit > a.max_splits) nsplit = a.max_splits;
+  const int L = a.seq_lens[b];
+  const int t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
+  const int pf = L > 0 ? t0 / P : 0;
+  const int pe = L > 0 ? (L + P - 1) / P : 0;
+  const int cp = a.pages_per_split;
+  int nsplit = (pe - pf + cp - 1) / cp;
+  nsplit = nsplit < 1 ? 1 : (nsplit > a.max_splits ? a.max_splits : nsplit);
   if (s >= nsplit) return;  // whole work-group, uniform
-
-  const int64_t plo = pf + static_cast<int64_t>(s) * c_pages;
-  const int64_t phi = (plo + c_pages < pe) ? plo + c_pages : pe;
-  const int64_t t_lo = L > 0 ? (t0 > plo * P ? t0 : plo * P) : 0;
-  const int64_t t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
+  const int plo = pf + s * cp;
+  const int phi = (plo + cp < pe) ? plo + cp : pe;
+  const int t_lo = L > 0 ? (t0 > plo * P ? t0 : plo * P) : 0;
+  const int t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
 
   const int G = a.group;
   const int h0 = kvh * G;
+  const int64_t qrow0 = static_cast<int64_t>(b) * a.num_q_heads + h0;
 
-  // q for the G heads of the group, this lane's elements, as float.
-  float qf[GT][DPL];
+  // q for the G heads of the group, this lane's elements.
+  using QReg = typename std::conditional<QPACK, uint32_t, float>::type;
+  constexpr int QW = QPACK ? DPL / 2 : DPL;
+  QReg qv[GT][QW];
+  if constexpr (QPACK) {
 #pragma unroll
-  for (int g = 0; g < GT; ++g) {
+    for (int g = 0; g < GT; ++g) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int d = v * SEG + c * E + e;
-        qf[g][v * E + e] =
-            g < G ? load_elem(a.q, (static_cast<int64_t>(b) * a.num_q_heads + h0 + g) * D + d, a.q_dtype) : 0.0f;
+      for (int v = 0; v < VPL; ++v) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (g < G)
+          u = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                              ((qrow0 + g) * D + v * SEG + c * E) * ELT);
+        qv[g][v * 4] = u.x;
+        qv[g][v * 4 + 1] = u.y;
+        qv[g][v * 4 + 2] = u.z;
+        qv[g][v * 4 + 3] = u.w;
       }
     }
+  } else {
+    auto load_q = [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
+      constexpr int QE = QT == DA_F32 ? 4 : 2;
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          if (g < G) {
+            load_row_f32<QT, E>(static_cast<const char*>(a.q) + ((qrow0 + g) * D + v * SEG + c * E) * QE,
+                                &qv[g][v * E]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) qv[g][v * E + e] = 0.0f;
+          }
+        }
+      }
+    };
+    if (a.q_dtype == DA_F32)
+      load_q(std::integral_constant<int, DA_F32>());
+    else if (a.q_dtype == DA_F16)
+      load_q(std::integral_constant<int, DA_F16>());
+    else
+      load_q(std::integral_constant<int, DA_BF16>());
   }
 
   float m[GT], l[GT], o[GT][DPL];
@@ -202,98 +304,164 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
 
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
-  const int64_t block_elems = static_cast<int64_t>(P) * D;             // one (page, head) block
-  const int64_t page_elems = block_elems * a.num_kv_heads;
+  const int64_t block_bytes = static_cast<int64_t>(P) * D * ELT;  // one (page, head) block
+  const int64_t page_bytes = block_bytes * a.num_kv_heads;
+  const int64_t head_bytes = block_bytes * kvh;
   const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-  const uint32_t lane_off = static_cast<uint32_t>((r * D + c * E) * LY::ELT);
+  const uint32_t lane_off = static_cast<uint32_t>((r * D + c * E) * ELT);
 
-  const int64_t tile_first = t_lo / TR;
-  const int64_t tile_end = (t_hi + TR - 1) / TR;
+  const int tile_first = t_lo / TR;
+  const int tile_end = (t_hi + TR - 1) / TR;
+  const int my_first = tile_first + wave;
+  const int ntiles = my_first < tile_end ? (tile_end - my_first + kWaves - 1) / kWaves : 0;
 
   struct Tile {
     uint4 k[NS][VPL];
     uint4 v[NS][VPL];
   };
 
-  // Issue the loads of one tile. Load groups wholly outside [t_lo, t_hi) are
-  // skipped (no page-table read, registers zeroed), so only pages holding
-  // attended keys are touched.
-  auto load_tile = [&](Tile& t, int64_t tile) {
-    const int64_t tb = tile * TR;
+  // Load cursor: the next tile to load, the page index and in-page row of
+  // each of its NS load groups, and their physical page ids (fetched one
+  // step ahead).
+  constexpr int STEP = kWaves * TR;
+  const int step_p = STEP / P;
+  const int step_r = STEP - step_p * P;
+  int cur_tile = my_first;
+  int cur_pi[NS], cur_off[NS], cur_phys[NS];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) {
+    const int gs = my_first * TR + ns * RPI;
+    cur_pi[ns] = gs / P;
+    cur_off[ns] = gs - cur_pi[ns] * P;
+  }
+  // Page ids are read for every group, live or not, from an index clamped to
+  // this split's own pages [plo, phi): always a mapped page, and the reads
+  // need no branch (a branch would make the compiler wait on each one).
+  // Rows of groups outside [t_lo, t_hi) are masked in compute().
+  const int pi_last = phi > plo ? phi - 1 : plo;
+  auto fetch_ids = [&]() {
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      const int64_t gs = tb + ns * RPI;
-      if (gs < t_hi && gs + RPI > t_lo) {
-        const int64_t pi = gs / P;
-        const int64_t phys = table_row[pi];
-        const int64_t off = (phys * a.num_kv_heads + kvh) * block_elems + (gs - pi * P) * D;
-        const char* kp = kbase + off * LY::ELT + lane_off;
-        const char* vp = vbase + off * LY::ELT + lane_off;
+      const int pi = cur_pi[ns] < plo ? plo : (cur_pi[ns] > pi_last ? pi_last : cur_pi[ns]);
+      cur_phys[ns] = table_row[pi];
+    }
+  };
+  auto advance = [&]() {
+    cur_tile += kWaves;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          t.k[ns][v] = *reinterpret_cast<const uint4*>(kp + v * SEG * LY::ELT);
-          t.v[ns][v] = *reinterpret_cast<const uint4*>(vp + v * SEG * LY::ELT);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          t.k[ns][v] = make_uint4(0, 0, 0, 0);
-          t.v[ns][v] = make_uint4(0, 0, 0, 0);
-        }
+    for (int ns = 0; ns < NS; ++ns) {
+      cur_pi[ns] += step_p;
+      cur_off[ns] += step_r;
+      if (cur_off[ns] >= P) {
+        cur_off[ns] -= P;
+        cur_pi[ns] += 1;
       }
     }
   };
+  // Issue the loads of the cursor tile, then move the cursor and fetch the
+  // next tile's page ids. A group outside [t_lo, t_hi) (only in the first and
+  // last tile of a split) reads rows of a page of this split that compute()
+  // masks out; the row offset is always inside its page.
+  auto issue = [&](Tile& t) {
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int64_t off = static_cast<int64_t>(cur_phys[ns]) * page_bytes + head_bytes +
+                          static_cast<int64_t>(cur_off[ns]) * (D * ELT);
+      const char* kp = kbase + off + lane_off;
+      const char* vp = vbase + off + lane_off;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        t.k[ns][v] = load16(kp + v * SEG * ELT);
+        t.v[ns][v] = load16(vp + v * SEG * ELT);
+      }
+    }
+    advance();
+    fetch_ids();
+  };
 
-  auto compute_tile = [&](const Tile& t, int64_t tile) {
-    const int64_t tb = tile * TR;
+  const float sl2 = a.scale_log2;
+  auto compute = [&](const Tile& t, int tile) {
+    const int tb = tile * TR;
     const bool full = tb >= t_lo && tb + TR <= t_hi;
     bool valid[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      const int64_t tok = tb + ns * RPI + r;
+      const int tok = tb + ns * RPI + r;
       valid[ns] = full || (tok >= t_lo && tok < t_hi);
     }
+    // q.k partial sums, then the row sums.
     float sc[NS][GT];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      float kf[DPL];
+      if constexpr (QPACK) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) unpack<KVT>(t.k[ns][v], kf + v * E);
+        for (int g = 0; g < GT; ++g) {
+          float acc = 0.0f;
 #pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float acc = 0.0f;
+          for (int v = 0; v < VPL; ++v) {
+            const uint4 u = t.k[ns][v];
+            acc = dot2<KVT>(qv[g][v * 4], u.x, acc);
+            acc = dot2<KVT>(qv[g][v * 4 + 1], u.y, acc);
+            acc = dot2<KVT>(qv[g][v * 4 + 2], u.z, acc);
+            acc = dot2<KVT>(qv[g][v * 4 + 3], u.w, acc);
+          }
+          sc[ns][g] = acc;
+        }
+      } else {
+        float kf[DPL];
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) acc = fmaf(qf[g][i], kf[i], acc);
-        sc[ns][g] = acc;
+        for (int v = 0; v < VPL; ++v) unpack<KVT>(t.k[ns][v], kf + v * E);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) acc = fmaf(qv[g][i], kf[i], acc);
+          sc[ns][g] = acc;
+        }
       }
     }
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        const float x = row_sum<LPR>(sc[ns][g]) * a.scale_log2;
+        const float x = row_sum<LPR>(sc[ns][g]) * sl2;
         sc[ns][g] = valid[ns] ? x : -INFINITY;
       }
     }
-    float p[NS][GT];
+    // Online softmax. O and l are rescaled only when some running max of the
+    // wave grew (a wave-uniform branch; a factor of exactly 1 is skipped).
+    float mn[GT];
+    bool grew = false;
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       float mt = sc[0][g];
 #pragma unroll
       for (int ns = 1; ns < NS; ++ns) mt = fmaxf(mt, sc[ns][g]);
-      const float mn = fmaxf(m[g], mt);
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float alpha = exp2_fast(m[g] - mu);
-      m[g] = mn;
+      mn[g] = fmaxf(m[g], mt);
+      grew |= mn[g] > m[g];
+    }
+    if (__any(grew)) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float mu = (mn[g] == -INFINITY) ? 0.0f : mn[g];
+        const float alpha = exp2_fast(m[g] - mu);
+        l[g] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[g][i] *= alpha;
+        m[g] = mn[g];
+      }
+    }
+    float p[NS][GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const float mu = (m[g] == -INFINITY) ? 0.0f : m[g];
       float ps = 0.0f;
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         p[ns][g] = exp2_fast(sc[ns][g] - mu);
         ps += p[ns][g];
       }
-      l[g] = l[g] * alpha + ps;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) o[g][i] *= alpha;
+      l[g] += ps;
     }
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
@@ -312,23 +480,33 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     }
   };
 
-  // Tiles tile_first + wave, + kWaves, ... with the next tile's loads in
-  // flight while the current one is computed.
-  int64_t tile = tile_first + wave;
-  if (tile < tile_end) {
-    Tile ta, tb;
-    load_tile(ta, tile);
-    while (true) {
-      const int64_t next = tile + kWaves;
-      if (next < tile_end) load_tile(tb, next);
-      compute_tile(ta, tile);
-      if (next >= tile_end) break;
-      tile = next;
-      const int64_t next2 = tile + kWaves;
-      if (next2 < tile_end) load_tile(ta, next2);
-      compute_tile(tb, tile);
-      if (next2 >= tile_end) break;
-      tile = next2;
+  // Ring of kPD + 1 tile buffers: tile n lives in buf[n % (kPD + 1)]. The
+  // steady-state loop only runs while every tile it issues exists, so its
+  // loads are unconditional and the compiler's wait counts stay exact (each
+  // compute waits only for its own tile, kPD tiles of loads stay in flight);
+  // the last tiles drain in an unrolled tail.
+  if (ntiles > 0) {
+    Tile buf[kPD + 1];
+    fetch_ids();
+#pragma unroll
+    for (int k = 0; k < kPD; ++k)
+      if (k < ntiles) issue(buf[k]);
+    int n = 0;
+    while (n + 2 * kPD < ntiles) {
+#pragma unroll
+      for (int j = 0; j <= kPD; ++j) {
+        issue(buf[(j + kPD) % (kPD + 1)]);
+        compute(buf[j], my_first + (n + j) * kWaves);
+      }
+      n += kPD + 1;
+    }
+    // Here ntiles - n <= 2 * kPD and n % (kPD + 1) == 0.
+#pragma unroll
+    for (int j = 0; j < 2 * kPD; ++j) {
+      if (n + j < ntiles) {
+        if (n + j + kPD < ntiles) issue(buf[(j + kPD) % (kPD + 1)]);
+        compute(buf[j % (kPD + 1)], my_first + (n + j) * kWaves);
+      }
     }
   }
 
@@ -383,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
       lsum += aw * sh_l[w][g];
       osum += aw * sh_o[w][g][d];
     }
-    const int64_t row = static_cast<int64_t>(b) * a.num_q_heads + h0 + g;
+    const int64_t row = qrow0 + g;
     if (nsplit == 1) {
       store_elem(a.out, row * D + d, a.out_dtype, lsum > 0.0f ? osum / lsum : 0.0f);
     } else {
@@ -397,13 +575,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
   }
 }
 
-template <int D, int KVT>
+template <int D, int KVT, bool QPACK>
 hipError_t launch_gt(const KernelArgs& a, int gt, dim3 grid, hipStream_t st) {
   switch (gt) {
-    case 1: hipLaunchKernelGGL((split_kernel<D, KVT, 1>), grid, dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((split_kernel<D, KVT, 2>), grid, dim3(kThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((split_kernel<D, KVT, 4>), grid, dim3(kThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((split_kernel<D, KVT, 8>), grid, dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((split_kernel<D, KVT, 1, QPACK>), grid, dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((split_kernel<D, KVT, 2, QPACK>), grid, dim3(kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((split_kernel<D, KVT, 4, QPACK>), grid, dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((split_kernel<D, KVT, 8, QPACK>), grid, dim3(kThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -411,10 +589,13 @@ hipError_t launch_gt(const KernelArgs& a, int gt, dim3 grid, hipStream_t st) {
 
 template <int D>
 hipError_t launch_kv(const KernelArgs& a, int kv, int gt, dim3 grid, hipStream_t st) {
+  const bool qpack = a.q_dtype == kv;
   switch (kv) {
-    case DA_F32: return launch_gt<D, DA_F32>(a, gt, grid, st);
-    case DA_F16: return launch_gt<D, DA_F16>(a, gt, grid, st);
-    case DA_BF16: return launch_gt<D, DA_BF16>(a, gt, grid, st);
+    case DA_F32: return launch_gt<D, DA_F32, false>(a, gt, grid, st);
+    case DA_F16:
+      return qpack ? launch_gt<D, DA_F16, true>(a, gt, grid, st) : launch_gt<D, DA_F16, false>(a, gt, grid, st);
+    case DA_BF16:
+      return qpack ? launch_gt<D, DA_BF16, true>(a, gt, grid, st) : launch_gt<D, DA_BF16, false>(a, gt, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

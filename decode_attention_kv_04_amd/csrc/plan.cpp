@@ -22,7 +22,7 @@ namespace {
 
 // Splits per KV head are sized so the split pass has about this many
 // work-groups per compute unit in total.
-constexpr int64_t kTargetGroupsPerCu = 4;
+constexpr int64_t kTargetGroupsPerCu = 9;
 // A split never holds fewer attended tokens than this (the pages' 256-token
 // switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
 constexpr int64_t kDefaultMinSplitTokens = 256;
@@ -92,6 +92,8 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
 
   const int64_t P = p->page_size;
   const int64_t cap = static_cast<int64_t>(p->max_pages_per_seq) * P;
+  // The kernels count tokens in int32, with a few tiles of headroom.
+  if (cap > static_cast<int64_t>(INT32_MAX) - 4096) return DA_ERR_UNSUPPORTED;
   for (int32_t b = 0; b < p->batch; ++b) {
     if (lens[b] < 0 || static_cast<int64_t>(lens[b]) > cap) return DA_ERR_INVALID;
   }

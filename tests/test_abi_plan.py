@@ -163,6 +163,7 @@ def test_empty_batch_plans(lib):
     (dict(out_dtype=-1), [10], B.DA_ERR_INVALID),
     (dict(num_q_heads=32, num_kv_heads=2), [10], B.DA_ERR_UNSUPPORTED),   # G = 16
     (dict(max_pages_per_seq=0), [10], B.DA_ERR_INVALID),
+    (dict(max_pages_per_seq=(1 << 31) // 16), [10], B.DA_ERR_UNSUPPORTED),  # token index would overflow int32
     (dict(max_pages_per_seq=4), [65], B.DA_ERR_INVALID),                  # 65 > 4 * 16
     (dict(), [-1], B.DA_ERR_INVALID),
 ])
