@@ -29,7 +29,7 @@ METRIC = "decode-attention µs/step + achieved HBM GB/s (% of peak), Llama-8B sh
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_long_batch_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kv_04_amd", "csrc", f)
-                  for f in ("decode_split.hip", "kernels.h")]
+                  for f in ("decode_split.hip", "decode_split_mfma.hip", "device_common.h", "kernels.h")]
 
 
 def kernel_hash() -> str:
@@ -271,7 +271,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "split pass (da::split_kernel)",
+            "kernel": ("split pass, q.K on the matrix cores (da::split_kernel_mfma)" if plan.info.split_kernel
+                       else "split pass, vector q.K (da::split_kernel)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

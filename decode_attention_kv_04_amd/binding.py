@@ -46,6 +46,7 @@ class PlanInfo(ctypes.Structure):
         ("pages_per_split", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("num_cus", ctypes.c_int32),
         ("split_work_groups", ctypes.c_int32), ("active_units", ctypes.c_int64),
         ("attended_keys", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+        ("split_kernel", ctypes.c_int32),
     ]
 
 

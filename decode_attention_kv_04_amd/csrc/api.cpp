@@ -84,8 +84,10 @@ da_status enqueue(const da_plan* plan, const da::KernelArgs& a, bool split, bool
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
   if (split) {
-    if (da::launch_split(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st) != hipSuccess)
-      return DA_ERR_HIP;
+    const hipError_t e = plan->split_kernel == 1
+                             ? da::launch_split_mfma(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st)
+                             : da::launch_split(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st);
+    if (e != hipSuccess) return DA_ERR_HIP;
   }
   if (combine && plan->max_splits > 1) {
     if (da::launch_combine(a, plan->p.head_dim, st) != hipSuccess) return DA_ERR_HIP;
@@ -126,6 +128,7 @@ da_status decode_attn_plan_info(da_plan_t plan, da_plan_info* info) {
   info->active_units = plan->active_units;
   info->attended_keys = plan->attended_keys;
   info->workspace_bytes = plan->ws_bytes;
+  info->split_kernel = plan->split_kernel;
   return DA_OK;
 }
 

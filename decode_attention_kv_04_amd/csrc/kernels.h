@@ -36,6 +36,10 @@ struct KernelArgs {
 // group_tile).
 hipError_t launch_split(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream);
 
+// Enqueue the split pass with q.K on the matrix cores (q and K/V share a
+// 16-bit type, head_dim 128, page size a multiple of 16).
+hipError_t launch_split_mfma(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream);
+
 // Enqueue the combine pass on `stream`.
 hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream);
 

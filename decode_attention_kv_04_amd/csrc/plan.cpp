@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <new>
 
 namespace da {
@@ -35,6 +36,16 @@ int64_t min_split_tokens() {
     if (end && *end == '\0' && v >= 1) return v;
   }
   return kDefaultMinSplitTokens;
+}
+
+// DECODE_ATTN_KERNEL=vector|matrix forces the split kernel (when the matrix
+// one supports the parameters); unset or anything else = automatic.
+int32_t forced_kernel() {
+  const char* s = std::getenv("DECODE_ATTN_KERNEL");
+  if (!s) return -1;
+  if (std::strcmp(s, "vector") == 0) return 0;
+  if (std::strcmp(s, "matrix") == 0) return 1;
+  return -1;
 }
 
 bool log_enabled() {
@@ -61,6 +72,11 @@ SeqRange seq_range(int64_t L, int64_t window, int64_t P) {
     r.pe = ceil_div(L, P);
   }
   return r;
+}
+
+bool matrix_kernel_supported(const da_params& p) {
+  return p.head_dim == 128 && (p.kv_dtype == DA_F16 || p.kv_dtype == DA_BF16) && p.q_dtype == p.kv_dtype &&
+         p.page_size % 16 == 0;
 }
 
 int32_t group_tile_for(int32_t G) {
@@ -104,6 +120,10 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   plan->group = G;
   plan->group_tile = gt;
   plan->num_cus = num_cus;
+  // q.K as a 16 x 32 x 16 matrix-core product per 16-key tile whenever the
+  // parameters allow it: with G query heads sharing the keys it is a dense
+  // contraction, and it takes the dot products and lane sums off the VALU.
+  plan->split_kernel = matrix_kernel_supported(*p) && forced_kernel() != 0 ? 1 : 0;
 
   // Attended pages per sequence.
   std::vector<int64_t> npages(p->batch);
@@ -155,9 +175,10 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
 
   if (log_enabled()) {
     std::fprintf(stderr,
-                 "decode_attn plan: B=%d Hq=%d Hkv=%d D=%d P=%d W=%d cus=%d pages/split=%lld "
+                 "decode_attn plan: B=%d Hq=%d Hkv=%d D=%d P=%d W=%d kernel=%s cus=%d pages/split=%lld "
                  "max_splits=%lld units=%lld keys=%lld ws=%zu\n",
                  p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, p->page_size, p->window,
+                 plan->split_kernel ? "matrix" : "vector",
                  num_cus, static_cast<long long>(c), static_cast<long long>(smax),
                  static_cast<long long>(plan->active_units), static_cast<long long>(plan->attended_keys),
                  plan->ws_bytes);

@@ -13,6 +13,7 @@ struct da_plan {
   da_params p;
   int32_t group = 1;           // G = H_q / H_kv
   int32_t group_tile = 1;      // compiled group width the kernels use (1, 2, 4 or 8)
+  int32_t split_kernel = 0;    // 0 = vector q.K, 1 = q.K on the matrix cores
   int32_t num_cus = 0;
   int32_t pages_per_split = 1; // c
   int32_t max_splits = 1;      // S_max
@@ -35,6 +36,9 @@ SeqRange seq_range(int64_t L, int64_t window, int64_t P);
 
 // Group width compiled for a GQA group size (0 if none is).
 int32_t group_tile_for(int32_t G);
+
+// Whether the matrix-core split kernel covers these parameters.
+bool matrix_kernel_supported(const da_params& p);
 
 // Validate parameters and lengths and build a plan for `num_cus` compute
 // units. On success *out owns a new plan.

@@ -93,6 +93,10 @@ typedef struct {
   int64_t active_units;      /* sum over b of splits(b) * H_kv                      */
   int64_t attended_keys;     /* sum over b of attended keys                         */
   size_t workspace_bytes;    /* bytes of device workspace `run` needs (0 if none)   */
+  int32_t split_kernel;      /* 0 = vector q.K (any parameters); 1 = q.K on the
+                                matrix cores (q and K/V share f16 or bf16,
+                                head_dim 128, page size a multiple of 16).
+                                DECODE_ATTN_KERNEL=vector forces 0.               */
 } da_plan_info;
 
 /*

@@ -1,5 +1,7 @@
 """Helpers shared by the GPU tests: run the library on a workload and compare
 with the oracle."""
+import contextlib
+import os
 import sys
 
 import numpy as np
@@ -16,10 +18,28 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+@contextlib.contextmanager
+def split_kernel(kind):
+    """kind: None / "auto" (the planner chooses) or "vector" / "matrix"."""
+    old = os.environ.get("DECODE_ATTN_KERNEL")
+    if kind and kind != "auto":
+        os.environ["DECODE_ATTN_KERNEL"] = kind
+    else:
+        os.environ.pop("DECODE_ATTN_KERNEL", None)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("DECODE_ATTN_KERNEL", None)
+        else:
+            os.environ["DECODE_ATTN_KERNEL"] = old
+
+
 def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None, page_table=None,
-            window=None, seq_lens=None, seq_lens_host=None, two_phase=False):
+            window=None, seq_lens=None, seq_lens_host=None, two_phase=False, kernel=None):
     """One decode_attn_run (or split + combine) on the workload's tensors;
-    returns (out tensor, plan). The output starts as NaN so unwritten rows show."""
+    returns (out tensor, plan). The output starts as NaN so unwritten rows show.
+    `kernel` = "vector" forces the vector split kernel; default: automatic."""
     q = w.q if q is None else q
     k_pool = w.k_pool if k_pool is None else k_pool
     v_pool = w.v_pool if v_pool is None else v_pool
@@ -30,7 +50,8 @@ def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None
     out_dtype = out_dtype or w.spec.out_dtype
     params = binding.params_for(q, k_pool, page_table, window=window, scale=w.scale, out_dtype=out_dtype,
                                 num_splits=num_splits)
-    plan = binding.decode_attn_plan(params, seq_lens_host, device=q.device.index)
+    with split_kernel(kernel):
+        plan = binding.decode_attn_plan(params, seq_lens_host, device=q.device.index)
     out = torch.full(q.shape, float("nan"), dtype=TORCH_DT[out_dtype], device=q.device)
     ws = binding.alloc_workspace(plan, q.device)
     if ws is not None:

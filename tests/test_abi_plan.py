@@ -134,6 +134,24 @@ def test_split_min_env_override(lib, monkeypatch):
     assert pl.pages_per_split >= 4 and pl.max_splits > 1
 
 
+def test_split_kernel_selection(lib, monkeypatch):
+    monkeypatch.delenv("DECODE_ATTN_KERNEL", raising=False)
+    assert plan(params(), [3060]).info.split_kernel == 1                       # f16, D 128, P 16
+    assert plan(params(q_dtype="bf16", kv_dtype="bf16"), [3060]).info.split_kernel == 1
+    assert plan(params(page_size=32, max_pages_per_seq=1024), [3060]).info.split_kernel == 1
+    assert plan(params(q_dtype="f32"), [3060]).info.split_kernel == 0           # q and KV differ
+    assert plan(params(q_dtype="f32", kv_dtype="f32"), [3060]).info.split_kernel == 0
+    assert plan(params(head_dim=64), [3060]).info.split_kernel == 0
+    assert plan(params(head_dim=256), [3060]).info.split_kernel == 0
+    assert plan(params(page_size=8, max_pages_per_seq=4096), [3060]).info.split_kernel == 0
+    assert plan(params(page_size=24, max_pages_per_seq=4096), [3060]).info.split_kernel == 0
+    monkeypatch.setenv("DECODE_ATTN_KERNEL", "vector")
+    assert plan(params(), [3060]).info.split_kernel == 0
+    monkeypatch.setenv("DECODE_ATTN_KERNEL", "matrix")
+    assert plan(params(), [3060]).info.split_kernel == 1
+    assert plan(params(head_dim=64), [3060]).info.split_kernel == 0             # unsupported: vector
+
+
 def test_empty_batch_plans(lib):
     pl = plan(params(batch=0), [])
     assert pl.max_splits == 1 and pl.workspace_bytes == 0

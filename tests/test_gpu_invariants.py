@@ -16,17 +16,22 @@ def make(spec, gpu, **kw):
     return wl.make_workload(spec.replace(**kw) if kw else spec, gpu)
 
 
-def test_run_to_run_bitwise_determinism(gpu):
+KERNELS = ["auto", "vector"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_run_to_run_bitwise_determinism(gpu, kernel):
     w = make(wl.LLAMA8B_3060, gpu)
-    a, _ = run_lib(w)
+    a, _ = run_lib(w, kernel=kernel)
     for _ in range(3):
-        b, _ = run_lib(w)
+        b, _ = run_lib(w, kernel=kernel)
         assert torch.equal(a, b)
 
 
-def test_page_permutation_is_bitwise(gpu):
-    w = make(wl.WIDE_GQA, gpu)
-    a, _ = run_lib(w, num_splits=3)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_page_permutation_is_bitwise(gpu, kernel):
+    w = make(wl.WIDE_GQA.replace(head_dim=128), gpu)
+    a, _ = run_lib(w, num_splits=3, kernel=kernel)
     g = torch.Generator().manual_seed(5)
     perm = torch.randperm(w.num_pages, generator=g).to(gpu)  # page p moves to perm[p]
     kp = torch.empty_like(w.k_pool)
@@ -34,26 +39,28 @@ def test_page_permutation_is_bitwise(gpu):
     kp[perm] = w.k_pool
     vp[perm] = w.v_pool
     table = perm.to(torch.int32)[w.page_table.long()]
-    b, _ = run_lib(w, num_splits=3, k_pool=kp, v_pool=vp, page_table=table.contiguous())
+    b, _ = run_lib(w, num_splits=3, k_pool=kp, v_pool=vp, page_table=table.contiguous(), kernel=kernel)
     assert torch.equal(a, b)
 
 
-def test_unattended_contents_do_not_matter(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_unattended_contents_do_not_matter(gpu, kernel):
     spec = wl.MIXED_WINDOW.replace(batch=4, lengths=("list", (100, 5000, 33, 4097)), window=1000, page_size=32)
     w = make(spec, gpu)
-    a, _ = run_lib(w)
+    a, _ = run_lib(w, kernel=kernel)
     kp = torch.where(torch.isnan(w.k_pool), torch.full_like(w.k_pool, 1000.0), w.k_pool)
     vp = torch.where(torch.isnan(w.v_pool), torch.full_like(w.v_pool, -7.0), w.v_pool)
-    b, _ = run_lib(w, k_pool=kp, v_pool=vp)
+    b, _ = run_lib(w, k_pool=kp, v_pool=vp, kernel=kernel)
     assert torch.isfinite(a).all()
     assert torch.equal(a, b)
 
 
-def test_single_key_returns_value_bitwise(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_single_key_returns_value_bitwise(gpu, kernel):
     for kv in ("f32", "f16", "bf16"):
         spec = wl.WorkloadSpec(f"one_{kv}", 3, 8, 2, 128, kv, kv, kv, 16, ("list", (1, 1, 1)), seed=3)
         w = make(spec, gpu)
-        out, _ = run_lib(w)
+        out, _ = run_lib(w, kernel=kernel)
         v = w.v_pool[w.page_table[:, 0].long(), :, 0, :]            # [B][Hkv][D]
         expect = v.repeat_interleave(4, dim=1)
         assert torch.equal(out, expect)
@@ -67,18 +74,20 @@ def test_single_key_returns_value_bitwise(gpu):
         assert torch.equal(out[b], v.expand(4, -1))
 
 
-def test_doubling_values_doubles_output_bitwise(gpu):
-    w = make(wl.WIDE_GQA, gpu)
-    a, _ = run_lib(w, out_dtype="f32")
-    b, _ = run_lib(w, out_dtype="f32", v_pool=w.v_pool * 2)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_doubling_values_doubles_output_bitwise(gpu, kernel):
+    w = make(wl.WIDE_GQA.replace(head_dim=128), gpu)
+    a, _ = run_lib(w, out_dtype="f32", kernel=kernel)
+    b, _ = run_lib(w, out_dtype="f32", v_pool=w.v_pool * 2, kernel=kernel)
     assert torch.equal(b, 2 * a)
 
 
-def test_window_at_least_length_is_bitwise_no_window(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_window_at_least_length_is_bitwise_no_window(gpu, kernel):
     spec = wl.LLAMA8B_3060.replace(batch=2, lengths=("list", (3060, 700)))
     w = make(spec, gpu)
-    a, _ = run_lib(w, window=0, num_splits=4)
-    b, _ = run_lib(w, window=3060, num_splits=4)
+    a, _ = run_lib(w, window=0, num_splits=4, kernel=kernel)
+    b, _ = run_lib(w, window=3060, num_splits=4, kernel=kernel)
     assert torch.equal(a, b)
 
 
@@ -133,12 +142,13 @@ def test_split_count_changes_within_tolerance(gpu):
         assert np.max(np.abs(o - outs[0])) < 1e-5
 
 
-def test_batch_independence_bitwise(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_batch_independence_bitwise(gpu, kernel):
     spec = wl.LLAMA8B_3060.replace(batch=3, lengths=("list", (3000, 3000, 3000)))
     w = make(spec, gpu)
-    a, _ = run_lib(w, num_splits=1)
+    a, _ = run_lib(w, num_splits=1, kernel=kernel)
     for b in range(3):
         lens = w.seq_lens_host[b:b + 1].clone()
         out, _ = run_lib(w, num_splits=1, q=w.q[b:b + 1].contiguous(), page_table=w.page_table[b:b + 1].contiguous(),
-                         seq_lens=lens.to(gpu), seq_lens_host=lens)
+                         seq_lens=lens.to(gpu), seq_lens_host=lens, kernel=kernel)
         assert torch.equal(out[0], a[b])

@@ -23,13 +23,18 @@ def make(spec, gpu, **kw):
 # The five named workloads
 # ---------------------------------------------------------------------------
 
+KERNELS = ["auto", "vector"]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("name", ["tiny", "llama8b_3060", "wide_gqa"])
-def test_small_named_workloads_full_output(gpu, name):
+def test_small_named_workloads_full_output(gpu, name, kernel):
     spec = wl.NAMED[name]
     w = make(spec, gpu)
-    out, plan = run_lib(w)
+    out, plan = run_lib(w, kernel=kernel)
     err, worst = check(out, oracle_for(w), spec.kv_dtype, spec.out_dtype, name)
-    say(f"  {name}: rel L2 {err:.2e} worst row {worst:.2e} splits {plan.max_splits}")
+    say(f"  {name}: rel L2 {err:.2e} worst row {worst:.2e} splits {plan.max_splits} "
+        f"kernel {plan.info.split_kernel}")
 
 
 def sample_rows(w, k):
@@ -46,12 +51,15 @@ def sample_rows(w, k):
     return picks[:k]
 
 
-def test_long_batch_full_size_sampled(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_long_batch_full_size_sampled(gpu, kernel):
     """Batch 32, 32/8 heads, D 128, fp16, 16k-32k tokens, spiky keys: the
     whole batch on the GPU in the planner's launch configuration (the one the
-    benchmark times), checked on sampled sequences."""
+    benchmark times, with the matrix-core split kernel), checked on sampled
+    sequences."""
     w = make(wl.LONG_BATCH, gpu)
-    out, plan = run_lib(w)
+    out, plan = run_lib(w, kernel=kernel)
+    assert plan.info.split_kernel == (1 if kernel == "auto" else 0)
     rows = sample_rows(w, 4)
     say(f"  plan: pages/split {plan.pages_per_split} max splits {plan.max_splits}; rows {rows}")
     ref = oracle_for(w, rows)
@@ -61,11 +69,12 @@ def test_long_batch_full_size_sampled(gpu):
     say(f"  long_batch: rel L2 {err:.2e} worst row {worst:.2e}")
 
 
-def test_mixed_window_full_size_sampled(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mixed_window_full_size_sampled(gpu, kernel):
     """Batch 64, window 4096, half short (1-256) and half long (32k-64k), bf16,
     32-token pages; pre-window pages hold NaN."""
     w = make(wl.MIXED_WINDOW, gpu)
-    out, plan = run_lib(w)
+    out, plan = run_lib(w, kernel=kernel)
     L = w.seq_lens_host.tolist()
     short = [b for b in range(len(L)) if L[b] <= 256][:3]
     long = [b for b in range(len(L)) if L[b] > 256][:3]
@@ -82,24 +91,28 @@ def test_mixed_window_full_size_sampled(gpu):
 # Sweeps at sizes the oracle finishes in seconds
 # ---------------------------------------------------------------------------
 
-def test_every_length_up_to_three_pages_and_3060(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_every_length_up_to_three_pages_and_3060(gpu, kernel):
     P = 16
     lens = list(range(0, 3 * P + 2)) + [3060]
     spec = wl.LLAMA8B_3060.replace(batch=len(lens), lengths=("list", tuple(lens)))
     w = make(spec, gpu)
+    ref = oracle_for(w)
     for ns in (0, 1, 2, 7):
-        out, _ = run_lib(w, num_splits=ns)
-        check(out, oracle_for(w), "f16", "f16", f"lengths splits={ns}")
+        out, _ = run_lib(w, num_splits=ns, kernel=kernel)
+        check(out, ref, "f16", "f16", f"lengths splits={ns}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("W", [1, 15, 16, 17, 199, 200, 201, 1000])
-def test_window_sweep(gpu, W):
+def test_window_sweep(gpu, W, kernel):
     lens = (200, 37, 1, 16, 17, 513)
     spec = wl.MIXED_WINDOW.replace(batch=len(lens), lengths=("list", lens), window=W, page_size=16)
     w = make(spec, gpu)
+    ref = oracle_for(w)
     for ns in (0, 1, 3):
-        out, _ = run_lib(w, num_splits=ns)
-        check(out, oracle_for(w), "bf16", "f32", f"window {W} splits={ns}")
+        out, _ = run_lib(w, num_splits=ns, kernel=kernel)
+        check(out, ref, "bf16", "f32", f"window {W} splits={ns}")
 
 
 GRID = [(G, D, kv) for G in (1, 2, 3, 4, 5, 6, 7, 8) for D in (64, 128, 256) for kv in ("f32", "f16", "bf16")]
@@ -111,27 +124,35 @@ def test_group_dim_dtype_grid(gpu, G, D, kv):
     spec = wl.WorkloadSpec(f"grid_G{G}_D{D}_{kv}", 3, G * Hkv, Hkv, D, kv, kv, "f32", 16,
                            ("list", (1, 300, 777)), seed=G * 1000 + D + len(kv), spike_frac=0.01)
     w = make(spec, gpu)
-    for ns in (0, 3):
-        out, _ = run_lib(w, num_splits=ns)
-        check(out, oracle_for(w), kv, "f32", f"G{G} D{D} {kv} splits={ns}")
+    ref = oracle_for(w)
+    kernels = ["auto", "vector"] if (D == 128 and kv != "f32") else ["auto"]
+    for kernel in kernels:
+        for ns in (0, 3):
+            out, plan = run_lib(w, num_splits=ns, kernel=kernel)
+            assert plan.info.split_kernel == (1 if (D == 128 and kv != "f32" and kernel == "auto") else 0)
+            check(out, ref, kv, "f32", f"G{G} D{D} {kv} splits={ns} kernel={kernel}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("P", [8, 16, 24, 32, 64])
-def test_page_sizes(gpu, P):
+def test_page_sizes(gpu, P, kernel):
     lens = (1, P - 1, P, P + 1, 5 * P + 3, 700)
     spec = wl.WIDE_GQA.replace(batch=len(lens), lengths=("list", lens), page_size=P, head_dim=128,
                                seed=40 + P)
     w = make(spec, gpu)
+    ref = oracle_for(w)
     for ns in (0, 1, 4):
-        out, _ = run_lib(w, num_splits=ns)
-        check(out, oracle_for(w), "bf16", "f32", f"P={P} splits={ns}")
+        out, plan = run_lib(w, num_splits=ns, kernel=kernel)
+        assert plan.info.split_kernel == (1 if (P % 16 == 0 and kernel == "auto") else 0)
+        check(out, ref, "bf16", "f32", f"P={P} splits={ns}")
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("ns", [1, 2, 3, 7, 10_000])
-def test_forced_split_counts(gpu, ns):
+def test_forced_split_counts(gpu, ns, kernel):
     spec = wl.LLAMA8B_3060.replace(batch=3, lengths=("list", (3060, 1000, 17)))
     w = make(spec, gpu)
-    out, plan = run_lib(w, num_splits=ns)
+    out, plan = run_lib(w, num_splits=ns, kernel=kernel)
     assert plan.max_splits == min(ns, math.ceil(3060 / 16))
     check(out, oracle_for(w), "f16", "f16", f"splits={ns}")
 
@@ -149,12 +170,13 @@ def test_mixed_dtypes(gpu, q_dt, kv_dt, out_dt):
         check(out, oracle_for(w), kv_dt, out_dt, f"{q_dt}/{kv_dt}/{out_dt}")
 
 
-def test_empty_and_ragged_batch(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_empty_and_ragged_batch(gpu, kernel):
     lens = (0, 1, 0, 4096, 2, 0)
     spec = wl.LLAMA8B_3060.replace(batch=len(lens), lengths=("list", lens))
     w = make(spec, gpu)
     for ns in (0, 1, 5):
-        out, _ = run_lib(w, num_splits=ns)
+        out, _ = run_lib(w, num_splits=ns, kernel=kernel)
         got = host64(out)
         for b, L in enumerate(lens):
             if L == 0:
@@ -175,11 +197,23 @@ def test_empty_batch_is_a_noop(gpu):
     torch.cuda.synchronize()
 
 
-def test_two_phase_api_equals_run(gpu):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_two_phase_api_equals_run(gpu, kernel):
     w = make(wl.LLAMA8B_3060, gpu)
-    a, _ = run_lib(w, num_splits=6)
-    b, _ = run_lib(w, num_splits=6, two_phase=True)
+    a, _ = run_lib(w, num_splits=6, kernel=kernel)
+    b, _ = run_lib(w, num_splits=6, two_phase=True, kernel=kernel)
     assert torch.equal(a, b)
+
+
+def test_vector_and_matrix_kernels_agree(gpu):
+    """The two split kernels on the same inputs: within fp32 rounding."""
+    spec = wl.LLAMA8B_3060.replace(batch=4, lengths=("list", (3060, 5000, 17, 999)), out_dtype="f32")
+    w = make(spec, gpu)
+    a, pa = run_lib(w, kernel="auto")
+    b, pb = run_lib(w, kernel="vector")
+    assert pa.info.split_kernel == 1 and pb.info.split_kernel == 0
+    rel = ((a - b).norm() / a.norm()).item()
+    assert rel < 2e-6
 
 
 def test_long_context_single_sequence_max_table(gpu):
