@@ -1,6 +1,6 @@
 // Split pass of paged decode attention for gfx950.
 //
-// One work-group of four wave64s owns one (split s, KV head j, sequence b):
+// One work-group of four wave64s owns one (KV head j, split s, sequence b):
 // the attended keys of pages [pf + s*c, pf + (s+1)*c) of sequence b. It reads
 // each K/V row of that range once for all G query heads of the GQA group
 // (mlx-runner pull 3, GQA-shared split attention commit: each K/V row is read
@@ -87,8 +87,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
                 E = LY::E, SEG = LY::SEG, ELT = LY::ELT;
   static_assert(!QPACK || KVT != DA_F32, "packed q needs a 16-bit KV type");
 
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
+  // KV head fastest: the H_kv work-groups of one page range are dispatched
+  // together, so their K/V blocks (adjacent in a page) are read at the same
+  // time.
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -471,7 +474,7 @@ hipError_t launch_kv(const KernelArgs& a, int kv, int gt, dim3 grid, hipStream_t
 }  // namespace
 
 hipError_t launch_split(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream) {
-  const dim3 grid(a.max_splits, a.num_kv_heads, a.batch);
+  const dim3 grid(a.num_kv_heads, a.max_splits, a.batch);
   switch (head_dim) {
     case 64: return launch_kv<64>(a, kv_dtype, group_tile, grid, stream);
     case 128: return launch_kv<128>(a, kv_dtype, group_tile, grid, stream);

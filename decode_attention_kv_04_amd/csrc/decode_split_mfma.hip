@@ -90,8 +90,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
   constexpr int TR = 16;        // keys per tile
   constexpr int RB = D * ELT;   // bytes per row
 
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
+  // KV head fastest: the H_kv work-groups of one page range are dispatched
+  // together, so their K/V blocks (adjacent in a page) are read at the same
+  // time.
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -390,7 +393,7 @@ hipError_t launch_kv(const KernelArgs& a, int kv, int gt, dim3 grid, hipStream_t
 }  // namespace
 
 hipError_t launch_split_mfma(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream) {
-  const dim3 grid(a.max_splits, a.num_kv_heads, a.batch);
+  const dim3 grid(a.num_kv_heads, a.max_splits, a.batch);
   switch (head_dim) {
     case 128: return launch_kv<128>(a, kv_dtype, group_tile, grid, stream);
     default: return hipErrorInvalidValue;

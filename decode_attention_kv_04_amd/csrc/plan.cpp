@@ -149,6 +149,8 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     c = std::min(c, max_np);
   }
   c = std::max<int64_t>(c, 1);
+  // The split index is the grid's y dimension (at most 65535 splits).
+  c = std::max<int64_t>(c, ceil_div(max_np, 65535));
   if (c > INT32_MAX) c = INT32_MAX;
   plan->pages_per_split = static_cast<int32_t>(c);
 
@@ -159,10 +161,6 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     plan->splits[b] = static_cast<int32_t>(s);
     smax = std::max(smax, s);
     plan->active_units += s * p->num_kv_heads;
-  }
-  if (smax > 65535 * 16) {  // grid x limit with headroom; unreachable for sane sizes
-    delete plan;
-    return DA_ERR_UNSUPPORTED;
   }
   plan->max_splits = static_cast<int32_t>(smax);
 

@@ -55,17 +55,17 @@ __global__ __launch_bounds__(kThreads) void read_chunk_kernel(const uint4* __res
 }
 
 // Gather pattern of a shuffled page pool: work-group w reads blocks
-// perm[w * per_wg + i] (4 KiB each) for i < per_wg, one wave per block per
-// trip, 4 x 16-byte loads per lane per block.
-template <bool NT>
+// perm[w * per_wg + i] (UNITS x 4 KiB each) for i < per_wg, one wave per
+// 4 KiB piece per trip, 4 x 16-byte loads per lane per piece.
+template <bool NT, int UNITS>
 __global__ __launch_bounds__(kThreads) void read_blocks_kernel(const u32x4* __restrict__ src, const int* perm,
                                                                int per_wg, int nblocks, uint32_t* sink) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t acc = 0;
-  for (int i = wave; i < per_wg; i += 4) {
-    const int idx = blockIdx.x * per_wg + i;
+  for (int i = wave; i < per_wg * UNITS; i += 4) {
+    const int idx = blockIdx.x * per_wg + i / UNITS;
     if (idx >= nblocks) break;
-    const u32x4* blk = src + static_cast<size_t>(perm[idx]) * 256;
+    const u32x4* blk = src + (static_cast<size_t>(perm[idx]) * UNITS + i % UNITS) * 256;
     u32x4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = NT ? __builtin_nontemporal_load(blk + u * 64 + lane) : blk[u * 64 + lane];
@@ -116,22 +116,44 @@ int da_probe_read_cfg(const void* src, size_t bytes, uint32_t* sink, int blocks,
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
+// As da_probe_read_blocks with blocks of `units` x 4 KiB (units 1, 2, 4 or 8);
+// perm values < bytes / (units * 4096).
+int da_probe_read_blocks_ex(const void* src, const int* perm, int nblocks, int per_wg, int nt, int units,
+                            uint32_t* sink, void* stream) {
+  if (!src || !perm || !sink || nblocks < 1 || per_wg < 1) return 1;
+  (void)hipGetLastError();
+  const int grid = (nblocks + per_wg - 1) / per_wg;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4* p = static_cast<const u32x4*>(src);
+#define DA_PROBE_LAUNCH(NTV, U) \
+  hipLaunchKernelGGL((read_blocks_kernel<NTV, U>), dim3(grid), dim3(kThreads), 0, st, p, perm, per_wg, nblocks, sink)
+  if (nt) {
+    switch (units) {
+      case 1: DA_PROBE_LAUNCH(true, 1); break;
+      case 2: DA_PROBE_LAUNCH(true, 2); break;
+      case 4: DA_PROBE_LAUNCH(true, 4); break;
+      case 8: DA_PROBE_LAUNCH(true, 8); break;
+      default: return 1;
+    }
+  } else {
+    switch (units) {
+      case 1: DA_PROBE_LAUNCH(false, 1); break;
+      case 2: DA_PROBE_LAUNCH(false, 2); break;
+      case 4: DA_PROBE_LAUNCH(false, 4); break;
+      case 8: DA_PROBE_LAUNCH(false, 8); break;
+      default: return 1;
+    }
+  }
+#undef DA_PROBE_LAUNCH
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 // Read `nblocks` 4 KiB blocks of `src` in the order of `perm` (device int32,
 // values < bytes / 4096), `per_wg` blocks per work-group; nt != 0 uses
 // nontemporal loads. The sink must hold ceil(nblocks / per_wg) * 256 uint32.
 int da_probe_read_blocks(const void* src, const int* perm, int nblocks, int per_wg, int nt, uint32_t* sink,
                          void* stream) {
-  if (!src || !perm || !sink || nblocks < 1 || per_wg < 1) return 1;
-  (void)hipGetLastError();
-  const int grid = (nblocks + per_wg - 1) / per_wg;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (nt)
-    hipLaunchKernelGGL(read_blocks_kernel<true>, dim3(grid), dim3(kThreads), 0, st, static_cast<const u32x4*>(src),
-                       perm, per_wg, nblocks, sink);
-  else
-    hipLaunchKernelGGL(read_blocks_kernel<false>, dim3(grid), dim3(kThreads), 0, st, static_cast<const u32x4*>(src),
-                       perm, per_wg, nblocks, sink);
-  return hipGetLastError() == hipSuccess ? 0 : 2;
+  return da_probe_read_blocks_ex(src, perm, nblocks, per_wg, nt, 1, sink, stream);
 }
 
 // Copy `bytes` (a multiple of 16, both pointers 16-byte aligned); 0 on success.
