@@ -61,9 +61,10 @@ da_status prepare(const da_plan* plan, const void* q, const void* k_pool, const 
   a->page_table = page_table;
   a->seq_lens = seq_lens;
   a->out = out;
-  a->ws_o = static_cast<float*>(workspace);
-  a->ws_ml = plan->ws_bytes > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_ml_offset)
-                                : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  const bool has_ws = plan->ws_bytes > 0;
+  a->ws_o = has_ws ? reinterpret_cast<float*>(ws + plan->ws_o_offset) : nullptr;
+  a->ws_ml = has_ws ? reinterpret_cast<float*>(ws + plan->ws_ml_offset) : nullptr;
   a->batch = p.batch;
   a->num_q_heads = p.num_q_heads;
   a->num_kv_heads = p.num_kv_heads;
@@ -171,7 +172,7 @@ da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out
   const da_params& p = plan->p;
   a.seq_lens = seq_lens;
   a.out = out;
-  a.ws_o = static_cast<float*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_o_offset);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_ml_offset);
   a.batch = p.batch;
   a.num_q_heads = p.num_q_heads;

@@ -16,34 +16,11 @@
 #include <cstdint>
 
 #include "decode_attn.h"
+#include "device_common.h"
 #include "kernels.h"
 
 namespace da {
 namespace {
-
-__device__ __forceinline__ void store_out(void* base, int64_t idx, int dtype, float x) {
-  if (dtype == DA_F32) {
-    static_cast<float*>(base)[idx] = x;
-  } else if (dtype == DA_F16) {
-    static_cast<_Float16*>(base)[idx] = static_cast<_Float16>(x);
-  } else {
-    uint32_t u = __float_as_uint(x);
-    uint32_t r = (x != x) ? 0x7fc00000u : u + 0x7fffu + ((u >> 16) & 1u);
-    static_cast<uint16_t*>(base)[idx] = static_cast<uint16_t>(r >> 16);
-  }
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
 
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(const KernelArgs a) {
@@ -61,30 +38,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const KernelArgs a) {
   if (nsplit > a.max_splits) nsplit = a.max_splits;
   if (nsplit <= 1) return;  // the split pass wrote this row
 
-  const int64_t base = (static_cast<int64_t>(b) * a.num_q_heads + h) * a.max_splits;
-  const float* ml = a.ws_ml + base * 2;
-  const float* os = a.ws_o + base * D;
-
-  float M = -INFINITY;
-  for (int64_t s = lane; s < nsplit; s += 64) M = fmaxf(M, ml[s * 2]);
-  M = wave_max(M);
-  const float Mu = (M == -INFINITY) ? 0.0f : M;
-
-  float lsum = 0.0f;
-  for (int64_t s = lane; s < nsplit; s += 64) lsum += __builtin_amdgcn_exp2f(ml[s * 2] - Mu) * ml[s * 2 + 1];
-  lsum = wave_sum(lsum);
-
-  float acc[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-  for (int64_t s = 0; s < nsplit; ++s) {
-    const float w = __builtin_amdgcn_exp2f(ml[s * 2] - Mu);
-#pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = fmaf(w, os[s * D + lane + 64 * i], acc[i]);
-  }
-  const int64_t row = (static_cast<int64_t>(b) * a.num_q_heads + h) * D;
-#pragma unroll
-  for (int i = 0; i < N; ++i) store_out(a.out, row + lane + 64 * i, a.out_dtype, lsum > 0.0f ? acc[i] / lsum : 0.0f);
+  merge_head_wave<D>(a, b, h, static_cast<int>(nsplit), lane);
 }
 
 }  // namespace

@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "decode_attn.h"
+#include "kernels.h"
 
 #ifndef DA_NT_LOADS
 #define DA_NT_LOADS 1
@@ -166,6 +167,94 @@ __device__ __forceinline__ void merge_into(float& m, float& l, float* o, float m
 #pragma unroll
   for (int i = 0; i < N; ++i) o[i] = o[i] * a1 + o2[i] * a2;
   m = M;
+}
+
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ float ldf(const float* p) { return *p; }
+
+// Merge the nsplit states of query head h of sequence b into its output row
+// (one wave; lane i owns elements i, i + 64, ...):
+//     M = max_s m_s,  w_s = 2^(m_s - M),  out = sum_s w_s O_s / sum_s w_s l_s
+// A state with m_s = -inf gets weight 0. Lane s holds (m_s, l_s) of each chunk
+// of 64 splits; the O rows of the first BATCH splits are loaded together with
+// them (one memory round trip when nsplit <= BATCH), later rows BATCH at a
+// time; the weights are broadcast with readlane. The order of every sum is
+// fixed, so results are identical run to run.
+template <int D>
+__device__ void merge_head_wave(const KernelArgs& a, int b, int h, int nsplit, int lane) {
+  constexpr int N = D / 64;
+  constexpr int BATCH = 16;
+  const int64_t base = (static_cast<int64_t>(b) * a.num_q_heads + h) * a.max_splits;
+  const float* ml = a.ws_ml + base * 2;
+  const float* os = a.ws_o + base * D;
+  auto load_rows = [&](float (&ov)[BATCH][N], int first, int cnt) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j)
+      if (j < cnt)
+#pragma unroll
+        for (int i = 0; i < N; ++i) ov[j][i] = ldf(os + static_cast<int64_t>(first + j) * D + lane + 64 * i);
+  };
+
+  float ov[BATCH][N];
+  load_rows(ov, 0, nsplit < BATCH ? nsplit : BATCH);
+  float m0 = -INFINITY, l0 = 0.0f;  // state `lane` of the first chunk
+  if (lane < nsplit) {
+    m0 = ldf(ml + 2 * lane);
+    l0 = ldf(ml + 2 * lane + 1);
+  }
+  float M = m0;
+  for (int s = 64 + lane; s < nsplit; s += 64) M = fmaxf(M, ldf(ml + 2 * s));
+  M = wave_max(M);
+  const float Mu = (M == -INFINITY) ? 0.0f : M;
+
+  float lsum = 0.0f;
+  float acc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    float mk = m0, lk = l0;
+    if (s0 > 0) {
+      mk = -INFINITY;
+      lk = 0.0f;
+      if (s0 + lane < nsplit) {
+        mk = ldf(ml + 2 * (s0 + lane));
+        lk = ldf(ml + 2 * (s0 + lane) + 1);
+      }
+    }
+    float w = 0.0f;
+    if (s0 + lane < nsplit) {
+      w = exp2_fast(mk - Mu);
+      lsum += w * lk;
+    }
+    const int cnt = nsplit - s0 < 64 ? nsplit - s0 : 64;
+    for (int j0 = 0; j0 < cnt; j0 += BATCH) {
+      if (s0 + j0 > 0) load_rows(ov, s0 + j0, cnt - j0);
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        if (j0 + j < cnt) {
+          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + j));
+#pragma unroll
+          for (int i = 0; i < N; ++i) acc[i] = fmaf(wj, ov[j][i], acc[i]);
+        }
+      }
+    }
+  }
+  lsum = wave_sum(lsum);
+  const int64_t row = (static_cast<int64_t>(b) * a.num_q_heads + h) * D;
+#pragma unroll
+  for (int i = 0; i < N; ++i) store_elem(a.out, row + lane + 64 * i, a.out_dtype, lsum > 0.0f ? acc[i] / lsum : 0.0f);
 }
 
 }  // namespace

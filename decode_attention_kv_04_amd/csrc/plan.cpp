@@ -166,8 +166,8 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
 
   if (smax > 1) {
     const size_t rows = static_cast<size_t>(p->batch) * p->num_q_heads * smax;
-    plan->ws_o_bytes = round_up(rows * p->head_dim * sizeof(float), 256);
-    plan->ws_ml_offset = plan->ws_o_bytes;
+    plan->ws_o_offset = 0;
+    plan->ws_ml_offset = plan->ws_o_offset + round_up(rows * p->head_dim * sizeof(float), 256);
     plan->ws_bytes = plan->ws_ml_offset + round_up(rows * 2 * sizeof(float), 256);
   }
 

@@ -20,7 +20,7 @@ struct da_plan {
   std::vector<int32_t> splits; // S_b per sequence
   int64_t active_units = 0;
   int64_t attended_keys = 0;
-  size_t ws_o_bytes = 0;       // [B][H_q][S_max][D] float
+  size_t ws_o_offset = 0;      // [B][H_q][S_max][D] float
   size_t ws_ml_offset = 0;     // [B][H_q][S_max][2] float (m, l) after the O block
   size_t ws_bytes = 0;
 };

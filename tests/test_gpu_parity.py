@@ -205,6 +205,36 @@ def test_two_phase_api_equals_run(gpu, kernel):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_reused_workspace_many_calls(gpu, kernel):
+    """One workspace across many runs, two plans and the two-phase API in
+    between: every call gives the same bits."""
+    from decode_attention_kv_04_amd import binding
+    from gpu_util import split_kernel, TORCH_DT
+    spec = wl.LLAMA8B_3060.replace(batch=3, lengths=("list", (3060, 1000, 17)))
+    w = make(spec, gpu)
+    ref, _ = run_lib(w, num_splits=7, kernel=kernel)
+    params = binding.params_for(w.q, w.k_pool, w.page_table, scale=w.scale, num_splits=7)
+    with split_kernel(kernel):
+        plan = binding.decode_attn_plan(params, w.seq_lens_host)
+        plan5 = binding.decode_attn_plan(binding.params_for(w.q, w.k_pool, w.page_table, scale=w.scale,
+                                                            num_splits=5), w.seq_lens_host)
+    ws = torch.full((max(plan.workspace_bytes, plan5.workspace_bytes),), 0xFF, dtype=torch.uint8, device=gpu)
+    out = torch.empty_like(w.q)
+    for i in range(6):
+        p = plan if i % 2 == 0 else plan5
+        out.fill_(float("nan"))
+        binding.decode_attn_run(p, w.q, w.k_pool, w.v_pool, w.page_table, w.seq_lens, out, ws)
+        if i == 3:
+            binding.decode_attn_split(p, w.q, w.k_pool, w.v_pool, w.page_table, w.seq_lens, out, ws)
+            binding.decode_attn_combine(p, w.seq_lens, out, ws)
+        torch.cuda.synchronize()
+        if p is plan:
+            assert torch.equal(out, ref)
+        else:
+            check(out, oracle_for(w), "f16", "f16", f"reuse {i}")
+
+
 def test_vector_and_matrix_kernels_agree(gpu):
     """The two split kernels on the same inputs: within fp32 rounding."""
     spec = wl.LLAMA8B_3060.replace(batch=4, lengths=("list", (3060, 5000, 17, 999)), out_dtype="f32")
