@@ -16,3 +16,4 @@ from .attention_f64 import (  # noqa: F401
     round_to,
     shard_state,
 )
+from .paged_cache import append_kv  # noqa: F401,E402
