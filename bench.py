@@ -156,6 +156,43 @@ def cpu_baseline(w, budget_s=12.0):
     }
 
 
+def measure_append(w, lib, params, stream, tokens, iters):
+    """Time decode_attn_append_kv writing `tokens` rows per sequence at the
+    end of each sequence's context (positions L-T .. L-1), with new rows equal
+    to the rows already there, so the pools keep their contents. Returns
+    {tokens, us, GB_s} where the bytes are the rows read plus the rows written."""
+    import ctypes as C
+
+    import torch
+    P = w.spec.page_size
+    dev = w.q.device
+    L = w.seq_lens.long()
+    pos = L[:, None] - tokens + torch.arange(tokens, device=dev)[None, :]          # [B][T]
+    valid = pos >= 0
+    posc = pos.clamp(min=0)
+    pages = w.page_table.long().gather(1, posc // P)
+    slots = posc % P
+    k_new = w.k_pool[pages, :, slots].contiguous()                                  # [B][T][H_kv][D]
+    v_new = w.v_pool[pages, :, slots].contiguous()
+    before = (L - tokens).to(torch.int32).contiguous()
+    rows = int(valid.sum().item())
+    row_bytes = w.spec.num_kv_heads * w.spec.head_dim * w.k_pool.element_size()
+    sptr = stream.cuda_stream
+    args = (C.byref(params), tokens, k_new.data_ptr(), v_new.data_ptr(), w.page_table.data_ptr(),
+            before.data_ptr(), w.k_pool.data_ptr(), w.v_pool.data_ptr(), sptr)
+
+    def append():
+        st = lib.decode_attn_append_kv(*args)
+        if st != 0:
+            raise RuntimeError(f"decode_attn_append_kv: status {st}")
+
+    append()
+    ms = time_on_stream(append, iters, stream)
+    moved = rows * row_bytes * 2 * 2
+    return {"tokens": tokens, "us": round(ms * 1e3, 2), "GB_s": round(moved / (ms * 1e-3) / 1e9, 1),
+            "bytes": moved}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +271,10 @@ def main():
     split_ms = time_on_stream(split_only, args.steps, stream)
     combine_ms = time_on_stream(combine_only, args.steps, stream) if plan.max_splits > 1 else 0.0
 
+    # K/V append (the step before the path): one token per sequence, and a
+    # 256-token suffix; written rows equal the resident rows.
+    append_stats = [measure_append(w, lib, params, stream, t, args.steps) for t in (1, 256)]
+
     ceilings = {}
     if not args.no_ceiling:
         ceilings = measure_ceilings(dev, sptr, stream)
@@ -282,6 +323,7 @@ def main():
             "avg_launch_us": round(split_ms * 1e3, 2),
         },
         "combine_us": round(combine_ms * 1e3, 2),
+        "append_kv": append_stats,
         "plan_host_us": round(plan_us, 1),
         "hbm_read_ceiling_GBps": ceilings.get("stream"),
         "gather4k_read_ceiling_GBps": ceilings.get("gather4k"),

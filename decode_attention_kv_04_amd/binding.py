@@ -20,8 +20,8 @@ DTYPE_CODES = {"f32": DA_F32, "f16": DA_F16, "bf16": DA_BF16}
 # Every symbol include/decode_attn.h declares.
 EXPORTS = (
     "decode_attn_plan", "decode_attn_plan_for_cus", "decode_attn_plan_info", "decode_attn_plan_splits",
-    "decode_attn_run", "decode_attn_split", "decode_attn_combine", "decode_attn_plan_destroy",
-    "decode_attn_status_str",
+    "decode_attn_run", "decode_attn_split", "decode_attn_combine", "decode_attn_append_kv",
+    "decode_attn_plan_destroy", "decode_attn_status_str",
 )
 
 
@@ -79,12 +79,13 @@ def load() -> ctypes.CDLL:
     lib.decode_attn_run.argtypes = run_args
     lib.decode_attn_split.argtypes = run_args
     lib.decode_attn_combine.argtypes = [vp, vp, vp, vp, sz, vp]
+    lib.decode_attn_append_kv.argtypes = [ctypes.POINTER(Params), i32, vp, vp, vp, vp, vp, vp, vp]
     lib.decode_attn_plan_destroy.argtypes = [vp]
     lib.decode_attn_plan_destroy.restype = None
     lib.decode_attn_status_str.argtypes = [ctypes.c_int]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
     for name in ("decode_attn_plan", "decode_attn_plan_for_cus", "decode_attn_plan_info", "decode_attn_run",
-                 "decode_attn_split", "decode_attn_combine"):
+                 "decode_attn_split", "decode_attn_combine", "decode_attn_append_kv"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -225,6 +226,15 @@ def decode_attn_combine(plan: Plan, seq_lens, out, workspace=None, stream=None):
                                     _stream(stream))
     if st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_combine")
+
+
+def decode_attn_append_kv(params: Params, k_new, v_new, page_table, seq_lens, k_pool, v_pool, stream=None):
+    """Write k_new / v_new ([B][T][H_kv][D]) after each sequence's seq_lens keys."""
+    tokens = int(k_new.shape[1]) if k_new is not None else 0
+    st = load().decode_attn_append_kv(ctypes.byref(params), tokens, _ptr(k_new), _ptr(v_new), _ptr(page_table),
+                                      _ptr(seq_lens), _ptr(k_pool), _ptr(v_pool), _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_append_kv")
 
 
 def params_for(q, k_pool, page_table, *, window=0, scale=None, out_dtype=None, num_splits=0) -> Params:

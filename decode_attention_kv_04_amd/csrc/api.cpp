@@ -188,6 +188,36 @@ da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out
   return enqueue(plan, a, false, true, stream);
 }
 
+da_status decode_attn_append_kv(const da_params* p, int32_t tokens, const void* k_new, const void* v_new,
+                                const int32_t* page_table, const int32_t* seq_lens, void* k_pool, void* v_pool,
+                                void* stream) {
+  if (!p || tokens < 0 || p->batch < 0 || p->num_kv_heads < 1 || p->page_size < 1 || p->max_pages_per_seq < 1)
+    return DA_ERR_INVALID;
+  if (p->kv_dtype != DA_F32 && p->kv_dtype != DA_F16 && p->kv_dtype != DA_BF16) return DA_ERR_INVALID;
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return DA_ERR_UNSUPPORTED;
+  if (p->batch > 65535 || tokens > 2147483647 / 2) return DA_ERR_UNSUPPORTED;
+  if (p->batch == 0 || tokens == 0) return DA_OK;
+  if (!k_new || !v_new || !page_table || !seq_lens || !k_pool || !v_pool) return DA_ERR_INVALID;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return DA_ERR_INVALID;
+  if (!aligned(page_table, 4) || !aligned(seq_lens, 4)) return DA_ERR_INVALID;
+  da::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.batch = p->batch;
+  a.tokens = tokens;
+  a.num_kv_heads = p->num_kv_heads;
+  a.page_size = p->page_size;
+  a.max_pages = p->max_pages_per_seq;
+  a.row_bytes = p->head_dim * (p->kv_dtype == DA_F32 ? 4 : 2);
+  (void)hipGetLastError();
+  if (da::launch_append(a, static_cast<hipStream_t>(stream)) != hipSuccess) return DA_ERR_HIP;
+  return DA_OK;
+}
+
 void decode_attn_plan_destroy(da_plan_t plan) { delete plan; }
 
 const char* decode_attn_status_str(da_status s) {

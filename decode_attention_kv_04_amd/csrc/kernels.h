@@ -31,6 +31,25 @@ struct KernelArgs {
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units
 };
 
+// Arguments of the K/V append.
+struct AppendArgs {
+  const void* k_new;  // [B][T][H_kv][D]
+  const void* v_new;
+  const int32_t* page_table;
+  const int32_t* seq_lens;  // keys before the append
+  void* k_pool;
+  void* v_pool;
+  int32_t batch;
+  int32_t tokens;  // T
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t row_bytes;  // D * elt, a multiple of 16
+};
+
+// Enqueue the K/V append (grid T x B) on `stream`.
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
 // Enqueue the split pass on `stream`. Returns hipSuccess or the launch error;
 // hipErrorInvalidValue if no kernel is compiled for (head_dim, kv_dtype,
 // group_tile).

@@ -267,3 +267,18 @@ def to_numpy_inputs(w: Workload, rows: Optional[Sequence[int]] = None) -> dict:
                 k_pool=host(w.k_pool[idx]), v_pool=host(w.v_pool[idx]),
                 page_table=new_table, seq_lens=np.array([lens[b] for b in rows], dtype=np.int64),
                 page_size=P, scale=w.scale, window=w.window)
+
+
+def make_new_rows(spec: WorkloadSpec, tokens: int, device="cpu", salt: int = 1):
+    """K and V rows for ``tokens`` new tokens per sequence, [B][T][H_kv][D] in
+    the KV dtype, N(0,1) drawn on ``device`` from a generator seeded by the
+    spec's seed and ``salt``."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(spec.seed * 1_000_003 + 7919 * salt + 5)
+    shape = (spec.batch, tokens, spec.num_kv_heads, spec.head_dim)
+    kv_t = DTYPES[spec.kv_dtype]
+    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(kv_t)
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(kv_t)
+    return k, v
+

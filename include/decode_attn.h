@@ -167,6 +167,28 @@ da_status decode_attn_split(da_plan_t plan, const void* q, const void* k_pool, c
 da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * decode_attn_append_kv: write T new K and V rows per sequence into the paged
+ * cache, after the keys it already holds (llm-web pull 8, commit on the
+ * batched suffix prefill: the new tokens' K/V are scattered at an offset
+ * equal to the resident prefix). For every b, t < T and KV head j, with
+ * pos = seq_lens[b] + t:
+ *     k_pool[page_table[b][pos / P]][j][pos % P][:] = k_new[b][t][j][:]
+ * and the same for V. No other byte of the pools changes.
+ *   p         uses batch, num_kv_heads, head_dim, page_size,
+ *             max_pages_per_seq and kv_dtype (the other fields are ignored).
+ *   k_new, v_new  [B][T][H_kv][D] kv_dtype, 16-byte aligned.
+ *   seq_lens  [B] int32, keys before the append (not updated here; the
+ *             caller adds T for the next step).
+ *   page_table must map every page the new rows land in; a row whose
+ *   position is negative or >= max_pages_per_seq * P is skipped.
+ * Enqueues one kernel on `stream`; no allocation, no host synchronisation.
+ * Returns DA_ERR_INVALID / DA_ERR_UNSUPPORTED for bad arguments.
+ */
+da_status decode_attn_append_kv(const da_params* p, int32_t tokens, const void* k_new, const void* v_new,
+                                const int32_t* page_table, const int32_t* seq_lens, void* k_pool, void* v_pool,
+                                void* stream);
+
 /* decode_attn_plan_destroy: free a plan (NULL is ignored). */
 void decode_attn_plan_destroy(da_plan_t plan);
 

@@ -252,3 +252,35 @@ def test_combine_argument_errors_and_noop(lib):
 def test_empty_batch_runs_without_launching(lib):
     pl = plan(params(batch=0), [])
     assert raw_run("decode_attn_run", pl, q=None, k=None, v=None, table=None, lens=None, out=None) == B.DA_OK
+
+
+# ---------------------------------------------------------------------------
+# K/V append argument errors (decided before any launch)
+# ---------------------------------------------------------------------------
+
+def raw_append(p, tokens=1, kn=FAKE, vn=FAKE, table=FAKE, lens=FAKE, kp=FAKE, vp=FAKE):
+    return B.load().decode_attn_append_kv(ctypes.byref(p) if p is not None else None, tokens, kn, vn, table,
+                                          lens, kp, vp, None)
+
+
+def test_append_argument_errors(lib):
+    p = params(batch=2)
+    assert raw_append(None) == B.DA_ERR_INVALID
+    assert raw_append(p, tokens=-1) == B.DA_ERR_INVALID
+    for name in ("kn", "vn", "table", "lens", "kp", "vp"):
+        assert raw_append(p, **{name: None}) == B.DA_ERR_INVALID, name
+    for name in ("kn", "vn", "kp", "vp"):
+        assert raw_append(p, **{name: FAKE + 8}) == B.DA_ERR_INVALID, name
+    for name in ("table", "lens"):
+        assert raw_append(p, **{name: FAKE + 2}) == B.DA_ERR_INVALID, name
+    assert raw_append(params(batch=2, head_dim=96)) == B.DA_ERR_UNSUPPORTED
+    assert raw_append(params(batch=2, num_kv_heads=0)) == B.DA_ERR_INVALID
+    assert raw_append(params(batch=70000)) == B.DA_ERR_UNSUPPORTED
+    bad = params(batch=2)
+    bad.kv_dtype = 7
+    assert raw_append(bad) == B.DA_ERR_INVALID
+
+
+def test_append_nothing_to_write_launches_nothing(lib):
+    assert raw_append(params(batch=2), tokens=0, kn=None, vn=None, table=None, lens=None, kp=None, vp=None) == B.DA_OK
+    assert raw_append(params(batch=0), tokens=3, kn=None, vn=None, table=None, lens=None, kp=None, vp=None) == B.DA_OK
