@@ -156,6 +156,37 @@ def cpu_baseline(w, budget_s=12.0):
     }
 
 
+FIXED_CHUNK = 1024
+
+
+def measure_fixed_order(w, binding, lib, dev, stream, iters):
+    """Time decode_attn_run in the fixed-order mode (planner-chosen chunks per
+    work-group) on the workload; {chunk_tokens, us, GB_s, chunks_per_work_group}."""
+    import torch
+    spec = w.spec
+    params = binding.params_for(w.q, w.k_pool, w.page_table, window=w.window, scale=w.scale,
+                                out_dtype=spec.out_dtype, fixed_chunk=FIXED_CHUNK)
+    plan = binding.decode_attn_plan(params, w.seq_lens_host, device=dev.index or 0)
+    out = torch.empty(w.q.shape, dtype={"f32": torch.float32, "f16": torch.float16,
+                                        "bf16": torch.bfloat16}[spec.out_dtype], device=dev)
+    ws = binding.alloc_workspace(plan, dev)
+    ptrs = [w.q.data_ptr(), w.k_pool.data_ptr(), w.v_pool.data_ptr(), w.page_table.data_ptr(),
+            w.seq_lens.data_ptr(), out.data_ptr(), ws.data_ptr(), plan.workspace_bytes, stream.cuda_stream]
+
+    def run():
+        st = lib.decode_attn_run(plan.handle, *ptrs)
+        if st != 0:
+            raise binding.DecodeAttnError(st, "decode_attn_run (fixed order)")
+
+    for _ in range(3):
+        run()
+    ms = time_on_stream(run, iters, stream)
+    return {"chunk_tokens": FIXED_CHUNK, "us": round(ms * 1e3, 2),
+            "GB_s": round(w.kv_bytes() / (ms * 1e-3) / 1e9, 1),
+            "chunks_per_work_group": plan.info.chunks_per_work_group,
+            "work_groups": plan.info.split_work_groups}
+
+
 def measure_append(w, lib, params, stream, tokens, iters):
     """Time decode_attn_append_kv writing `tokens` rows per sequence at the
     end of each sequence's context (positions L-T .. L-1), with new rows equal
@@ -271,6 +302,10 @@ def main():
     split_ms = time_on_stream(split_only, args.steps, stream)
     combine_ms = time_on_stream(combine_only, args.steps, stream) if plan.max_splits > 1 else 0.0
 
+    # The fixed-order mode (output bitwise independent of the split count) on
+    # the same batch: whole step, chunks of FIXED_CHUNK tokens.
+    fixed = measure_fixed_order(w, binding, lib, dev, stream, args.steps)
+
     # K/V append (the step before the path): one token per sequence, and a
     # 256-token suffix; written rows equal the resident rows.
     append_stats = [measure_append(w, lib, params, stream, t, args.steps) for t in (1, 256)]
@@ -323,6 +358,7 @@ def main():
             "avg_launch_us": round(split_ms * 1e3, 2),
         },
         "combine_us": round(combine_ms * 1e3, 2),
+        "fixed_order": fixed,
         "append_kv": append_stats,
         "plan_host_us": round(plan_us, 1),
         "hbm_read_ceiling_GBps": ceilings.get("stream"),

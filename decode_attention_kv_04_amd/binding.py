@@ -37,7 +37,7 @@ class Params(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("window", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
-        ("num_splits", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32), ("fixed_chunk", ctypes.c_int32),
     ]
 
 
@@ -46,7 +46,7 @@ class PlanInfo(ctypes.Structure):
         ("pages_per_split", ctypes.c_int32), ("max_splits", ctypes.c_int32), ("num_cus", ctypes.c_int32),
         ("split_work_groups", ctypes.c_int32), ("active_units", ctypes.c_int64),
         ("attended_keys", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-        ("split_kernel", ctypes.c_int32),
+        ("split_kernel", ctypes.c_int32), ("chunks_per_work_group", ctypes.c_int32),
     ]
 
 
@@ -99,13 +99,14 @@ decode_attn_status_str = status_str
 
 
 def make_params(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, *, window=0,
-                scale=None, q_dtype="f16", kv_dtype="f16", out_dtype="f16", num_splits=0) -> Params:
+                scale=None, q_dtype="f16", kv_dtype="f16", out_dtype="f16", num_splits=0,
+                fixed_chunk=0) -> Params:
     def code(t):
         return DTYPE_CODES[t] if isinstance(t, str) else int(t)
     return Params(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                   int(max_pages_per_seq), int(window),
                   float(scale if scale is not None else (head_dim ** -0.5 if head_dim > 0 else 1.0)),
-                  code(q_dtype), code(kv_dtype), code(out_dtype), int(num_splits))
+                  code(q_dtype), code(kv_dtype), code(out_dtype), int(num_splits), int(fixed_chunk))
 
 
 class Plan:
@@ -237,7 +238,8 @@ def decode_attn_append_kv(params: Params, k_new, v_new, page_table, seq_lens, k_
         raise DecodeAttnError(st, "decode_attn_append_kv")
 
 
-def params_for(q, k_pool, page_table, *, window=0, scale=None, out_dtype=None, num_splits=0) -> Params:
+def params_for(q, k_pool, page_table, *, window=0, scale=None, out_dtype=None, num_splits=0,
+               fixed_chunk=0) -> Params:
     """da_params from tensor shapes and dtypes."""
     import torch
     names = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
@@ -246,7 +248,7 @@ def params_for(q, k_pool, page_table, *, window=0, scale=None, out_dtype=None, n
     assert D == D2, "q and the pools disagree on head_dim"
     return make_params(B, Hq, Hkv, D, P, page_table.shape[1], window=window, scale=scale,
                        q_dtype=names[q.dtype], kv_dtype=names[k_pool.dtype],
-                       out_dtype=out_dtype or names[q.dtype], num_splits=num_splits)
+                       out_dtype=out_dtype or names[q.dtype], num_splits=num_splits, fixed_chunk=fixed_chunk)
 
 
 def alloc_workspace(plan: Plan, device):
@@ -258,11 +260,11 @@ def alloc_workspace(plan: Plan, device):
 
 
 def decode_attention(q, k_pool, v_pool, page_table, seq_lens, seq_lens_host=None, *, window=0, scale=None,
-                     out_dtype=None, num_splits=0, out=None, workspace=None, stream=None):
+                     out_dtype=None, num_splits=0, fixed_chunk=0, out=None, workspace=None, stream=None):
     """Plan, allocate (output and workspace, through torch) and run one step."""
     import torch
     params = params_for(q, k_pool, page_table, window=window, scale=scale, out_dtype=out_dtype,
-                        num_splits=num_splits)
+                        num_splits=num_splits, fixed_chunk=fixed_chunk)
     host = seq_lens_host if seq_lens_host is not None else seq_lens.cpu()
     plan = decode_attn_plan(params, host, device=q.device.index)
     dt = {DA_F32: torch.float32, DA_F16: torch.float16, DA_BF16: torch.bfloat16}[params.out_dtype]

@@ -74,11 +74,17 @@ da_status prepare(const da_plan* plan, const void* q, const void* k_pool, const 
   a->window = p.window;
   a->pages_per_split = plan->pages_per_split;
   a->max_splits = plan->max_splits;
+  a->chunks_per_group = plan->chunks_per_group;
+  a->split_groups = plan->split_groups;
   a->q_dtype = p.q_dtype;
   a->out_dtype = p.out_dtype;
   a->scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
   return DA_OK;
 }
+
+// The combine pass runs when some sequence has several splits, and always in
+// the fixed-order mode (every row goes through the chunk-order merge).
+bool needs_combine(const da_plan* plan) { return plan->max_splits > 1 || plan->chunks_per_group > 0; }
 
 da_status enqueue(const da_plan* plan, const da::KernelArgs& a, bool split, bool combine, void* stream) {
   if (plan->p.batch == 0) return DA_OK;
@@ -90,7 +96,7 @@ da_status enqueue(const da_plan* plan, const da::KernelArgs& a, bool split, bool
                              : da::launch_split(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st);
     if (e != hipSuccess) return DA_ERR_HIP;
   }
-  if (combine && plan->max_splits > 1) {
+  if (combine && needs_combine(plan)) {
     if (da::launch_combine(a, plan->p.head_dim, st) != hipSuccess) return DA_ERR_HIP;
   }
   return DA_OK;
@@ -125,11 +131,12 @@ da_status decode_attn_plan_info(da_plan_t plan, da_plan_info* info) {
   info->pages_per_split = plan->pages_per_split;
   info->max_splits = plan->max_splits;
   info->num_cus = plan->num_cus;
-  info->split_work_groups = plan->max_splits * plan->p.num_kv_heads * plan->p.batch;
+  info->split_work_groups = plan->split_groups * plan->p.num_kv_heads * plan->p.batch;
   info->active_units = plan->active_units;
   info->attended_keys = plan->attended_keys;
   info->workspace_bytes = plan->ws_bytes;
   info->split_kernel = plan->split_kernel;
+  info->chunks_per_work_group = plan->chunks_per_group;
   return DA_OK;
 }
 
@@ -167,7 +174,7 @@ da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out
     if (!workspace || workspace_bytes < plan->ws_bytes) return DA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return DA_ERR_INVALID;
   }
-  if (plan->max_splits <= 1) return DA_OK;
+  if (!needs_combine(plan)) return DA_OK;
   da::KernelArgs a{};
   const da_params& p = plan->p;
   a.seq_lens = seq_lens;
@@ -183,6 +190,8 @@ da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out
   a.window = p.window;
   a.pages_per_split = plan->pages_per_split;
   a.max_splits = plan->max_splits;
+  a.chunks_per_group = plan->chunks_per_group;
+  a.split_groups = plan->split_groups;
   a.q_dtype = p.q_dtype;
   a.out_dtype = p.out_dtype;
   return enqueue(plan, a, false, true, stream);

@@ -8,6 +8,9 @@
 //     M = max_s m_s,  w_s = 2^(m_s - M),  out = sum_s w_s O_s / sum_s w_s l_s
 // A split with no attended key (m_s = -inf) gets weight 0 (never -inf minus
 // -inf). The order of the sums is fixed, so results are identical run to run.
+// In the fixed-order mode the states are those of fixed-length chunks, whose
+// count depends only on the sequence, so the merge is the same whatever the
+// number of split work-groups.
 //
 // One wave64 per (query head, sequence); lane i owns elements i, i+64, ... of
 // the row, so every load of O_s is one contiguous 256-byte-per-64-lane read.
@@ -36,7 +39,11 @@ __global__ __launch_bounds__(64) void combine_kernel(const KernelArgs a) {
   const int64_t pe = L > 0 ? (L + P - 1) / P : 0;
   int64_t nsplit = (pe - pf + a.pages_per_split - 1) / a.pages_per_split;
   if (nsplit > a.max_splits) nsplit = a.max_splits;
-  if (nsplit <= 1) return;  // the split pass wrote this row
+  if (a.chunks_per_group > 0) {
+    if (nsplit < 1) nsplit = 1;  // fixed-order mode: every row is merged here
+  } else if (nsplit <= 1) {
+    return;  // the split pass wrote this row
+  }
 
   merge_head_wave<D>(a, b, h, static_cast<int>(nsplit), lane);
 }

@@ -393,7 +393,8 @@ hipError_t launch_kv(const KernelArgs& a, int kv, int gt, dim3 grid, hipStream_t
 }  // namespace
 
 hipError_t launch_split_mfma(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream) {
-  const dim3 grid(a.num_kv_heads, a.max_splits, a.batch);
+  if (a.chunks_per_group > 0) return hipErrorInvalidValue;  // the fixed-order mode runs on the vector kernel
+  const dim3 grid(a.num_kv_heads, a.split_groups, a.batch);
   switch (head_dim) {
     case 128: return launch_kv<128>(a, kv_dtype, group_tile, grid, stream);
     default: return hipErrorInvalidValue;

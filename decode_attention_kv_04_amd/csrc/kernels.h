@@ -24,8 +24,10 @@ struct KernelArgs {
   int32_t page_size;
   int32_t max_pages;      // page-table row stride
   int32_t window;
-  int32_t pages_per_split;
-  int32_t max_splits;
+  int32_t pages_per_split;  // pages per split (fixed-order mode: per chunk)
+  int32_t max_splits;       // state slots per query head in the workspace
+  int32_t chunks_per_group; // 0 = default mode; else fixed-order mode, chunks per work-group
+  int32_t split_groups;     // split work-groups per (sequence, KV head)
   int32_t q_dtype;        // da_dtype
   int32_t out_dtype;      // da_dtype
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units

@@ -87,12 +87,84 @@ int32_t group_tile_for(int32_t G) {
   return 0;
 }
 
+namespace {
+
+// Pages per split that give the split pass about kTargetGroupsPerCu
+// work-groups per compute unit, at least the minimum split length.
+int64_t heuristic_split_pages(int64_t total_np, int64_t max_np, int64_t num_kv_heads, int64_t num_cus, int64_t P) {
+  const int64_t work = total_np * num_kv_heads;  // page-heads to stream
+  const int64_t target = num_cus * kTargetGroupsPerCu;
+  int64_t c = ceil_div(work, target);
+  c = std::max(c, ceil_div(min_split_tokens(), P));
+  return std::min(c, max_np);
+}
+
+// Workspace: O block [B][H_q][S_max][D] then (m, l) block [B][H_q][S_max][2].
+void size_workspace(da_plan* plan) {
+  const da_params& p = plan->p;
+  const size_t rows = static_cast<size_t>(p.batch) * p.num_q_heads * plan->max_splits;
+  plan->ws_o_offset = 0;
+  plan->ws_ml_offset = plan->ws_o_offset + round_up(rows * p.head_dim * sizeof(float), 256);
+  plan->ws_bytes = plan->ws_ml_offset + round_up(rows * 2 * sizeof(float), 256);
+}
+
+void log_plan(const da_plan* plan) {
+  if (!log_enabled()) return;
+  const da_params& p = plan->p;
+  std::fprintf(stderr,
+               "decode_attn plan: B=%d Hq=%d Hkv=%d D=%d P=%d W=%d kernel=%s cus=%d pages/split=%d "
+               "max_splits=%d split_groups=%d chunks/group=%d units=%lld keys=%lld ws=%zu\n",
+               p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size, p.window,
+               plan->split_kernel ? "matrix" : "vector", plan->num_cus, plan->pages_per_split, plan->max_splits,
+               plan->split_groups, plan->chunks_per_group, static_cast<long long>(plan->active_units),
+               static_cast<long long>(plan->attended_keys), plan->ws_bytes);
+}
+
+// Fixed-order mode: chunks of fixed_chunk / P pages from each sequence's
+// first attended page; a state slot per chunk; each split work-group takes
+// chunks_per_group consecutive chunks; the combine always runs.
+da_status finish_fixed_plan(da_plan* plan, const std::vector<int64_t>& npages, int64_t max_np, int64_t total_np) {
+  const da_params& p = plan->p;
+  const int64_t cp = p.fixed_chunk / p.page_size;
+  int64_t max_chunks = 1;
+  for (int64_t n : npages) max_chunks = std::max(max_chunks, ceil_div(n, cp));
+  if (max_chunks > INT32_MAX / 2) {
+    delete plan;
+    return DA_ERR_UNSUPPORTED;
+  }
+  int64_t cpg;
+  if (p.num_splits > 0) {
+    cpg = ceil_div(max_chunks, std::min<int64_t>(p.num_splits, max_chunks));
+  } else {
+    const int64_t c = max_np > 0 ? heuristic_split_pages(total_np, max_np, p.num_kv_heads, plan->num_cus,
+                                                         p.page_size)
+                                 : 1;
+    cpg = std::min(max_chunks, std::max<int64_t>(1, ceil_div(c, cp)));
+  }
+  cpg = std::max(cpg, ceil_div(max_chunks, 65535));  // the grid's y extent
+  plan->pages_per_split = static_cast<int32_t>(cp);
+  plan->max_splits = static_cast<int32_t>(max_chunks);
+  plan->chunks_per_group = static_cast<int32_t>(cpg);
+  plan->split_groups = static_cast<int32_t>(ceil_div(max_chunks, cpg));
+  plan->splits.resize(p.batch);
+  for (int32_t b = 0; b < p.batch; ++b) {
+    const int64_t nc = std::max<int64_t>(1, ceil_div(npages[b], cp));
+    plan->splits[b] = static_cast<int32_t>(nc);
+    plan->active_units += ceil_div(nc, cpg) * p.num_kv_heads;
+  }
+  size_workspace(plan);
+  log_plan(plan);
+  return DA_OK;
+}
+
+}  // namespace
+
 da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da_plan** out) {
   if (!p || !out) return DA_ERR_INVALID;
   if (p->batch < 0 || p->num_q_heads < 1 || p->num_kv_heads < 1) return DA_ERR_INVALID;
   if (p->num_q_heads % p->num_kv_heads != 0) return DA_ERR_INVALID;
   if (p->head_dim < 1 || p->page_size < 1) return DA_ERR_INVALID;
-  if (p->window < 0 || p->num_splits < 0) return DA_ERR_INVALID;
+  if (p->window < 0 || p->num_splits < 0 || p->fixed_chunk < 0) return DA_ERR_INVALID;
   if (!std::isfinite(p->scale)) return DA_ERR_INVALID;
   if (!valid_dtype(p->q_dtype) || !valid_dtype(p->kv_dtype) || !valid_dtype(p->out_dtype))
     return DA_ERR_INVALID;
@@ -107,6 +179,8 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   if (p->batch > 65535 || p->num_kv_heads > 65535) return DA_ERR_UNSUPPORTED;
 
   const int64_t P = p->page_size;
+  if (p->fixed_chunk % P != 0) return DA_ERR_INVALID;
+  const bool fixed = p->fixed_chunk > 0;
   const int64_t cap = static_cast<int64_t>(p->max_pages_per_seq) * P;
   // The kernels count tokens in int32, with a few tiles of headroom.
   if (cap > static_cast<int64_t>(INT32_MAX) - 4096) return DA_ERR_UNSUPPORTED;
@@ -123,7 +197,8 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // q.K as a 16 x 32 x 16 matrix-core product per 16-key tile whenever the
   // parameters allow it: with G query heads sharing the keys it is a dense
   // contraction, and it takes the dot products and lane sums off the VALU.
-  plan->split_kernel = matrix_kernel_supported(*p) && forced_kernel() != 0 ? 1 : 0;
+  // The fixed-order mode runs on the vector kernel.
+  plan->split_kernel = !fixed && matrix_kernel_supported(*p) && forced_kernel() != 0 ? 1 : 0;
 
   // Attended pages per sequence.
   std::vector<int64_t> npages(p->batch);
@@ -136,17 +211,19 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     plan->attended_keys += r.t1 - r.t0;
   }
 
+  if (fixed) {
+    const da_status st = finish_fixed_plan(plan, npages, max_np, total_np);
+    if (st == DA_OK) *out = plan;
+    return st;
+  }
+
   int64_t c;
   if (max_np == 0) {
     c = 1;
   } else if (p->num_splits > 0) {
     c = ceil_div(max_np, p->num_splits);
   } else {
-    const int64_t work = total_np * p->num_kv_heads;  // page-heads to stream
-    const int64_t target = static_cast<int64_t>(num_cus) * kTargetGroupsPerCu;
-    c = ceil_div(work, target);
-    c = std::max(c, ceil_div(min_split_tokens(), P));
-    c = std::min(c, max_np);
+    c = heuristic_split_pages(total_np, max_np, p->num_kv_heads, num_cus, P);
   }
   c = std::max<int64_t>(c, 1);
   // The split index is the grid's y dimension (at most 65535 splits).
@@ -163,24 +240,9 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     plan->active_units += s * p->num_kv_heads;
   }
   plan->max_splits = static_cast<int32_t>(smax);
-
-  if (smax > 1) {
-    const size_t rows = static_cast<size_t>(p->batch) * p->num_q_heads * smax;
-    plan->ws_o_offset = 0;
-    plan->ws_ml_offset = plan->ws_o_offset + round_up(rows * p->head_dim * sizeof(float), 256);
-    plan->ws_bytes = plan->ws_ml_offset + round_up(rows * 2 * sizeof(float), 256);
-  }
-
-  if (log_enabled()) {
-    std::fprintf(stderr,
-                 "decode_attn plan: B=%d Hq=%d Hkv=%d D=%d P=%d W=%d kernel=%s cus=%d pages/split=%lld "
-                 "max_splits=%lld units=%lld keys=%lld ws=%zu\n",
-                 p->batch, p->num_q_heads, p->num_kv_heads, p->head_dim, p->page_size, p->window,
-                 plan->split_kernel ? "matrix" : "vector",
-                 num_cus, static_cast<long long>(c), static_cast<long long>(smax),
-                 static_cast<long long>(plan->active_units), static_cast<long long>(plan->attended_keys),
-                 plan->ws_bytes);
-  }
+  plan->split_groups = plan->max_splits;
+  if (smax > 1) size_workspace(plan);
+  log_plan(plan);
   *out = plan;
   return DA_OK;
 }

@@ -15,8 +15,10 @@ struct da_plan {
   int32_t group_tile = 1;      // compiled group width the kernels use (1, 2, 4 or 8)
   int32_t split_kernel = 0;    // 0 = vector q.K, 1 = q.K on the matrix cores
   int32_t num_cus = 0;
-  int32_t pages_per_split = 1; // c
-  int32_t max_splits = 1;      // S_max
+  int32_t pages_per_split = 1; // c (fixed-order mode: pages per chunk)
+  int32_t max_splits = 1;      // S_max: state slots per query head (fixed-order mode: chunks)
+  int32_t chunks_per_group = 0;// fixed-order mode: chunks per split work-group (0 = default mode)
+  int32_t split_groups = 1;    // split work-groups per (sequence, KV head): the grid's y extent
   std::vector<int32_t> splits; // S_b per sequence
   int64_t active_units = 0;
   int64_t attended_keys = 0;

@@ -80,6 +80,19 @@ typedef struct {
   da_dtype q_dtype, kv_dtype, out_dtype;
   int32_t num_splits;        /* 0 = the planner decides; > 0 caps the splits of the
                                 longest sequence at this count (1 = no split)       */
+  int32_t fixed_chunk;       /* 0 = default mode. > 0 = fixed-order mode: the
+                                attended range of each sequence is cut into chunks
+                                of this many tokens (a multiple of page_size),
+                                counted from its first attended page; each chunk's
+                                softmax state is computed the same way whichever
+                                work-group computes it, and the states are merged
+                                in chunk order, so the output is bitwise the same
+                                for every num_splits (mlx-runner pull 3, split
+                                decode attention test: split and unsplit paths
+                                agree bit for bit because the partials are merged
+                                in one fixed order). num_splits then counts
+                                work-groups per sequence and KV head, each taking
+                                consecutive chunks.                              */
 } da_params;
 
 typedef struct da_plan* da_plan_t;
@@ -97,6 +110,10 @@ typedef struct {
                                 matrix cores (q and K/V share f16 or bf16,
                                 head_dim 128, page size a multiple of 16).
                                 DECODE_ATTN_KERNEL=vector forces 0.               */
+  int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
+                                work-group computes (0 in the default mode). In
+                                that mode pages_per_split is the chunk length in
+                                pages and max_splits the most chunks of a sequence. */
 } da_plan_info;
 
 /*

@@ -36,10 +36,11 @@ def split_kernel(kind):
 
 
 def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None, page_table=None,
-            window=None, seq_lens=None, seq_lens_host=None, two_phase=False, kernel=None):
+            window=None, seq_lens=None, seq_lens_host=None, two_phase=False, kernel=None, fixed_chunk=0):
     """One decode_attn_run (or split + combine) on the workload's tensors;
     returns (out tensor, plan). The output starts as NaN so unwritten rows show.
-    `kernel` = "vector" forces the vector split kernel; default: automatic."""
+    `kernel` = "vector" forces the vector split kernel; default: automatic.
+    `fixed_chunk` > 0 selects the fixed-order mode with chunks of that many tokens."""
     q = w.q if q is None else q
     k_pool = w.k_pool if k_pool is None else k_pool
     v_pool = w.v_pool if v_pool is None else v_pool
@@ -49,7 +50,7 @@ def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None
     window = w.window if window is None else window
     out_dtype = out_dtype or w.spec.out_dtype
     params = binding.params_for(q, k_pool, page_table, window=window, scale=w.scale, out_dtype=out_dtype,
-                                num_splits=num_splits)
+                                num_splits=num_splits, fixed_chunk=fixed_chunk)
     with split_kernel(kernel):
         plan = binding.decode_attn_plan(params, seq_lens_host, device=q.device.index)
     out = torch.full(q.shape, float("nan"), dtype=TORCH_DT[out_dtype], device=q.device)

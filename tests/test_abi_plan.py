@@ -152,6 +152,52 @@ def test_split_kernel_selection(lib, monkeypatch):
     assert plan(params(head_dim=64), [3060]).info.split_kernel == 0             # unsupported: vector
 
 
+# ---------------------------------------------------------------------------
+# fixed-order mode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ns,cpg", [(1, 12), (2, 6), (5, 3), (12, 1), (10_000, 1)])
+def test_fixed_order_chunks_and_groups(lib, ns, cpg):
+    lens = [3060, 100, 0, 2049]
+    pl = plan(params(batch=4, num_splits=ns, fixed_chunk=256), lens)
+    assert pl.pages_per_split == 16                     # chunk length in pages
+    assert pl.max_splits == 12                          # ceil(192 / 16) chunks of the longest sequence
+    assert [pl.splits(b) for b in range(4)] == [12, 1, 1, 9]
+    assert pl.info.chunks_per_work_group == cpg
+    assert pl.info.split_work_groups == math.ceil(12 / cpg) * 8 * 4
+    assert pl.info.split_kernel == 0                    # the fixed-order mode runs on the vector kernel
+    rows = 4 * 32 * 12
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert pl.workspace_bytes == r256(rows * 128 * 4) + r256(rows * 2 * 4)
+
+
+def test_fixed_order_always_has_a_workspace(lib):
+    pl = plan(params(num_splits=1, fixed_chunk=4096), [100])
+    assert pl.max_splits == 1 and pl.info.chunks_per_work_group == 1
+    assert pl.workspace_bytes > 0                       # every row goes through the chunk-order merge
+
+
+@pytest.mark.parametrize("L,W,P,chunk", [(65536, 4096, 32, 512), (40001, 4096, 32, 1024), (33, 1, 16, 16),
+                                         (5000, 1000, 16, 256), (0, 0, 16, 256)])
+def test_fixed_order_chunk_count_follows_attended_pages(lib, L, W, P, chunk):
+    pl = plan(params(page_size=P, window=W, max_pages_per_seq=4096, fixed_chunk=chunk), [L])
+    assert pl.splits(0) == max(1, math.ceil(attended_pages(L, W, P) / (chunk // P)))
+
+
+def test_fixed_order_heuristic_fills_the_chip(lib):
+    lens = [16384 + (i * 523) % 16384 for i in range(32)]
+    pl = plan(params(batch=32, fixed_chunk=512), lens)
+    default = plan(params(batch=32), lens)
+    # about as many pages per work-group as the default split, in whole chunks
+    assert pl.info.chunks_per_work_group == math.ceil(default.pages_per_split / 32)
+    assert pl.info.active_units >= 256 * 2
+
+
+@pytest.mark.parametrize("chunk", [-16, 8, 24, 100])
+def test_fixed_order_rejects_chunks_off_the_page_grid(lib, chunk):
+    assert status_of(params(fixed_chunk=chunk), [3060]) == B.DA_ERR_INVALID
+
+
 def test_empty_batch_plans(lib):
     pl = plan(params(batch=0), [])
     assert pl.max_splits == 1 and pl.workspace_bytes == 0
