@@ -17,3 +17,4 @@ from .attention_f64 import (  # noqa: F401
     shard_state,
 )
 from .paged_cache import append_kv  # noqa: F401,E402
+from .multi_query import prefill_attention  # noqa: F401,E402
