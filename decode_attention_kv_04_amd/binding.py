@@ -37,7 +37,7 @@ class Params(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("window", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
-        ("num_splits", ctypes.c_int32), ("fixed_chunk", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32), ("fixed_chunk", ctypes.c_int32), ("query_len", ctypes.c_int32),
     ]
 
 
@@ -100,13 +100,14 @@ decode_attn_status_str = status_str
 
 def make_params(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, *, window=0,
                 scale=None, q_dtype="f16", kv_dtype="f16", out_dtype="f16", num_splits=0,
-                fixed_chunk=0) -> Params:
+                fixed_chunk=0, query_len=1) -> Params:
     def code(t):
         return DTYPE_CODES[t] if isinstance(t, str) else int(t)
     return Params(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                   int(max_pages_per_seq), int(window),
                   float(scale if scale is not None else (head_dim ** -0.5 if head_dim > 0 else 1.0)),
-                  code(q_dtype), code(kv_dtype), code(out_dtype), int(num_splits), int(fixed_chunk))
+                  code(q_dtype), code(kv_dtype), code(out_dtype), int(num_splits), int(fixed_chunk),
+                  int(query_len))
 
 
 class Plan:
@@ -240,15 +241,20 @@ def decode_attn_append_kv(params: Params, k_new, v_new, page_table, seq_lens, k_
 
 def params_for(q, k_pool, page_table, *, window=0, scale=None, out_dtype=None, num_splits=0,
                fixed_chunk=0) -> Params:
-    """da_params from tensor shapes and dtypes."""
+    """da_params from tensor shapes and dtypes; q is [B][H_q][D] (one query
+    token per sequence) or [B][T][H_q][D] (T new tokens per sequence)."""
     import torch
     names = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
-    B, Hq, D = q.shape
+    if q.dim() == 4:
+        B, T, Hq, D = q.shape
+    else:
+        (B, Hq, D), T = q.shape, 1
     _, Hkv, P, D2 = k_pool.shape
     assert D == D2, "q and the pools disagree on head_dim"
     return make_params(B, Hq, Hkv, D, P, page_table.shape[1], window=window, scale=scale,
                        q_dtype=names[q.dtype], kv_dtype=names[k_pool.dtype],
-                       out_dtype=out_dtype or names[q.dtype], num_splits=num_splits, fixed_chunk=fixed_chunk)
+                       out_dtype=out_dtype or names[q.dtype], num_splits=num_splits, fixed_chunk=fixed_chunk,
+                       query_len=T)
 
 
 def alloc_workspace(plan: Plan, device):

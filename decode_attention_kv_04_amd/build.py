@@ -33,7 +33,8 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 HOST_SOURCES = ["plan.cpp", "api.cpp"]
-KERNEL_SOURCES = ["decode_split.hip", "decode_split_mfma.hip", "decode_combine.hip", "append_kv.hip"]
+KERNEL_SOURCES = ["decode_split.hip", "decode_split_mfma.hip", "decode_combine.hip", "append_kv.hip",
+                  "decode_multi.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 

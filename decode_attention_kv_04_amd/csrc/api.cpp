@@ -76,6 +76,8 @@ da_status prepare(const da_plan* plan, const void* q, const void* k_pool, const 
   a->max_splits = plan->max_splits;
   a->chunks_per_group = plan->chunks_per_group;
   a->split_groups = plan->split_groups;
+  a->query_len = plan->query_len;
+  a->rows_per_group = plan->rows_per_group;
   a->q_dtype = p.q_dtype;
   a->out_dtype = p.out_dtype;
   a->scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
@@ -91,9 +93,13 @@ da_status enqueue(const da_plan* plan, const da::KernelArgs& a, bool split, bool
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
   if (split) {
-    const hipError_t e = plan->split_kernel == 1
-                             ? da::launch_split_mfma(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st)
-                             : da::launch_split(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st);
+    hipError_t e;
+    if (plan->split_kernel == 2)
+      e = da::launch_multi(a, plan->p.head_dim, plan->p.kv_dtype, plan->rows_per_group, st);
+    else if (plan->split_kernel == 1)
+      e = da::launch_split_mfma(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st);
+    else
+      e = da::launch_split(a, plan->p.head_dim, plan->p.kv_dtype, plan->group_tile, st);
     if (e != hipSuccess) return DA_ERR_HIP;
   }
   if (combine && needs_combine(plan)) {
@@ -192,6 +198,8 @@ da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out
   a.max_splits = plan->max_splits;
   a.chunks_per_group = plan->chunks_per_group;
   a.split_groups = plan->split_groups;
+  a.query_len = plan->query_len;
+  a.rows_per_group = plan->rows_per_group;
   a.q_dtype = p.q_dtype;
   a.out_dtype = p.out_dtype;
   return enqueue(plan, a, false, true, stream);

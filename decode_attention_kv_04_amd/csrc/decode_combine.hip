@@ -45,12 +45,52 @@ __global__ __launch_bounds__(64) void combine_kernel(const KernelArgs a) {
     return;  // the split pass wrote this row
   }
 
-  merge_head_wave<D>(a, b, h, static_cast<int>(nsplit), lane);
+  merge_head_wave<D>(a, static_cast<int64_t>(b) * a.num_q_heads + h, static_cast<int>(nsplit), lane);
+}
+
+// Several new tokens per sequence: one wave per (query head, token, sequence).
+// The split count of a row is that of its row block (rows_per_group
+// consecutive (token, head) rows of one KV head), whose keys run from the
+// window start of its first token to its last token.
+template <int D>
+__global__ __launch_bounds__(64) void combine_multi_kernel(const KernelArgs a) {
+  const int h = blockIdx.x;
+  const int t = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int T = a.query_len;
+  const int G = a.group;
+  const int R = T * G;
+  const int P = a.page_size;
+  const int L = a.seq_lens[b];
+  const int r = t * G + (h - (h / G) * G);
+  const int r_first = r / a.rows_per_group * a.rows_per_group;
+  const int r_last = (r_first + a.rows_per_group < R ? r_first + a.rows_per_group : R) - 1;
+  int hi_blk = L - T + r_last / G + 1;
+  hi_blk = hi_blk < 0 ? 0 : hi_blk;
+  int lo_blk = a.window > 0 ? L - T + r_first / G + 1 - a.window : 0;
+  lo_blk = lo_blk < 0 ? 0 : (lo_blk > hi_blk ? hi_blk : lo_blk);
+  const int pf = lo_blk / P;
+  const int pe = (hi_blk + P - 1) / P;
+  int nsplit = (pe - pf + a.pages_per_split - 1) / a.pages_per_split;
+  if (nsplit > a.max_splits) nsplit = a.max_splits;
+  if (nsplit <= 1) return;  // the split pass wrote this row
+  merge_head_wave<D>(a, (static_cast<int64_t>(b) * T + t) * a.num_q_heads + h, nsplit, lane);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream) {
+  if (a.query_len > 1) {
+    const dim3 grid(a.num_q_heads, a.query_len, a.batch);
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL(combine_multi_kernel<64>, grid, dim3(64), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(combine_multi_kernel<128>, grid, dim3(64), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(combine_multi_kernel<256>, grid, dim3(64), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(a.num_q_heads, a.batch);
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, stream, a); break;

@@ -184,7 +184,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float ldf(const float* p) { return *p; }
 
-// Merge the nsplit states of query head h of sequence b into its output row
+// Merge the nsplit states of query row `qrow` (the flat index of (sequence,
+// query head), or of (sequence, new token, query head)) into its output row
 // (one wave; lane i owns elements i, i + 64, ...):
 //     M = max_s m_s,  w_s = 2^(m_s - M),  out = sum_s w_s O_s / sum_s w_s l_s
 // A state with m_s = -inf gets weight 0. Lane s holds (m_s, l_s) of each chunk
@@ -193,10 +194,10 @@ __device__ __forceinline__ float ldf(const float* p) { return *p; }
 // time; the weights are broadcast with readlane. The order of every sum is
 // fixed, so results are identical run to run.
 template <int D>
-__device__ void merge_head_wave(const KernelArgs& a, int b, int h, int nsplit, int lane) {
+__device__ void merge_head_wave(const KernelArgs& a, int64_t qrow, int nsplit, int lane) {
   constexpr int N = D / 64;
   constexpr int BATCH = 16;
-  const int64_t base = (static_cast<int64_t>(b) * a.num_q_heads + h) * a.max_splits;
+  const int64_t base = qrow * a.max_splits;
   const float* ml = a.ws_ml + base * 2;
   const float* os = a.ws_o + base * D;
   auto load_rows = [&](float (&ov)[BATCH][N], int first, int cnt) {
@@ -252,7 +253,7 @@ __device__ void merge_head_wave(const KernelArgs& a, int b, int h, int nsplit, i
     }
   }
   lsum = wave_sum(lsum);
-  const int64_t row = (static_cast<int64_t>(b) * a.num_q_heads + h) * D;
+  const int64_t row = qrow * D;
 #pragma unroll
   for (int i = 0; i < N; ++i) store_elem(a.out, row + lane + 64 * i, a.out_dtype, lsum > 0.0f ? acc[i] / lsum : 0.0f);
 }

@@ -28,6 +28,8 @@ struct KernelArgs {
   int32_t max_splits;       // state slots per query head in the workspace
   int32_t chunks_per_group; // 0 = default mode; else fixed-order mode, chunks per work-group
   int32_t split_groups;     // split work-groups per (sequence, KV head)
+  int32_t query_len;        // T new tokens per sequence (1 = single-query decode)
+  int32_t rows_per_group;   // multi-token kernel: query rows (token, head) per work-group
   int32_t q_dtype;        // da_dtype
   int32_t out_dtype;      // da_dtype
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units
@@ -60,6 +62,9 @@ hipError_t launch_split(const KernelArgs& a, int head_dim, int kv_dtype, int gro
 // Enqueue the split pass with q.K on the matrix cores (q and K/V share a
 // 16-bit type, head_dim 128, page size a multiple of 16).
 hipError_t launch_split_mfma(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream);
+
+// Enqueue the multi-token split pass (query_len > 1) on `stream`.
+hipError_t launch_multi(const KernelArgs& a, int head_dim, int kv_dtype, int rows_per_group, hipStream_t stream);
 
 // Enqueue the combine pass on `stream`.
 hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream);

@@ -157,6 +157,78 @@ da_status finish_fixed_plan(da_plan* plan, const std::vector<int64_t>& npages, i
   return DA_OK;
 }
 
+// Several new tokens per sequence: rows (token, head) of one KV head are cut
+// into blocks of rows_per_group; a block sees keys from the window start of
+// its first token to its last token, and those pages are split with one split
+// length for the whole batch.
+da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
+  const da_params& p = plan->p;
+  const int64_t P = p.page_size;
+  const int64_t T = plan->query_len;
+  const int64_t G = plan->group;
+  const int64_t R = T * G;
+  const int64_t QB = R <= 32 ? 32 : 64;
+  const int64_t nrb = ceil_div(R, QB);
+  plan->split_kernel = 2;
+  plan->rows_per_group = static_cast<int32_t>(QB);
+  plan->attended_keys = 0;  // counted per new token below
+  if (nrb > 65535) {
+    delete plan;
+    return DA_ERR_UNSUPPORTED;
+  }
+  // Attended pages of every (sequence, row block).
+  std::vector<int64_t> blk_pages(static_cast<size_t>(p.batch) * nrb);
+  int64_t max_np = 0, total_np = 0;
+  for (int32_t b = 0; b < p.batch; ++b) {
+    const int64_t L = lens[b];
+    for (int64_t rb = 0; rb < nrb; ++rb) {
+      const int64_t r0 = rb * QB, r1 = std::min(R, r0 + QB) - 1;
+      const int64_t hi = L - T + r1 / G + 1;
+      const int64_t lo = p.window > 0 ? std::max<int64_t>(0, L - T + r0 / G + 1 - p.window) : 0;
+      const int64_t np = ceil_div(hi, P) - lo / P;
+      blk_pages[b * nrb + rb] = np;
+      max_np = std::max(max_np, np);
+      total_np += np;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t pos = L - T + t;
+      plan->attended_keys += p.window > 0 ? std::min<int64_t>(pos + 1, p.window) : pos + 1;
+    }
+  }
+  int64_t c;
+  if (max_np == 0) {
+    c = 1;
+  } else if (p.num_splits > 0) {
+    c = ceil_div(max_np, p.num_splits);
+  } else {
+    c = heuristic_split_pages(total_np, max_np, p.num_kv_heads, plan->num_cus, P);
+  }
+  c = std::max<int64_t>(c, 1);
+  c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));  // grid y = row blocks x splits
+  if (c > INT32_MAX) c = INT32_MAX;
+  plan->pages_per_split = static_cast<int32_t>(c);
+  plan->splits.assign(p.batch, 1);
+  int64_t smax = 1;
+  for (int32_t b = 0; b < p.batch; ++b) {
+    for (int64_t rb = 0; rb < nrb; ++rb) {
+      const int64_t sb = std::max<int64_t>(1, ceil_div(blk_pages[b * nrb + rb], c));
+      plan->splits[b] = static_cast<int32_t>(std::max<int64_t>(plan->splits[b], sb));
+      smax = std::max(smax, sb);
+      plan->active_units += sb * p.num_kv_heads;
+    }
+  }
+  plan->max_splits = static_cast<int32_t>(smax);
+  plan->split_groups = static_cast<int32_t>(nrb * smax);
+  if (smax > 1) {
+    const size_t rows = static_cast<size_t>(p.batch) * T * p.num_q_heads * smax;
+    plan->ws_o_offset = 0;
+    plan->ws_ml_offset = round_up(rows * p.head_dim * sizeof(float), 256);
+    plan->ws_bytes = plan->ws_ml_offset + round_up(rows * 2 * sizeof(float), 256);
+  }
+  log_plan(plan);
+  return DA_OK;
+}
+
 }  // namespace
 
 da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da_plan** out) {
@@ -164,7 +236,7 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   if (p->batch < 0 || p->num_q_heads < 1 || p->num_kv_heads < 1) return DA_ERR_INVALID;
   if (p->num_q_heads % p->num_kv_heads != 0) return DA_ERR_INVALID;
   if (p->head_dim < 1 || p->page_size < 1) return DA_ERR_INVALID;
-  if (p->window < 0 || p->num_splits < 0 || p->fixed_chunk < 0) return DA_ERR_INVALID;
+  if (p->window < 0 || p->num_splits < 0 || p->fixed_chunk < 0 || p->query_len < 0) return DA_ERR_INVALID;
   if (!std::isfinite(p->scale)) return DA_ERR_INVALID;
   if (!valid_dtype(p->q_dtype) || !valid_dtype(p->kv_dtype) || !valid_dtype(p->out_dtype))
     return DA_ERR_INVALID;
@@ -188,9 +260,19 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     if (lens[b] < 0 || static_cast<int64_t>(lens[b]) > cap) return DA_ERR_INVALID;
   }
 
+  const int32_t T = p->query_len > 1 ? p->query_len : 1;
+  if (T > 1) {
+    if (p->q_dtype != p->kv_dtype || (p->kv_dtype != DA_F16 && p->kv_dtype != DA_BF16)) return DA_ERR_UNSUPPORTED;
+    if (fixed) return DA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(T) * G > (static_cast<int64_t>(1) << 24)) return DA_ERR_UNSUPPORTED;
+    for (int32_t b = 0; b < p->batch; ++b)
+      if (lens[b] < T) return DA_ERR_INVALID;  // the new tokens' keys are in the cache
+  }
+
   da_plan* plan = new (std::nothrow) da_plan();
   if (!plan) return DA_ERR_INVALID;
   plan->p = *p;
+  plan->query_len = T;
   plan->group = G;
   plan->group_tile = gt;
   plan->num_cus = num_cus;
@@ -211,6 +293,11 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     plan->attended_keys += r.t1 - r.t0;
   }
 
+  if (plan->query_len > 1) {
+    const da_status st = finish_multi_plan(plan, lens);
+    if (st == DA_OK) *out = plan;
+    return st;
+  }
   if (fixed) {
     const da_status st = finish_fixed_plan(plan, npages, max_np, total_np);
     if (st == DA_OK) *out = plan;

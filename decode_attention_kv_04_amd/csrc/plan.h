@@ -13,12 +13,14 @@ struct da_plan {
   da_params p;
   int32_t group = 1;           // G = H_q / H_kv
   int32_t group_tile = 1;      // compiled group width the kernels use (1, 2, 4 or 8)
-  int32_t split_kernel = 0;    // 0 = vector q.K, 1 = q.K on the matrix cores
+  int32_t split_kernel = 0;    // 0 = vector q.K, 1 = q.K on the matrix cores, 2 = multi-token
   int32_t num_cus = 0;
   int32_t pages_per_split = 1; // c (fixed-order mode: pages per chunk)
   int32_t max_splits = 1;      // S_max: state slots per query head (fixed-order mode: chunks)
   int32_t chunks_per_group = 0;// fixed-order mode: chunks per split work-group (0 = default mode)
   int32_t split_groups = 1;    // split work-groups per (sequence, KV head): the grid's y extent
+  int32_t query_len = 1;       // T new tokens per sequence
+  int32_t rows_per_group = 0;  // multi-token kernel: (token, head) rows per work-group
   std::vector<int32_t> splits; // S_b per sequence
   int64_t active_units = 0;
   int64_t attended_keys = 0;

@@ -72,6 +72,7 @@ class WorkloadSpec:
     shuffle: bool = True
     max_pages_per_seq: Optional[int] = None
     scale: Optional[float] = None  # default 1/sqrt(head_dim)
+    query_len: int = 1             # T new tokens per sequence (the last T keys); q is [B][T][H_q][D] if T > 1
 
     @property
     def group(self) -> int:
@@ -96,8 +97,17 @@ LONG_BATCH = WorkloadSpec("llama8b_b32_l16k-32k_f16_spiky", 32, 32, 8, 128, "f16
 MIXED_WINDOW = WorkloadSpec("llama8b_b64_window4096_mixed_bf16", 64, 32, 8, 128, "bf16", "bf16", "f32",
                             32, ("mixed", (1, 256), (32768, 65536)), seed=5, window=4096)
 
+# Several new tokens per sequence: a suffix prefill of 128 tokens behind a
+# cached prefix, and checking 4 drafted tokens on the batched long-context
+# shape.
+SUFFIX_PREFILL = WorkloadSpec("llama8b_b4_suffix128_l2k-8k_f16", 4, 32, 8, 128, "f16", "f16", "f16", 16,
+                              ("uniform", 2048, 8192), seed=6, query_len=128)
+VERIFY_LONG = WorkloadSpec("llama8b_b32_verify4_l16k-32k_f16", 32, 32, 8, 128, "f16", "f16", "f16", 16,
+                           ("uniform", 16384, 32768), seed=7, query_len=4, max_pages_per_seq=2048)
+
 NAMED = {"tiny": TINY, "llama8b_3060": LLAMA8B_3060, "wide_gqa": WIDE_GQA,
-         "long_batch": LONG_BATCH, "mixed_window": MIXED_WINDOW}
+         "long_batch": LONG_BATCH, "mixed_window": MIXED_WINDOW,
+         "suffix_prefill": SUFFIX_PREFILL, "verify_long": VERIFY_LONG}
 
 
 @dataclasses.dataclass
@@ -119,13 +129,9 @@ class Workload:
         return self.spec.page_size
 
     def attended(self) -> list:
-        """(first key, end key) of the attended range of every sequence."""
-        out = []
-        w = self.window
-        for L in self.seq_lens_host.tolist():
-            Leff = min(L, w) if w > 0 else L
-            out.append((L - Leff, L))
-        return out
+        """(first key, end key) of the keys any query of each sequence
+        attends (with T new tokens, from the first one's window start)."""
+        return [(first_attended(L, self.spec.query_len, self.window), L) for L in self.seq_lens_host.tolist()]
 
     def kv_bytes(self) -> int:
         """Bytes of K and V that the method must read: each attended key row
@@ -133,6 +139,11 @@ class Workload:
         s = self.spec
         keys = sum(e - b for b, e in self.attended())
         return keys * s.num_kv_heads * s.head_dim * ELT_BYTES[s.kv_dtype] * 2
+
+
+def first_attended(L: int, T: int, window: int) -> int:
+    """First key any of the T newest tokens of a sequence of L keys attends."""
+    return max(0, L - T + 1 - window) if window > 0 else 0
 
 
 def draw_lengths(spec: WorkloadSpec, gen: torch.Generator) -> list:
@@ -174,7 +185,9 @@ def make_workload(spec: WorkloadSpec, device="cpu", lengths: Optional[Sequence[i
     assert Hq % Hkv == 0
     cpu_gen = torch.Generator().manual_seed(spec.seed)
     lens = list(lengths) if lengths is not None else draw_lengths(spec, cpu_gen)
+    T = spec.query_len
     assert len(lens) == B and all(L >= 0 for L in lens)
+    assert T == 1 or all(L >= T for L in lens), "every sequence must hold its T new tokens"
     npages = [(L + P - 1) // P for L in lens]
     total = sum(npages)
     num_pages = total + 1
@@ -198,7 +211,8 @@ def make_workload(spec: WorkloadSpec, device="cpu", lengths: Optional[Sequence[i
                                dtype=torch.float32))
     kv_t = DTYPES[spec.kv_dtype]
     vg = _value_generator(device, spec.seed)
-    q = torch.randn((B, Hq, D), generator=vg, device=device, dtype=torch.float32).to(DTYPES[spec.q_dtype])
+    q_shape = (B, Hq, D) if T == 1 else (B, T, Hq, D)
+    q = torch.randn(q_shape, generator=vg, device=device, dtype=torch.float32).to(DTYPES[spec.q_dtype])
 
     pools = []
     table_dev = table.to(device)
@@ -208,8 +222,7 @@ def make_workload(spec: WorkloadSpec, device="cpu", lengths: Optional[Sequence[i
             L = lens[b]
             if L == 0:
                 continue
-            Leff = min(L, window) if window > 0 else L
-            t0 = L - Leff
+            t0 = first_attended(L, T, window)
             p_first = t0 // P
             npw = npages[b] - p_first
             vals = torch.randn((npw, Hkv, P, D), generator=vg, device=device, dtype=torch.float32)

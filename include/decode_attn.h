@@ -93,6 +93,16 @@ typedef struct {
                                 in one fixed order). num_splits then counts
                                 work-groups per sequence and KV head, each taking
                                 consecutive chunks.                              */
+  int32_t query_len;         /* T, new tokens per sequence; 0 or 1 = one query
+                                token (decode). T > 1 (llm-web pull 8, commit on
+                                the batched suffix prefill: several new tokens
+                                attend the cache after their K/V were written
+                                behind the resident prefix): q and out are
+                                [B][T][H_q][D]; token t of sequence b sits at
+                                position L_b - T + t and attends the keys at
+                                positions <= its own (the last `window` of them
+                                if window > 0). Needs L_b >= T, q_dtype ==
+                                kv_dtype in {f16, bf16} and fixed_chunk == 0.  */
 } da_params;
 
 typedef struct da_plan* da_plan_t;
@@ -109,7 +119,9 @@ typedef struct {
   int32_t split_kernel;      /* 0 = vector q.K (any parameters); 1 = q.K on the
                                 matrix cores (q and K/V share f16 or bf16,
                                 head_dim 128, page size a multiple of 16).
-                                DECODE_ATTN_KERNEL=vector forces 0.               */
+                                DECODE_ATTN_KERNEL=vector forces 0. 2 = the
+                                multi-token kernel (query_len > 1; q.K and P.V
+                                on the matrix cores).                            */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in

@@ -72,8 +72,9 @@ def host64(t):
 
 def oracle_for(w, rows=None):
     a = workloads.to_numpy_inputs(w, rows)
-    return oracle.decode_attention(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"],
-                                   a["page_size"], a["scale"], a["window"])
+    fn = oracle.prefill_attention if a["q"].ndim == 4 else oracle.decode_attention
+    return fn(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"], a["page_size"], a["scale"],
+              a["window"])
 
 
 def check(got, ref, kv_dtype, out_dtype, label=""):

@@ -198,6 +198,53 @@ def test_fixed_order_rejects_chunks_off_the_page_grid(lib, chunk):
     assert status_of(params(fixed_chunk=chunk), [3060]) == B.DA_ERR_INVALID
 
 
+# ---------------------------------------------------------------------------
+# several new tokens per sequence
+# ---------------------------------------------------------------------------
+
+def test_multi_token_plans(lib):
+    lens = [16, 3000, 700]
+    pl = plan(params(batch=3, query_len=16), lens)
+    assert pl.info.split_kernel == 2
+    # 16 tokens x G 4 = 64 rows per KV head: one row block of 64
+    S = pl.max_splits
+    assert pl.info.split_work_groups == 1 * S * 8 * 3
+    T = 16
+    assert pl.info.attended_keys == sum(sum(L - T + t + 1 for t in range(T)) for L in lens)
+    rows = 3 * T * 32 * S
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert pl.workspace_bytes == (r256(rows * 128 * 4) + r256(rows * 2 * 4) if S > 1 else 0)
+    # forced: the longest row block's pages over num_splits
+    pl = plan(params(batch=3, query_len=16, num_splits=5), lens)
+    assert pl.max_splits == 5 and pl.pages_per_split == math.ceil(math.ceil(3000 / 16) / 5)
+    # 2 tokens x G 4 = 8 rows: blocks of 32 rows
+    pl = plan(params(batch=1, query_len=2, num_splits=1), [100])
+    assert pl.info.split_work_groups == 8 and pl.workspace_bytes == 0
+
+
+def test_multi_token_window_keys(lib):
+    T, W = 8, 100
+    pl = plan(params(batch=1, query_len=T, window=W), [5000])
+    assert pl.info.attended_keys == T * W
+
+
+@pytest.mark.parametrize("kw,lens,code", [
+    (dict(query_len=4), [3], B.DA_ERR_INVALID),                                  # L < T
+    (dict(query_len=-1), [30], B.DA_ERR_INVALID),
+    (dict(query_len=4, q_dtype="f32", kv_dtype="f32", out_dtype="f32"), [30], B.DA_ERR_UNSUPPORTED),
+    (dict(query_len=4, q_dtype="f32"), [30], B.DA_ERR_UNSUPPORTED),             # q and KV differ
+    (dict(query_len=4, fixed_chunk=256), [30], B.DA_ERR_UNSUPPORTED),
+])
+def test_multi_token_rejects(lib, kw, lens, code):
+    assert status_of(params(batch=len(lens), **kw), lens) == code
+
+
+def test_query_len_zero_and_one_are_decode(lib):
+    for T in (0, 1):
+        pl = plan(params(query_len=T), [3060])
+        assert pl.info.split_kernel in (0, 1)
+
+
 def test_empty_batch_plans(lib):
     pl = plan(params(batch=0), [])
     assert pl.max_splits == 1 and pl.workspace_bytes == 0

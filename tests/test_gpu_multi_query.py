@@ -1,0 +1,156 @@
+"""Several new tokens per sequence (causal attention over the paged cache)
+on the GPU through the C-ABI, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_04_amd import workloads as wl
+
+from gpu_util import TORCH_DT, check, host64, oracle_for, run_lib, say
+
+pytestmark = pytest.mark.gpu
+
+
+def spec_of(T, G, D, kv, out, P, lens, W, Hkv=2, seed=41):
+    return wl.WorkloadSpec(f"mq_T{T}_G{G}_D{D}_{kv}_P{P}_W{W}", len(lens), G * Hkv, Hkv, D, kv, kv, out, P,
+                           ("list", tuple(lens)), seed=seed, window=W, query_len=T)
+
+
+GRID = [
+    # T, G, D, kv, out, P, lens, W
+    (2, 4, 128, "f16", "f16", 16, (2, 3, 100, 1000), 0),
+    (3, 1, 64, "bf16", "f32", 16, (3, 17, 600), 0),
+    (8, 8, 128, "bf16", "f32", 8, (8, 9, 31, 777), 0),
+    (16, 4, 64, "f16", "f32", 32, (16, 50, 2000), 0),
+    (16, 4, 128, "f16", "f16", 16, (16, 300, 3000), 100),
+    (33, 3, 128, "bf16", "bf16", 24, (33, 34, 500), 0),
+    (64, 2, 256, "bf16", "f32", 16, (64, 70, 1500), 0),
+    (128, 4, 128, "f16", "f16", 16, (128, 130, 1000), 0),
+    (128, 4, 128, "f16", "f32", 16, (200, 1500), 64),
+    (5, 8, 256, "f16", "f32", 64, (5, 900), 7),
+]
+
+
+@pytest.mark.parametrize("T,G,D,kv,out,P,lens,W", GRID)
+@pytest.mark.parametrize("splits", [0, 3])
+def test_matches_oracle(gpu, T, G, D, kv, out, P, lens, W, splits):
+    spec = spec_of(T, G, D, kv, out, P, lens, W)
+    say(f"[multi] {spec.name} lens={lens} splits={splits}")
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w, num_splits=splits)
+    assert plan.info.split_kernel == 2
+    err, worst = check(got, oracle_for(w), kv, out, spec.name)
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
+
+
+def test_llama_shape_heads(gpu):
+    spec = spec_of(24, 4, 128, "bf16", "f32", 16, (24, 900, 2500), 0, Hkv=8)
+    w = wl.make_workload(spec, gpu)
+    got, _ = run_lib(w)
+    check(got, oracle_for(w), "bf16", "f32", spec.name)
+
+
+def test_split_counts_agree_within_tolerance(gpu):
+    spec = spec_of(16, 4, 128, "f16", "f32", 16, (16, 3000, 1234), 0)
+    w = wl.make_workload(spec, gpu)
+    ref = oracle_for(w)
+    outs = []
+    for ns in (1, 2, 7, 1_000_000):
+        got, plan = run_lib(w, num_splits=ns)
+        err, worst = check(got, ref, "f16", "f32", f"splits={ns}")
+        say(f"[multi] splits={ns}: rel L2 {err:.2e}, worst sequence {worst:.2e}")
+        outs.append(host64(got))
+    # P enters P.V as f16 relative to each split's running max, so split
+    # counts differ by about one f16 rounding of P (~2e-4), not by fp32 noise.
+    for o in outs[1:]:
+        assert oracle.relative_l2(o, outs[0]) < 1e-3
+
+
+def test_two_phase_run_to_run_and_page_permutation_are_bitwise(gpu):
+    spec = spec_of(12, 4, 128, "bf16", "f32", 16, (12, 700, 2100), 0)
+    w = wl.make_workload(spec, gpu)
+    a, plan = run_lib(w, num_splits=4)
+    assert plan.max_splits > 1
+    b, _ = run_lib(w, num_splits=4, two_phase=True)
+    assert torch.equal(a, b)
+    for _ in range(2):
+        c, _ = run_lib(w, num_splits=4)
+        assert torch.equal(a, c)
+    g = torch.Generator().manual_seed(3)
+    perm = torch.randperm(w.num_pages, generator=g).to(gpu)
+    kp = torch.empty_like(w.k_pool)
+    vp = torch.empty_like(w.v_pool)
+    kp[perm] = w.k_pool
+    vp[perm] = w.v_pool
+    table = perm.to(torch.int32)[w.page_table.long()].contiguous()
+    d, _ = run_lib(w, num_splits=4, k_pool=kp, v_pool=vp, page_table=table)
+    assert torch.equal(a, d)
+
+
+# bf16 P enters P.V as a hi + lo pair (error ~1e-6); f16 P is rounded once
+# to f16 (~2e-4), while the single-query kernels keep P in fp32.
+@pytest.mark.parametrize("kv,tol", [("bf16", 5e-6), ("f16", 1e-3)])
+def test_each_token_matches_decode_over_the_cut_cache(gpu, kv, tol):
+    """Token t of the multi-token pass agrees (within tolerance; other
+    kernel) with a single-query decode whose length stops at its position."""
+    T = 8
+    spec = spec_of(T, 4, 128, kv, "f32", 16, (8, 500, 2049), 0)
+    w = wl.make_workload(spec, gpu)
+    multi, _ = run_lib(w)
+    for t in range(T):
+        cut = (w.seq_lens_host - T + t + 1).to(torch.int32)
+        one, _ = run_lib(w, q=w.q[:, t].contiguous(), seq_lens=cut.to(gpu), seq_lens_host=cut, out_dtype="f32")
+        rel = ((multi[:, t] - one).norm() / one.norm()).item()
+        assert rel < tol, f"token {t}: {rel:.3e}"
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_window_one_returns_each_tokens_own_value_bitwise(gpu, kv):
+    T = 16
+    spec = spec_of(T, 4, 128, kv, kv, 16, (16, 40, 333), 1)
+    w = wl.make_workload(spec, gpu)
+    got, _ = run_lib(w)
+    for b, L in enumerate(spec.lengths[1]):
+        pos = torch.arange(L - T, L)
+        pages = w.page_table[b, (pos // 16).to(gpu)].long()
+        v = w.v_pool[pages, :, (pos % 16).to(gpu)]              # [T][H_kv][D]
+        assert torch.equal(got[b], v.repeat_interleave(4, dim=1))
+
+
+def sampled_decode_oracle(w, pairs):
+    """Oracle values for sampled (sequence, token) pairs: decode over the
+    cache cut at the token's position (equal to the multi-token oracle)."""
+    out = {}
+    T = w.spec.query_len
+    for b, t in pairs:
+        a = wl.to_numpy_inputs(w, [b])
+        L = int(a["seq_lens"][0])
+        out[(b, t)] = oracle.decode_attention(a["q"][:, t], a["k_pool"], a["v_pool"], a["page_table"],
+                                              np.array([L - T + t + 1]), a["page_size"], a["scale"],
+                                              a["window"])[0]
+    return out
+
+
+@pytest.mark.parametrize("name", ["suffix_prefill", "verify_long"])
+def test_full_size_workloads_sampled(gpu, name):
+    spec = wl.NAMED[name]
+    say(f"[multi] {spec.name} full size")
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w)
+    say(f"  pages/split {plan.pages_per_split}, max splits {plan.max_splits}, "
+        f"work-groups {plan.info.split_work_groups}")
+    T = spec.query_len
+    pairs = [(0, 0), (0, T - 1), (1, T // 2), (spec.batch - 1, T - 1), (spec.batch // 2, 1)]
+    ref = sampled_decode_oracle(w, pairs)
+    g = np.stack([host64(got[b, t]) for b, t in pairs])
+    r = np.stack([ref[p] for p in pairs])
+    check(g[:, None], r[:, None], spec.kv_dtype, spec.out_dtype, name)
+    assert torch.isfinite(got).all()
+
+
+def test_whole_context_is_new(gpu):
+    spec = spec_of(40, 2, 64, "bf16", "f32", 8, (40, 40, 40), 0)
+    w = wl.make_workload(spec, gpu)
+    got, _ = run_lib(w)
+    check(got, oracle_for(w), "bf16", "f32", "L == T")
