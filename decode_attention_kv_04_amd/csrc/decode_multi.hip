@@ -22,10 +22,11 @@
 // operand: contraction index 8*q + j is key 4q + j (j < 4) or 16 + 4q + j - 4.
 //
 // Staging. Each tile of 32 keys is read from HBM once per work-group with
-// 16-byte loads into registers (the next tile's loads are in flight while the
-// current tile is computed) and written to LDS: K row-major, V transposed
+// 16-byte loads into a ring of registers (several tiles ahead of the one being
+// computed) and written to one of two LDS buffers: K row-major, V transposed
 // (dims as rows, keys in contraction order) so both MFMA operands are single
-// 16-byte LDS reads. V rows outside the split's attended keys are stored as
+// 16-byte LDS reads. One barrier per tile: tile m+1 is written to one buffer
+// while tile m is computed from the other. V rows outside the split's attended keys are stored as
 // zeros (they may hold NaN and would poison 0 * V), scores outside a row's own
 // keys become -inf by select.
 //
@@ -74,9 +75,137 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs only (probabilities)
 }
 
+// K/V loads of the multi-token kernels go through the caches normally: a
+// thread's segments of one row arrive over several instructions, and a
+// streaming (non-temporal) hint lets the line leave the cache between them
+// (measured: 1.7x the time on the long-context verify workload).
+__device__ __forceinline__ uint4 ldg16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
 // LDS barrier that does not wait for outstanding global loads: the next
 // tile's K/V loads stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One 32-key tile for the 16 query rows of a wave: S^T = K Q^T from the K
+// tile (row-major, row stride KS), masking to the row's keys [lo_r, hi_r),
+// online-softmax update of (m, lpart, O^T), O^T += V^T P^T from the
+// transposed V tile (row stride VS). Lane (col, q4) holds row col's scores
+// for keys tb + 16*kb + 4*q4 + i and its output dims 16*nb + 4*q4 + i.
+template <int D, int KVT, int KS, int VS>
+__device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* sv, int tb, const uint4 (&qb)[D / 32],
+                                            int lo_r, int hi_r, float sl2, int col, int q4, float& m, float& lpart,
+                                            mq_float4 (&o)[D / 16]) {
+  constexpr int NKS = D / 32;
+  constexpr int NDB = D / 16;
+  mq_float4 sacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    sacc[kb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint4 ka = *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
+      sacc[kb] = mfma<KVT>(ka, qb[ks], sacc[kb]);
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = tb + kb * 16 + q4 * 4 + i;
+      const float v = sacc[kb][i] * sl2;
+      x[kb * 4 + i] = (key >= lo_r && key < hi_r) ? v : -INFINITY;
+    }
+  }
+  float mt = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(m, mt);
+  if (__any(mn > m)) {
+    const float mu = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = exp2_fast(m - mu);
+    lpart *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb) o[nb] *= alpha;
+    m = mn;
+  }
+  const float mu = m == -INFINITY ? 0.0f : m;
+  float pr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pr[j] = exp2_fast(x[j] - mu);
+    lpart += pr[j];
+  }
+  // P^T as the B operand: contraction index 8*q4 + j holds pr[j].
+  if constexpr (KVT == DA_F16) {
+    uint4 pb;
+    pb.x = f16_bits(pr[0]) | (f16_bits(pr[1]) << 16);
+    pb.y = f16_bits(pr[2]) | (f16_bits(pr[3]) << 16);
+    pb.z = f16_bits(pr[4]) | (f16_bits(pr[5]) << 16);
+    pb.w = f16_bits(pr[6]) | (f16_bits(pr[7]) << 16);
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb) {
+      const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
+      o[nb] = mfma<KVT>(va, pb, o[nb]);
+    }
+  } else {
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      hi[j] = bf16_bits(pr[j]);
+      lo[j] = bf16_bits(pr[j] - __builtin_bit_cast(float, hi[j] << 16));
+    }
+    uint4 ph, pl;
+    ph.x = hi[0] | (hi[1] << 16);
+    ph.y = hi[2] | (hi[3] << 16);
+    ph.z = hi[4] | (hi[5] << 16);
+    ph.w = hi[6] | (hi[7] << 16);
+    pl.x = lo[0] | (lo[1] << 16);
+    pl.y = lo[2] | (lo[3] << 16);
+    pl.z = lo[4] | (lo[5] << 16);
+    pl.w = lo[6] | (lo[7] << 16);
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb) {
+      const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
+      o[nb] = mfma<KVT>(va, ph, o[nb]);
+      o[nb] = mfma<KVT>(va, pl, o[nb]);
+    }
+  }
+}
+
+// Block of query rows [r_first, r_last] of one KV head and its key range:
+// the keys any of its tokens sees, [lo, hi), and the split's part of them.
+struct RowBlock {
+  int r_first, r_last, lo, hi, pf, pe, nsplit;
+};
+
+__device__ __forceinline__ RowBlock row_block(const KernelArgs& a, int rb, int qb_rows, int L) {
+  RowBlock k;
+  const int T = a.query_len, G = a.group, R = T * G, P = a.page_size;
+  k.r_first = rb * qb_rows;
+  k.r_last = (k.r_first + qb_rows < R ? k.r_first + qb_rows : R) - 1;
+  int hi = L - T + k.r_last / G + 1;
+  hi = hi < 0 ? 0 : hi;
+  int lo = a.window > 0 ? L - T + k.r_first / G + 1 - a.window : 0;
+  lo = lo < 0 ? 0 : (lo > hi ? hi : lo);
+  k.lo = lo;
+  k.hi = hi;
+  k.pf = lo / P;
+  k.pe = (hi + P - 1) / P;
+  int ns = (k.pe - k.pf + a.pages_per_split - 1) / a.pages_per_split;
+  k.nsplit = ns < 1 ? 1 : (ns > a.max_splits ? a.max_splits : ns);
+  return k;
+}
+
+// Tiles of K/V loads kept in flight per work-group while one is computed.
+#ifndef DA_MQ_PREFETCH
+#define DA_MQ_PREFETCH 3
+#endif
+template <int D>
+constexpr int prefetch_tiles() {
+  return D >= 256 ? 1 : DA_MQ_PREFETCH;
+}
 
 template <int D, int KVT, int NQ>
 __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
@@ -85,14 +214,15 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   constexpr int ROWB = D * 2;           // bytes per K/V row
   constexpr int ROWV = D / 8;           // 16-byte vectors per row
   constexpr int NV = KT * ROWV / NT;    // vectors per thread per tensor per tile
-  constexpr int KSTEP = NT / ROWV;      // key distance between a thread's vectors
   constexpr int KS = D + KPAD;          // K row stride in LDS (elements)
   constexpr int VS = KT + VPAD;         // transposed-V row stride (elements)
   constexpr int NKS = D / 32;           // k-steps of q.K
   constexpr int NDB = D / 16;           // 16-dim blocks of P.V
-  static_assert(NV >= 1 && NV * NT == KT * ROWV && NT % ROWV == 0, "staging split");
-  __shared__ __align__(16) uint16_t sk[KT * KS];
-  __shared__ __align__(16) uint16_t sv[D * VS];
+  constexpr int PD = prefetch_tiles<D>();
+  static_assert(NV >= 1 && NV * NT == KT * ROWV, "staging split");
+  // Two LDS buffers: one tile is computed while the next one is written.
+  __shared__ __align__(16) uint16_t sk[2][KT * KS];
+  __shared__ __align__(16) uint16_t sv[2][D * VS];
 
   const int kvh = blockIdx.x;
   const int b = blockIdx.z;
@@ -162,165 +292,114 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   const int tile_first = t_lo / KT;
   const int ntiles = t_hi > t_lo ? (t_hi + KT - 1) / KT - tile_first : 0;
 
-  // Staging: thread vector i covers key kk0 + i*KSTEP of the tile, 16-byte
-  // segment `seg` of its row. Page cursor per vector, page ids fetched one
-  // tile ahead, indices clamped to this split's pages.
-  const int seg = tid % ROWV;
-  const int kk0 = tid / ROWV;
+  // Staging map: the 32 lanes of each half wave take the 32 keys of the tile
+  // (one key per thread, so one page lookup per tile) and thread t holds the
+  // 16-byte segments t/32 + i*SSTEP of its key's row. A transposed V write of
+  // a wave then covers two V^T rows at 32 consecutive contraction positions:
+  // 32 different LDS banks. Page indices are clamped to this split's pages.
+  constexpr int SSTEP = NT / KT;
+  static_assert(NV * SSTEP == ROWV, "segments per thread");
+  const int kk = tid % KT;
+  const int sg0 = tid / KT;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   const int64_t block_bytes = static_cast<int64_t>(P) * ROWB;
   const int64_t page_bytes = block_bytes * a.num_kv_heads;
-  const int64_t head_bytes = block_bytes * kvh + seg * 16;
+  const int64_t head_bytes = block_bytes * kvh + sg0 * 16;
   const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
   const int pi_last = phi > plo ? phi - 1 : plo;
-  int cpi[NV], coff[NV], cphys[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int pos = tile_first * KT + kk0 + i * KSTEP;
-    cpi[i] = pos / P;
-    coff[i] = pos - cpi[i] * P;
-  }
+  // Page cursor of this thread's key, page id fetched one tile ahead.
+  int cpi = (tile_first * KT + kk) / P;
+  int coff = tile_first * KT + kk - cpi * P;
+  int cphys = 0;
   auto fetch_ids = [&]() {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int pi = cpi[i] < plo ? plo : (cpi[i] > pi_last ? pi_last : cpi[i]);
-      pi = pi < a.max_pages ? pi : a.max_pages - 1;
-      cphys[i] = table_row[pi];
-    }
+    int pi = cpi < plo ? plo : (cpi > pi_last ? pi_last : cpi);
+    pi = pi < a.max_pages ? pi : a.max_pages - 1;
+    cphys = table_row[pi];
   };
   auto advance = [&]() {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      coff[i] += KT;
-      while (coff[i] >= P) {
-        coff[i] -= P;
-        cpi[i] += 1;
-      }
+    coff += KT;
+    while (coff >= P) {
+      coff -= P;
+      cpi += 1;
     }
   };
-  uint4 rk[NV], rv[NV];
-  auto issue = [&]() {
+  struct Tile {
+    uint4 k[NV];
+    uint4 v[NV];
+  };
+  auto issue = [&](Tile& tl) {
+    const int64_t off = static_cast<int64_t>(cphys) * page_bytes + head_bytes + static_cast<int64_t>(coff) * ROWB;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int64_t off = static_cast<int64_t>(cphys[i]) * page_bytes + head_bytes +
-                          static_cast<int64_t>(coff[i]) * ROWB;
-      rk[i] = load16(kbase + off);
-      rv[i] = load16(vbase + off);
+      tl.k[i] = ldg16(kbase + off + i * SSTEP * 16);
+      tl.v[i] = ldg16(vbase + off + i * SSTEP * 16);
     }
     advance();
     fetch_ids();
   };
-  // Registers -> LDS: K row-major, V transposed into contraction order, V
-  // rows outside [t_lo, t_hi) as zeros.
-  auto stage = [&](int tb) {
+  // Registers -> LDS buffer `buf`: K row-major, V transposed into
+  // contraction order, V rows outside [t_lo, t_hi) as zeros.
+  const int kp = kpos(kk);
+  auto stage = [&](const Tile& tl, int buf, int tb) {
+    const int pos = tb + kk;
+    const bool live = pos >= t_lo && pos < t_hi;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int kk = kk0 + i * KSTEP;
-      *reinterpret_cast<uint4*>(&sk[kk * KS + seg * 8]) = rk[i];
-      const int pos = tb + kk;
-      const bool live = pos >= t_lo && pos < t_hi;
-      const uint32_t w[4] = {live ? rv[i].x : 0u, live ? rv[i].y : 0u, live ? rv[i].z : 0u, live ? rv[i].w : 0u};
-      const int kp = kpos(kk);
+      const int sg = sg0 + i * SSTEP;
+      *reinterpret_cast<uint4*>(&sk[buf][kk * KS + sg * 8]) = tl.k[i];
+      const uint32_t w[4] = {live ? tl.v[i].x : 0u, live ? tl.v[i].y : 0u, live ? tl.v[i].z : 0u,
+                             live ? tl.v[i].w : 0u};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sv[(seg * 8 + 2 * e) * VS + kp] = static_cast<uint16_t>(w[e] & 0xFFFFu);
-        sv[(seg * 8 + 2 * e + 1) * VS + kp] = static_cast<uint16_t>(w[e] >> 16);
+        sv[buf][(sg * 8 + 2 * e) * VS + kp] = static_cast<uint16_t>(w[e] & 0xFFFFu);
+        sv[buf][(sg * 8 + 2 * e + 1) * VS + kp] = static_cast<uint16_t>(w[e] >> 16);
       }
     }
   };
 
+  // Waves whose 16 rows are all past the block's last row only stage.
+  const bool wave_rows = r_first + wave * 16 <= r_last;
   const float sl2 = a.scale_log2;
-  auto compute = [&](int tb) {
-    // S^T for keys tb + 16*kb + 4*q4 + i of this lane's row.
-    mq_float4 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
-        sacc[kb] = mfma<KVT>(ka, qb[ks], sacc[kb]);
-      }
-    }
-    float x[8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = tb + kb * 16 + q4 * 4 + i;
-        const float v = sacc[kb][i] * sl2;
-        x[kb * 4 + i] = (key >= lo_r && key < hi_r) ? v : -INFINITY;
-      }
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    if (__any(mn > m)) {
-      const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float alpha = exp2_fast(m - mu);
-      lpart *= alpha;
-#pragma unroll
-      for (int nb = 0; nb < NDB; ++nb) o[nb] *= alpha;
-      m = mn;
-    }
-    const float mu = m == -INFINITY ? 0.0f : m;
-    float pr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pr[j] = exp2_fast(x[j] - mu);
-      lpart += pr[j];
-    }
-    // P^T as the B operand: contraction index 8*q4 + j holds pr[j].
-    if constexpr (KVT == DA_F16) {
-      uint4 pb;
-      pb.x = f16_bits(pr[0]) | (f16_bits(pr[1]) << 16);
-      pb.y = f16_bits(pr[2]) | (f16_bits(pr[3]) << 16);
-      pb.z = f16_bits(pr[4]) | (f16_bits(pr[5]) << 16);
-      pb.w = f16_bits(pr[6]) | (f16_bits(pr[7]) << 16);
-#pragma unroll
-      for (int nb = 0; nb < NDB; ++nb) {
-        const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
-        o[nb] = mfma<KVT>(va, pb, o[nb]);
-      }
-    } else {
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        hi[j] = bf16_bits(pr[j]);
-        lo[j] = bf16_bits(pr[j] - __builtin_bit_cast(float, hi[j] << 16));
-      }
-      uint4 ph, pl;
-      ph.x = hi[0] | (hi[1] << 16);
-      ph.y = hi[2] | (hi[3] << 16);
-      ph.z = hi[4] | (hi[5] << 16);
-      ph.w = hi[6] | (hi[7] << 16);
-      pl.x = lo[0] | (lo[1] << 16);
-      pl.y = lo[2] | (lo[3] << 16);
-      pl.z = lo[4] | (lo[5] << 16);
-      pl.w = lo[6] | (lo[7] << 16);
-#pragma unroll
-      for (int nb = 0; nb < NDB; ++nb) {
-        const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
-        o[nb] = mfma<KVT>(va, ph, o[nb]);
-        o[nb] = mfma<KVT>(va, pl, o[nb]);
-      }
-    }
+  auto compute = [&](int buf, int tb) {
+    if (!wave_rows) return;  // wave-uniform
+    attend_tile<D, KVT, KS, VS>(sk[buf], sv[buf], tb, qb, lo_r, hi_r, sl2, col, q4, m, lpart, o);
   };
 
+  // Tile m's loads go to ring slot m % (PD + 1) PD tiles ahead; at step m
+  // (one barrier) tile m+1 is written to LDS buffer (m+1) % 2 while tile m
+  // is computed from buffer m % 2. The steady-state loop issues only tiles
+  // that exist, so its loads are unconditional and the compiler's wait
+  // counts stay exact; the last tiles drain in an unrolled tail.
   if (ntiles > 0) {
+    Tile ring[PD + 1];
     fetch_ids();
-    issue();
-    for (int n = 0; n < ntiles; ++n) {
-      const int tb = (tile_first + n) * KT;
-      lds_barrier();  // every wave is done reading the previous tile
-      stage(tb);
-      if (n + 1 < ntiles) issue();
-      lds_barrier();  // the tile is in LDS
-      compute(tb);
+#pragma unroll
+    for (int k = 0; k < PD; ++k)
+      if (k < ntiles) issue(ring[k]);
+    stage(ring[0], 0, tile_first * KT);
+    int n = 0;
+    while (n + 2 * PD + 1 < ntiles) {
+#pragma unroll
+      for (int j = 0; j <= PD; ++j) {
+        const int m = n + j;
+        issue(ring[(j + PD) % (PD + 1)]);  // tile m + PD
+        lds_barrier();
+        stage(ring[(j + 1) % (PD + 1)], (m + 1) & 1, (tile_first + m + 1) * KT);
+        compute(m & 1, (tile_first + m) * KT);
+      }
+      n += PD + 1;
+    }
+    // Here ntiles - n <= 2 * PD + 1 and n % (PD + 1) == 0.
+#pragma unroll
+    for (int j = 0; j <= 2 * PD + 1; ++j) {
+      const int m = n + j;
+      if (m < ntiles) {
+        if (m + PD < ntiles) issue(ring[(j + PD) % (PD + 1)]);
+        lds_barrier();
+        if (m + 1 < ntiles) stage(ring[(j + 1) % (PD + 1)], (m + 1) & 1, (tile_first + m + 1) * KT);
+        compute(m & 1, (tile_first + m) * KT);
+      }
     }
   }
 
@@ -348,12 +427,201 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   }
 }
 
+
+// At most 16 query rows per KV head (a few drafted tokens): the four waves
+// share the rows and split the keys. Wave w computes tiles w, w+4, w+8, ...
+// of the split, each staged through the wave's own LDS region (no barrier in
+// the key loop; one tile of loads in flight while the previous one is
+// computed), and the four per-wave states are merged through LDS at the end
+// in wave order.
+template <int D, int KVT>
+__global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
+  constexpr int KW = 4;                 // waves, each on its own tiles
+  constexpr int ROWB = D * 2;
+  constexpr int ROWV = D / 8;
+  constexpr int NVW = KT * ROWV / 64;   // vectors per lane per tensor per tile
+  constexpr int KS = D + KPAD;
+  constexpr int VS = KT + VPAD;
+  constexpr int NKS = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int WAVE_LDS = KT * KS + D * VS;  // 16-bit elements per wave
+  static_assert(NVW >= 1 && NVW * 2 == ROWV, "staging split");
+  __shared__ __align__(16) uint16_t lds[KW * WAVE_LDS];
+
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.z;
+  const int S = a.max_splits;
+  const int rb = blockIdx.y / S;
+  const int s = blockIdx.y - rb * S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+  const int T = a.query_len, G = a.group, P = a.page_size, W = a.window;
+  const int L = a.seq_lens[b];
+
+  const RowBlock blk = row_block(a, rb, 16, L);
+  if (s >= blk.nsplit) return;  // whole work-group, uniform
+  const int plo = blk.pf + s * a.pages_per_split;
+  const int phi = plo + a.pages_per_split < blk.pe ? plo + a.pages_per_split : blk.pe;
+  const int t_lo = blk.lo > plo * P ? blk.lo : plo * P;
+  const int t_hi = blk.hi < phi * P ? blk.hi : phi * P;
+
+  const int r = blk.r_first + col;
+  const bool row_ok = r <= blk.r_last;
+  const int t = row_ok ? r / G : 0;
+  const int g = row_ok ? r - t * G : 0;
+  const int p_r = L - T + t;
+  int hi_r = p_r + 1 < t_hi ? p_r + 1 : t_hi;
+  int lo_r = W > 0 ? p_r + 1 - W : 0;
+  lo_r = lo_r > t_lo ? lo_r : t_lo;
+  if (!row_ok) hi_r = lo_r;
+  const int64_t qrow = (static_cast<int64_t>(b) * T + t) * a.num_q_heads + kvh * G + g;
+
+  uint4 qb[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qb[ks] = make_uint4(0, 0, 0, 0);
+    if (row_ok)
+      qb[ks] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + (qrow * D + ks * 32 + q4 * 8) * 2);
+  }
+  float m = -INFINITY, lpart = 0.0f;
+  mq_float4 o[NDB];
+#pragma unroll
+  for (int nb = 0; nb < NDB; ++nb) o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint16_t* sk = lds + wave * WAVE_LDS;
+  uint16_t* sv = sk + KT * KS;
+  const int tile_first = t_lo / KT;
+  const int tile_end = t_hi > t_lo ? (t_hi + KT - 1) / KT : tile_first;
+  const int my_first = tile_first + wave;
+  const int ntiles = my_first < tile_end ? (tile_end - my_first + KW - 1) / KW : 0;
+
+  // Staging map as in the row-block kernel, within the wave: lane l takes
+  // key l % 32 of the tile and the 16-byte segments l/32 + 2i of its row.
+  const int kk = lane % KT;
+  const int sg0 = lane / KT;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  const int64_t block_bytes = static_cast<int64_t>(P) * ROWB;
+  const int64_t page_bytes = block_bytes * a.num_kv_heads;
+  const int64_t head_bytes = block_bytes * kvh + sg0 * 16;
+  const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
+  const int pi_last = phi > plo ? phi - 1 : plo;
+  // Page cursor of this lane's key, advanced by KW tiles a step; the page id
+  // is fetched one step ahead.
+  int cpi = (my_first * KT + kk) / P;
+  int coff = my_first * KT + kk - cpi * P;
+  int cphys = 0;
+  auto fetch_id = [&]() {
+    int pi = cpi < plo ? plo : (cpi > pi_last ? pi_last : cpi);
+    pi = pi < a.max_pages ? pi : a.max_pages - 1;
+    cphys = table_row[pi];
+  };
+  uint4 rk[NVW], rv[NVW];
+  auto issue = [&]() {
+    const int64_t off = static_cast<int64_t>(cphys) * page_bytes + head_bytes + static_cast<int64_t>(coff) * ROWB;
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) {
+      rk[i] = ldg16(kbase + off + i * 2 * 16);
+      rv[i] = ldg16(vbase + off + i * 2 * 16);
+    }
+    coff += KW * KT;
+    while (coff >= P) {
+      coff -= P;
+      ++cpi;
+    }
+    fetch_id();
+  };
+  const int kp = kpos(kk);
+  auto stage = [&](int tb) {
+    const int pos = tb + kk;
+    const bool live = pos >= t_lo && pos < t_hi;
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) {
+      const int sg = sg0 + 2 * i;
+      *reinterpret_cast<uint4*>(&sk[kk * KS + sg * 8]) = rk[i];
+      const uint32_t w4[4] = {live ? rv[i].x : 0u, live ? rv[i].y : 0u, live ? rv[i].z : 0u, live ? rv[i].w : 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[(sg * 8 + 2 * e) * VS + kp] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
+        sv[(sg * 8 + 2 * e + 1) * VS + kp] = static_cast<uint16_t>(w4[e] >> 16);
+      }
+    }
+  };
+
+  const float sl2 = a.scale_log2;
+  if (ntiles > 0) {
+    fetch_id();
+    issue();
+    for (int n = 0; n < ntiles; ++n) {
+      const int tb = (my_first + n * KW) * KT;
+      stage(tb);  // this wave's region only; LDS operations of a wave stay in order
+      if (n + 1 < ntiles) issue();
+      attend_tile<D, KVT, KS, VS>(sk, sv, tb, qb, lo_r, hi_r, sl2, col, q4, m, lpart, o);
+    }
+  }
+
+  // Merge the four waves' states (same rows) in wave order.
+  float l = lpart + __shfl_xor(lpart, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  __syncthreads();  // every wave is done with its staging region
+  float* mo = reinterpret_cast<float*>(lds);             // [KW][16][D] O of each wave
+  float* mm = mo + KW * 16 * D;                          // [KW][16] m
+  float* ml = mm + KW * 16;                              // [KW][16] l
+  static_assert((KW * 16 * D + 2 * KW * 16) * 4 <= KW * WAVE_LDS * 2, "merge fits the staging LDS");
+#pragma unroll
+  for (int nb = 0; nb < NDB; ++nb)
+    *reinterpret_cast<mq_float4*>(&mo[(wave * 16 + col) * D + nb * 16 + q4 * 4]) = o[nb];
+  if (q4 == 0) {
+    mm[wave * 16 + col] = m;
+    ml[wave * 16 + col] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * D; idx += 256) {
+    const int rr = idx / D;
+    const int d = idx - rr * D;
+    const int row = blk.r_first + rr;
+    if (row > blk.r_last) break;  // rows are in order: every later idx is past too
+    float M = mm[rr];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) M = fmaxf(M, mm[w * 16 + rr]);
+    const float Mu = M == -INFINITY ? 0.0f : M;
+    float lsum = 0.0f, osum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      const float aw = exp2_fast(mm[w * 16 + rr] - Mu);
+      lsum += aw * ml[w * 16 + rr];
+      osum += aw * mo[(w * 16 + rr) * D + d];
+    }
+    const int tt = row / G;
+    const int gg = row - tt * G;
+    const int64_t orow = (static_cast<int64_t>(b) * T + tt) * a.num_q_heads + kvh * G + gg;
+    if (blk.nsplit == 1) {
+      store_elem(a.out, orow * D + d, a.out_dtype, lsum > 0.0f ? osum / lsum : 0.0f);
+    } else {
+      const int64_t srow = orow * S + s;
+      a.ws_o[srow * D + d] = osum;
+      if (d == 0) {
+        a.ws_ml[srow * 2] = M;
+        a.ws_ml[srow * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
-  switch (rows) {
-    case 32: hipLaunchKernelGGL((multi_kernel<D, KVT, 2>), grid, dim3(128), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((multi_kernel<D, KVT, 4>), grid, dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
+  if (rows == 64) {
+    hipLaunchKernelGGL((multi_kernel<D, KVT, 4>), grid, dim3(256), 0, st, a);
+  } else if (rows == 16) {
+    if constexpr (D <= 128)
+      hipLaunchKernelGGL((multi_keys_kernel<D, KVT>), grid, dim3(256), 0, st, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -38,13 +38,16 @@ int64_t min_split_tokens() {
   return kDefaultMinSplitTokens;
 }
 
-// DECODE_ATTN_KERNEL=vector|matrix forces the split kernel (when the matrix
-// one supports the parameters); unset or anything else = automatic.
+// DECODE_ATTN_KERNEL=vector|matrix forces the single-query split kernel
+// (when the matrix one supports the parameters); DECODE_ATTN_KERNEL=rows
+// makes the multi-token pass use 64-row blocks even for 16 rows or fewer;
+// unset or anything else = automatic.
 int32_t forced_kernel() {
   const char* s = std::getenv("DECODE_ATTN_KERNEL");
   if (!s) return -1;
   if (std::strcmp(s, "vector") == 0) return 0;
   if (std::strcmp(s, "matrix") == 0) return 1;
+  if (std::strcmp(s, "rows") == 0) return 2;
   return -1;
 }
 
@@ -167,7 +170,9 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   const int64_t T = plan->query_len;
   const int64_t G = plan->group;
   const int64_t R = T * G;
-  const int64_t QB = R <= 32 ? 32 : 64;
+  // Up to 16 rows (D <= 128): four waves share the rows and split the keys;
+  // otherwise four waves of 16 rows share each key tile.
+  const int64_t QB = (R <= 16 && p.head_dim <= 128 && forced_kernel() != 2) ? 16 : 64;
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);

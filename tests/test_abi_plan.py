@@ -217,7 +217,7 @@ def test_multi_token_plans(lib):
     # forced: the longest row block's pages over num_splits
     pl = plan(params(batch=3, query_len=16, num_splits=5), lens)
     assert pl.max_splits == 5 and pl.pages_per_split == math.ceil(math.ceil(3000 / 16) / 5)
-    # 2 tokens x G 4 = 8 rows: blocks of 32 rows
+    # 2 tokens x G 4 = 8 rows: one block of 64 rows
     pl = plan(params(batch=1, query_len=2, num_splits=1), [100])
     assert pl.info.split_work_groups == 8 and pl.workspace_bytes == 0
 
