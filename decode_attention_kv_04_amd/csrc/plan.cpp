@@ -24,6 +24,12 @@ namespace {
 // Splits per KV head are sized so the split pass has about this many
 // work-groups per compute unit in total.
 constexpr int64_t kTargetGroupsPerCu = 9;
+// The multi-token kernel with 64-row blocks does matrix work on every key it
+// loads: it is fastest with one round of resident work-groups (2 per compute
+// unit at head_dim 128, by registers), so each row block's keys are split
+// only as far as needed to fill that round (a sweep of split counts on
+// 16..512-token suffixes over 0.5-8k-token contexts).
+int64_t resident_row_groups_per_cu(int32_t head_dim) { return head_dim <= 64 ? 4 : (head_dim <= 128 ? 2 : 1); }
 // A split never holds fewer attended tokens than this (the pages' 256-token
 // switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
 constexpr int64_t kDefaultMinSplitTokens = 256;
@@ -92,11 +98,13 @@ int32_t group_tile_for(int32_t G) {
 
 namespace {
 
-// Pages per split that give the split pass about kTargetGroupsPerCu
-// work-groups per compute unit, at least the minimum split length.
-int64_t heuristic_split_pages(int64_t total_np, int64_t max_np, int64_t num_kv_heads, int64_t num_cus, int64_t P) {
+// Pages per split that give the split pass about `per_cu` work-groups per
+// compute unit (kTargetGroupsPerCu by default), at least the minimum split
+// length.
+int64_t heuristic_split_pages(int64_t total_np, int64_t max_np, int64_t num_kv_heads, int64_t num_cus, int64_t P,
+                              int64_t per_cu = kTargetGroupsPerCu) {
   const int64_t work = total_np * num_kv_heads;  // page-heads to stream
-  const int64_t target = num_cus * kTargetGroupsPerCu;
+  const int64_t target = num_cus * per_cu;
   int64_t c = ceil_div(work, target);
   c = std::max(c, ceil_div(min_split_tokens(), P));
   return std::min(c, max_np);
@@ -206,7 +214,15 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   } else if (p.num_splits > 0) {
     c = ceil_div(max_np, p.num_splits);
   } else {
-    c = heuristic_split_pages(total_np, max_np, p.num_kv_heads, plan->num_cus, P);
+    if (QB == 16) {
+      c = heuristic_split_pages(total_np, max_np, p.num_kv_heads, plan->num_cus, P);
+    } else {
+      const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * nrb;
+      const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim),
+                                    blocks);
+      c = ceil_div(max_np, std::max<int64_t>(1, want));
+      c = std::min(max_np, std::max(c, ceil_div(min_split_tokens(), P)));
+    }
   }
   c = std::max<int64_t>(c, 1);
   c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));  // grid y = row blocks x splits
