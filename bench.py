@@ -12,6 +12,11 @@ value   = algorithmic KV bytes per step / step time (GB/s), where the
 roofline: the split kernel alone, timed with HIP events on the stream it is
           launched on, against the 8 TB/s HBM peak.
 cpu_baseline: the f64 CPU oracle on a bounded sample of the same batch.
+Also reported, each timed the same way: the fixed-order mode on the same
+batch (fixed_order), several new tokens per sequence on their own workloads
+(multi_token: a 4-token check over the long-context batch and a 128-token
+suffix prefill, each against its HBM or matrix-core roofline) and the K/V
+append of 1 and 256 tokens per sequence (append_kv).
 """
 import argparse
 import ctypes
@@ -136,8 +141,8 @@ def cpu_baseline(w, budget_s=12.0):
     for b in range(spec.batch):
         a = workloads.to_numpy_inputs(w, [b])
         t = time.perf_counter()
-        oracle.decode_attention(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"],
-                                a["page_size"], a["scale"], a["window"])
+        fn = oracle.prefill_attention if a["q"].ndim == 4 else oracle.decode_attention
+        fn(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"], a["page_size"], a["scale"], a["window"])
         spent += time.perf_counter() - t
         t0, t1 = w.attended()[b]
         done_bytes += (t1 - t0) * spec.num_kv_heads * spec.head_dim * elt * 2
@@ -187,6 +192,62 @@ def measure_fixed_order(w, binding, lib, dev, stream, iters):
             "work_groups": plan.info.split_work_groups}
 
 
+MFMA_PEAK_TFLOPS_16BIT = 2500.0  # dense f16/bf16 matrix-core peak
+MULTI_TOKEN_WORKLOADS = ("verify_long", "suffix_prefill")
+
+
+def attention_flops(w):
+    """2 FLOPs per multiply-add of q.k and of p.v: 4*D per (query head, key)."""
+    T = w.spec.query_len
+    keys = 0
+    for L in w.seq_lens_host.tolist():
+        for t in range(T):
+            p = L - T + t
+            keys += min(p + 1, w.window) if w.window > 0 else p + 1
+    return keys * w.spec.num_q_heads * w.spec.head_dim * 4
+
+
+def measure_multi_token(binding, workloads, lib, dev, stream, iters):
+    """Several new tokens per sequence: time decode_attn_run on each
+    multi-token workload and place it against its roofline (HBM when the
+    FLOPs per algorithmic byte are below the 16-bit matrix-core ridge,
+    matrix cores otherwise)."""
+    import torch
+    ridge = MFMA_PEAK_TFLOPS_16BIT * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    res = []
+    for name in MULTI_TOKEN_WORKLOADS:
+        spec = workloads.NAMED[name]
+        w = workloads.make_workload(spec, dev)
+        params = binding.params_for(w.q, w.k_pool, w.page_table, window=w.window, scale=w.scale,
+                                    out_dtype=spec.out_dtype)
+        plan = binding.decode_attn_plan(params, w.seq_lens_host, device=dev.index or 0)
+        out = torch.empty(w.q.shape, dtype=workloads.DTYPES[spec.out_dtype], device=dev)
+        ws = binding.alloc_workspace(plan, dev)
+        ptrs = [w.q.data_ptr(), w.k_pool.data_ptr(), w.v_pool.data_ptr(), w.page_table.data_ptr(),
+                w.seq_lens.data_ptr(), out.data_ptr(), ws.data_ptr() if ws is not None else None,
+                plan.workspace_bytes, stream.cuda_stream]
+
+        def run():
+            st = lib.decode_attn_run(plan.handle, *ptrs)
+            if st != 0:
+                raise binding.DecodeAttnError(st, f"decode_attn_run ({name})")
+
+        for _ in range(3):
+            run()
+        ms = time_on_stream(run, iters, stream)
+        by, fl = w.kv_bytes(), attention_flops(w)
+        gbs, tfs = by / (ms * 1e-3) / 1e9, fl / (ms * 1e-3) / 1e12
+        hbm = fl / by < ridge
+        res.append({"workload": spec.name, "query_len": spec.query_len, "us": round(ms * 1e3, 2),
+                    "GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 1), "bound": "hbm" if hbm else "mfma",
+                    "frac": round(gbs / HBM_PEAK_GBPS if hbm else tfs / MFMA_PEAK_TFLOPS_16BIT, 4),
+                    "algorithmic_bytes": by, "flops": fl, "work_groups": plan.info.split_work_groups})
+        print(f"[bench] {name}: {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del w, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def measure_append(w, lib, params, stream, tokens, iters):
     """Time decode_attn_append_kv writing `tokens` rows per sequence at the
     end of each sequence's context (positions L-T .. L-1), with new rows equal
@@ -234,6 +295,7 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the planner decides")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-multi-token", action="store_true", help="skip the multi-token workloads")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy a buffer of known size once (counter calibration)")
     args = ap.parse_args()
@@ -306,6 +368,9 @@ def main():
     # the same batch: whole step, chunks of FIXED_CHUNK tokens.
     fixed = measure_fixed_order(w, binding, lib, dev, stream, args.steps)
 
+    # Several new tokens per sequence (drafted-token check, suffix prefill).
+    multi = [] if args.no_multi_token else measure_multi_token(binding, workloads, lib, dev, stream, args.steps)
+
     # K/V append (the step before the path): one token per sequence, and a
     # 256-token suffix; written rows equal the resident rows.
     append_stats = [measure_append(w, lib, params, stream, t, args.steps) for t in (1, 256)]
@@ -347,8 +412,9 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("split pass, q.K on the matrix cores (da::split_kernel_mfma)" if plan.info.split_kernel
-                       else "split pass, vector q.K (da::split_kernel)"),
+            "kernel": {0: "split pass, vector q.K (da::split_kernel)",
+                       1: "split pass, q.K on the matrix cores (da::split_kernel_mfma)",
+                       2: "multi-token split pass (da::multi_kernel / da::multi_keys_kernel)"}[plan.info.split_kernel],
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -359,6 +425,7 @@ def main():
         },
         "combine_us": round(combine_ms * 1e3, 2),
         "fixed_order": fixed,
+        "multi_token": multi,
         "append_kv": append_stats,
         "plan_host_us": round(plan_us, 1),
         "hbm_read_ceiling_GBps": ceilings.get("stream"),
