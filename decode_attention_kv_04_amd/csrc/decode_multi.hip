@@ -85,91 +85,159 @@ __device__ __forceinline__ uint4 ldg16(const char* p) { return *reinterpret_cast
 // tile's K/V loads stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One 32-key tile for the 16 query rows of a wave: S^T = K Q^T from the K
-// tile (row-major, row stride KS), masking to the row's keys [lo_r, hi_r),
-// online-softmax update of (m, lpart, O^T), O^T += V^T P^T from the
-// transposed V tile (row stride VS). Lane (col, q4) holds row col's scores
-// for keys tb + 16*kb + 4*q4 + i and its output dims 16*nb + 4*q4 + i.
-template <int D, int KVT, int KS, int VS>
-__device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* sv, int tb, const uint4 (&qb)[D / 32],
-                                            int lo_r, int hi_r, float sl2, int col, int q4, float& m, float& lpart,
-                                            mq_float4 (&o)[D / 16]) {
+// One lane's share of 16 query rows of a wave: the row in column `col` of
+// the MFMA tiles (its q as the B operand of S^T = K Q^T, its keys within the
+// split, its online-softmax state and output dims 16*nb + 4*q4 + i).
+template <int D>
+struct RowGroup {
+  uint4 qb[D / 32];
+  int lo, hi;     // keys [lo, hi) of the row within the split (empty if no row)
+  int64_t qrow;   // flat (sequence, token, query head) index
+  bool ok;        // a real row
+  float m, lpart;
+  mq_float4 o[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void init_rows(RowGroup<D>& g, const KernelArgs& a, int r, int r_last, int b, int kvh,
+                                          int L, int t_lo, int t_hi, int q4) {
+  const int T = a.query_len, G = a.group;
+  g.ok = r <= r_last;
+  const int t = g.ok ? r / G : 0;
+  const int gh = g.ok ? r - t * G : 0;
+  const int p = L - T + t;
+  g.hi = p + 1 < t_hi ? p + 1 : t_hi;
+  g.lo = a.window > 0 ? p + 1 - a.window : 0;
+  g.lo = g.lo > t_lo ? g.lo : t_lo;
+  if (!g.ok) g.hi = g.lo;
+  g.qrow = (static_cast<int64_t>(b) * T + t) * a.num_q_heads + kvh * G + gh;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    g.qb[ks] = make_uint4(0, 0, 0, 0);
+    if (g.ok)
+      g.qb[ks] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + (g.qrow * D + ks * 32 + q4 * 8) * 2);
+  }
+  g.m = -INFINITY;
+  g.lpart = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) g.o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// One 32-key tile for NR row groups of a wave, sharing each operand read:
+// S^T = K Q^T from the K tile (row-major, row stride KS), masking to each
+// row's keys, online-softmax update, O^T += V^T P^T from the transposed V
+// tile (row stride VS). Lane (col, q4) holds its rows' scores for keys
+// tb + 16*kb + 4*q4 + i.
+template <int D, int KVT, int KS, int VS, int NR>
+__device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* sv, int tb, RowGroup<D> (&rg)[NR],
+                                            float sl2, int col, int q4) {
   constexpr int NKS = D / 32;
   constexpr int NDB = D / 16;
-  mq_float4 sacc[2];
+  mq_float4 sacc[NR][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    sacc[kb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g = 0; g < NR; ++g)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int kb = 0; kb < 2; ++kb) sacc[g][kb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       const uint4 ka = *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
-      sacc[kb] = mfma<KVT>(ka, qb[ks], sacc[kb]);
+#pragma unroll
+      for (int g = 0; g < NR; ++g) sacc[g][kb] = mfma<KVT>(ka, rg[g].qb[ks], sacc[g][kb]);
     }
   }
-  float x[8];
+  // P^T as the B operand of each row group: contraction index 8*q4 + j.
+  uint4 ph[NR], pl[NR];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int g = 0; g < NR; ++g) {
+    float x[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = tb + kb * 16 + q4 * 4 + i;
-      const float v = sacc[kb][i] * sl2;
-      x[kb * 4 + i] = (key >= lo_r && key < hi_r) ? v : -INFINITY;
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = tb + kb * 16 + q4 * 4 + i;
+        const float v = sacc[g][kb][i] * sl2;
+        x[kb * 4 + i] = (key >= rg[g].lo && key < rg[g].hi) ? v : -INFINITY;
+      }
     }
-  }
-  float mt = x[0];
+    float mt = x[0];
 #pragma unroll
-  for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float mn = fmaxf(m, mt);
-  if (__any(mn > m)) {
-    const float mu = mn == -INFINITY ? 0.0f : mn;
-    const float alpha = exp2_fast(m - mu);
-    lpart *= alpha;
+    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(rg[g].m, mt);
+    if (__any(mn > rg[g].m)) {
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      const float alpha = exp2_fast(rg[g].m - mu);
+      rg[g].lpart *= alpha;
 #pragma unroll
-    for (int nb = 0; nb < NDB; ++nb) o[nb] *= alpha;
-    m = mn;
-  }
-  const float mu = m == -INFINITY ? 0.0f : m;
-  float pr[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    pr[j] = exp2_fast(x[j] - mu);
-    lpart += pr[j];
-  }
-  // P^T as the B operand: contraction index 8*q4 + j holds pr[j].
-  if constexpr (KVT == DA_F16) {
-    uint4 pb;
-    pb.x = f16_bits(pr[0]) | (f16_bits(pr[1]) << 16);
-    pb.y = f16_bits(pr[2]) | (f16_bits(pr[3]) << 16);
-    pb.z = f16_bits(pr[4]) | (f16_bits(pr[5]) << 16);
-    pb.w = f16_bits(pr[6]) | (f16_bits(pr[7]) << 16);
-#pragma unroll
-    for (int nb = 0; nb < NDB; ++nb) {
-      const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
-      o[nb] = mfma<KVT>(va, pb, o[nb]);
+      for (int nb = 0; nb < NDB; ++nb) rg[g].o[nb] *= alpha;
+      rg[g].m = mn;
     }
-  } else {
-    uint32_t hi[8], lo[8];
+    const float mu = rg[g].m == -INFINITY ? 0.0f : rg[g].m;
+    float pr[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      hi[j] = bf16_bits(pr[j]);
-      lo[j] = bf16_bits(pr[j] - __builtin_bit_cast(float, hi[j] << 16));
+      pr[j] = exp2_fast(x[j] - mu);
+      rg[g].lpart += pr[j];
     }
-    uint4 ph, pl;
-    ph.x = hi[0] | (hi[1] << 16);
-    ph.y = hi[2] | (hi[3] << 16);
-    ph.z = hi[4] | (hi[5] << 16);
-    ph.w = hi[6] | (hi[7] << 16);
-    pl.x = lo[0] | (lo[1] << 16);
-    pl.y = lo[2] | (lo[3] << 16);
-    pl.z = lo[4] | (lo[5] << 16);
-    pl.w = lo[6] | (lo[7] << 16);
+    if constexpr (KVT == DA_F16) {
+      ph[g].x = f16_bits(pr[0]) | (f16_bits(pr[1]) << 16);
+      ph[g].y = f16_bits(pr[2]) | (f16_bits(pr[3]) << 16);
+      ph[g].z = f16_bits(pr[4]) | (f16_bits(pr[5]) << 16);
+      ph[g].w = f16_bits(pr[6]) | (f16_bits(pr[7]) << 16);
+    } else {
+      uint32_t hi[8], lo[8];
 #pragma unroll
-    for (int nb = 0; nb < NDB; ++nb) {
-      const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
-      o[nb] = mfma<KVT>(va, ph, o[nb]);
-      o[nb] = mfma<KVT>(va, pl, o[nb]);
+      for (int j = 0; j < 8; ++j) {
+        hi[j] = bf16_bits(pr[j]);
+        lo[j] = bf16_bits(pr[j] - __builtin_bit_cast(float, hi[j] << 16));
+      }
+      ph[g].x = hi[0] | (hi[1] << 16);
+      ph[g].y = hi[2] | (hi[3] << 16);
+      ph[g].z = hi[4] | (hi[5] << 16);
+      ph[g].w = hi[6] | (hi[7] << 16);
+      pl[g].x = lo[0] | (lo[1] << 16);
+      pl[g].y = lo[2] | (lo[3] << 16);
+      pl[g].z = lo[4] | (lo[5] << 16);
+      pl[g].w = lo[6] | (lo[7] << 16);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NDB; ++nb) {
+    const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
+      rg[g].o[nb] = mfma<KVT>(va, ph[g], rg[g].o[nb]);
+      if constexpr (KVT != DA_F16) rg[g].o[nb] = mfma<KVT>(va, pl[g], rg[g].o[nb]);
+    }
+  }
+}
+
+// The row's l is split over its four lanes (one per key group): sum them,
+// then write O / l (one split) or the state (m, l, O) to slot s.
+template <int D>
+__device__ __forceinline__ void finish_rows(const KernelArgs& a, RowGroup<D>& g, int nsplit, int s, int q4) {
+  float l = g.lpart + __shfl_xor(g.lpart, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!g.ok) return;
+  if (nsplit == 1) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_elem(a.out, g.qrow * D + nb * 16 + q4 * 4 + i, a.out_dtype, l > 0.0f ? g.o[nb][i] * inv : 0.0f);
+    }
+  } else {
+    const int64_t srow = g.qrow * a.max_splits + s;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+      *reinterpret_cast<mq_float4*>(a.ws_o + srow * D + nb * 16 + q4 * 4) = g.o[nb];
+    if (q4 == 0) {
+      a.ws_ml[srow * 2] = g.m;
+      a.ws_ml[srow * 2 + 1] = l;
     }
   }
 }
@@ -202,15 +270,18 @@ __device__ __forceinline__ RowBlock row_block(const KernelArgs& a, int rb, int q
 #ifndef DA_MQ_PREFETCH
 #define DA_MQ_PREFETCH 3
 #endif
-template <int D>
+template <int D, int NR>
 constexpr int prefetch_tiles() {
-  return D >= 256 ? 1 : DA_MQ_PREFETCH;
+  return (D >= 256 || NR > 1) ? 1 : DA_MQ_PREFETCH;
 }
 
-template <int D, int KVT, int NQ>
+// NR: row groups of 16 per wave. Two groups per wave (sharing every K and
+// V^T operand read) were measured slower at head_dim 128 (one wave per SIMD
+// by registers), so the launch uses NR = 1.
+template <int D, int KVT, int NQ, int NR>
 __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   constexpr int NT = 64 * NQ;           // threads
-  constexpr int QB = 16 * NQ;           // query rows per work-group
+  constexpr int QB = 16 * NQ * NR;      // query rows per work-group
   constexpr int ROWB = D * 2;           // bytes per K/V row
   constexpr int ROWV = D / 8;           // 16-byte vectors per row
   constexpr int NV = KT * ROWV / NT;    // vectors per thread per tensor per tile
@@ -218,7 +289,7 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   constexpr int VS = KT + VPAD;         // transposed-V row stride (elements)
   constexpr int NKS = D / 32;           // k-steps of q.K
   constexpr int NDB = D / 16;           // 16-dim blocks of P.V
-  constexpr int PD = prefetch_tiles<D>();
+  constexpr int PD = prefetch_tiles<D, NR>();
   static_assert(NV >= 1 && NV * NT == KT * ROWV, "staging split");
   // Two LDS buffers: one tile is computed while the next one is written.
   __shared__ __align__(16) uint16_t sk[2][KT * KS];
@@ -263,31 +334,11 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   const int t_lo = lo_blk > plo * P ? lo_blk : plo * P;
   const int t_hi = hi_blk < phi * P ? hi_blk : phi * P;
 
-  // This lane's query row and its own keys within the split.
-  const int r = r_first + wave * 16 + col;
-  const bool row_ok = r <= r_last;
-  const int t = row_ok ? r / G : 0;
-  const int g = row_ok ? r - t * G : 0;
-  const int p_r = L - T + t;
-  int hi_r = p_r + 1 < t_hi ? p_r + 1 : t_hi;
-  int lo_r = W > 0 ? p_r + 1 - W : 0;
-  lo_r = lo_r > t_lo ? lo_r : t_lo;
-  if (!row_ok) hi_r = lo_r;  // no keys
-  const int64_t qrow = (static_cast<int64_t>(b) * T + t) * a.num_q_heads + kvh * G + g;
-
-  // q as the B operand of S^T = K Q^T: dims 32*ks + 8*q4 .. +8 of this row.
-  uint4 qb[NKS];
+  // This lane's query rows (one per row group) and their keys in the split.
+  RowGroup<D> rg[NR];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    qb[ks] = make_uint4(0, 0, 0, 0);
-    if (row_ok)
-      qb[ks] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + (qrow * D + ks * 32 + q4 * 8) * 2);
-  }
-
-  float m = -INFINITY, lpart = 0.0f;
-  mq_float4 o[NDB];
-#pragma unroll
-  for (int nb = 0; nb < NDB; ++nb) o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g = 0; g < NR; ++g)
+    init_rows(rg[g], a, r_first + (wave * NR + g) * 16 + col, r_last, b, kvh, L, t_lo, t_hi, q4);
 
   const int tile_first = t_lo / KT;
   const int ntiles = t_hi > t_lo ? (t_hi + KT - 1) / KT - tile_first : 0;
@@ -358,12 +409,12 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
     }
   };
 
-  // Waves whose 16 rows are all past the block's last row only stage.
-  const bool wave_rows = r_first + wave * 16 <= r_last;
+  // Waves whose rows are all past the block's last row only stage.
+  const bool wave_rows = r_first + wave * NR * 16 <= r_last;
   const float sl2 = a.scale_log2;
   auto compute = [&](int buf, int tb) {
     if (!wave_rows) return;  // wave-uniform
-    attend_tile<D, KVT, KS, VS>(sk[buf], sv[buf], tb, qb, lo_r, hi_r, sl2, col, q4, m, lpart, o);
+    attend_tile<D, KVT, KS, VS, NR>(sk[buf], sv[buf], tb, rg, sl2, col, q4);
   };
 
   // Tile m's loads go to ring slot m % (PD + 1) PD tiles ahead; at step m
@@ -403,28 +454,8 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
     }
   }
 
-  // The row's l is split over its four lanes (one per key group).
-  float l = lpart + __shfl_xor(lpart, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (!row_ok) return;
-  if (nsplit == 1) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < NDB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store_elem(a.out, qrow * D + nb * 16 + q4 * 4 + i, a.out_dtype, l > 0.0f ? o[nb][i] * inv : 0.0f);
-    }
-  } else {
-    const int64_t srow = qrow * S + s;
-#pragma unroll
-    for (int nb = 0; nb < NDB; ++nb)
-      *reinterpret_cast<mq_float4*>(a.ws_o + srow * D + nb * 16 + q4 * 4) = o[nb];
-    if (q4 == 0) {
-      a.ws_ml[srow * 2] = m;
-      a.ws_ml[srow * 2 + 1] = l;
-    }
-  }
+  for (int g = 0; g < NR; ++g) finish_rows(a, rg[g], nsplit, s, q4);
 }
 
 
@@ -468,28 +499,8 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
   const int t_lo = blk.lo > plo * P ? blk.lo : plo * P;
   const int t_hi = blk.hi < phi * P ? blk.hi : phi * P;
 
-  const int r = blk.r_first + col;
-  const bool row_ok = r <= blk.r_last;
-  const int t = row_ok ? r / G : 0;
-  const int g = row_ok ? r - t * G : 0;
-  const int p_r = L - T + t;
-  int hi_r = p_r + 1 < t_hi ? p_r + 1 : t_hi;
-  int lo_r = W > 0 ? p_r + 1 - W : 0;
-  lo_r = lo_r > t_lo ? lo_r : t_lo;
-  if (!row_ok) hi_r = lo_r;
-  const int64_t qrow = (static_cast<int64_t>(b) * T + t) * a.num_q_heads + kvh * G + g;
-
-  uint4 qb[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    qb[ks] = make_uint4(0, 0, 0, 0);
-    if (row_ok)
-      qb[ks] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + (qrow * D + ks * 32 + q4 * 8) * 2);
-  }
-  float m = -INFINITY, lpart = 0.0f;
-  mq_float4 o[NDB];
-#pragma unroll
-  for (int nb = 0; nb < NDB; ++nb) o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
+  RowGroup<D> rg[1];
+  init_rows(rg[0], a, blk.r_first + col, blk.r_last, b, kvh, L, t_lo, t_hi, q4);
 
   uint16_t* sk = lds + wave * WAVE_LDS;
   uint16_t* sv = sk + KT * KS;
@@ -559,12 +570,12 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
       const int tb = (my_first + n * KW) * KT;
       stage(tb);  // this wave's region only; LDS operations of a wave stay in order
       if (n + 1 < ntiles) issue();
-      attend_tile<D, KVT, KS, VS>(sk, sv, tb, qb, lo_r, hi_r, sl2, col, q4, m, lpart, o);
+      attend_tile<D, KVT, KS, VS, 1>(sk, sv, tb, rg, sl2, col, q4);
     }
   }
 
   // Merge the four waves' states (same rows) in wave order.
-  float l = lpart + __shfl_xor(lpart, 16, 64);
+  float l = rg[0].lpart + __shfl_xor(rg[0].lpart, 16, 64);
   l += __shfl_xor(l, 32, 64);
   __syncthreads();  // every wave is done with its staging region
   float* mo = reinterpret_cast<float*>(lds);             // [KW][16][D] O of each wave
@@ -573,9 +584,9 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
   static_assert((KW * 16 * D + 2 * KW * 16) * 4 <= KW * WAVE_LDS * 2, "merge fits the staging LDS");
 #pragma unroll
   for (int nb = 0; nb < NDB; ++nb)
-    *reinterpret_cast<mq_float4*>(&mo[(wave * 16 + col) * D + nb * 16 + q4 * 4]) = o[nb];
+    *reinterpret_cast<mq_float4*>(&mo[(wave * 16 + col) * D + nb * 16 + q4 * 4]) = rg[0].o[nb];
   if (q4 == 0) {
-    mm[wave * 16 + col] = m;
+    mm[wave * 16 + col] = rg[0].m;
     ml[wave * 16 + col] = l;
   }
   __syncthreads();
@@ -614,7 +625,7 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
   if (rows == 64) {
-    hipLaunchKernelGGL((multi_kernel<D, KVT, 4>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((multi_kernel<D, KVT, 4, 1>), grid, dim3(256), 0, st, a);
   } else if (rows == 16) {
     if constexpr (D <= 128)
       hipLaunchKernelGGL((multi_keys_kernel<D, KVT>), grid, dim3(256), 0, st, a);

@@ -76,7 +76,9 @@ __device__ __forceinline__ void row_bcast_all(float x, float* out) {
   }
 }
 
-template <int D, int KVT, int GT>
+// FIXED: fixed-order mode (chunks_per_group consecutive chunks per
+// work-group, one state per chunk; a chunk's state depends only on its keys).
+template <int D, int KVT, int GT, bool FIXED>
 __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a) {
   static_assert(KVT == DA_F16 || KVT == DA_BF16, "matrix-core path needs a 16-bit KV type");
   static_assert(D == 128, "head_dim (256 does not fit the register budget in this layout)");
@@ -111,11 +113,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
   const int cp = a.pages_per_split;
   int nsplit = (pe - pf + cp - 1) / cp;
   nsplit = nsplit < 1 ? 1 : (nsplit > a.max_splits ? a.max_splits : nsplit);
-  if (s >= nsplit) return;  // whole work-group, uniform
-  const int plo = pf + s * cp;
-  const int phi = (plo + cp < pe) ? plo + cp : pe;
-  const int t_lo = L > 0 ? (t0 > plo * P ? t0 : plo * P) : 0;
-  const int t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
+  // Splits (chunks in the fixed-order mode) [k_begin, k_end) of this group.
+  const int k_begin = FIXED ? s * a.chunks_per_group : s;
+  if (k_begin >= nsplit) return;  // whole work-group, uniform
+  const int k_end = FIXED ? (k_begin + a.chunks_per_group < nsplit ? k_begin + a.chunks_per_group : nsplit)
+                          : k_begin + 1;
 
   const int G = a.group;
   const int h0 = kvh * G;
@@ -130,13 +132,6 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
       qb[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + ((qrow0 + c) * D + 32 * j + 8 * r) * ELT);
   }
 
-  float m = -INFINITY, l = 0.0f;  // head c, row slot r
-  float o[GT][DPL];
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) o[g][i] = 0.0f;
-
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   const int64_t block_bytes = static_cast<int64_t>(P) * RB;
@@ -146,236 +141,261 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
   const uint32_t k_lane_off = static_cast<uint32_t>(key_of_lane * RB + 8 * r * ELT);
   const uint32_t v_lane_off = static_cast<uint32_t>(r * RB + c * E * ELT);
 
-  const int tile_first = t_lo / TR;
-  const int tile_end = (t_hi + TR - 1) / TR;
-  const int my_first = tile_first + wave;
-  const int ntiles = my_first < tile_end ? (tile_end - my_first + kWaves - 1) / kWaves : 0;
-
-  struct Tile {
-    uint4 k[NJ];
-    uint4 v[4][VPL];
-  };
-
-  // Load cursor (one page per tile: P is a multiple of 16).
-  constexpr int STEP = kWaves * TR;
-  const int step_p = STEP / P;
-  const int step_r = STEP - step_p * P;
-  const int pi_last = phi > plo ? phi - 1 : plo;
-  int cur_pi = (my_first * TR) / P;
-  int cur_off = my_first * TR - cur_pi * P;
-  int cur_phys = 0;
-  auto fetch_id = [&]() {
-    const int pi = cur_pi < plo ? plo : (cur_pi > pi_last ? pi_last : cur_pi);
-    cur_phys = table_row[pi];
-  };
-  auto issue = [&](Tile& t) {
-    const int64_t off = static_cast<int64_t>(cur_phys) * page_bytes + head_bytes + static_cast<int64_t>(cur_off) * RB;
-    const char* kp = kbase + off + k_lane_off;
-    const char* vp = vbase + off + v_lane_off;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) t.k[j] = load16(kp + 32 * j * ELT);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) t.v[i][v] = load16(vp + 4 * i * RB + v * SEG * ELT);
-    cur_pi += step_p;
-    cur_off += step_r;
-    if (cur_off >= P) {
-      cur_off -= P;
-      cur_pi += 1;
-    }
-    fetch_id();
-  };
-
-  const float sl2 = a.scale_log2;
-  // One tile. FULL: every row of the tile is attended (no masking at all);
-  // otherwise rows outside [t_lo, t_hi) get score -inf and zero V rows.
-  auto compute = [&](const Tile& t, int tile, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    const int tb = tile * TR;
-    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc = mfma_16x16x32<KVT>(t.k[j], qb[j], acc);
-    bool valid[4];
-    float x[4];  // scores in base-2 units
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (FULL) {
-        valid[i] = true;
-        x[i] = acc[i] * sl2;
-      } else {
-        const int tok = tb + 4 * i + r;
-        valid[i] = tok >= t_lo && tok < t_hi;
-        x[i] = valid[i] ? acc[i] * sl2 : -INFINITY;
-      }
-    }
-    const float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    const float mn = fmaxf(m, mt);
-    // P.V for this tile given the running max (p = 2^(x - m)).
-    auto accumulate = [&]() {
-      const float mu = (m == -INFINITY) ? 0.0f : m;
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[i] - mu);
-      l += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float pb[GT];
-        row_bcast_all<GT>(p[i], pb);
-        if constexpr (FULL) {
-          // Each V element is widened inside its FMA (v_fma_mix for fp16).
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) {
-            const uint32_t w[4] = {t.v[i][v].x, t.v[i][v].y, t.v[i][v].z, t.v[i][v].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-#pragma unroll
-              for (int g = 0; g < GT; ++g) {
-                o[g][v * E + 2 * k] = fmaf(pb[g], lo16_to_f32<KVT>(w[k]), o[g][v * E + 2 * k]);
-                o[g][v * E + 2 * k + 1] = fmaf(pb[g], hi16_to_f32<KVT>(w[k]), o[g][v * E + 2 * k + 1]);
-              }
-            }
-          }
-        } else {
-          float vf[DPL];
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) unpack<KVT>(t.v[i][v], vf + v * E);
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) vf[e] = valid[i] ? vf[e] : 0.0f;
-#pragma unroll
-          for (int g = 0; g < GT; ++g)
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) o[g][e] = fmaf(pb[g], vf[e], o[g][e]);
-        }
-      }
-    };
-    // O and l are rescaled only when some running max of the wave grew; the
-    // accumulation is written out in both arms so that the common arm keeps
-    // O in place.
-    if (__any(c < G && mn > m)) {
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
-      const float alpha = exp2_fast(m - mu);
-      l *= alpha;
-      m = mn;
-      float ab[GT];
-      row_bcast_all<GT>(alpha, ab);
-#pragma unroll
-      for (int g = 0; g < GT; ++g)
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) o[g][i] *= ab[g];
-      accumulate();
-    } else {
-      accumulate();
-    }
-  };
-  auto compute_tile = [&](const Tile& t, int tile) {
-    const int tb = tile * TR;
-    if (tb >= t_lo && tb + TR <= t_hi)
-      compute(t, tile, std::true_type());
-    else
-      compute(t, tile, std::false_type());
-  };
-
-  // Ring of kPD + 1 tiles, steady state with unconditional loads, unrolled
-  // drain (as in the vector kernel).
-  if (ntiles > 0) {
-    Tile buf[kPD + 1];
-    fetch_id();
-#pragma unroll
-    for (int k = 0; k < kPD; ++k)
-      if (k < ntiles) issue(buf[k]);
-    int n = 0;
-    while (n + 2 * kPD < ntiles) {
-#pragma unroll
-      for (int j = 0; j <= kPD; ++j) {
-        issue(buf[(j + kPD) % (kPD + 1)]);
-        compute_tile(buf[j], my_first + (n + j) * kWaves);
-      }
-      n += kPD + 1;
-    }
-#pragma unroll
-    for (int j = 0; j < 2 * kPD; ++j) {
-      if (n + j < ntiles) {
-        if (n + j + kPD < ntiles) issue(buf[(j + kPD) % (kPD + 1)]);
-        compute_tile(buf[j % (kPD + 1)], my_first + (n + j) * kWaves);
-      }
-    }
-  }
-
-  // Every lane of row slot r takes (m, l) of each head g from lane (r, g);
-  // then the four row slots are merged with lane shuffles.
-  float mb[GT], lb[GT];
-  row_bcast_all<GT>(m, mb);
-  row_bcast_all<GT>(l, lb);
-#pragma unroll
-  for (int off = 16; off < 64; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float m2 = __shfl_xor(mb[g], off, 64);
-      const float l2 = __shfl_xor(lb[g], off, 64);
-      float o2[DPL];
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) o2[i] = __shfl_xor(o[g][i], off, 64);
-      merge_into<DPL>(mb[g], lb[g], o[g], m2, l2, o2);
-    }
-  }
-
-  // Merge the four waves through LDS and write the result.
   __shared__ float sh_o[kWaves][GT][D];
   __shared__ float sh_m[kWaves][GT];
   __shared__ float sh_l[kWaves][GT];
-  if (r == 0) {
+
+  for (int k = k_begin; k < k_end; ++k) {
+    // Attended tokens of this split (chunk): [t_lo, t_hi).
+    const int plo = pf + k * cp;
+    const int phi = (plo + cp < pe) ? plo + cp : pe;
+    const int t_lo = L > 0 ? (t0 > plo * P ? t0 : plo * P) : 0;
+    const int t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
+
+    float m = -INFINITY, l = 0.0f;  // head c, row slot r
+    float o[GT][DPL];
 #pragma unroll
     for (int g = 0; g < GT; ++g)
 #pragma unroll
-      for (int v = 0; v < VPL; ++v)
+      for (int i = 0; i < DPL; ++i) o[g][i] = 0.0f;
+
+    const int tile_first = t_lo / TR;
+    const int tile_end = (t_hi + TR - 1) / TR;
+    const int my_first = tile_first + wave;
+    const int ntiles = my_first < tile_end ? (tile_end - my_first + kWaves - 1) / kWaves : 0;
+
+    struct Tile {
+      uint4 k[NJ];
+      uint4 v[4][VPL];
+    };
+
+    // Load cursor (one page per tile: P is a multiple of 16).
+    constexpr int STEP = kWaves * TR;
+    const int step_p = STEP / P;
+    const int step_r = STEP - step_p * P;
+    const int pi_last = phi > plo ? phi - 1 : plo;
+    int cur_pi = (my_first * TR) / P;
+    int cur_off = my_first * TR - cur_pi * P;
+    int cur_phys = 0;
+    auto fetch_id = [&]() {
+      const int pi = cur_pi < plo ? plo : (cur_pi > pi_last ? pi_last : cur_pi);
+      cur_phys = table_row[pi];
+    };
+    auto issue = [&](Tile& t) {
+      const int64_t off = static_cast<int64_t>(cur_phys) * page_bytes + head_bytes + static_cast<int64_t>(cur_off) * RB;
+      const char* kp = kbase + off + k_lane_off;
+      const char* vp = vbase + off + v_lane_off;
 #pragma unroll
-        for (int e = 0; e < E; ++e) sh_o[wave][g][v * SEG + c * E + e] = o[g][v * E + e];
-    if (c == 0) {
+      for (int j = 0; j < NJ; ++j) t.k[j] = load16(kp + 32 * j * ELT);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) t.v[i][v] = load16(vp + 4 * i * RB + v * SEG * ELT);
+      cur_pi += step_p;
+      cur_off += step_r;
+      if (cur_off >= P) {
+        cur_off -= P;
+        cur_pi += 1;
+      }
+      fetch_id();
+    };
+
+    const float sl2 = a.scale_log2;
+    // One tile. FULL: every row of the tile is attended (no masking at all);
+    // otherwise rows outside [t_lo, t_hi) get score -inf and zero V rows.
+    auto compute = [&](const Tile& t, int tile, auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const int tb = tile * TR;
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc = mfma_16x16x32<KVT>(t.k[j], qb[j], acc);
+      bool valid[4];
+      float x[4];  // scores in base-2 units
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (FULL) {
+          valid[i] = true;
+          x[i] = acc[i] * sl2;
+        } else {
+          const int tok = tb + 4 * i + r;
+          valid[i] = tok >= t_lo && tok < t_hi;
+          x[i] = valid[i] ? acc[i] * sl2 : -INFINITY;
+        }
+      }
+      const float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      const float mn = fmaxf(m, mt);
+      // P.V for this tile given the running max (p = 2^(x - m)).
+      auto accumulate = [&]() {
+        const float mu = (m == -INFINITY) ? 0.0f : m;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = exp2_fast(x[i] - mu);
+        l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float pb[GT];
+          row_bcast_all<GT>(p[i], pb);
+          if constexpr (FULL) {
+            // Each V element is widened inside its FMA (v_fma_mix for fp16).
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+              const uint32_t w[4] = {t.v[i][v].x, t.v[i][v].y, t.v[i][v].z, t.v[i][v].w};
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                  o[g][v * E + 2 * k] = fmaf(pb[g], lo16_to_f32<KVT>(w[k]), o[g][v * E + 2 * k]);
+                  o[g][v * E + 2 * k + 1] = fmaf(pb[g], hi16_to_f32<KVT>(w[k]), o[g][v * E + 2 * k + 1]);
+                }
+              }
+            }
+          } else {
+            float vf[DPL];
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) unpack<KVT>(t.v[i][v], vf + v * E);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) vf[e] = valid[i] ? vf[e] : 0.0f;
+#pragma unroll
+            for (int g = 0; g < GT; ++g)
+#pragma unroll
+              for (int e = 0; e < DPL; ++e) o[g][e] = fmaf(pb[g], vf[e], o[g][e]);
+          }
+        }
+      };
+      // O and l are rescaled only when some running max of the wave grew; the
+      // accumulation is written out in both arms so that the common arm keeps
+      // O in place.
+      if (__any(c < G && mn > m)) {
+        const float mu = (mn == -INFINITY) ? 0.0f : mn;
+        const float alpha = exp2_fast(m - mu);
+        l *= alpha;
+        m = mn;
+        float ab[GT];
+        row_bcast_all<GT>(alpha, ab);
+#pragma unroll
+        for (int g = 0; g < GT; ++g)
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) o[g][i] *= ab[g];
+        accumulate();
+      } else {
+        accumulate();
+      }
+    };
+    auto compute_tile = [&](const Tile& t, int tile) {
+      const int tb = tile * TR;
+      if (tb >= t_lo && tb + TR <= t_hi)
+        compute(t, tile, std::true_type());
+      else
+        compute(t, tile, std::false_type());
+    };
+
+    // Ring of kPD + 1 tiles, steady state with unconditional loads, unrolled
+    // drain (as in the vector kernel).
+    if (ntiles > 0) {
+      Tile buf[kPD + 1];
+      fetch_id();
+#pragma unroll
+      for (int k = 0; k < kPD; ++k)
+        if (k < ntiles) issue(buf[k]);
+      int n = 0;
+      while (n + 2 * kPD < ntiles) {
+#pragma unroll
+        for (int j = 0; j <= kPD; ++j) {
+          issue(buf[(j + kPD) % (kPD + 1)]);
+          compute_tile(buf[j], my_first + (n + j) * kWaves);
+        }
+        n += kPD + 1;
+      }
+#pragma unroll
+      for (int j = 0; j < 2 * kPD; ++j) {
+        if (n + j < ntiles) {
+          if (n + j + kPD < ntiles) issue(buf[(j + kPD) % (kPD + 1)]);
+          compute_tile(buf[j % (kPD + 1)], my_first + (n + j) * kWaves);
+        }
+      }
+    }
+
+    // Every lane of row slot r takes (m, l) of each head g from lane (r, g);
+    // then the four row slots are merged with lane shuffles.
+    float mb[GT], lb[GT];
+    row_bcast_all<GT>(m, mb);
+    row_bcast_all<GT>(l, lb);
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
 #pragma unroll
       for (int g = 0; g < GT; ++g) {
-        sh_m[wave][g] = mb[g];
-        sh_l[wave][g] = lb[g];
+        const float m2 = __shfl_xor(mb[g], off, 64);
+        const float l2 = __shfl_xor(lb[g], off, 64);
+        float o2[DPL];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o2[i] = __shfl_xor(o[g][i], off, 64);
+        merge_into<DPL>(mb[g], lb[g], o[g], m2, l2, o2);
       }
     }
-  }
-  __syncthreads();
 
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = sh_m[0][g];
+    // Merge the four waves through LDS and write the result.
+    if (r == 0) {
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][g]);
-    const float Mu = (M == -INFINITY) ? 0.0f : M;
-    float lsum = 0.0f, osum = 0.0f;
+      for (int g = 0; g < GT; ++g)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float aw = exp2_fast(sh_m[w][g] - Mu);
-      lsum += aw * sh_l[w][g];
-      osum += aw * sh_o[w][g][d];
-    }
-    const int64_t row = qrow0 + g;
-    if (nsplit == 1) {
-      store_elem(a.out, row * D + d, a.out_dtype, lsum > 0.0f ? osum / lsum : 0.0f);
-    } else {
-      const int64_t srow = row * a.max_splits + s;
-      a.ws_o[srow * D + d] = osum;
-      if (d == 0) {
-        a.ws_ml[srow * 2] = M;
-        a.ws_ml[srow * 2 + 1] = lsum;
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+          for (int e = 0; e < E; ++e) sh_o[wave][g][v * SEG + c * E + e] = o[g][v * E + e];
+      if (c == 0) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          sh_m[wave][g] = mb[g];
+          sh_l[wave][g] = lb[g];
+        }
       }
     }
-  }
+    __syncthreads();
+
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int g = idx / D;
+      const int d = idx - g * D;
+      float M = sh_m[0][g];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][g]);
+      const float Mu = (M == -INFINITY) ? 0.0f : M;
+      float lsum = 0.0f, osum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float aw = exp2_fast(sh_m[w][g] - Mu);
+        lsum += aw * sh_l[w][g];
+        osum += aw * sh_o[w][g][d];
+      }
+      const int64_t row = qrow0 + g;
+      if (!FIXED && nsplit == 1) {
+        store_elem(a.out, row * D + d, a.out_dtype, lsum > 0.0f ? osum / lsum : 0.0f);
+      } else {
+        const int64_t srow = row * a.max_splits + k;
+        a.ws_o[srow * D + d] = osum;
+        if (d == 0) {
+          a.ws_ml[srow * 2] = M;
+          a.ws_ml[srow * 2 + 1] = lsum;
+        }
+      }
+    }
+    if constexpr (FIXED) __syncthreads();  // the next chunk rewrites the LDS
+  }  // chunks
+}
+
+template <int D, int KVT, int GT>
+void launch_mode(const KernelArgs& a, dim3 grid, hipStream_t st) {
+  if (a.chunks_per_group > 0)
+    hipLaunchKernelGGL((split_kernel_mfma<D, KVT, GT, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((split_kernel_mfma<D, KVT, GT, false>), grid, dim3(kThreads), 0, st, a);
 }
 
 template <int D, int KVT>
 hipError_t launch_gt(const KernelArgs& a, int gt, dim3 grid, hipStream_t st) {
   switch (gt) {
-    case 1: hipLaunchKernelGGL((split_kernel_mfma<D, KVT, 1>), grid, dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((split_kernel_mfma<D, KVT, 2>), grid, dim3(kThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((split_kernel_mfma<D, KVT, 4>), grid, dim3(kThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((split_kernel_mfma<D, KVT, 8>), grid, dim3(kThreads), 0, st, a); break;
+    case 1: launch_mode<D, KVT, 1>(a, grid, st); break;
+    case 2: launch_mode<D, KVT, 2>(a, grid, st); break;
+    case 4: launch_mode<D, KVT, 4>(a, grid, st); break;
+    case 8: launch_mode<D, KVT, 8>(a, grid, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -393,7 +413,6 @@ hipError_t launch_kv(const KernelArgs& a, int kv, int gt, dim3 grid, hipStream_t
 }  // namespace
 
 hipError_t launch_split_mfma(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream) {
-  if (a.chunks_per_group > 0) return hipErrorInvalidValue;  // the fixed-order mode runs on the vector kernel
   const dim3 grid(a.num_kv_heads, a.split_groups, a.batch);
   switch (head_dim) {
     case 128: return launch_kv<128>(a, kv_dtype, group_tile, grid, stream);

@@ -300,8 +300,7 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // q.K as a 16 x 32 x 16 matrix-core product per 16-key tile whenever the
   // parameters allow it: with G query heads sharing the keys it is a dense
   // contraction, and it takes the dot products and lane sums off the VALU.
-  // The fixed-order mode runs on the vector kernel.
-  plan->split_kernel = !fixed && matrix_kernel_supported(*p) && forced_kernel() != 0 ? 1 : 0;
+  plan->split_kernel = matrix_kernel_supported(*p) && forced_kernel() != 0 ? 1 : 0;
 
   // Attended pages per sequence.
   std::vector<int64_t> npages(p->batch);

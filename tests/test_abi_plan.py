@@ -165,7 +165,7 @@ def test_fixed_order_chunks_and_groups(lib, ns, cpg):
     assert [pl.splits(b) for b in range(4)] == [12, 1, 1, 9]
     assert pl.info.chunks_per_work_group == cpg
     assert pl.info.split_work_groups == math.ceil(12 / cpg) * 8 * 4
-    assert pl.info.split_kernel == 0                    # the fixed-order mode runs on the vector kernel
+    assert pl.info.split_kernel == 1                    # f16, D 128: the matrix-core kernel, fixed-order variant
     rows = 4 * 32 * 12
     r256 = lambda x: (x + 255) // 256 * 256
     assert pl.workspace_bytes == r256(rows * 128 * 4) + r256(rows * 2 * 4)

@@ -18,6 +18,7 @@ def all_split_counts_agree(w, chunk, splits=SPLITS, **kw):
     outs = []
     for ns in splits:
         out, plan = run_lib(w, num_splits=ns, fixed_chunk=chunk, **kw)
+        assert plan.info.chunks_per_work_group >= 1
         say(f"  splits={ns}: chunks/group {plan.info.chunks_per_work_group}, "
             f"work-groups {plan.info.split_work_groups}, chunks {plan.max_splits}")
         outs.append(out)
@@ -26,13 +27,14 @@ def all_split_counts_agree(w, chunk, splits=SPLITS, **kw):
     return outs[0]
 
 
+@pytest.mark.parametrize("kernel", ["auto", "vector"])
 @pytest.mark.parametrize("name,chunk", [("tiny", 16), ("tiny", 64), ("llama8b_3060", 256),
                                         ("llama8b_3060", 1024), ("wide_gqa", 512)])
-def test_named_workloads_bitwise_across_splits(gpu, name, chunk):
+def test_named_workloads_bitwise_across_splits(gpu, name, chunk, kernel):
     spec = wl.NAMED[name]
-    say(f"[fixed-order] {spec.name} chunk={chunk}")
+    say(f"[fixed-order] {spec.name} chunk={chunk} kernel={kernel}")
     w = wl.make_workload(spec, gpu)
-    out = all_split_counts_agree(w, chunk)
+    out = all_split_counts_agree(w, chunk, kernel=kernel)
     check(out, oracle_for(w), spec.kv_dtype, spec.out_dtype, f"{name} fixed {chunk}")
 
 
@@ -45,11 +47,12 @@ def test_mixed_window_full_size_bitwise_across_splits(gpu):
     check(out[rows], oracle_for(w, rows), spec.kv_dtype, spec.out_dtype, "mixed_window fixed")
 
 
-def test_long_batch_full_size_bitwise_across_splits(gpu):
+@pytest.mark.parametrize("kernel", ["auto", "vector"])
+def test_long_batch_full_size_bitwise_across_splits(gpu, kernel):
     spec = wl.LONG_BATCH
-    say(f"[fixed-order] {spec.name} full size")
+    say(f"[fixed-order] {spec.name} full size kernel={kernel}")
     w = wl.make_workload(spec, gpu)
-    out = all_split_counts_agree(w, 1024, splits=[0, 1, 5, 1_000_000])
+    out = all_split_counts_agree(w, 1024, splits=[0, 1, 5, 1_000_000], kernel=kernel)
     rows = [0, 13, 31]
     check(out[rows], oracle_for(w, rows), spec.kv_dtype, spec.out_dtype, "long_batch fixed")
 
@@ -77,12 +80,13 @@ def test_grid_bitwise_across_splits(gpu, G, D, qd, kvd, od, P):
     assert torch.all(out[0] == 0)   # an empty sequence gives a zero row
 
 
+@pytest.mark.parametrize("kernel", ["auto", "vector"])
 @pytest.mark.parametrize("W", [1, 100, 1000, 4096])
-def test_window_bitwise_across_splits(gpu, W):
+def test_window_bitwise_across_splits(gpu, W, kernel):
     spec = wl.LLAMA8B_3060.replace(batch=3, lengths=("list", (3060, 777, 5000)), window=W)
-    say(f"[fixed-order] window {W}")
+    say(f"[fixed-order] window {W} kernel={kernel}")
     w = wl.make_workload(spec, gpu)
-    out = all_split_counts_agree(w, 256)
+    out = all_split_counts_agree(w, 256, kernel=kernel)
     check(out, oracle_for(w), "f16", "f16", f"window {W}")
 
 
@@ -94,6 +98,14 @@ def test_one_page_chunks_and_one_chunk(gpu):
         say(f"[fixed-order] chunk {chunk}")
         out = all_split_counts_agree(w, chunk, splits=[1, 3, 1_000_000])
         check(out, ref, spec.kv_dtype, spec.out_dtype, f"chunk {chunk}")
+
+
+def test_matrix_and_vector_kernels_agree_within_tolerance(gpu):
+    w = wl.make_workload(wl.LLAMA8B_3060.replace(batch=2, lengths=("list", (3060, 1200)), out_dtype="f32"), gpu)
+    a, pa = run_lib(w, fixed_chunk=512)
+    b, pb = run_lib(w, fixed_chunk=512, kernel="vector")
+    assert pa.info.split_kernel == 1 and pb.info.split_kernel == 0
+    assert ((a - b).norm() / b.norm()).item() < 2e-6
 
 
 def test_two_phase_equals_run_and_workspace_contents_do_not_matter(gpu):

@@ -44,6 +44,18 @@ def test_matches_oracle(gpu, T, G, D, kv, out, P, lens, W, splits):
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
 
 
+# Forced block shape: 64-row blocks even for 16 rows or fewer.
+@pytest.mark.parametrize("kernel", ["rows"])
+@pytest.mark.parametrize("T,G,D,kv,out,P,lens,W", [GRID[0], GRID[2], GRID[3], GRID[5], GRID[7], GRID[8]])
+def test_forced_block_shapes_match_oracle(gpu, kernel, T, G, D, kv, out, P, lens, W):
+    spec = spec_of(T, G, D, kv, out, P, lens, W)
+    say(f"[multi] {spec.name} kernel={kernel}")
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w, num_splits=2, kernel=kernel)
+    err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} {kernel}")
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
+
+
 def test_llama_shape_heads(gpu):
     spec = spec_of(24, 4, 128, "bf16", "f32", 16, (24, 900, 2500), 0, Hkv=8)
     w = wl.make_workload(spec, gpu)
