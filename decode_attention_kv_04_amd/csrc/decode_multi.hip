@@ -554,14 +554,13 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
     pi = pi < a.max_pages ? pi : a.max_pages - 1;
     cphys = table_row[pi];
   };
+  // K and V of a tile are loaded and staged separately: the next tile's K
+  // loads are issued before this tile's V is staged, so a wave has loads in
+  // flight while it waits for V and while it computes.
   uint4 rk[NVW], rv[NVW];
-  auto issue = [&]() {
-    const int64_t off = static_cast<int64_t>(cphys) * page_bytes + head_bytes + static_cast<int64_t>(coff) * ROWB;
-#pragma unroll
-    for (int i = 0; i < NVW; ++i) {
-      rk[i] = ldg16(kbase + off + i * 2 * 16);
-      rv[i] = ldg16(vbase + off + i * 2 * 16);
-    }
+  int64_t noff = 0;  // byte offset of this lane's row segment in the tile being loaded
+  auto next_tile = [&]() {
+    noff = static_cast<int64_t>(cphys) * page_bytes + head_bytes + static_cast<int64_t>(coff) * ROWB;
     coff += KW * KT;
     while (coff >= P) {
       coff -= P;
@@ -569,25 +568,41 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
     }
     fetch_id();
   };
-  auto stage = [&](int tb) {
+  auto issue_k = [&]() {
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) rk[i] = ldg16(kbase + noff + i * 2 * 16);
+  };
+  auto issue_v = [&]() {
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) rv[i] = ldg16(vbase + noff + i * 2 * 16);
+  };
+  auto stage_k = [&]() {
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) *reinterpret_cast<uint4*>(&sk[kk * KS + (sg0 + 2 * i) * 8]) = rk[i];
+  };
+  auto stage_v = [&](int tb) {
     const int pos = tb + kk;
     const bool live = pos >= t_lo && pos < t_hi;
 #pragma unroll
-    for (int i = 0; i < NVW; ++i) {
-      const int sg = sg0 + 2 * i;
-      *reinterpret_cast<uint4*>(&sk[kk * KS + sg * 8]) = rk[i];
-      stage_v_pair<VS>(sv, kk, sg, rv[i], live);
-    }
+    for (int i = 0; i < NVW; ++i) stage_v_pair<VS>(sv, kk, sg0 + 2 * i, rv[i], live);
   };
 
   const float sl2 = a.scale_log2;
   if (ntiles > 0) {
     fetch_id();
-    issue();
+    next_tile();
+    issue_k();
+    issue_v();
     for (int n = 0; n < ntiles; ++n) {
       const int tb = (my_first + n * KW) * KT;
-      stage(tb);  // this wave's region only; LDS operations of a wave stay in order
-      if (n + 1 < ntiles) issue();
+      const bool more = n + 1 < ntiles;
+      stage_k();  // this wave's region only; LDS operations of a wave stay in order
+      if (more) {
+        next_tile();
+        issue_k();
+      }
+      stage_v(tb);
+      if (more) issue_v();
       attend_tile<D, KVT, KS, VS, 1>(sk, sv, tb, rg, sl2, col, q4);
     }
   }
