@@ -173,17 +173,28 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* 
     }
   }
   // P^T as the B operand of each row group: contraction index 8*q4 + j.
+  // Tiles inside every row's keys (all but the causal diagonal and the
+  // split and window edges) skip the per-key masks: a wave-uniform branch.
+  bool inside = true;
+#pragma unroll
+  for (int g = 0; g < NR; ++g) inside = inside && tb >= rg[g].lo && tb + 32 <= rg[g].hi;
+  const bool full = __all(inside);
   uint4 ph[NR], pl[NR];
 #pragma unroll
   for (int g = 0; g < NR; ++g) {
     float x[8];
+    if (full) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int j = 0; j < 8; ++j) x[j] = sacc[g][j >> 2][j & 3] * sl2;
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = tb + kb * 16 + q4 * 4 + i;
-        const float v = sacc[g][kb][i] * sl2;
-        x[kb * 4 + i] = (key >= rg[g].lo && key < rg[g].hi) ? v : -INFINITY;
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = tb + kb * 16 + q4 * 4 + i;
+          const float v = sacc[g][kb][i] * sl2;
+          x[kb * 4 + i] = (key >= rg[g].lo && key < rg[g].hi) ? v : -INFINITY;
+        }
       }
     }
     float mt = x[0];
