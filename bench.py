@@ -366,7 +366,7 @@ def main():
 
     # The fixed-order mode (output bitwise independent of the split count) on
     # the same batch: whole step, chunks of FIXED_CHUNK tokens.
-    fixed = measure_fixed_order(w, binding, lib, dev, stream, args.steps)
+    fixed = measure_fixed_order(w, binding, lib, dev, stream, args.steps) if spec.query_len == 1 else None
 
     # Several new tokens per sequence (drafted-token check, suffix prefill).
     multi = [] if args.no_multi_token else measure_multi_token(binding, workloads, lib, dev, stream, args.steps)
