@@ -12,8 +12,9 @@
 // count depends only on the sequence, so the merge is the same whatever the
 // number of split work-groups.
 //
-// One wave64 per (query head, sequence); lane i owns elements i, i+64, ... of
-// the row, so every load of O_s is one contiguous 256-byte-per-64-lane read.
+// One wave64 per (query head, sequence), four waves per work-group; lane i
+// owns elements i, i+64, ... of the row, so every load of O_s is one
+// contiguous 256-byte-per-64-lane read.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -25,12 +26,14 @@
 namespace da {
 namespace {
 
+constexpr int kRowsPerGroup = 4;  // one wave per row, four rows per work-group
+
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(const KernelArgs a) {
-  constexpr int N = D / 64;
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const KernelArgs a) {
+  const int h = blockIdx.x * kRowsPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  if (h >= a.num_q_heads) return;  // whole wave
 
   const int P = a.page_size;
   const int64_t L = a.seq_lens[b];
@@ -53,11 +56,12 @@ __global__ __launch_bounds__(64) void combine_kernel(const KernelArgs a) {
 // consecutive (token, head) rows of one KV head), whose keys run from the
 // window start of its first token to its last token.
 template <int D>
-__global__ __launch_bounds__(64) void combine_multi_kernel(const KernelArgs a) {
-  const int h = blockIdx.x;
+__global__ __launch_bounds__(64 * kRowsPerGroup) void combine_multi_kernel(const KernelArgs a) {
+  const int h = blockIdx.x * kRowsPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  if (h >= a.num_q_heads) return;  // whole wave
   const int T = a.query_len;
   const int G = a.group;
   const int R = T * G;
@@ -82,20 +86,22 @@ __global__ __launch_bounds__(64) void combine_multi_kernel(const KernelArgs a) {
 
 hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream) {
   if (a.query_len > 1) {
-    const dim3 grid(a.num_q_heads, a.query_len, a.batch);
+    const dim3 grid((a.num_q_heads + kRowsPerGroup - 1) / kRowsPerGroup, a.query_len, a.batch);
+    const dim3 block(64 * kRowsPerGroup);
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL(combine_multi_kernel<64>, grid, dim3(64), 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(combine_multi_kernel<128>, grid, dim3(64), 0, stream, a); break;
-      case 256: hipLaunchKernelGGL(combine_multi_kernel<256>, grid, dim3(64), 0, stream, a); break;
+      case 64: hipLaunchKernelGGL(combine_multi_kernel<64>, grid, block, 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(combine_multi_kernel<128>, grid, block, 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(combine_multi_kernel<256>, grid, block, 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
-  const dim3 grid(a.num_q_heads, a.batch);
+  const dim3 grid((a.num_q_heads + kRowsPerGroup - 1) / kRowsPerGroup, a.batch);
+  const dim3 block(64 * kRowsPerGroup);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(64), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
