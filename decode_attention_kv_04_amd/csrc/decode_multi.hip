@@ -153,12 +153,13 @@ __device__ __forceinline__ void init_rows(RowGroup<D>& g, const KernelArgs& a, i
 // row's keys, online-softmax update, O^T += V^T P^T from the transposed V
 // tile (row stride VS). Lane (col, q4) holds its rows' scores for keys
 // tb + 16*kb + 4*q4 + i.
-template <int D, int KVT, int KS, int VS, int NR>
-__device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* sv, int tb, RowGroup<D> (&rg)[NR],
-                                            float sl2, int col, int q4) {
+// S^T of a 32-key tile for NR row groups. The K operand (16 keys x 32 dims
+// per MFMA) comes from the K tile in LDS (row stride KS) or, with KREG, from
+// registers already in operand layout: kreg[kb * D/32 + ks].
+template <int D, int KVT, int KS, int NR, bool KREG>
+__device__ __forceinline__ void tile_scores(const uint16_t* sk, const uint4* kreg, const RowGroup<D> (&rg)[NR],
+                                            int col, int q4, mq_float4 (&sacc)[NR][2]) {
   constexpr int NKS = D / 32;
-  constexpr int NDB = D / 16;
-  mq_float4 sacc[NR][2];
 #pragma unroll
   for (int g = 0; g < NR; ++g)
 #pragma unroll
@@ -167,11 +168,23 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* 
   for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint4 ka = *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
+      uint4 ka;
+      if constexpr (KREG)
+        ka = kreg[kb * NKS + ks];
+      else
+        ka = *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
 #pragma unroll
       for (int g = 0; g < NR; ++g) sacc[g][kb] = mfma<KVT>(ka, rg[g].qb[ks], sacc[g][kb]);
     }
   }
+}
+
+// Masking, online-softmax update and O^T += V^T P^T of a 32-key tile whose
+// scores are in sacc, for NR row groups; V^T from LDS (row stride VS).
+template <int D, int KVT, int VS, int NR>
+__device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], const uint16_t* sv, int tb,
+                                            RowGroup<D> (&rg)[NR], float sl2, int col, int q4) {
+  constexpr int NDB = D / 16;
   // P^T as the B operand of each row group: contraction index 8*q4 + j.
   // Tiles inside every row's keys (all but the causal diagonal and the
   // split and window edges) skip the per-key masks: a wave-uniform branch.
@@ -256,6 +269,13 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* 
   }
 }
 
+template <int D, int KVT, int KS, int VS, int NR>
+__device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* sv, int tb, RowGroup<D> (&rg)[NR],
+                                            float sl2, int col, int q4) {
+  mq_float4 sacc[NR][2];
+  tile_scores<D, KVT, KS, NR, false>(sk, nullptr, rg, col, q4, sacc);
+  tile_update<D, KVT, VS, NR>(sacc, sv, tb, rg, sl2, col, q4);
+}
 // The row's l is split over its four lanes (one per key group): sum them,
 // then write O / l (one split) or the state (m, l, O) to slot s.
 template <int D>
@@ -510,7 +530,7 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
   constexpr int VS = KT + VPAD;
   constexpr int NKS = D / 32;
   constexpr int NDB = D / 16;
-  constexpr int WAVE_LDS = KT * KS + D * VS;  // 16-bit elements per wave
+  constexpr int WAVE_LDS = D * VS;  // 16-bit elements per wave: its transposed V tile
   static_assert(NVW >= 1 && NVW * 2 == ROWV, "staging split");
   __shared__ __align__(16) uint16_t lds[KW * WAVE_LDS];
 
@@ -537,8 +557,7 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
   RowGroup<D> rg[1];
   init_rows(rg[0], a, blk.r_first + col, blk.r_last, b, kvh, L, t_lo, t_hi, q4);
 
-  uint16_t* sk = lds + wave * WAVE_LDS;
-  uint16_t* sv = sk + KT * KS;
+  uint16_t* sv = lds + wave * WAVE_LDS;
   const int tile_first = t_lo / KT;
   const int tile_end = t_hi > t_lo ? (t_hi + KT - 1) / KT : tile_first;
   const int my_first = tile_first + wave;
@@ -565,10 +584,12 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
     pi = pi < a.max_pages ? pi : a.max_pages - 1;
     cphys = table_row[pi];
   };
-  // K and V of a tile are loaded and staged separately: the next tile's K
-  // loads are issued before this tile's V is staged, so a wave has loads in
-  // flight while it waits for V and while it computes.
-  uint4 rk[NVW], rv[NVW];
+  // K goes straight from HBM into registers in MFMA operand layout (lane
+  // (col, q4) holds keys col and 16 + col, dims 32*ks + 8*q4 .. +8); only V
+  // is staged through LDS. The next tile's K loads are issued as soon as
+  // this tile's scores are computed and its V loads once its V is staged, so
+  // a wave keeps loads in flight while it waits and computes.
+  uint4 kreg[2 * NKS], rv[NVW];
   int64_t noff = 0;  // byte offset of this lane's row segment in the tile being loaded
   auto next_tile = [&]() {
     noff = static_cast<int64_t>(cphys) * page_bytes + head_bytes + static_cast<int64_t>(coff) * ROWB;
@@ -580,16 +601,19 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
     fetch_id();
   };
   auto issue_k = [&]() {
+    // Row offsets of keys col and 16 + col, from the lanes that hold them
+    // (lanes 0..31 hold keys 0..31 at segment 0).
+    const int64_t off0 = __shfl(noff, col, 64);
+    const int64_t off1 = __shfl(noff, 16 + col, 64);
 #pragma unroll
-    for (int i = 0; i < NVW; ++i) rk[i] = ldg16(kbase + noff + i * 2 * 16);
+    for (int ks = 0; ks < NKS; ++ks) {
+      kreg[ks] = ldg16(kbase + off0 + ks * 64 + q4 * 16);
+      kreg[NKS + ks] = ldg16(kbase + off1 + ks * 64 + q4 * 16);
+    }
   };
   auto issue_v = [&]() {
 #pragma unroll
     for (int i = 0; i < NVW; ++i) rv[i] = ldg16(vbase + noff + i * 2 * 16);
-  };
-  auto stage_k = [&]() {
-#pragma unroll
-    for (int i = 0; i < NVW; ++i) *reinterpret_cast<uint4*>(&sk[kk * KS + (sg0 + 2 * i) * 8]) = rk[i];
   };
   auto stage_v = [&](int tb) {
     const int pos = tb + kk;
@@ -607,14 +631,15 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
     for (int n = 0; n < ntiles; ++n) {
       const int tb = (my_first + n * KW) * KT;
       const bool more = n + 1 < ntiles;
-      stage_k();  // this wave's region only; LDS operations of a wave stay in order
+      mq_float4 sacc[1][2];
+      tile_scores<D, KVT, KS, 1, true>(nullptr, kreg, rg, col, q4, sacc);
       if (more) {
         next_tile();
         issue_k();
       }
-      stage_v(tb);
+      stage_v(tb);  // this wave's region only; LDS operations of a wave stay in order
       if (more) issue_v();
-      attend_tile<D, KVT, KS, VS, 1>(sk, sv, tb, rg, sl2, col, q4);
+      tile_update<D, KVT, VS, 1>(sacc, sv, tb, rg, sl2, col, q4);
     }
   }
 
