@@ -191,11 +191,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     const int t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
 
     float m[GT], l[GT], o[GT][DPL];
-  #pragma unroll
+#pragma unroll
     for (int g = 0; g < GT; ++g) {
       m[g] = -INFINITY;
       l[g] = 0.0f;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < DPL; ++i) o[g][i] = 0.0f;
     }
 
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     const int step_r = STEP - step_p * P;
     int cur_tile = my_first;
     int cur_pi[NS], cur_off[NS], cur_phys[NS];
-  #pragma unroll
+#pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       const int gs = my_first * TR + ns * RPI;
       cur_pi[ns] = gs / P;
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     // Rows of groups outside [t_lo, t_hi) are masked in compute().
     const int pi_last = phi > plo ? phi - 1 : plo;
     auto fetch_ids = [&]() {
-  #pragma unroll
+#pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const int pi = cur_pi[ns] < plo ? plo : (cur_pi[ns] > pi_last ? pi_last : cur_pi[ns]);
         cur_phys[ns] = table_row[pi];
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     };
     auto advance = [&]() {
       cur_tile += kWaves;
-  #pragma unroll
+#pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         cur_pi[ns] += step_p;
         cur_off[ns] += step_r;
@@ -252,13 +252,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     // last tile of a split) reads rows of a page of this split that compute()
     // masks out; the row offset is always inside its page.
     auto issue = [&](Tile& t) {
-  #pragma unroll
+#pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const int64_t off = static_cast<int64_t>(cur_phys[ns]) * page_bytes + head_bytes +
                             static_cast<int64_t>(cur_off[ns]) * (D * ELT);
         const char* kp = kbase + off + lane_off;
         const char* vp = vbase + off + lane_off;
-  #pragma unroll
+#pragma unroll
         for (int v = 0; v < VPL; ++v) {
           t.k[ns][v] = load16(kp + v * SEG * ELT);
           t.v[ns][v] = load16(vp + v * SEG * ELT);
@@ -272,20 +272,20 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
       const int tb = tile * TR;
       const bool full = tb >= t_lo && tb + TR <= t_hi;
       bool valid[NS];
-  #pragma unroll
+#pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         const int tok = tb + ns * RPI + r;
         valid[ns] = full || (tok >= t_lo && tok < t_hi);
       }
       // q.k partial sums, then the row sums.
       float sc[NS][GT];
-  #pragma unroll
+#pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         if constexpr (QPACK) {
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < GT; ++g) {
             float acc = 0.0f;
-  #pragma unroll
+#pragma unroll
             for (int v = 0; v < VPL; ++v) {
               const uint4 u = t.k[ns][v];
               acc = dot2<KVT>(qv[g][v * 4], u.x, acc);
@@ -297,20 +297,20 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
           }
         } else {
           float kf[DPL];
-  #pragma unroll
+#pragma unroll
           for (int v = 0; v < VPL; ++v) unpack<KVT>(t.k[ns][v], kf + v * E);
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < GT; ++g) {
             float acc = 0.0f;
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < DPL; ++i) acc = fmaf(qv[g][i], kf[i], acc);
             sc[ns][g] = acc;
           }
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < GT; ++g) {
           const float x = row_sum<LPR>(sc[ns][g]) * sl2;
           sc[ns][g] = valid[ns] ? x : -INFINITY;
@@ -320,49 +320,49 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
       // wave grew (a wave-uniform branch; a factor of exactly 1 is skipped).
       float mn[GT];
       bool grew = false;
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < GT; ++g) {
         float mt = sc[0][g];
-  #pragma unroll
+#pragma unroll
         for (int ns = 1; ns < NS; ++ns) mt = fmaxf(mt, sc[ns][g]);
-        mn[g] = fmaxf(m[g], mt);
+        mn[g] = mt > m[g] + DA_RESCALE_SLACK ? mt : m[g];  // moves only past the rescale slack
         grew |= mn[g] > m[g];
       }
       if (__any(grew)) {
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < GT; ++g) {
           const float mu = (mn[g] == -INFINITY) ? 0.0f : mn[g];
           const float alpha = exp2_fast(m[g] - mu);
           l[g] *= alpha;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < DPL; ++i) o[g][i] *= alpha;
           m[g] = mn[g];
         }
       }
       float p[NS][GT];
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < GT; ++g) {
         const float mu = (m[g] == -INFINITY) ? 0.0f : m[g];
         float ps = 0.0f;
-  #pragma unroll
+#pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
           p[ns][g] = exp2_fast(sc[ns][g] - mu);
           ps += p[ns][g];
         }
         l[g] += ps;
       }
-  #pragma unroll
+#pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
         float vf[DPL];
-  #pragma unroll
+#pragma unroll
         for (int v = 0; v < VPL; ++v) unpack<KVT>(t.v[ns][v], vf + v * E);
         if (!full) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < DPL; ++i) vf[i] = valid[ns] ? vf[i] : 0.0f;
         }
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < GT; ++g) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < DPL; ++i) o[g][i] = fmaf(p[ns][g], vf[i], o[g][i]);
         }
       }
@@ -376,12 +376,12 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     if (ntiles > 0) {
       Tile buf[kPD + 1];
       fetch_ids();
-  #pragma unroll
+#pragma unroll
       for (int k = 0; k < kPD; ++k)
         if (k < ntiles) issue(buf[k]);
       int n = 0;
       while (n + 2 * kPD < ntiles) {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j <= kPD; ++j) {
           issue(buf[(j + kPD) % (kPD + 1)]);
           compute(buf[j], my_first + (n + j) * kWaves);
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
         n += kPD + 1;
       }
       // Here ntiles - n <= 2 * kPD and n % (kPD + 1) == 0.
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < 2 * kPD; ++j) {
         if (n + j < ntiles) {
           if (n + j + kPD < ntiles) issue(buf[(j + kPD) % (kPD + 1)]);
@@ -399,14 +399,14 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
     }
 
     // Merge the RPI row slots of the wave (lanes with the same c).
-  #pragma unroll
+#pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < GT; ++g) {
         const float m2 = __shfl_xor(m[g], off, 64);
         const float l2 = __shfl_xor(l[g], off, 64);
         float o2[DPL];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < DPL; ++i) o2[i] = __shfl_xor(o[g][i], off, 64);
         merge_into<DPL>(m[g], l[g], o[g], m2, l2, o2);
       }
@@ -414,16 +414,16 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
 
     // Merge the four waves through LDS and write the result.
     if (r == 0) {
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < GT; ++g) {
-  #pragma unroll
+#pragma unroll
         for (int v = 0; v < VPL; ++v) {
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < E; ++e) sh_o[wave][g][v * SEG + c * E + e] = o[g][v * E + e];
         }
       }
       if (c == 0) {
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < GT; ++g) {
           sh_m[wave][g] = m[g];
           sh_l[wave][g] = l[g];
@@ -436,11 +436,11 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
       const int g = idx / D;
       const int d = idx - g * D;
       float M = sh_m[0][g];
-  #pragma unroll
+#pragma unroll
       for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][g]);
       const float Mu = (M == -INFINITY) ? 0.0f : M;
       float lsum = 0.0f, osum = 0.0f;
-  #pragma unroll
+#pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float aw = exp2_fast(sh_m[w][g] - Mu);
         lsum += aw * sh_l[w][g];

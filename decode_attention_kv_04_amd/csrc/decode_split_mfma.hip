@@ -44,6 +44,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPD = DA_MFMA_PREFETCH_TILES;  // tiles in flight per wave while one is computed
+constexpr float kRescaleSlack = DA_RESCALE_SLACK;
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
@@ -223,7 +224,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
         }
       }
       const float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      const float mn = fmaxf(m, mt);
+      // The reference max moves only past the rescale slack.
+      const float mn = mt > m + kRescaleSlack ? mt : m;
       // P.V for this tile given the running max (p = 2^(x - m)).
       auto accumulate = [&]() {
         const float mu = (m == -INFINITY) ? 0.0f : m;

@@ -12,6 +12,14 @@
 #define DA_NT_LOADS 1
 #endif
 
+// Online softmax: the reference max of a state moves only when a score
+// exceeds it by more than this (base-2 units). Probabilities then stay below
+// 2^slack (finite, exact range for fp32 sums and 16-bit P) and the rescale
+// of O happens rarely after the first keys. 0 = move on every increase.
+#ifndef DA_RESCALE_SLACK
+#define DA_RESCALE_SLACK 8.0f
+#endif
+
 namespace da {
 namespace {
 
