@@ -1,5 +1,5 @@
 /*
- * decode_attn.h - paged single-query decode attention on MI355X (gfx950).
+ * decode_attn.h - paged decode attention on MI355X (gfx950).
  *
  * One decode step: every sequence b has one query token with H_q heads and a
  * KV cache of L_b keys stored in fixed-size pages. For every query head h the
@@ -11,6 +11,12 @@
  * H_q / H_kv consecutive query heads of a GQA group share, and the attended
  * keys are the last `window` keys (all L_b keys when window = 0 or window >=
  * L_b). A sequence with no attended key gets a zero row.
+ *
+ * With query_len = T > 1 (da_params) every sequence has T new tokens, the
+ * last T keys of its cache: token t sits at position L_b - T + t and attends
+ * the keys at positions <= its own (the last `window` of them). An optional
+ * fixed-order mode makes the output bitwise independent of the split count,
+ * and decode_attn_append_kv writes new K/V rows into the pages.
  *
  * Passages this follows:
  *   - TVM pull 20426 "webgpu-decode-attention", commit message of the sharded
@@ -26,6 +32,11 @@
  *   - llm-web pull 8, commits on build-time constants and on pipeline
  *     creation errors: head_dim / dtype / window fixed per pipeline before
  *     launch; errors surface at creation and the caller picks a fallback.
+ *     Its commit on the batched suffix prefill: new tokens' K/V scattered
+ *     after the resident prefix, attention of several new tokens over the
+ *     cache.
+ *   - mlx-runner pull 3, split decode attention test: split and unsplit
+ *     paths agree bit for bit when the partials merge in one fixed order.
  *
  * Conventions
  *   - Pointers are device pointers unless their name starts with host_.
@@ -33,12 +44,12 @@
  *     or frees device memory. A plan is a small host object owned by the
  *     caller and released with decode_attn_plan_destroy.
  *   - Tensors are dense and row-major:
- *       q           [B][H_q][D]                      q_dtype
+ *       q           [B][H_q][D] ([B][T][H_q][D] when T > 1)   q_dtype
  *       k_pool      [num_pages][H_kv][P][D]          kv_dtype
  *       v_pool      [num_pages][H_kv][P][D]          kv_dtype
  *       page_table  [B][max_pages_per_seq]           int32, logical -> physical page
  *       seq_lens    [B]                              int32, keys in the cache
- *       out         [B][H_q][D]                      out_dtype
+ *       out         [B][H_q][D] ([B][T][H_q][D] when T > 1)   out_dtype
  *     Key t of sequence b, KV head j, is row t % P of block
  *     (page_table[b][t / P], j) of the pools. Only the pages holding attended
  *     keys are read; rows outside the attended range (the tail of the last
