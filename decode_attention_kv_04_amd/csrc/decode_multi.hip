@@ -46,7 +46,7 @@ namespace da {
 namespace {
 
 constexpr int KT = 32;   // keys per tile
-constexpr float kSlack = 8.0f;  // see attend_tile
+constexpr float kSlack = 8.0f;  // see tile_update
 constexpr int KPAD = 8;  // LDS padding (16-bit elements) per K row
 constexpr int VPAD = 8;  // LDS padding per transposed V row
 
@@ -269,13 +269,6 @@ __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], const uint
   }
 }
 
-template <int D, int KVT, int KS, int VS, int NR>
-__device__ __forceinline__ void attend_tile(const uint16_t* sk, const uint16_t* sv, int tb, RowGroup<D> (&rg)[NR],
-                                            float sl2, int col, int q4) {
-  mq_float4 sacc[NR][2];
-  tile_scores<D, KVT, KS, NR, false>(sk, nullptr, rg, col, q4, sacc);
-  tile_update<D, KVT, VS, NR>(sacc, sv, tb, rg, sl2, col, q4);
-}
 // The row's l is split over its four lanes (one per key group): sum them,
 // then write O / l (one split) or the state (m, l, O) to slot s.
 template <int D>
@@ -467,9 +460,14 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   // Waves whose rows are all past the block's last row only stage.
   const bool wave_rows = r_first + wave * NR * 16 <= r_last;
   const float sl2 = a.scale_log2;
-  auto compute = [&](int buf, int tb) {
-    if (!wave_rows) return;  // wave-uniform
-    attend_tile<D, KVT, KS, VS, NR>(sk[buf], sv[buf], tb, rg, sl2, col, q4);
+  // A step computes tile m's scores, writes tile m+1 to the other LDS
+  // buffer while those matrix products run, then finishes tile m.
+  mq_float4 sacc[NR][2];
+  auto scores = [&](int buf) {
+    if (wave_rows) tile_scores<D, KVT, KS, NR, false>(sk[buf], nullptr, rg, col, q4, sacc);
+  };
+  auto finish = [&](int buf, int tb) {
+    if (wave_rows) tile_update<D, KVT, VS, NR>(sacc, sv[buf], tb, rg, sl2, col, q4);
   };
 
   // Tile m's loads go to ring slot m % (PD + 1) PD tiles ahead; at step m
@@ -491,8 +489,9 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
         const int m = n + j;
         issue(ring[(j + PD) % (PD + 1)]);  // tile m + PD
         lds_barrier();
+        scores(m & 1);
         stage(ring[(j + 1) % (PD + 1)], (m + 1) & 1, (tile_first + m + 1) * KT);
-        compute(m & 1, (tile_first + m) * KT);
+        finish(m & 1, (tile_first + m) * KT);
       }
       n += PD + 1;
     }
@@ -503,8 +502,9 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
       if (m < ntiles) {
         if (m + PD < ntiles) issue(ring[(j + PD) % (PD + 1)]);
         lds_barrier();
+        scores(m & 1);
         if (m + 1 < ntiles) stage(ring[(j + 1) % (PD + 1)], (m + 1) & 1, (tile_first + m + 1) * KT);
-        compute(m & 1, (tile_first + m) * KT);
+        finish(m & 1, (tile_first + m) * KT);
       }
     }
   }
