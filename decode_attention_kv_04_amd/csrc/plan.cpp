@@ -285,7 +285,8 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   if (T > 1) {
     if (p->q_dtype != p->kv_dtype || (p->kv_dtype != DA_F16 && p->kv_dtype != DA_BF16)) return DA_ERR_UNSUPPORTED;
     if (fixed) return DA_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(T) * G > (static_cast<int64_t>(1) << 24)) return DA_ERR_UNSUPPORTED;
+    // T is the combine grid's y extent; T * G rows are counted in int32.
+    if (T > 65535 || static_cast<int64_t>(T) * G > (static_cast<int64_t>(1) << 24)) return DA_ERR_UNSUPPORTED;
     for (int32_t b = 0; b < p->batch; ++b)
       if (lens[b] < T) return DA_ERR_INVALID;  // the new tokens' keys are in the cache
   }

@@ -112,8 +112,9 @@ typedef struct {
                                 [B][T][H_q][D]; token t of sequence b sits at
                                 position L_b - T + t and attends the keys at
                                 positions <= its own (the last `window` of them
-                                if window > 0). Needs L_b >= T, q_dtype ==
-                                kv_dtype in {f16, bf16} and fixed_chunk == 0.  */
+                                if window > 0). Needs L_b >= T, T <= 65535,
+                                q_dtype == kv_dtype in {f16, bf16} and
+                                fixed_chunk == 0.                              */
 } da_params;
 
 typedef struct da_plan* da_plan_t;

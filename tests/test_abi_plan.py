@@ -234,6 +234,7 @@ def test_multi_token_window_keys(lib):
     (dict(query_len=4, q_dtype="f32", kv_dtype="f32", out_dtype="f32"), [30], B.DA_ERR_UNSUPPORTED),
     (dict(query_len=4, q_dtype="f32"), [30], B.DA_ERR_UNSUPPORTED),             # q and KV differ
     (dict(query_len=4, fixed_chunk=256), [30], B.DA_ERR_UNSUPPORTED),
+    (dict(query_len=65536, max_pages_per_seq=8192), [65536], B.DA_ERR_UNSUPPORTED),   # combine grid limit
 ])
 def test_multi_token_rejects(lib, kw, lens, code):
     assert status_of(params(batch=len(lens), **kw), lens) == code
