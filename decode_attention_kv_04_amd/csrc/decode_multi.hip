@@ -9,8 +9,10 @@
 // (all keys up to itself, or the last W of them with a window).
 //
 // Query rows. The T*G (token, head) pairs that share KV head j form the rows
-// r = t*G + g of one contraction; a work-group takes QB = 16*NQ consecutive
-// rows (NQ wave64s, 16 rows each) and one split of the keys those rows see.
+// r = t*G + g of one contraction. multi_kernel: a work-group takes 64
+// consecutive rows (4 wave64s, 16 rows each) and one split of the keys those
+// rows see. multi_keys_kernel (at most 16 rows): the 4 waves share the rows
+// and split the keys.
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
 //   S^T = K Q^T    A = 16 keys x 32 dims of K,  B = 32 dims x 16 rows of q
 //   O^T += V^T P^T A = 16 dims x 32 keys of V,  B = 32 keys x 16 rows of P
@@ -21,14 +23,16 @@
 // the order that lets each lane pass its own eight probabilities as its B
 // operand: contraction index 8*q + j is key 4q + j (j < 4) or 16 + 4q + j - 4.
 //
-// Staging. Each tile of 32 keys is read from HBM once per work-group with
-// 16-byte loads into a ring of registers (several tiles ahead of the one being
-// computed) and written to one of two LDS buffers: K row-major, V transposed
-// (dims as rows, keys in contraction order) so both MFMA operands are single
-// 16-byte LDS reads. One barrier per tile: tile m+1 is written to one buffer
-// while tile m is computed from the other. V rows outside the split's attended keys are stored as
-// zeros (they may hold NaN and would poison 0 * V), scores outside a row's own
-// keys become -inf by select.
+// Staging (multi_kernel). Each tile of 32 keys is read from HBM once per
+// work-group with 16-byte loads into a ring of registers (several tiles ahead
+// of the one being computed) and written to one of two LDS buffers: K
+// row-major, V transposed (dims as rows, keys in contraction order) so both
+// MFMA operands are single 16-byte LDS reads. One barrier per tile: tile m+1
+// is written to one buffer while tile m is computed from the other.
+// multi_keys_kernel loads K straight into operand registers and stages only
+// V, through each wave's own LDS region. V rows outside the split's attended
+// keys are stored as zeros (they may hold NaN and would poison 0 * V); scores
+// outside a row's own keys become -inf by select.
 //
 // Softmax precision: P enters the P.V product as f16 for f16 K/V and as a
 // bf16 hi + lo pair (two products) for bf16 K/V, since one bf16 rounding of P
@@ -45,10 +49,10 @@
 namespace da {
 namespace {
 
-constexpr int KT = 32;   // keys per tile
-constexpr float kSlack = 8.0f;  // see tile_update
-constexpr int KPAD = 8;  // LDS padding (16-bit elements) per K row
-constexpr int VPAD = 8;  // LDS padding per transposed V row
+constexpr int KT = 32;          // keys per tile
+constexpr float kSlack = 8.0f;  // rescale slack of the reference max, see tile_update
+constexpr int KPAD = 8;         // LDS padding (16-bit elements) per K row
+constexpr int VPAD = 8;         // LDS padding per transposed V row
 
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 mq_bf168 __attribute__((ext_vector_type(8)));
@@ -93,8 +97,11 @@ template <int VS>
 __device__ __forceinline__ void stage_v_pair(uint16_t* sv, int kk, int sg, const uint4& v, bool live) {
   const uint32_t w0 = live ? v.x : 0u, w1 = live ? v.y : 0u, w2 = live ? v.z : 0u, w3 = live ? v.w : 0u;
   const bool odd = kk & 1;
-  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? w0 : w2), 0xB1, 0xF, 0xF, false));
-  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? w1 : w3), 0xB1, 0xF, 0xF, false));
+  // quad_perm [1,0,3,2]: exchange with the neighbouring lane
+  const uint32_t r0 =
+      static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? w0 : w2), 0xB1, 0xF, 0xF, false));
+  const uint32_t r1 =
+      static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? w1 : w3), 0xB1, 0xF, 0xF, false));
   const uint32_t ev0 = odd ? r0 : w0, ev1 = odd ? r1 : w1;  // even key, this lane's 4 dims
   const uint32_t od0 = odd ? w2 : r0, od1 = odd ? w3 : r1;  // odd key
   const int d0 = 8 * sg + (odd ? 4 : 0);
@@ -148,11 +155,6 @@ __device__ __forceinline__ void init_rows(RowGroup<D>& g, const KernelArgs& a, i
   for (int nb = 0; nb < D / 16; ++nb) g.o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// One 32-key tile for NR row groups of a wave, sharing each operand read:
-// S^T = K Q^T from the K tile (row-major, row stride KS), masking to each
-// row's keys, online-softmax update, O^T += V^T P^T from the transposed V
-// tile (row stride VS). Lane (col, q4) holds its rows' scores for keys
-// tb + 16*kb + 4*q4 + i.
 // S^T of a 32-key tile for NR row groups. The K operand (16 keys x 32 dims
 // per MFMA) comes from the K tile in LDS (row stride KS) or, with KREG, from
 // registers already in operand layout: kreg[kb * D/32 + ks].
@@ -185,14 +187,13 @@ template <int D, int KVT, int VS, int NR>
 __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], const uint16_t* sv, int tb,
                                             RowGroup<D> (&rg)[NR], float sl2, int col, int q4) {
   constexpr int NDB = D / 16;
-  // P^T as the B operand of each row group: contraction index 8*q4 + j.
   // Tiles inside every row's keys (all but the causal diagonal and the
   // split and window edges) skip the per-key masks: a wave-uniform branch.
   bool inside = true;
 #pragma unroll
   for (int g = 0; g < NR; ++g) inside = inside && tb >= rg[g].lo && tb + 32 <= rg[g].hi;
   const bool full = __all(inside);
-  uint4 ph[NR], pl[NR];
+  uint4 ph[NR], pl[NR];  // P^T as the B operand of each row group: contraction index 8*q4 + j
 #pragma unroll
   for (int g = 0; g < NR; ++g) {
     float x[8];
