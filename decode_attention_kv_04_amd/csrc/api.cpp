@@ -78,6 +78,9 @@ da_status prepare(const da_plan* plan, const void* q, const void* k_pool, const 
   a->split_groups = plan->split_groups;
   a->query_len = plan->query_len;
   a->rows_per_group = plan->rows_per_group;
+  a->len_offset = 0;
+  a->rows_per_seq = p.num_q_heads;
+  a->row_base = 0;
   a->q_dtype = p.q_dtype;
   a->out_dtype = p.out_dtype;
   a->scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
@@ -88,10 +91,29 @@ da_status prepare(const da_plan* plan, const void* q, const void* k_pool, const 
 // the fixed-order mode (every row goes through the chunk-order merge).
 bool needs_combine(const da_plan* plan) { return plan->max_splits > 1 || plan->chunks_per_group > 0; }
 
+da_status enqueue_one(const da_plan* plan, const da::KernelArgs& a, bool split, bool combine, hipStream_t st);
+
 da_status enqueue(const da_plan* plan, const da::KernelArgs& a, bool split, bool combine, void* stream) {
   if (plan->p.batch == 0) return DA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
+  if (!plan->per_token) return enqueue_one(plan, a, split, combine, st);
+  // One single-query pass per new token t: L - (T - 1 - t) keys, rows of
+  // token t (q, out and workspace hold all T tokens' rows).
+  const int32_t T = plan->query_len;
+  for (int32_t t = 0; t < T; ++t) {
+    da::KernelArgs at = a;
+    at.query_len = 1;
+    at.len_offset = T - 1 - t;
+    at.rows_per_seq = T * plan->p.num_q_heads;
+    at.row_base = t * plan->p.num_q_heads;
+    const da_status s = enqueue_one(plan, at, split, combine, st);
+    if (s != DA_OK) return s;
+  }
+  return DA_OK;
+}
+
+da_status enqueue_one(const da_plan* plan, const da::KernelArgs& a, bool split, bool combine, hipStream_t st) {
   if (split) {
     hipError_t e;
     if (plan->split_kernel == 2)
@@ -200,6 +222,9 @@ da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out
   a.split_groups = plan->split_groups;
   a.query_len = plan->query_len;
   a.rows_per_group = plan->rows_per_group;
+  a.len_offset = 0;
+  a.rows_per_seq = p.num_q_heads;
+  a.row_base = 0;
   a.q_dtype = p.q_dtype;
   a.out_dtype = p.out_dtype;
   return enqueue(plan, a, false, true, stream);

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const Kerne
   if (h >= a.num_q_heads) return;  // whole wave
 
   const int P = a.page_size;
-  const int64_t L = a.seq_lens[b];
+  const int64_t L = a.seq_lens[b] - a.len_offset;
   const int64_t t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
   const int64_t pf = L > 0 ? t0 / P : 0;
   const int64_t pe = L > 0 ? (L + P - 1) / P : 0;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const Kerne
     return;  // the split pass wrote this row
   }
 
-  merge_head_wave<D>(a, static_cast<int64_t>(b) * a.num_q_heads + h, static_cast<int>(nsplit), lane);
+  merge_head_wave<D>(a, static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h, static_cast<int>(nsplit), lane);
 }
 
 // Several new tokens per sequence: one wave per (query head, token, sequence).

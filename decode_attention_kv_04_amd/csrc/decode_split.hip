@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
   // Attended tokens of this split: [t_lo, t_hi). Token counts fit int32 (the
   // planner bounds max_pages_per_seq * page_size).
   const int P = a.page_size;
-  const int L = a.seq_lens[b];
+  const int L = a.seq_lens[b] - a.len_offset;
   const int t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
   const int pf = L > 0 ? t0 / P : 0;
   const int pe = L > 0 ? (L + P - 1) / P : 0;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const KernelArgs a) {
 
   const int G = a.group;
   const int h0 = kvh * G;
-  const int64_t qrow0 = static_cast<int64_t>(b) * a.num_q_heads + h0;
+  const int64_t qrow0 = static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h0;
 
   // q for the G heads of the group, this lane's elements.
   using QReg = typename std::conditional<QPACK, uint32_t, float>::type;

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
   const int key_of_lane = (c & 3) * 4 + (c >> 2);
 
   const int P = a.page_size;
-  const int L = a.seq_lens[b];
+  const int L = a.seq_lens[b] - a.len_offset;
   const int t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
   const int pf = L > 0 ? t0 / P : 0;
   const int pe = L > 0 ? (L + P - 1) / P : 0;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
 
   const int G = a.group;
   const int h0 = kvh * G;
-  const int64_t qrow0 = static_cast<int64_t>(b) * a.num_q_heads + h0;
+  const int64_t qrow0 = static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h0;
 
   // q of head c as the B operand: dims [32j + 8r, +8) for k-step j.
   uint4 qb[NJ];

@@ -29,6 +29,12 @@ struct KernelArgs {
   int32_t chunks_per_group; // 0 = default mode; else fixed-order mode, chunks per work-group
   int32_t split_groups;     // split work-groups per (sequence, KV head)
   int32_t query_len;        // T new tokens per sequence (1 = single-query decode)
+  // Single-query kernels run once per new token when the multi-token kernels
+  // do not cover the dtypes: token t sees L - len_offset keys and its q, out
+  // and workspace rows are b * rows_per_seq + row_base + h. Decode: 0, H_q, 0.
+  int32_t len_offset;
+  int32_t rows_per_seq;
+  int32_t row_base;
   int32_t rows_per_group;   // multi-token kernel: query rows (token, head) per work-group
   int32_t q_dtype;        // da_dtype
   int32_t out_dtype;      // da_dtype

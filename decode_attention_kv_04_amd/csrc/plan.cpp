@@ -113,7 +113,7 @@ int64_t heuristic_split_pages(int64_t total_np, int64_t max_np, int64_t num_kv_h
 // Workspace: O block [B][H_q][S_max][D] then (m, l) block [B][H_q][S_max][2].
 void size_workspace(da_plan* plan) {
   const da_params& p = plan->p;
-  const size_t rows = static_cast<size_t>(p.batch) * p.num_q_heads * plan->max_splits;
+  const size_t rows = static_cast<size_t>(p.batch) * p.num_q_heads * plan->max_splits * plan->query_len;
   plan->ws_o_offset = 0;
   plan->ws_ml_offset = plan->ws_o_offset + round_up(rows * p.head_dim * sizeof(float), 256);
   plan->ws_bytes = plan->ws_ml_offset + round_up(rows * 2 * sizeof(float), 256);
@@ -282,8 +282,12 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   }
 
   const int32_t T = p->query_len > 1 ? p->query_len : 1;
+  // Several new tokens: the multi-token kernels when q and K/V share f16 or
+  // bf16; otherwise (or with DECODE_ATTN_KERNEL=vector) the single-query
+  // kernels once per token.
+  const bool multi_dtypes = p->q_dtype == p->kv_dtype && (p->kv_dtype == DA_F16 || p->kv_dtype == DA_BF16);
+  const bool per_token = T > 1 && (!multi_dtypes || forced_kernel() == 0);
   if (T > 1) {
-    if (p->q_dtype != p->kv_dtype || (p->kv_dtype != DA_F16 && p->kv_dtype != DA_BF16)) return DA_ERR_UNSUPPORTED;
     if (fixed) return DA_ERR_UNSUPPORTED;
     // T is the combine grid's y extent; T * G rows are counted in int32.
     if (T > 65535 || static_cast<int64_t>(T) * G > (static_cast<int64_t>(1) << 24)) return DA_ERR_UNSUPPORTED;
@@ -295,6 +299,7 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   if (!plan) return DA_ERR_INVALID;
   plan->p = *p;
   plan->query_len = T;
+  plan->per_token = per_token;
   plan->group = G;
   plan->group_tile = gt;
   plan->num_cus = num_cus;
@@ -314,7 +319,7 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     plan->attended_keys += r.t1 - r.t0;
   }
 
-  if (plan->query_len > 1) {
+  if (plan->query_len > 1 && !per_token) {
     const da_status st = finish_multi_plan(plan, lens);
     if (st == DA_OK) *out = plan;
     return st;
@@ -349,6 +354,18 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   }
   plan->max_splits = static_cast<int32_t>(smax);
   plan->split_groups = plan->max_splits;
+  if (per_token) {
+    // Token t runs as a decode over L - (T - 1 - t) keys: the splits above
+    // (from the full lengths) cover every token; the workspace holds every
+    // token's states; the attended keys are counted per token.
+    plan->attended_keys = 0;
+    for (int32_t b = 0; b < p->batch; ++b)
+      for (int64_t t = 0; t < T; ++t) {
+        const int64_t pos = static_cast<int64_t>(lens[b]) - T + t;
+        plan->attended_keys += p->window > 0 ? std::min<int64_t>(pos + 1, p->window) : pos + 1;
+      }
+    plan->active_units *= T;
+  }
   if (smax > 1) size_workspace(plan);
   log_plan(plan);
   *out = plan;

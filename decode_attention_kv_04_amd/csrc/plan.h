@@ -21,6 +21,7 @@ struct da_plan {
   int32_t split_groups = 1;    // split work-groups per (sequence, KV head): the grid's y extent
   int32_t query_len = 1;       // T new tokens per sequence
   int32_t rows_per_group = 0;  // multi-token kernel: (token, head) rows per work-group
+  bool per_token = false;      // T > 1 on the single-query kernels, one launch per token
   std::vector<int32_t> splits; // S_b per sequence
   int64_t active_units = 0;
   int64_t attended_keys = 0;

@@ -112,9 +112,13 @@ typedef struct {
                                 [B][T][H_q][D]; token t of sequence b sits at
                                 position L_b - T + t and attends the keys at
                                 positions <= its own (the last `window` of them
-                                if window > 0). Needs L_b >= T, T <= 65535,
-                                q_dtype == kv_dtype in {f16, bf16} and
-                                fixed_chunk == 0.                              */
+                                if window > 0). Needs L_b >= T, T <= 65535
+                                and fixed_chunk == 0. q and K/V sharing f16 or
+                                bf16 run the multi-token kernels (both products
+                                on the matrix cores); other dtype combinations
+                                (or DECODE_ATTN_KERNEL=vector) run the
+                                single-query kernels once per token (meant for
+                                a few tokens).                                 */
 } da_params;
 
 typedef struct da_plan* da_plan_t;
@@ -133,7 +137,8 @@ typedef struct {
                                 head_dim 128, page size a multiple of 16).
                                 DECODE_ATTN_KERNEL=vector forces 0. 2 = the
                                 multi-token kernel (query_len > 1; q.K and P.V
-                                on the matrix cores).                            */
+                                on the matrix cores). A query_len > 1 plan with
+                                0 runs the vector kernel once per token.         */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in

@@ -231,13 +231,31 @@ def test_multi_token_window_keys(lib):
 @pytest.mark.parametrize("kw,lens,code", [
     (dict(query_len=4), [3], B.DA_ERR_INVALID),                                  # L < T
     (dict(query_len=-1), [30], B.DA_ERR_INVALID),
-    (dict(query_len=4, q_dtype="f32", kv_dtype="f32", out_dtype="f32"), [30], B.DA_ERR_UNSUPPORTED),
-    (dict(query_len=4, q_dtype="f32"), [30], B.DA_ERR_UNSUPPORTED),             # q and KV differ
     (dict(query_len=4, fixed_chunk=256), [30], B.DA_ERR_UNSUPPORTED),
     (dict(query_len=65536, max_pages_per_seq=8192), [65536], B.DA_ERR_UNSUPPORTED),   # combine grid limit
 ])
 def test_multi_token_rejects(lib, kw, lens, code):
     assert status_of(params(batch=len(lens), **kw), lens) == code
+
+
+@pytest.mark.parametrize("kw", [dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), dict(q_dtype="f32"),
+                                dict(head_dim=64, q_dtype="bf16", kv_dtype="f32")])
+def test_multi_token_other_dtypes_run_per_token(lib, kw):
+    T, lens = 4, [3060, 40]
+    pl = plan(params(batch=2, query_len=T, num_splits=6, **kw), lens)
+    assert pl.info.split_kernel == 0                       # the vector single-query kernel, once per token
+    assert pl.info.attended_keys == sum(sum(L - T + t + 1 for t in range(T)) for L in lens)
+    D = kw.get("head_dim", 128)
+    rows = 2 * T * 32 * pl.max_splits                       # every token's states
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert pl.workspace_bytes == r256(rows * D * 4) + r256(rows * 2 * 4)
+
+
+def test_forced_vector_runs_multi_token_per_token(lib, monkeypatch):
+    monkeypatch.setenv("DECODE_ATTN_KERNEL", "vector")
+    assert plan(params(batch=1, query_len=4), [100]).info.split_kernel == 0
+    monkeypatch.delenv("DECODE_ATTN_KERNEL")
+    assert plan(params(batch=1, query_len=4), [100]).info.split_kernel == 2
 
 
 def test_query_len_zero_and_one_are_decode(lib):

@@ -166,3 +166,31 @@ def test_whole_context_is_new(gpu):
     w = wl.make_workload(spec, gpu)
     got, _ = run_lib(w)
     check(got, oracle_for(w), "bf16", "f32", "L == T")
+
+
+# Dtype combinations the multi-token kernels do not take (f32 K/V, q and K/V
+# of different types) and a forced vector kernel run the single-query
+# kernels once per token.
+PER_TOKEN = [
+    # T, G, D, q, kv, out, P, lens, W, kernel
+    (4, 4, 128, "f32", "f32", "f32", 16, (4, 100, 3000), 0, "auto"),
+    (3, 2, 64, "f32", "f16", "f32", 16, (3, 700), 0, "auto"),
+    (5, 8, 256, "bf16", "f32", "f32", 8, (5, 50, 999), 7, "auto"),
+    (8, 4, 128, "f16", "f16", "f16", 16, (8, 2000, 333), 0, "vector"),
+    (6, 2, 128, "bf16", "bf16", "f32", 32, (6, 4100), 300, "vector"),
+]
+
+
+@pytest.mark.parametrize("T,G,D,qd,kv,out,P,lens,W,kernel", PER_TOKEN)
+@pytest.mark.parametrize("splits", [0, 3])
+def test_per_token_path_matches_oracle(gpu, T, G, D, qd, kv, out, P, lens, W, kernel, splits):
+    spec = wl.WorkloadSpec(f"pt_T{T}_G{G}_D{D}_{qd}_{kv}", len(lens), 2 * G, 2, D, qd, kv, out, P,
+                           ("list", tuple(lens)), seed=43, window=W, query_len=T)
+    say(f"[per-token] {spec.name} lens={lens} kernel={kernel} splits={splits}")
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w, num_splits=splits, kernel=kernel)
+    assert plan.info.split_kernel == 0
+    err, worst = check(got, oracle_for(w), kv, out, spec.name)
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
+    two, _ = run_lib(w, num_splits=splits, kernel=kernel, two_phase=True)
+    assert torch.equal(got, two)
