@@ -116,6 +116,7 @@ class Plan:
     def __init__(self, handle: int, params: Params):
         self.handle = ctypes.c_void_p(handle)
         self.params = params
+        self._lib = load()  # the library that made the plan also frees it
         info = PlanInfo()
         st = load().decode_attn_plan_info(self.handle, ctypes.byref(info))
         if st != DA_OK:
@@ -139,7 +140,7 @@ class Plan:
 
     def close(self):
         if self.handle:
-            load().decode_attn_plan_destroy(self.handle)
+            self._lib.decode_attn_plan_destroy(self.handle)
             self.handle = ctypes.c_void_p(0)
 
     def __del__(self):
