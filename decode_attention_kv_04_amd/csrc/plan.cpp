@@ -314,6 +314,17 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   for (int32_t b = 0; b < p->batch; ++b) {
     SeqRange r = seq_range(lens[b], p->window, P);
     npages[b] = r.pe - r.pf;
+    if (per_token) {
+      // Token t attends the keys of a sequence of L - (T-1-t): with a window
+      // the page count depends on the window's alignment, so the splits must
+      // cover the largest count over the tokens. The counts repeat with the
+      // length modulo P (and only grow with L below the window), so the last
+      // P + 1 tokens hold the largest.
+      for (int64_t t = std::max<int64_t>(0, T - P - 1); t < T; ++t) {
+        const SeqRange rt = seq_range(static_cast<int64_t>(lens[b]) - (T - 1 - t), p->window, P);
+        npages[b] = std::max(npages[b], rt.pe - rt.pf);
+      }
+    }
     max_np = std::max(max_np, npages[b]);
     total_np += npages[b];
     plan->attended_keys += r.t1 - r.t0;

@@ -251,6 +251,16 @@ def test_multi_token_other_dtypes_run_per_token(lib, kw):
     assert pl.workspace_bytes == r256(rows * D * 4) + r256(rows * 2 * 4)
 
 
+@pytest.mark.parametrize("L,T,W,P,ns", [(2407, 40, 100, 8, 0), (2407, 40, 100, 8, 3), (5000, 9, 33, 16, 0),
+                                         (999, 17, 250, 24, 4), (64, 64, 7, 8, 0)])
+def test_per_token_splits_cover_every_token(lib, L, T, W, P, ns):
+    pl = plan(params(batch=1, query_len=T, window=W, page_size=P, max_pages_per_seq=8192, q_dtype="f32",
+                     kv_dtype="f32", out_dtype="f32", num_splits=ns), [L])
+    worst = max(attended_pages(L - (T - 1 - t), W, P) for t in range(T))
+    assert pl.splits(0) >= math.ceil(worst / pl.pages_per_split)
+    assert pl.max_splits >= pl.splits(0)
+
+
 def test_forced_vector_runs_multi_token_per_token(lib, monkeypatch):
     monkeypatch.setenv("DECODE_ATTN_KERNEL", "vector")
     assert plan(params(batch=1, query_len=4), [100]).info.split_kernel == 0

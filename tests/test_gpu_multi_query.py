@@ -178,6 +178,10 @@ PER_TOKEN = [
     (5, 8, 256, "bf16", "f32", "f32", 8, (5, 50, 999), 7, "auto"),
     (8, 4, 128, "f16", "f16", "f16", 16, (8, 2000, 333), 0, "vector"),
     (6, 2, 128, "bf16", "bf16", "f32", 32, (6, 4100), 300, "vector"),
+    # windows whose page count changes with the token's alignment (regression:
+    # the splits must cover the largest count over the tokens)
+    (40, 2, 128, "f16", "f16", "f32", 8, (2407,), 100, "vector"),
+    (9, 4, 64, "f32", "f32", "f32", 16, (700, 9, 4000), 33, "auto"),
 ]
 
 

@@ -1,0 +1,58 @@
+"""Seeded random configurations through the C-ABI against the oracle: head
+counts, head_dim, dtypes, page size, lengths (including 0 and page
+boundaries), windows, forced split counts, new-token counts and the
+fixed-order mode, drawn from one generator so a failure names its case."""
+import numpy as np
+import pytest
+
+from decode_attention_kv_04_amd import workloads as wl
+
+from gpu_util import check, oracle_for, run_lib, say
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16", "bf16"]
+
+
+def draw_case(i):
+    rng = np.random.default_rng(1000 + i)
+    G = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    Hkv = int(rng.integers(1, 4))
+    D = int(rng.choice([64, 128, 256]))
+    P = int(rng.choice([8, 16, 24, 32, 64]))
+    kv = str(rng.choice(DTYPES))
+    T = int(rng.choice([1, 1, 1, 2, 3, 7, 16, 40]))
+    if T > 1 and rng.random() < 0.7 and kv != "f32":
+        q = kv                                 # the multi-token kernels' dtypes
+    else:
+        q = str(rng.choice(DTYPES))
+    out = str(rng.choice(DTYPES))
+    B = int(rng.integers(1, 5))
+    lens = []
+    for _ in range(B):
+        kind = rng.random()
+        if kind < 0.15:
+            L = 0 if T == 1 else T
+        elif kind < 0.35:
+            L = int(rng.integers(1, 4)) * P + int(rng.integers(-1, 2))
+        else:
+            L = int(rng.integers(1, 3000))
+        lens.append(max(L, T if T > 1 else 0))
+    W = int(rng.choice([0, 0, 1, 7, 100, 1000]))
+    splits = int(rng.choice([0, 0, 1, 2, 5, 1000]))
+    fixed = 0
+    if T == 1 and rng.random() < 0.25:
+        fixed = P * int(rng.integers(1, 9))
+    return dict(G=G, Hkv=Hkv, D=D, P=P, kv=kv, q=q, out=out, T=T, lens=lens, W=W, splits=splits, fixed=fixed)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_config_matches_oracle(gpu, i):
+    c = draw_case(i)
+    say(f"[random {i}] {c}")
+    spec = wl.WorkloadSpec(f"rand{i}", len(c["lens"]), c["G"] * c["Hkv"], c["Hkv"], c["D"], c["q"], c["kv"], c["out"],
+                           c["P"], ("list", tuple(c["lens"])), seed=2000 + i, window=c["W"], query_len=c["T"])
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w, num_splits=c["splits"], fixed_chunk=c["fixed"])
+    err, worst = check(got, oracle_for(w), c["kv"], c["out"], f"case {i}")
+    say(f"  kernel {plan.info.split_kernel}: rel L2 {err:.2e}, worst sequence {worst:.2e}")
