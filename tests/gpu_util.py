@@ -77,17 +77,27 @@ def oracle_for(w, rows=None):
               a["window"])
 
 
+BF16_ROUNDING = 2.0 ** -8  # largest relative error of rounding to bf16 (half a step at 8 significant bits)
+
+
 def check(got, ref, kv_dtype, out_dtype, label=""):
     """Relative L2 over the whole output and per sequence, within the bound
-    for the KV dtype (1e-5 fp32, 1e-3 fp16/bf16, fp32 accumulation); a bf16
-    output is compared with the bf16-rounded oracle."""
+    for the KV dtype (1e-5 fp32, 1e-3 fp16/bf16, fp32 accumulation).
+
+    A bf16 output cannot meet that bar (its own rounding is ~1.6e-3 relative
+    L2), and against the bf16-rounded oracle any tiny difference next to a
+    rounding boundary becomes a whole bf16 step (near-zero elements included).
+    It is held to the bound that follows from the arithmetic: the rounding
+    adds at most 2^-8 of each element, so the relative L2 against the exact
+    oracle is at most the KV bound plus 2^-8. (The same computation at fp32
+    output, in the same suites, is held to the KV bound itself.)"""
     got = host64(got) if isinstance(got, torch.Tensor) else got
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
-    if out_dtype == "bf16":
-        ref = oracle.round_to(ref, "bf16")
     tol = KV_TOL[kv_dtype]
     if out_dtype == "f16" and kv_dtype == "f32":
         tol = 1e-3  # fp16 output rounding alone is ~2e-4
+    if out_dtype == "bf16":
+        tol = tol + BF16_ROUNDING
     err = oracle.relative_l2(got, ref)
     rows = oracle.relative_l2_per_row(got, ref)
     worst = max(rows) if rows else 0.0

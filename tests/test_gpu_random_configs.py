@@ -46,7 +46,7 @@ def draw_case(i):
     return dict(G=G, Hkv=Hkv, D=D, P=P, kv=kv, q=q, out=out, T=T, lens=lens, W=W, splits=splits, fixed=fixed)
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(160))
 def test_random_config_matches_oracle(gpu, i):
     c = draw_case(i)
     say(f"[random {i}] {c}")
