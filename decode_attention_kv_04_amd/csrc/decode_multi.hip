@@ -9,10 +9,13 @@
 // (all keys up to itself, or the last W of them with a window).
 //
 // Query rows. The T*G (token, head) pairs that share KV head j form the rows
-// r = t*G + g of one contraction. multi_kernel: a work-group takes 64
-// consecutive rows (4 wave64s, 16 rows each) and one split of the keys those
-// rows see. multi_keys_kernel (at most 16 rows): the 4 waves share the rows
-// and split the keys.
+// r = t*G + g of one contraction. Row-block kernels: a work-group takes 64
+// or 128 consecutive rows (4 wave64s, one or two groups of 16 rows each) and
+// one split of the keys those rows see; multi_dma_kernel (head_dim 128)
+// stages K/V through a ring of LDS buffers filled by direct global -> LDS
+// loads, multi_kernel (head_dim 64 and 256) through registers.
+// multi_keys_kernel (at most 16 rows): the 4 waves share the rows and split
+// the keys.
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
 //   S^T = K Q^T    A = 16 keys x 32 dims of K,  B = 32 dims x 16 rows of q
 //   O^T += V^T P^T A = 16 dims x 32 keys of V,  B = 32 keys x 16 rows of P
@@ -23,7 +26,8 @@
 // the order that lets each lane pass its own eight probabilities as its B
 // operand: contraction index 8*q + j is key 4q + j (j < 4) or 16 + 4q + j - 4.
 //
-// Staging (multi_kernel). Each tile of 32 keys is read from HBM once per
+// Staging (multi_kernel; multi_dma_kernel is described at its definition).
+// Each tile of 32 keys is read from HBM once per
 // work-group with 16-byte loads into a ring of registers (several tiles ahead
 // of the one being computed) and written to one of two LDS buffers: K
 // row-major, V transposed (dims as rows, keys in contraction order) so both
@@ -155,12 +159,10 @@ __device__ __forceinline__ void init_rows(RowGroup<D>& g, const KernelArgs& a, i
   for (int nb = 0; nb < D / 16; ++nb) g.o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// S^T of a 32-key tile for NR row groups. The K operand (16 keys x 32 dims
-// per MFMA) comes from the K tile in LDS (row stride KS) or, with KREG, from
-// registers already in operand layout: kreg[kb * D/32 + ks].
-template <int D, int KVT, int KS, int NR, bool KREG>
-__device__ __forceinline__ void tile_scores(const uint16_t* sk, const uint4* kreg, const RowGroup<D> (&rg)[NR],
-                                            int col, int q4, mq_float4 (&sacc)[NR][2]) {
+// S^T of a 32-key tile for NR row groups. kop(kb, ks) returns this lane's K
+// operand (16 keys x 32 dims per MFMA): keys 16*kb + col, dims 32*ks + 8*q4.
+template <int D, int KVT, int NR, class KOp>
+__device__ __forceinline__ void tile_scores(KOp&& kop, const RowGroup<D> (&rg)[NR], mq_float4 (&sacc)[NR][2]) {
   constexpr int NKS = D / 32;
 #pragma unroll
   for (int g = 0; g < NR; ++g)
@@ -170,11 +172,7 @@ __device__ __forceinline__ void tile_scores(const uint16_t* sk, const uint4* kre
   for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      uint4 ka;
-      if constexpr (KREG)
-        ka = kreg[kb * NKS + ks];
-      else
-        ka = *reinterpret_cast<const uint4*>(&sk[(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
+      const uint4 ka = kop(kb, ks);
 #pragma unroll
       for (int g = 0; g < NR; ++g) sacc[g][kb] = mfma<KVT>(ka, rg[g].qb[ks], sacc[g][kb]);
     }
@@ -182,10 +180,13 @@ __device__ __forceinline__ void tile_scores(const uint16_t* sk, const uint4* kre
 }
 
 // Masking, online-softmax update and O^T += V^T P^T of a 32-key tile whose
-// scores are in sacc, for NR row groups; V^T from LDS (row stride VS).
-template <int D, int KVT, int VS, int NR>
-__device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], const uint16_t* sv, int tb,
-                                            RowGroup<D> (&rg)[NR], float sl2, int col, int q4) {
+// scores are in sacc, for NR row groups. vop(nb, full) returns this lane's
+// V^T operand: dim 16*nb + col, the eight keys of its contraction positions
+// 8*q4 .. 8*q4 + 7; `full` is true when every key of the tile is inside
+// every row's keys.
+template <int D, int KVT, int NR, class VOp>
+__device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], VOp&& vop, int tb, RowGroup<D> (&rg)[NR],
+                                            float sl2, int q4) {
   constexpr int NDB = D / 16;
   // Tiles inside every row's keys (all but the causal diagonal and the
   // split and window edges) skip the per-key masks: a wave-uniform branch.
@@ -214,14 +215,17 @@ __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], const uint
     float mt = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     // The reference max moves only when a score exceeds it by more than
     // kSlack (base-2 units): probabilities stay below 2^kSlack, exactly
     // representable in range for f16/bf16 P and fp32 sums, and the rescale
     // of O (held in accumulation registers) is rare after the first tiles.
-    const bool grow = mt > rg[g].m + kSlack;
-    if (__any(grow)) {
+    // The row's reference is shared by its four lanes (one per key group),
+    // and the row maximum over them is needed only when some lane's own
+    // maximum exceeds the reference by more than the slack.
+    if (__any(mt > rg[g].m + kSlack)) {
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const bool grow = mt > rg[g].m + kSlack;
       const float mn = grow ? mt : rg[g].m;
       const float mu = mn == -INFINITY ? 0.0f : mn;
       const float alpha = exp2_fast(rg[g].m - mu);
@@ -261,7 +265,7 @@ __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], const uint
   }
 #pragma unroll
   for (int nb = 0; nb < NDB; ++nb) {
-    const uint4 va = *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]);
+    const uint4 va = vop(nb, full);
 #pragma unroll
     for (int g = 0; g < NR; ++g) {
       rg[g].o[nb] = mfma<KVT>(va, ph[g], rg[g].o[nb]);
@@ -465,10 +469,19 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   // buffer while those matrix products run, then finishes tile m.
   mq_float4 sacc[NR][2];
   auto scores = [&](int buf) {
-    if (wave_rows) tile_scores<D, KVT, KS, NR, false>(sk[buf], nullptr, rg, col, q4, sacc);
+    if (wave_rows)
+      tile_scores<D, KVT, NR>(
+          [&](int kb, int ks) {
+            return *reinterpret_cast<const uint4*>(&sk[buf][(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
+          },
+          rg, sacc);
   };
   auto finish = [&](int buf, int tb) {
-    if (wave_rows) tile_update<D, KVT, VS, NR>(sacc, sv[buf], tb, rg, sl2, col, q4);
+    if (wave_rows)
+      tile_update<D, KVT, NR>(
+          sacc,
+          [&](int nb, bool) { return *reinterpret_cast<const uint4*>(&sv[buf][(nb * 16 + col) * VS + q4 * 8]); },
+          tb, rg, sl2, q4);
   };
 
   // Tile m's loads go to ring slot m % (PD + 1) PD tiles ahead; at step m
@@ -514,6 +527,243 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
   for (int g = 0; g < NR; ++g) finish_rows(a, rg[g], nsplit, s, q4);
 }
 
+
+// ---------------------------------------------------------------------------
+// Row-block kernel with direct global -> LDS staging (head_dim 128).
+//
+// The K and V tiles go from HBM into LDS without passing through registers:
+// global_load_lds_dwordx4 writes lane i's 16 bytes at a wave-uniform LDS
+// address + 16 i, so a wave instruction fills 1 KiB (four 256-byte key rows).
+// Tiles are kept in a ring of NS LDS stages, NS - 1 tiles ahead of the one
+// being computed, and every wave loads its own 8 keys of each tile (one page,
+// as pages hold a multiple of 8 keys), so a tile costs a wave one scalar page
+// lookup and four load instructions.
+//
+// Layout of a stage: K and V both row-major (key rows of 256 bytes), the
+// 16-byte segment c of tile key k stored in slot c ^ swz(k). A K operand read
+// (16 keys, one segment each) then touches 16 different slots, and V^T is
+// read with the 16-bit transposing LDS read (ds_read_b64_tr_b16): within each
+// 16-lane group, lane i receives element i % 4 of the 8-byte rows addressed
+// by lanes (i % 16) / 4 + 4 j, j = 0..3. Lane (col, q4) addresses dims
+// 16 nb + 4 (col % 4) .. +3 of key 4 q4 + col / 4 (and that key + 16), so
+// it receives dim 16 nb + col of keys 4 q4 + j (and 16 + 4 q4 + j): its V^T
+// operand in the contraction order of the P operand. The 16 addresses of a
+// group cover four keys and two segments each, eight different slots.
+//
+// V rows outside the split's keys are not zeroed in LDS (the load cannot);
+// tiles that straddle those keys clear them in the operand instead.
+// ---------------------------------------------------------------------------
+
+// Slot permutation: a bijection on k mod 16, and (swz(k) >> 1) & 3 = k & 3
+// differs across each aligned group of four keys.
+__device__ __forceinline__ int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+
+// One wave's 1 KiB global -> LDS copy: lane i's 16 bytes from `src` land at
+// LDS byte address lds_base + 16 i (lds_base wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+}
+
+// Wait until at most N of this wave's global loads (the copies above among
+// them) are outstanding. Loads complete in order.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  // (a C-style cast is the address-space conversion to a 32-bit LDS offset)
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+typedef short mq_short4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr(const uint16_t* p) {
+  const mq_short4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) mq_short4*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Stages in the LDS ring (NS - 1 tiles in flight). 2 and 3 measured the
+// same on the 128- and 512-token suffixes; 3 leaves more slack for latency.
+constexpr int kLdsStages = 3;
+
+template <int KVT, int NS, int NR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3 : 2))) void multi_dma_kernel(
+    const KernelArgs a) {
+  constexpr int D = 128;
+  constexpr int QB = 64 * NR;      // query rows per work-group (4 waves x NR groups of 16)
+  constexpr int ROWB = D * 2;      // bytes per K/V row
+  constexpr int TILE = KT * D;     // 16-bit elements per K (or V) tile
+  constexpr int LOADS = 4;         // copies per wave per tile (2 K, 2 V)
+  static_assert(NS >= 2 && 2 * NS * TILE * 2 <= 65536, "LDS ring");
+  __shared__ __align__(1024) uint16_t sk[NS][TILE];
+  __shared__ __align__(1024) uint16_t sv[NS][TILE];
+
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.z;
+  const int S = a.max_splits;
+  const int rb = blockIdx.y / S;
+  const int s = blockIdx.y - rb * S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int q4 = lane >> 4;
+
+  const int T = a.query_len;
+  const int G = a.group;
+  const int R = T * G;
+  const int P = a.page_size;
+  const int W = a.window;
+  const int L = a.seq_lens[b];
+
+  const int r_first = rb * QB;
+  if (r_first >= R) return;
+  const int r_last = (r_first + QB < R ? r_first + QB : R) - 1;
+  int hi_blk = L - T + r_last / G + 1;
+  hi_blk = hi_blk < 0 ? 0 : hi_blk;
+  int lo_blk = W > 0 ? L - T + r_first / G + 1 - W : 0;
+  lo_blk = lo_blk < 0 ? 0 : (lo_blk > hi_blk ? hi_blk : lo_blk);
+  const int pf = lo_blk / P;
+  const int pe = (hi_blk + P - 1) / P;
+  const int cp = a.pages_per_split;
+  int nsplit = (pe - pf + cp - 1) / cp;
+  nsplit = nsplit < 1 ? 1 : (nsplit > S ? S : nsplit);
+  if (s >= nsplit) return;  // whole work-group, uniform
+  const int plo = pf + s * cp;
+  const int phi = plo + cp < pe ? plo + cp : pe;
+  const int t_lo = lo_blk > plo * P ? lo_blk : plo * P;
+  const int t_hi = hi_blk < phi * P ? hi_blk : phi * P;
+
+  RowGroup<D> rg[NR];
+#pragma unroll
+  for (int g = 0; g < NR; ++g)
+    init_rows(rg[g], a, r_first + (wave * NR + g) * 16 + col, r_last, b, kvh, L, t_lo, t_hi, q4);
+  const bool wave_rows = r_first + wave * NR * 16 <= r_last;
+  // Let the q loads land here, in a wait the compiler sees: its own wait
+  // before their first use would otherwise sit inside the key loop and wait
+  // for every copy in flight on each tile (vmcnt(0), other counters at
+  // their maximum: the gfx9 encoding).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  const int tile_first = t_lo / KT;
+  const int ntiles = t_hi > t_lo ? (t_hi + KT - 1) / KT - tile_first : 0;
+
+  // Copies: this wave's keys 8 w .. 8 w + 7 of a tile; lane i of copy j
+  // takes key 8 w + 4 j + i / 16 and fills slot i % 16 of its row.
+  const int64_t block_bytes = static_cast<int64_t>(P) * ROWB;
+  const int64_t page_bytes = block_bytes * a.num_kv_heads;
+  const char* kbase = static_cast<const char*>(a.k_pool) + block_bytes * kvh;
+  const char* vbase = static_cast<const char*>(a.v_pool) + block_bytes * kvh;
+  const int krow = lane >> 4;
+  const int slot = lane & 15;
+  const int loff0 = krow * ROWB + 16 * (slot ^ swz(8 * wave + krow));
+  const int loff1 = (krow + 4) * ROWB + 16 * (slot ^ swz(8 * wave + krow + 4));
+  // The page table is not written while the kernel runs: reading it through
+  // the constant address space lets the wave-uniform lookups below be scalar
+  // loads (the copies' memory clobbers would otherwise force vector loads,
+  // whose wait would also wait for every copy in flight).
+  const __attribute__((address_space(4))) int32_t* table_row =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + static_cast<int64_t>(b) * a.max_pages);
+  const int pi_last = phi > plo ? phi - 1 : plo;
+  // Wave-uniform cursor: page and in-page position of key 8 w of the next
+  // tile to load; its physical page id is read one tile ahead.
+  int cpi = (tile_first * KT + 8 * wave) / P;
+  int coff = tile_first * KT + 8 * wave - cpi * P;
+  int cphys = 0;
+  auto fetch_id = [&]() {
+    int pi = cpi < plo ? plo : (cpi > pi_last ? pi_last : cpi);
+    pi = pi < a.max_pages ? pi : a.max_pages - 1;
+    cphys = table_row[pi];
+  };
+  auto issue = [&](int stage) {
+    const int64_t off = static_cast<int64_t>(cphys) * page_bytes + static_cast<int64_t>(coff) * ROWB;
+    const uint32_t lk = lds_address(&sk[stage][8 * wave * D]);
+    const uint32_t lv = lds_address(&sv[stage][8 * wave * D]);
+    dma16(kbase + off + loff0, lk);
+    dma16(kbase + off + loff1, lk + 4 * ROWB);
+    dma16(vbase + off + loff0, lv);
+    dma16(vbase + off + loff1, lv + 4 * ROWB);
+    coff += KT;
+    while (coff >= P) {
+      coff -= P;
+      ++cpi;
+    }
+    fetch_id();
+  };
+
+  // Operand addresses (16-bit elements within a stage).
+  const int fk = swz(col);
+  const int vkey = 4 * q4 + (col >> 2);
+  const int fv = swz(vkey);
+  const int vbc = (col & 3) >> 1;
+  const int vh = (col & 1) * 4;
+  const float sl2 = a.scale_log2;
+
+  if (ntiles > 0) {
+    fetch_id();
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+      if (k < ntiles) issue(k);
+    int stage = 0;
+    for (int m = 0; m < ntiles; ++m) {
+      // This wave's copies of tile m are done once at most the copies of
+      // the later tiles already issued are outstanding; the barrier then
+      // makes every wave's copies visible and ends every wave's reads of the
+      // stage the next copy overwrites.
+      if (m + NS - 2 < ntiles)
+        wait_loads<(NS - 2) * LOADS>();
+      else
+        wait_loads<0>();
+      lds_barrier();
+      if (m + NS - 1 < ntiles) issue(stage == 0 ? NS - 1 : stage - 1);
+      if (wave_rows) {
+        const uint16_t* ks_ = sk[stage];
+        const uint16_t* vs_ = sv[stage];
+        const int tb = (tile_first + m) * KT;
+        mq_float4 sacc[NR][2];
+        tile_scores<D, KVT, NR>(
+            [&](int kb, int kstep) {
+              return *reinterpret_cast<const uint4*>(&ks_[(kb * 16 + col) * D + (((4 * kstep + q4) ^ fk) * 8)]);
+            },
+            rg, sacc);
+        // All V^T operands of the tile are read before the softmax so that
+        // their latency hides behind it. V rows of keys outside [t_lo, t_hi)
+        // may hold anything: tiles that straddle those keys clear them in
+        // the operand (keys 4 q4 + j and 16 + 4 q4 + j, two per dword).
+        uint4 vt[D / 16];
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) {
+          const uint16_t* p = &vs_[vkey * D + (((2 * nb + vbc) ^ fv) * 8) + vh];
+          const uint2 lo = read_tr(p);
+          const uint2 hi = read_tr(p + 16 * D);
+          vt[nb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        if (tb < t_lo || tb + KT > t_hi) {
+          uint32_t vmask[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int k0 = tb + (d >> 1) * 16 + 4 * q4 + (d & 1) * 2;
+            vmask[d] = ((k0 >= t_lo && k0 < t_hi) ? 0x0000FFFFu : 0u) |
+                       ((k0 + 1 >= t_lo && k0 + 1 < t_hi) ? 0xFFFF0000u : 0u);
+          }
+#pragma unroll
+          for (int nb = 0; nb < D / 16; ++nb) {
+            vt[nb].x &= vmask[0];
+            vt[nb].y &= vmask[1];
+            vt[nb].z &= vmask[2];
+            vt[nb].w &= vmask[3];
+          }
+        }
+        tile_update<D, KVT, NR>(
+            sacc, [&](int nb, bool) { return vt[nb]; },
+            tb, rg, sl2, q4);
+      }
+      stage = stage == NS - 1 ? 0 : stage + 1;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NR; ++g) finish_rows(a, rg[g], nsplit, s, q4);
+}
 
 // At most 16 query rows per KV head (a few drafted tokens): the four waves
 // share the rows and split the keys. Wave w computes tiles w, w+4, w+8, ...
@@ -633,14 +883,16 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
       const int tb = (my_first + n * KW) * KT;
       const bool more = n + 1 < ntiles;
       mq_float4 sacc[1][2];
-      tile_scores<D, KVT, KS, 1, true>(nullptr, kreg, rg, col, q4, sacc);
+      tile_scores<D, KVT, 1>([&](int kb, int ks) { return kreg[kb * NKS + ks]; }, rg, sacc);
       if (more) {
         next_tile();
         issue_k();
       }
       stage_v(tb);  // this wave's region only; LDS operations of a wave stay in order
       if (more) issue_v();
-      tile_update<D, KVT, VS, 1>(sacc, sv, tb, rg, sl2, col, q4);
+      tile_update<D, KVT, 1>(
+          sacc, [&](int nb, bool) { return *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]); }, tb,
+          rg, sl2, q4);
     }
   }
 
@@ -695,7 +947,15 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
   if (rows == 64) {
-    hipLaunchKernelGGL((multi_kernel<D, KVT, 4, 1>), grid, dim3(256), 0, st, a);
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((multi_dma_kernel<KVT, kLdsStages, 1>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((multi_kernel<D, KVT, 4, 1>), grid, dim3(256), 0, st, a);
+  } else if (rows == 128) {
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((multi_dma_kernel<KVT, kLdsStages, 2>), grid, dim3(256), 0, st, a);
+    else
+      return hipErrorInvalidValue;
   } else if (rows == 16) {
     if constexpr (D <= 128)
       hipLaunchKernelGGL((multi_keys_kernel<D, KVT>), grid, dim3(256), 0, st, a);

@@ -24,12 +24,25 @@ namespace {
 // Splits per KV head are sized so the split pass has about this many
 // work-groups per compute unit in total.
 constexpr int64_t kTargetGroupsPerCu = 9;
-// The multi-token kernel with 64-row blocks does matrix work on every key it
-// loads: it is fastest with one round of resident work-groups (2 per compute
-// unit at head_dim 128, by registers), so each row block's keys are split
-// only as far as needed to fill that round (a sweep of split counts on
-// 16..512-token suffixes over 0.5-8k-token contexts).
-int64_t resident_row_groups_per_cu(int32_t head_dim) { return head_dim <= 64 ? 4 : (head_dim <= 128 ? 2 : 1); }
+// The multi-token row-block kernels do matrix work on every key they load:
+// they are fastest with one round of resident work-groups, so each row
+// block's keys are split only as far as needed to fill that round (a sweep
+// of split counts on 16..512-token suffixes over 0.5-8k-token contexts).
+// Resident work-groups per compute unit, by registers and LDS: the head_dim
+// 128 kernel holds 3 (64-row blocks) or 2 (128-row blocks).
+int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
+  if (head_dim == 128) return rows == 128 ? 2 : 3;
+  return head_dim <= 64 ? 4 : 1;
+}
+// Rows per block at head_dim 128: 128 (two 16-row groups per wave sharing
+// every K/V operand read) measured 3-6 % faster than 64 on 32..512-token
+// suffixes; DECODE_ATTN_MQ_ROWS=64 or 128 overrides it.
+int64_t mq_rows_d128() {
+  const char* s = std::getenv("DECODE_ATTN_MQ_ROWS");
+  if (s && std::strcmp(s, "64") == 0) return 64;
+  if (s && std::strcmp(s, "128") == 0) return 128;
+  return 128;
+}
 // A split never holds fewer attended tokens than this (the pages' 256-token
 // switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
 constexpr int64_t kDefaultMinSplitTokens = 256;
@@ -180,7 +193,8 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   const int64_t R = T * G;
   // Up to 16 rows (D <= 128): four waves share the rows and split the keys;
   // otherwise four waves of 16 rows share each key tile.
-  const int64_t QB = (R <= 16 && p.head_dim <= 128 && forced_kernel() != 2) ? 16 : 64;
+  const int64_t QB = (R <= 16 && p.head_dim <= 128 && forced_kernel() != 2) ? 16
+                     : (p.head_dim == 128 ? mq_rows_d128() : 64);
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);
@@ -218,7 +232,7 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
       c = heuristic_split_pages(total_np, max_np, p.num_kv_heads, plan->num_cus, P);
     } else {
       const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * nrb;
-      const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim),
+      const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim, QB),
                                     blocks);
       c = ceil_div(max_np, std::max<int64_t>(1, want));
       c = std::min(max_np, std::max(c, ceil_div(min_split_tokens(), P)));

@@ -35,6 +35,23 @@ def split_kernel(kind):
             os.environ["DECODE_ATTN_KERNEL"] = old
 
 
+@contextlib.contextmanager
+def mq_rows(rows):
+    """Rows per block of the head_dim-128 multi-token kernel ("64" / "128"; None = default)."""
+    old = os.environ.get("DECODE_ATTN_MQ_ROWS")
+    if rows:
+        os.environ["DECODE_ATTN_MQ_ROWS"] = str(rows)
+    else:
+        os.environ.pop("DECODE_ATTN_MQ_ROWS", None)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("DECODE_ATTN_MQ_ROWS", None)
+        else:
+            os.environ["DECODE_ATTN_MQ_ROWS"] = old
+
+
 def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None, page_table=None,
             window=None, seq_lens=None, seq_lens_host=None, two_phase=False, kernel=None, fixed_chunk=0):
     """One decode_attn_run (or split + combine) on the workload's tensors;

@@ -7,7 +7,7 @@ import torch
 import oracle
 from decode_attention_kv_04_amd import workloads as wl
 
-from gpu_util import TORCH_DT, check, host64, oracle_for, run_lib, say
+from gpu_util import TORCH_DT, check, host64, mq_rows, oracle_for, run_lib, say
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,22 @@ def test_forced_block_shapes_match_oracle(gpu, kernel, T, G, D, kv, out, P, lens
     w = wl.make_workload(spec, gpu)
     got, plan = run_lib(w, num_splits=2, kernel=kernel)
     err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} {kernel}")
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
+
+
+# Both block sizes of the head_dim-128 kernel (one or two 16-row groups per
+# wave), with forced splits so that blocks start and end inside pages and
+# tiles; the two must agree with each other to the f16-P rounding.
+@pytest.mark.parametrize("rows", ["64", "128"])
+@pytest.mark.parametrize("T,G,D,kv,out,P,lens,W", [g for g in GRID if g[2] == 128])
+def test_row_block_sizes_match_oracle(gpu, rows, T, G, D, kv, out, P, lens, W):
+    spec = spec_of(T, G, D, kv, out, P, lens, W)
+    say(f"[multi] {spec.name} rows={rows}")
+    w = wl.make_workload(spec, gpu)
+    with mq_rows(rows):
+        got, plan = run_lib(w, num_splits=3, kernel="rows")
+    assert plan.info.split_kernel == 2
+    err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} rows {rows}")
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
 
 
