@@ -41,7 +41,9 @@
 // Softmax precision: P enters the P.V product as f16 for f16 K/V and as a
 // bf16 hi + lo pair (two products) for bf16 K/V, since one bf16 rounding of P
 // alone costs more than the 1e-3 relative-L2 budget; scores, softmax state and
-// accumulation are fp32.
+// accumulation are fp32. The row sums l are taken on the matrix cores from
+// the same rounded P (a ones operand), so numerator and denominator use
+// identical weights.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -61,6 +63,9 @@ constexpr int VPAD = 8;         // LDS padding per transposed V row
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 mq_bf168 __attribute__((ext_vector_type(8)));
 typedef float mq_float4 __attribute__((ext_vector_type(4)));
+typedef float mq_float2 __attribute__((ext_vector_type(2)));
+typedef _Float16 mq_half2 __attribute__((ext_vector_type(2)));
+typedef __bf16 mq_bf162 __attribute__((ext_vector_type(2)));
 
 template <int KVT>
 __device__ __forceinline__ mq_float4 mfma(const uint4& a, const uint4& b, mq_float4 c) {
@@ -74,15 +79,6 @@ __device__ __forceinline__ mq_float4 mfma(const uint4& a, const uint4& b, mq_flo
 
 // Contraction position of key k (0..31) of a tile in the P.V product.
 __device__ __forceinline__ int kpos(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
-
-// Round to nearest even: f32 -> f16 bits / bf16 bits.
-__device__ __forceinline__ uint32_t f16_bits(float x) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
-}
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs only (probabilities)
-}
 
 // K/V loads of the multi-token kernels go through the caches normally: a
 // thread's segments of one row arrive over several instructions, and a
@@ -130,7 +126,8 @@ struct RowGroup {
   int lo, hi;     // keys [lo, hi) of the row within the split (empty if no row)
   int64_t qrow;   // flat (sequence, token, query head) index
   bool ok;        // a real row
-  float m, lpart;
+  float m;
+  mq_float4 lsum;  // row sum of P from the matrix cores: register 0 of lane (col, k-group 0)
   mq_float4 o[D / 16];
 };
 
@@ -154,7 +151,7 @@ __device__ __forceinline__ void init_rows(RowGroup<D>& g, const KernelArgs& a, i
       g.qb[ks] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + (g.qrow * D + ks * 32 + q4 * 8) * 2);
   }
   g.m = -INFINITY;
-  g.lpart = 0.0f;
+  g.lsum = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) g.o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
 }
@@ -179,11 +176,68 @@ __device__ __forceinline__ void tile_scores(KOp&& kop, const RowGroup<D> (&rg)[N
   }
 }
 
+// P of one row group from its eight raw scores x (probabilities
+// exp2(x * sl2 + nmu)), as the B operand of the P.V products: pairs rounded
+// to nearest even and packed by one conversion each; for bf16 a hi + lo
+// pair of operands.
+template <int KVT>
+__device__ __forceinline__ void make_p(const float (&x)[8], float sl2, float nmu, uint4& ph, uint4& pl) {
+  float pr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pr[j] = exp2_fast(fmaf(x[j], sl2, nmu));
+  uint32_t w[4];
+  if constexpr (KVT == DA_F16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(mq_float2{pr[2 * j], pr[2 * j + 1]}, mq_half2));
+    ph = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint32_t wl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(mq_float2{pr[2 * j], pr[2 * j + 1]}, mq_bf162));
+      const float h0 = __builtin_bit_cast(float, w[j] << 16);
+      const float h1 = __builtin_bit_cast(float, w[j] & 0xFFFF0000u);
+      wl[j] = __builtin_bit_cast(uint32_t,
+                                 __builtin_convertvector(mq_float2{pr[2 * j] - h0, pr[2 * j + 1] - h1}, mq_bf162));
+    }
+    ph = make_uint4(w[0], w[1], w[2], w[3]);
+    pl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+  }
+}
+
+// O^T += V^T P^T and the row sums of P for NR row groups. The sums run on
+// the matrix cores (one more product per row group instead of eight
+// additions per lane): a 16 x 32 operand whose row 0 is ones gives
+// sum_k P[k][row] in row 0 of the result, over the rounded P that also
+// enters O. vop(nb) returns this lane's V^T operand: dim 16*nb + col, the
+// eight keys of its contraction positions 8*q4 .. 8*q4 + 7.
+template <int D, int KVT, int NR, class VOp>
+__device__ __forceinline__ void pv_products(const uint4 (&ph)[NR], const uint4 (&pl)[NR], VOp&& vop,
+                                            RowGroup<D> (&rg)[NR]) {
+  constexpr uint32_t one2 = KVT == DA_F16 ? 0x3C003C00u : 0x3F803F80u;
+  const uint32_t o = (threadIdx.x & 15) == 0 ? one2 : 0u;
+  const uint4 ones = make_uint4(o, o, o, o);
+#pragma unroll
+  for (int g = 0; g < NR; ++g) {
+    rg[g].lsum = mfma<KVT>(ones, ph[g], rg[g].lsum);
+    if constexpr (KVT != DA_F16) rg[g].lsum = mfma<KVT>(ones, pl[g], rg[g].lsum);
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    const uint4 va = vop(nb);
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
+      rg[g].o[nb] = mfma<KVT>(va, ph[g], rg[g].o[nb]);
+      if constexpr (KVT != DA_F16) rg[g].o[nb] = mfma<KVT>(va, pl[g], rg[g].o[nb]);
+    }
+  }
+}
+
 // Masking, online-softmax update and O^T += V^T P^T of a 32-key tile whose
 // scores are in sacc, for NR row groups. vop(nb, full) returns this lane's
-// V^T operand: dim 16*nb + col, the eight keys of its contraction positions
-// 8*q4 .. 8*q4 + 7; `full` is true when every key of the tile is inside
-// every row's keys.
+// V^T operand (as for pv_products); `full` is true when every key of the
+// tile is inside every row's keys.
 template <int D, int KVT, int NR, class VOp>
 __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], VOp&& vop, int tb, RowGroup<D> (&rg)[NR],
                                             float sl2, int q4) {
@@ -197,24 +251,25 @@ __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], VOp&& vop,
   uint4 ph[NR], pl[NR];  // P^T as the B operand of each row group: contraction index 8*q4 + j
 #pragma unroll
   for (int g = 0; g < NR; ++g) {
-    float x[8];
-    if (full) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = sacc[g][j >> 2][j & 3] * sl2;
-    } else {
+    // Raw scores (the scale is applied inside the exponent's fma); keys
+    // outside the row's range become -inf by select, in place.
+    if (!full) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = tb + kb * 16 + q4 * 4 + i;
-          const float v = sacc[g][kb][i] * sl2;
-          x[kb * 4 + i] = (key >= rg[g].lo && key < rg[g].hi) ? v : -INFINITY;
+          sacc[g][kb][i] = (key >= rg[g].lo && key < rg[g].hi) ? sacc[g][kb][i] : -INFINITY;
         }
       }
     }
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = sacc[g][j >> 2][j & 3];
     float mt = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    mt *= sl2;  // = the largest scaled score (the scale is positive)
     // The reference max moves only when a score exceeds it by more than
     // kSlack (base-2 units): probabilities stay below 2^kSlack, exactly
     // representable in range for f16/bf16 P and fp32 sums, and the rescale
@@ -229,57 +284,44 @@ __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], VOp&& vop,
       const float mn = grow ? mt : rg[g].m;
       const float mu = mn == -INFINITY ? 0.0f : mn;
       const float alpha = exp2_fast(rg[g].m - mu);
-      rg[g].lpart *= alpha;
+      rg[g].lsum *= alpha;
 #pragma unroll
       for (int nb = 0; nb < NDB; ++nb) rg[g].o[nb] *= alpha;
       rg[g].m = mn;
     }
-    const float mu = rg[g].m == -INFINITY ? 0.0f : rg[g].m;
-    float pr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pr[j] = exp2_fast(x[j] - mu);
-      rg[g].lpart += pr[j];
-    }
-    if constexpr (KVT == DA_F16) {
-      ph[g].x = f16_bits(pr[0]) | (f16_bits(pr[1]) << 16);
-      ph[g].y = f16_bits(pr[2]) | (f16_bits(pr[3]) << 16);
-      ph[g].z = f16_bits(pr[4]) | (f16_bits(pr[5]) << 16);
-      ph[g].w = f16_bits(pr[6]) | (f16_bits(pr[7]) << 16);
-    } else {
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        hi[j] = bf16_bits(pr[j]);
-        lo[j] = bf16_bits(pr[j] - __builtin_bit_cast(float, hi[j] << 16));
-      }
-      ph[g].x = hi[0] | (hi[1] << 16);
-      ph[g].y = hi[2] | (hi[3] << 16);
-      ph[g].z = hi[4] | (hi[5] << 16);
-      ph[g].w = hi[6] | (hi[7] << 16);
-      pl[g].x = lo[0] | (lo[1] << 16);
-      pl[g].y = lo[2] | (lo[3] << 16);
-      pl[g].z = lo[4] | (lo[5] << 16);
-      pl[g].w = lo[6] | (lo[7] << 16);
-    }
+    make_p<KVT>(x, sl2, rg[g].m == -INFINITY ? 0.0f : -rg[g].m, ph[g], pl[g]);
   }
-#pragma unroll
-  for (int nb = 0; nb < NDB; ++nb) {
-    const uint4 va = vop(nb, full);
-#pragma unroll
-    for (int g = 0; g < NR; ++g) {
-      rg[g].o[nb] = mfma<KVT>(va, ph[g], rg[g].o[nb]);
-      if constexpr (KVT != DA_F16) rg[g].o[nb] = mfma<KVT>(va, pl[g], rg[g].o[nb]);
-    }
-  }
+  pv_products<D, KVT, NR>(ph, pl, [&](int nb) { return vop(nb, full); }, rg);
 }
 
-// The row's l is split over its four lanes (one per key group): sum them,
-// then write O / l (one split) or the state (m, l, O) to slot s.
+// The common tile of the row-block kernel with the LDS ring: every key
+// inside every row's keys and no score above its row's reference by more
+// than the slack (the caller checked both), so there is nothing to mask and
+// no reference moves; the same arithmetic as tile_update.
+template <int D, int KVT, int NR, class VOp>
+__device__ __forceinline__ void tile_update_plain(const mq_float4 (&sacc)[NR][2], VOp&& vop, RowGroup<D> (&rg)[NR],
+                                                  float sl2) {
+  uint4 ph[NR], pl[NR];
+#pragma unroll
+  for (int g = 0; g < NR; ++g) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = sacc[g][j >> 2][j & 3];
+    make_p<KVT>(x, sl2, rg[g].m == -INFINITY ? 0.0f : -rg[g].m, ph[g], pl[g]);
+  }
+  pv_products<D, KVT, NR>(ph, pl, vop, rg);
+}
+
+// The row's l, from register 0 of the row's lane in k-group 0.
+template <int D>
+__device__ __forceinline__ float row_sum(const RowGroup<D>& g) {
+  return __shfl(g.lsum[0], static_cast<int>(threadIdx.x & 15), 64);
+}
+
+// Write O / l (one split) or the state (m, l, O) to slot s.
 template <int D>
 __device__ __forceinline__ void finish_rows(const KernelArgs& a, RowGroup<D>& g, int nsplit, int s, int q4) {
-  float l = g.lpart + __shfl_xor(g.lpart, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  const float l = row_sum(g);
   if (!g.ok) return;
   if (nsplit == 1) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
@@ -547,16 +589,18 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
 // by lanes (i % 16) / 4 + 4 j, j = 0..3. Lane (col, q4) addresses dims
 // 16 nb + 4 (col % 4) .. +3 of key 4 q4 + col / 4 (and that key + 16), so
 // it receives dim 16 nb + col of keys 4 q4 + j (and 16 + 4 q4 + j): its V^T
-// operand in the contraction order of the P operand. The 16 addresses of a
-// group cover four keys and two segments each, eight different slots.
+// operand in the contraction order of the P operand.
 //
 // V rows outside the split's keys are not zeroed in LDS (the load cannot);
 // tiles that straddle those keys clear them in the operand instead.
 // ---------------------------------------------------------------------------
 
-// Slot permutation: a bijection on k mod 16, and (swz(k) >> 1) & 3 = k & 3
-// differs across each aligned group of four keys.
-__device__ __forceinline__ int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+// Slot permutation, for LDS reads served 256 bytes (64 banks of 4 bytes) at
+// a time: a bijection on k mod 16 (the 16 keys of a K operand read fall in
+// 16 different slots), and swz(k) >> 1 = k mod 8 differs across the eight
+// keys that 32 lanes of a transposing V read address, two segments each,
+// so those 32 lanes read 32 different 8-byte units.
+__device__ __forceinline__ int swz(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
 
 // One wave's 1 KiB global -> LDS copy: lane i's 16 bytes from `src` land at
 // LDS byte address lds_base + 16 i (lds_base wave-uniform).
@@ -614,7 +658,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3
   const int R = T * G;
   const int P = a.page_size;
   const int W = a.window;
-  const int L = a.seq_lens[b];
+  // Wave-uniform in a scalar register, so that every tile and range test
+  // derived from it is a scalar branch.
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
 
   const int r_first = rb * QB;
   if (r_first >= R) return;
@@ -638,7 +684,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3
 #pragma unroll
   for (int g = 0; g < NR; ++g)
     init_rows(rg[g], a, r_first + (wave * NR + g) * 16 + col, r_last, b, kvh, L, t_lo, t_hi, q4);
-  const bool wave_rows = r_first + wave * NR * 16 <= r_last;
   // Let the q loads land here, in a wait the compiler sees: its own wait
   // before their first use would otherwise sit inside the key loop and wait
   // for every copy in flight on each tile (vmcnt(0), other counters at
@@ -705,60 +750,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3
     for (int k = 0; k < NS - 1; ++k)
       if (k < ntiles) issue(k);
     int stage = 0;
-    for (int m = 0; m < ntiles; ++m) {
-      // This wave's copies of tile m are done once at most the copies of
-      // the later tiles already issued are outstanding; the barrier then
-      // makes every wave's copies visible and ends every wave's reads of the
-      // stage the next copy overwrites.
+    int m = 0;
+    mq_float4 sacc[NR][2];
+    uint4 vt[D / 16];
+    // Start of tile m: its copies landed (this wave's: at most the copies of
+    // the later tiles already issued are outstanding; every wave's: the
+    // barrier, which also ends every wave's reads of the stage the next copy
+    // overwrites), the copy NS - 1 tiles ahead goes out, then S^T and all
+    // V^T operands of the tile (read before the softmax so that their
+    // latency hides behind it).
+    auto begin_tile = [&]() {
       if (m + NS - 2 < ntiles)
         wait_loads<(NS - 2) * LOADS>();
       else
         wait_loads<0>();
       lds_barrier();
       if (m + NS - 1 < ntiles) issue(stage == 0 ? NS - 1 : stage - 1);
-      if (wave_rows) {
-        const uint16_t* ks_ = sk[stage];
-        const uint16_t* vs_ = sv[stage];
+      const uint16_t* ks_ = sk[stage];
+      const uint16_t* vs_ = sv[stage];
+      tile_scores<D, KVT, NR>(
+          [&](int kb, int kstep) {
+            return *reinterpret_cast<const uint4*>(&ks_[(kb * 16 + col) * D + (((4 * kstep + q4) ^ fk) * 8)]);
+          },
+          rg, sacc);
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) {
+        const uint16_t* p = &vs_[vkey * D + (((2 * nb + vbc) ^ fv) * 8) + vh];
+        const uint2 lo = read_tr(p);
+        const uint2 hi = read_tr(p + 16 * D);
+        vt[nb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    };
+    // Waves whose rows all lie past the block's last row compute too (on
+    // zero q; nothing of theirs is written): a branch around the work would
+    // put every accumulator through a join, and the compiler then copies
+    // them on each tile. Likewise the tiles that need masks or move a
+    // reference leave the inner loop for the general update below, so that
+    // the inner loop carries O only through its matrix products.
+    while (m < ntiles) {
+      for (; m < ntiles; ++m) {
+        begin_tile();
         const int tb = (tile_first + m) * KT;
-        mq_float4 sacc[NR][2];
-        tile_scores<D, KVT, NR>(
-            [&](int kb, int kstep) {
-              return *reinterpret_cast<const uint4*>(&ks_[(kb * 16 + col) * D + (((4 * kstep + q4) ^ fk) * 8)]);
-            },
-            rg, sacc);
-        // All V^T operands of the tile are read before the softmax so that
-        // their latency hides behind it. V rows of keys outside [t_lo, t_hi)
-        // may hold anything: tiles that straddle those keys clear them in
-        // the operand (keys 4 q4 + j and 16 + 4 q4 + j, two per dword).
-        uint4 vt[D / 16];
+        if (tb < t_lo || tb + KT > t_hi) break;  // straddles the split's keys
+        bool plain = true;
+#pragma unroll
+        for (int g = 0; g < NR; ++g) {
+          float mt = sacc[g][0][0];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sacc[g][j >> 2][j & 3]);
+          plain = plain && (!rg[g].ok || (tb >= rg[g].lo && tb + KT <= rg[g].hi && mt * sl2 <= rg[g].m + kSlack));
+        }
+        if (!__all(plain)) break;
+        tile_update_plain<D, KVT, NR>(sacc, [&](int nb) { return vt[nb]; }, rg, sl2);
+        stage = stage == NS - 1 ? 0 : stage + 1;
+      }
+      if (m >= ntiles) break;
+      // Tile m, already begun: V rows of keys outside [t_lo, t_hi) may
+      // hold anything, so tiles that straddle those keys clear them in the
+      // operand (keys 4 q4 + j and 16 + 4 q4 + j, two per dword); then the
+      // general update with masks and reference moves.
+      const int tb = (tile_first + m) * KT;
+      if (tb < t_lo || tb + KT > t_hi) {
+        uint32_t vmask[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int k0 = tb + (d >> 1) * 16 + 4 * q4 + (d & 1) * 2;
+          vmask[d] = ((k0 >= t_lo && k0 < t_hi) ? 0x0000FFFFu : 0u) |
+                     ((k0 + 1 >= t_lo && k0 + 1 < t_hi) ? 0xFFFF0000u : 0u);
+        }
 #pragma unroll
         for (int nb = 0; nb < D / 16; ++nb) {
-          const uint16_t* p = &vs_[vkey * D + (((2 * nb + vbc) ^ fv) * 8) + vh];
-          const uint2 lo = read_tr(p);
-          const uint2 hi = read_tr(p + 16 * D);
-          vt[nb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          vt[nb].x &= vmask[0];
+          vt[nb].y &= vmask[1];
+          vt[nb].z &= vmask[2];
+          vt[nb].w &= vmask[3];
         }
-        if (tb < t_lo || tb + KT > t_hi) {
-          uint32_t vmask[4];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const int k0 = tb + (d >> 1) * 16 + 4 * q4 + (d & 1) * 2;
-            vmask[d] = ((k0 >= t_lo && k0 < t_hi) ? 0x0000FFFFu : 0u) |
-                       ((k0 + 1 >= t_lo && k0 + 1 < t_hi) ? 0xFFFF0000u : 0u);
-          }
-#pragma unroll
-          for (int nb = 0; nb < D / 16; ++nb) {
-            vt[nb].x &= vmask[0];
-            vt[nb].y &= vmask[1];
-            vt[nb].z &= vmask[2];
-            vt[nb].w &= vmask[3];
-          }
-        }
-        tile_update<D, KVT, NR>(
-            sacc, [&](int nb, bool) { return vt[nb]; },
-            tb, rg, sl2, q4);
       }
+      tile_update<D, KVT, NR>(sacc, [&](int nb, bool) { return vt[nb]; }, tb, rg, sl2, q4);
       stage = stage == NS - 1 ? 0 : stage + 1;
+      ++m;
     }
   }
 #pragma unroll
@@ -897,8 +967,7 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
   }
 
   // Merge the four waves' states (same rows) in wave order.
-  float l = rg[0].lpart + __shfl_xor(rg[0].lpart, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  const float l = row_sum(rg[0]);
   __syncthreads();  // every wave is done with its staging region
   float* mo = reinterpret_cast<float*>(lds);             // [KW][16][D] O of each wave
   float* mm = mo + KW * 16 * D;                          // [KW][16] m
