@@ -595,12 +595,14 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
 // tiles that straddle those keys clear them in the operand instead.
 // ---------------------------------------------------------------------------
 
-// Slot permutation, for LDS reads served 256 bytes (64 banks of 4 bytes) at
-// a time: a bijection on k mod 16 (the 16 keys of a K operand read fall in
-// 16 different slots), and swz(k) >> 1 = k mod 8 differs across the eight
-// keys that 32 lanes of a transposing V read address, two segments each,
-// so those 32 lanes read 32 different 8-byte units.
-__device__ __forceinline__ int swz(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
+// Slot permutation, for the LDS's 64 banks of 4 bytes as measured on gfx950:
+// a 16-byte read serves 8 lanes at a time from 128 bytes, an 8-byte read 32
+// lanes from 256 bytes. swz(k) mod 8 differs across each aligned group of 8
+// keys (the 8 lanes of a K operand read that are served together, one key
+// each, fall in 8 different 16-byte slots of the 128 bytes), and swz(k) >> 1
+// = k mod 8 differs across the 8 keys that 32 lanes of a transposing V read
+// address, two segments each (32 different 8-byte units).
+__device__ __forceinline__ int swz(int k) { return ((k & 7) << 1) | (((k >> 2) ^ (k >> 3)) & 1); }
 
 // One wave's 1 KiB global -> LDS copy: lane i's 16 bytes from `src` land at
 // LDS byte address lds_base + 16 i (lds_base wave-uniform).
