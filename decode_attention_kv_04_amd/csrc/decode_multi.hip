@@ -595,13 +595,14 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
 // tiles that straddle those keys clear them in the operand instead.
 // ---------------------------------------------------------------------------
 
-// Slot permutation, for the LDS's 64 banks of 4 bytes as measured on gfx950:
-// a 16-byte read serves 8 lanes at a time from 128 bytes, an 8-byte read 32
-// lanes from 256 bytes. swz(k) mod 8 differs across each aligned group of 8
-// keys (the 8 lanes of a K operand read that are served together, one key
-// each, fall in 8 different 16-byte slots of the 128 bytes), and swz(k) >> 1
-// = k mod 8 differs across the 8 keys that 32 lanes of a transposing V read
-// address, two segments each (32 different 8-byte units).
+// Slot permutation. swz(k) >> 1 = k mod 8 differs across the 8 keys that 32
+// lanes of a transposing V read address, two segments each, so those lanes
+// read 32 different 8-byte units of the 64 four-byte banks: measured free of
+// bank conflicts on gfx950. swz is a bijection on k mod 16 and on k mod 8
+// within each aligned group of 8, so the 16 keys of a K operand read fall
+// in different slots; 16-byte reads in this pattern still measured 2-way
+// conflicted (as did the plain k-times-2 permutation), against none for 16
+// lanes reading 256 contiguous bytes.
 __device__ __forceinline__ int swz(int k) { return ((k & 7) << 1) | (((k >> 2) ^ (k >> 3)) & 1); }
 
 // One wave's 1 KiB global -> LDS copy: lane i's 16 bytes from `src` land at
