@@ -24,13 +24,17 @@ namespace {
 // Splits per KV head are sized so the split pass has about this many
 // work-groups per compute unit in total.
 constexpr int64_t kTargetGroupsPerCu = 9;
-// The multi-token row-block kernels do matrix work on every key they load:
-// they are fastest with one round of resident work-groups, so each row
-// block's keys are split only as far as needed to fill that round (a sweep
-// of split counts on 16..512-token suffixes over 0.5-8k-token contexts).
-// Resident work-groups per compute unit, by registers and LDS: the head_dim
-// 128 kernel holds 3 (64-row blocks) or 2 (128-row blocks).
+// The multi-token kernels are fastest with one round of resident
+// work-groups, so each row block's keys are split only as far as needed to
+// fill that round, sized by the longest sequence (a sweep of split counts on
+// 16..512-token suffixes over 0.5-8k-token contexts; and on the 4-token check
+// over the long batch: 2 splits per sequence, one round, 586 us, 3 per
+// sequence 684 us with the last round half empty, and the decode target of
+// 9 work-groups per CU 626 us). Resident work-groups per compute unit, by
+// registers and LDS: the key-split kernel (16 rows) 4 at head_dim 64, 2 at
+// 128; the head_dim-128 row kernel 3 (64-row blocks) or 2 (128-row blocks).
 int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
+  if (rows == 16) return head_dim <= 64 ? 4 : 2;
   if (head_dim == 128) return rows == 128 ? 2 : 3;
   return head_dim <= 64 ? 4 : 1;
 }
@@ -228,15 +232,11 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   } else if (p.num_splits > 0) {
     c = ceil_div(max_np, p.num_splits);
   } else {
-    if (QB == 16) {
-      c = heuristic_split_pages(total_np, max_np, p.num_kv_heads, plan->num_cus, P);
-    } else {
-      const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * nrb;
-      const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim, QB),
-                                    blocks);
-      c = ceil_div(max_np, std::max<int64_t>(1, want));
-      c = std::min(max_np, std::max(c, ceil_div(min_split_tokens(), P)));
-    }
+    const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * nrb;
+    const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim, QB),
+                                  blocks);
+    c = ceil_div(max_np, std::max<int64_t>(1, want));
+    c = std::min(max_np, std::max(c, ceil_div(min_split_tokens(), P)));
   }
   c = std::max<int64_t>(c, 1);
   c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));  // grid y = row blocks x splits
