@@ -39,8 +39,9 @@ int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
   return head_dim <= 64 ? 4 : 1;
 }
 // Rows per block at head_dim 128: 128 (two 16-row groups per wave sharing
-// every K/V operand read) measured 3-6 % faster than 64 on 32..512-token
-// suffixes; DECODE_ATTN_MQ_ROWS=64 or 128 overrides it.
+// every K/V operand read) measured 15 % faster than 64 on 128- and
+// 512-token suffixes, 5 % on 24..32 and even on 8..16 (where half of a
+// 128-row block is empty); DECODE_ATTN_MQ_ROWS=64 or 128 overrides it.
 int64_t mq_rows_d128() {
   const char* s = std::getenv("DECODE_ATTN_MQ_ROWS");
   if (s && std::strcmp(s, "64") == 0) return 64;
