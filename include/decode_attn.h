@@ -136,9 +136,14 @@ typedef struct {
                                 matrix cores (q and K/V share f16 or bf16,
                                 head_dim 128, page size a multiple of 16).
                                 DECODE_ATTN_KERNEL=vector forces 0. 2 = the
-                                multi-token kernel (query_len > 1; q.K and P.V
-                                on the matrix cores). A query_len > 1 plan with
-                                0 runs the vector kernel once per token.         */
+                                multi-token kernels (query_len > 1; q.K and P.V
+                                on the matrix cores): the T*G rows of a KV head
+                                in blocks of 16 (keys split over the waves) or,
+                                beyond 16 rows or with DECODE_ATTN_KERNEL=rows,
+                                of 64 (head_dim 64, 256) or 128 (head_dim 128;
+                                DECODE_ATTN_MQ_ROWS=64 selects 64). A
+                                query_len > 1 plan with 0 runs the vector kernel
+                                once per token.                                  */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in

@@ -29,6 +29,11 @@ GRID = [
     (128, 4, 128, "f16", "f16", 16, (128, 130, 1000), 0),
     (128, 4, 128, "f16", "f32", 16, (200, 1500), 64),
     (5, 8, 256, "f16", "f32", 64, (5, 900), 7),
+    # head_dim-128 row blocks over large pages (a tile inside one page; the
+    # copies' page cursor steps within it) and the largest page size
+    (40, 4, 128, "f16", "f32", 64, (40, 700, 5000), 0),
+    (20, 2, 128, "bf16", "bf16", 1024, (20, 3000), 500),
+    (130, 1, 128, "f16", "f16", 8, (130, 131, 2000), 0),
 ]
 
 
