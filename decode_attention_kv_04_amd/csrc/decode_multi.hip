@@ -26,13 +26,13 @@
 // the order that lets each lane pass its own eight probabilities as its B
 // operand: contraction index 8*q + j is key 4q + j (j < 4) or 16 + 4q + j - 4.
 //
-// Staging (multi_kernel; multi_dma_kernel is described at its definition).
-// Each tile of 32 keys is read from HBM once per
-// work-group with 16-byte loads into a ring of registers (several tiles ahead
-// of the one being computed) and written to one of two LDS buffers: K
-// row-major, V transposed (dims as rows, keys in contraction order) so both
-// MFMA operands are single 16-byte LDS reads. One barrier per tile: tile m+1
-// is written to one buffer while tile m is computed from the other.
+// Staging in multi_kernel (multi_dma_kernel's is described at its
+// definition): each tile of 32 keys is read from HBM once per work-group
+// with 16-byte loads into a ring of registers (several tiles ahead of the
+// one being computed) and written to one of two LDS buffers: K row-major, V
+// transposed (dims as rows, keys in contraction order) so both MFMA operands
+// are single 16-byte LDS reads. One barrier per tile: tile m+1 is written to
+// one buffer while tile m is computed from the other.
 // multi_keys_kernel loads K straight into operand registers and stages only
 // V, through each wave's own LDS region. V rows outside the split's attended
 // keys are stored as zeros (they may hold NaN and would poison 0 * V); scores
@@ -606,7 +606,13 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
 __device__ __forceinline__ int swz(int k) { return ((k & 7) << 1) | (((k >> 2) ^ (k >> 3)) & 1); }
 
 // One wave's 1 KiB global -> LDS copy: lane i's 16 bytes from `src` land at
-// LDS byte address lds_base + 16 i (lds_base wave-uniform).
+// LDS byte address lds_base + 16 i (lds_base wave-uniform, passed in m0).
+// Written as inline assembly: through the compiler's builtin, its wait
+// analysis (which cannot tell which LDS bytes a pending copy writes) puts a
+// wait for every copy in flight before each LDS read, which would empty the
+// ring on every tile. The waits are explicit instead (wait_loads), and the
+// compiler's own waits stay correct: copies it does not know of only make
+// its counts conservative, as loads complete in order.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
