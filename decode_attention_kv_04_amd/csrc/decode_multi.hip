@@ -11,9 +11,9 @@
 // Query rows. The T*G (token, head) pairs that share KV head j form the rows
 // r = t*G + g of one contraction. Row-block kernels: a work-group takes 64
 // or 128 consecutive rows (4 wave64s, one or two groups of 16 rows each) and
-// one split of the keys those rows see; multi_dma_kernel (head_dim 128)
+// one split of the keys those rows see; multi_dma_kernel (head_dim 64, 128)
 // stages K/V through a ring of LDS buffers filled by direct global -> LDS
-// loads, multi_kernel (head_dim 64 and 256) through registers.
+// loads, multi_kernel (head_dim 256) through registers.
 // multi_keys_kernel (at most 16 rows): the 4 waves share the rows and split
 // the keys.
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
@@ -571,17 +571,17 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Row-block kernel with direct global -> LDS staging (head_dim 128).
+// Row-block kernel with direct global -> LDS staging (head_dim 64 and 128).
 //
 // The K and V tiles go from HBM into LDS without passing through registers:
 // global_load_lds_dwordx4 writes lane i's 16 bytes at a wave-uniform LDS
-// address + 16 i, so a wave instruction fills 1 KiB (four 256-byte key rows).
-// Tiles are kept in a ring of NS LDS stages, NS - 1 tiles ahead of the one
-// being computed, and every wave loads its own 8 keys of each tile (one page,
-// as pages hold a multiple of 8 keys), so a tile costs a wave one scalar page
-// lookup and four load instructions.
+// address + 16 i, so a wave instruction fills 1 KiB (four 256-byte or eight
+// 128-byte key rows). Tiles are kept in a ring of NS LDS stages, NS - 1
+// tiles ahead of the one being computed, and every wave loads its own 8 keys
+// of each tile (one page, as pages hold a multiple of 8 keys), so a tile
+// costs a wave one scalar page lookup and D / 32 load instructions.
 //
-// Layout of a stage: K and V both row-major (key rows of 256 bytes), the
+// Layout of a stage: K and V both row-major (key rows of 2 D bytes), the
 // 16-byte segment c of tile key k stored in slot c ^ swz(k). A K operand read
 // (16 keys, one segment each) then touches 16 different slots, and V^T is
 // read with the 16-bit transposing LDS read (ds_read_b64_tr_b16): within each
@@ -603,7 +603,17 @@ __global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
 // in different slots; 16-byte reads in this pattern still measured 2-way
 // conflicted (as did the plain k-times-2 permutation), against none for 16
 // lanes reading 256 contiguous bytes.
-__device__ __forceinline__ int swz(int k) { return ((k & 7) << 1) | (((k >> 2) ^ (k >> 3)) & 1); }
+// At head_dim 64 (128-byte rows, two per 256 bytes of banks) the same two
+// properties hold for the pair (row parity, slot): swz is a bijection on
+// (k >> 1) mod 8 within each row parity, and its bits 1-2 equal (k >> 1)
+// mod 4.
+template <int D>
+__device__ __forceinline__ int swz(int k) {
+  if constexpr (D == 64)
+    return (((k >> 1) & 3) << 1) | ((k >> 3) & 1);
+  else
+    return ((k & 7) << 1) | (((k >> 2) ^ (k >> 3)) & 1);
+}
 
 // One wave's 1 KiB global -> LDS copy: lane i's 16 bytes from `src` land at
 // LDS byte address lds_base + 16 i (lds_base wave-uniform, passed in m0).
@@ -639,14 +649,17 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t* p) {
 // same on the 128- and 512-token suffixes; 3 leaves more slack for latency.
 constexpr int kLdsStages = 3;
 
-template <int KVT, int NS, int NR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3 : 2))) void multi_dma_kernel(
-    const KernelArgs a) {
-  constexpr int D = 128;
+template <int D, int KVT, int NS, int NR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? (NR == 1 ? 4 : 3) : (NR == 1 ? 3 : 2)))) void
+multi_dma_kernel(const KernelArgs a) {
+  static_assert(D == 64 || D == 128, "row layout and slot permutation of the LDS ring");
   constexpr int QB = 64 * NR;      // query rows per work-group (4 waves x NR groups of 16)
   constexpr int ROWB = D * 2;      // bytes per K/V row
   constexpr int TILE = KT * D;     // 16-bit elements per K (or V) tile
-  constexpr int LOADS = 4;         // copies per wave per tile (2 K, 2 V)
+  constexpr int NSEG = D / 8;      // 16-byte segments per key row
+  constexpr int KPC = 1024 / ROWB; // key rows per 1 KiB copy
+  constexpr int NCP = 8 / KPC;     // copies per wave per tile and tensor
+  constexpr int LOADS = 2 * NCP;   // copies per wave per tile (K and V)
   static_assert(NS >= 2 && 2 * NS * TILE * 2 <= 65536, "LDS ring");
   __shared__ __align__(1024) uint16_t sk[NS][TILE];
   __shared__ __align__(1024) uint16_t sv[NS][TILE];
@@ -703,15 +716,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3
   const int ntiles = t_hi > t_lo ? (t_hi + KT - 1) / KT - tile_first : 0;
 
   // Copies: this wave's keys 8 w .. 8 w + 7 of a tile; lane i of copy j
-  // takes key 8 w + 4 j + i / 16 and fills slot i % 16 of its row.
+  // takes key 8 w + KPC j + i / NSEG and fills slot i % NSEG of its row.
   const int64_t block_bytes = static_cast<int64_t>(P) * ROWB;
   const int64_t page_bytes = block_bytes * a.num_kv_heads;
   const char* kbase = static_cast<const char*>(a.k_pool) + block_bytes * kvh;
   const char* vbase = static_cast<const char*>(a.v_pool) + block_bytes * kvh;
-  const int krow = lane >> 4;
-  const int slot = lane & 15;
-  const int loff0 = krow * ROWB + 16 * (slot ^ swz(8 * wave + krow));
-  const int loff1 = (krow + 4) * ROWB + 16 * (slot ^ swz(8 * wave + krow + 4));
+  const int krow = lane / NSEG;
+  const int slot = lane % NSEG;
+  int loff[NCP];
+#pragma unroll
+  for (int j = 0; j < NCP; ++j)
+    loff[j] = (KPC * j + krow) * ROWB + 16 * (slot ^ swz<D>(8 * wave + KPC * j + krow));
   // The page table is not written while the kernel runs: reading it through
   // the constant address space lets the wave-uniform lookups below be scalar
   // loads (the copies' memory clobbers would otherwise force vector loads,
@@ -733,10 +748,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3
     const int64_t off = static_cast<int64_t>(cphys) * page_bytes + static_cast<int64_t>(coff) * ROWB;
     const uint32_t lk = lds_address(&sk[stage][8 * wave * D]);
     const uint32_t lv = lds_address(&sv[stage][8 * wave * D]);
-    dma16(kbase + off + loff0, lk);
-    dma16(kbase + off + loff1, lk + 4 * ROWB);
-    dma16(vbase + off + loff0, lv);
-    dma16(vbase + off + loff1, lv + 4 * ROWB);
+#pragma unroll
+    for (int j = 0; j < NCP; ++j) dma16(kbase + off + loff[j], lk + 1024 * j);
+#pragma unroll
+    for (int j = 0; j < NCP; ++j) dma16(vbase + off + loff[j], lv + 1024 * j);
     coff += KT;
     while (coff >= P) {
       coff -= P;
@@ -746,9 +761,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NR == 1 ? 3
   };
 
   // Operand addresses (16-bit elements within a stage).
-  const int fk = swz(col);
+  const int fk = swz<D>(col);
   const int vkey = 4 * q4 + (col >> 2);
-  const int fv = swz(vkey);
+  const int fv = swz<D>(vkey);
   const int vbc = (col & 3) >> 1;
   const int vh = (col & 1) * 4;
   const float sl2 = a.scale_log2;
@@ -1025,13 +1040,13 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
   if (rows == 64) {
-    if constexpr (D == 128)
-      hipLaunchKernelGGL((multi_dma_kernel<KVT, kLdsStages, 1>), grid, dim3(256), 0, st, a);
+    if constexpr (D <= 128)
+      hipLaunchKernelGGL((multi_dma_kernel<D, KVT, kLdsStages, 1>), grid, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((multi_kernel<D, KVT, 4, 1>), grid, dim3(256), 0, st, a);
   } else if (rows == 128) {
-    if constexpr (D == 128)
-      hipLaunchKernelGGL((multi_dma_kernel<KVT, kLdsStages, 2>), grid, dim3(256), 0, st, a);
+    if constexpr (D <= 128)
+      hipLaunchKernelGGL((multi_dma_kernel<D, KVT, kLdsStages, 2>), grid, dim3(256), 0, st, a);
     else
       return hipErrorInvalidValue;
   } else if (rows == 16) {

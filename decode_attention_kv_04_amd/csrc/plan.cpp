@@ -32,17 +32,20 @@ constexpr int64_t kTargetGroupsPerCu = 9;
 // sequence 684 us with the last round half empty, and the decode target of
 // 9 work-groups per CU 626 us). Resident work-groups per compute unit, by
 // registers and LDS: the key-split kernel (16 rows) 4 at head_dim 64, 2 at
-// 128; the head_dim-128 row kernel 3 (64-row blocks) or 2 (128-row blocks).
+// 128; the LDS-ring row kernel 5 / 3 (64- / 128-row blocks) at head_dim 64
+// and 3 / 2 at 128; the register-staged row kernel at head_dim 256 1.
 int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
   if (rows == 16) return head_dim <= 64 ? 4 : 2;
+  if (head_dim == 64) return rows == 128 ? 3 : 5;
   if (head_dim == 128) return rows == 128 ? 2 : 3;
-  return head_dim <= 64 ? 4 : 1;
+  return 1;
 }
-// Rows per block at head_dim 128: 128 (two 16-row groups per wave sharing
-// every K/V operand read) measured 15 % faster than 64 on 128- and
-// 512-token suffixes, 5 % on 24..32 and even on 8..16 (where half of a
-// 128-row block is empty); DECODE_ATTN_MQ_ROWS=64 or 128 overrides it.
-int64_t mq_rows_d128() {
+// Rows per block of the LDS-ring row kernel (head_dim 64 and 128): 128 (two
+// 16-row groups per wave sharing every K/V operand read) measured 15 %
+// faster than 64 at head_dim 128 on 128- and 512-token suffixes, 5 % on
+// 24..32 and even on 8..16 (where half of a 128-row block is empty);
+// DECODE_ATTN_MQ_ROWS=64 or 128 overrides it.
+int64_t mq_rows() {
   const char* s = std::getenv("DECODE_ATTN_MQ_ROWS");
   if (s && std::strcmp(s, "64") == 0) return 64;
   if (s && std::strcmp(s, "128") == 0) return 128;
@@ -199,7 +202,7 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   // Up to 16 rows (D <= 128): four waves share the rows and split the keys;
   // otherwise four waves of 16 rows share each key tile.
   const int64_t QB = (R <= 16 && p.head_dim <= 128 && forced_kernel() != 2) ? 16
-                     : (p.head_dim == 128 ? mq_rows_d128() : 64);
+                     : (p.head_dim <= 128 ? mq_rows() : 64);
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);
