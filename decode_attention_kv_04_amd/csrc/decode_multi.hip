@@ -9,13 +9,11 @@
 // (all keys up to itself, or the last W of them with a window).
 //
 // Query rows. The T*G (token, head) pairs that share KV head j form the rows
-// r = t*G + g of one contraction. Row-block kernels: a work-group takes 64
+// r = t*G + g of one contraction. multi_dma_kernel: a work-group takes 64
 // or 128 consecutive rows (4 wave64s, one or two groups of 16 rows each) and
-// one split of the keys those rows see; multi_dma_kernel (head_dim 64, 128)
-// stages K/V through a ring of LDS buffers filled by direct global -> LDS
-// loads, multi_kernel (head_dim 256) through registers.
-// multi_keys_kernel (at most 16 rows): the 4 waves share the rows and split
-// the keys.
+// one split of the keys those rows see, K/V staged through a ring of LDS
+// buffers filled by direct global -> LDS loads. multi_keys_kernel (at most
+// 16 rows, head_dim <= 128): the 4 waves share the rows and split the keys.
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
 //   S^T = K Q^T    A = 16 keys x 32 dims of K,  B = 32 dims x 16 rows of q
 //   O^T += V^T P^T A = 16 dims x 32 keys of V,  B = 32 keys x 16 rows of P
@@ -26,17 +24,13 @@
 // the order that lets each lane pass its own eight probabilities as its B
 // operand: contraction index 8*q + j is key 4q + j (j < 4) or 16 + 4q + j - 4.
 //
-// Staging in multi_kernel (multi_dma_kernel's is described at its
-// definition): each tile of 32 keys is read from HBM once per work-group
-// with 16-byte loads into a ring of registers (several tiles ahead of the
-// one being computed) and written to one of two LDS buffers: K row-major, V
-// transposed (dims as rows, keys in contraction order) so both MFMA operands
-// are single 16-byte LDS reads. One barrier per tile: tile m+1 is written to
-// one buffer while tile m is computed from the other.
+// Staging: multi_dma_kernel's is described at its definition.
 // multi_keys_kernel loads K straight into operand registers and stages only
-// V, through each wave's own LDS region. V rows outside the split's attended
-// keys are stored as zeros (they may hold NaN and would poison 0 * V); scores
-// outside a row's own keys become -inf by select.
+// V, transposed (dims as rows, keys in contraction order) so that its MFMA
+// operand is one 16-byte LDS read, through each wave's own LDS region. V
+// rows outside the split's attended keys are zeroed (they may hold NaN and
+// would poison 0 * V); scores outside a row's own keys become -inf by
+// select.
 //
 // Softmax precision: P enters the P.V product as f16 for f16 K/V and as a
 // bf16 hi + lo pair (two products) for bf16 K/V, since one bf16 rounding of P
@@ -57,7 +51,6 @@ namespace {
 
 constexpr int KT = 32;          // keys per tile
 constexpr float kSlack = 8.0f;  // rescale slack of the reference max, see tile_update
-constexpr int KPAD = 8;         // LDS padding (16-bit elements) per K row
 constexpr int VPAD = 8;         // LDS padding per transposed V row
 
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
@@ -367,209 +360,6 @@ __device__ __forceinline__ RowBlock row_block(const KernelArgs& a, int rb, int q
   return k;
 }
 
-// Tiles of K/V loads kept in flight per work-group while one is computed.
-// 3 measured best on the 128-token suffix prefill (1: +20 %, 4-6: +1-4 %).
-#ifndef DA_MQ_PREFETCH
-#define DA_MQ_PREFETCH 3
-#endif
-template <int D, int NR>
-constexpr int prefetch_tiles() {
-  return (D >= 256 || NR > 1) ? 1 : DA_MQ_PREFETCH;
-}
-
-// NR: row groups of 16 per wave. Two groups per wave (sharing every K and
-// V^T operand read) were measured slower at head_dim 128 (one wave per SIMD
-// by registers), so the launch uses NR = 1.
-template <int D, int KVT, int NQ, int NR>
-__global__ __launch_bounds__(64 * NQ) void multi_kernel(const KernelArgs a) {
-  constexpr int NT = 64 * NQ;           // threads
-  constexpr int QB = 16 * NQ * NR;      // query rows per work-group
-  constexpr int ROWB = D * 2;           // bytes per K/V row
-  constexpr int ROWV = D / 8;           // 16-byte vectors per row
-  constexpr int NV = KT * ROWV / NT;    // vectors per thread per tensor per tile
-  constexpr int KS = D + KPAD;          // K row stride in LDS (elements)
-  constexpr int VS = KT + VPAD;         // transposed-V row stride (elements)
-  constexpr int NKS = D / 32;           // k-steps of q.K
-  constexpr int NDB = D / 16;           // 16-dim blocks of P.V
-  constexpr int PD = prefetch_tiles<D, NR>();
-  static_assert(NV >= 1 && NV * NT == KT * ROWV, "staging split");
-  // Two LDS buffers: one tile is computed while the next one is written.
-  __shared__ __align__(16) uint16_t sk[2][KT * KS];
-  __shared__ __align__(16) uint16_t sv[2][D * VS];
-
-  const int kvh = blockIdx.x;
-  const int b = blockIdx.z;
-  const int S = a.max_splits;
-  const int rb = blockIdx.y / S;
-  const int s = blockIdx.y - rb * S;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15;  // query row within the wave's 16
-  const int q4 = lane >> 4;   // k-group of the MFMA operands
-
-  const int T = a.query_len;
-  const int G = a.group;
-  const int R = T * G;
-  const int P = a.page_size;
-  const int W = a.window;
-  const int L = a.seq_lens[b];
-
-  // Rows of this work-group and the keys any of them sees: [lo_blk, hi_blk).
-  const int r_first = rb * QB;
-  if (r_first >= R) return;
-  const int r_last = (r_first + QB < R ? r_first + QB : R) - 1;
-  const int t_min = r_first / G;
-  const int t_max = r_last / G;
-  int hi_blk = L - T + t_max + 1;
-  hi_blk = hi_blk < 0 ? 0 : hi_blk;
-  int lo_blk = W > 0 ? L - T + t_min + 1 - W : 0;
-  lo_blk = lo_blk < 0 ? 0 : (lo_blk > hi_blk ? hi_blk : lo_blk);
-  const int pf = lo_blk / P;
-  const int pe = (hi_blk + P - 1) / P;
-  const int cp = a.pages_per_split;
-  int nsplit = (pe - pf + cp - 1) / cp;
-  nsplit = nsplit < 1 ? 1 : (nsplit > S ? S : nsplit);
-  if (s >= nsplit) return;  // whole work-group, uniform
-  const int plo = pf + s * cp;
-  const int phi = plo + cp < pe ? plo + cp : pe;
-  const int t_lo = lo_blk > plo * P ? lo_blk : plo * P;
-  const int t_hi = hi_blk < phi * P ? hi_blk : phi * P;
-
-  // This lane's query rows (one per row group) and their keys in the split.
-  RowGroup<D> rg[NR];
-#pragma unroll
-  for (int g = 0; g < NR; ++g)
-    init_rows(rg[g], a, r_first + (wave * NR + g) * 16 + col, r_last, b, kvh, L, t_lo, t_hi, q4);
-
-  const int tile_first = t_lo / KT;
-  const int ntiles = t_hi > t_lo ? (t_hi + KT - 1) / KT - tile_first : 0;
-
-  // Staging map: the 32 lanes of each half wave take the 32 keys of the tile
-  // (one key per thread, so one page lookup per tile) and thread t holds the
-  // 16-byte segments t/32 + i*SSTEP of its key's row. A transposed V write of
-  // a wave then covers two V^T rows at 32 consecutive contraction positions:
-  // 32 different LDS banks. Page indices are clamped to this split's pages.
-  constexpr int SSTEP = NT / KT;
-  static_assert(NV * SSTEP == ROWV, "segments per thread");
-  const int kk = tid % KT;
-  const int sg0 = tid / KT;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-  const int64_t block_bytes = static_cast<int64_t>(P) * ROWB;
-  const int64_t page_bytes = block_bytes * a.num_kv_heads;
-  const int64_t head_bytes = block_bytes * kvh + sg0 * 16;
-  const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-  const int pi_last = phi > plo ? phi - 1 : plo;
-  // Page cursor of this thread's key, page id fetched one tile ahead.
-  int cpi = (tile_first * KT + kk) / P;
-  int coff = tile_first * KT + kk - cpi * P;
-  int cphys = 0;
-  auto fetch_ids = [&]() {
-    int pi = cpi < plo ? plo : (cpi > pi_last ? pi_last : cpi);
-    pi = pi < a.max_pages ? pi : a.max_pages - 1;
-    cphys = table_row[pi];
-  };
-  auto advance = [&]() {
-    coff += KT;
-    while (coff >= P) {
-      coff -= P;
-      cpi += 1;
-    }
-  };
-  struct Tile {
-    uint4 k[NV];
-    uint4 v[NV];
-  };
-  auto issue = [&](Tile& tl) {
-    const int64_t off = static_cast<int64_t>(cphys) * page_bytes + head_bytes + static_cast<int64_t>(coff) * ROWB;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      tl.k[i] = ldg16(kbase + off + i * SSTEP * 16);
-      tl.v[i] = ldg16(vbase + off + i * SSTEP * 16);
-    }
-    advance();
-    fetch_ids();
-  };
-  // Registers -> LDS buffer `buf`: K row-major, V transposed into
-  // contraction order, V rows outside [t_lo, t_hi) as zeros.
-  auto stage = [&](const Tile& tl, int buf, int tb) {
-    const int pos = tb + kk;
-    const bool live = pos >= t_lo && pos < t_hi;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int sg = sg0 + i * SSTEP;
-      *reinterpret_cast<uint4*>(&sk[buf][kk * KS + sg * 8]) = tl.k[i];
-      stage_v_pair<VS>(sv[buf], kk, sg, tl.v[i], live);
-    }
-  };
-
-  // Waves whose rows are all past the block's last row only stage.
-  const bool wave_rows = r_first + wave * NR * 16 <= r_last;
-  const float sl2 = a.scale_log2;
-  // A step computes tile m's scores, writes tile m+1 to the other LDS
-  // buffer while those matrix products run, then finishes tile m.
-  mq_float4 sacc[NR][2];
-  auto scores = [&](int buf) {
-    if (wave_rows)
-      tile_scores<D, KVT, NR>(
-          [&](int kb, int ks) {
-            return *reinterpret_cast<const uint4*>(&sk[buf][(kb * 16 + col) * KS + ks * 32 + q4 * 8]);
-          },
-          rg, sacc);
-  };
-  auto finish = [&](int buf, int tb) {
-    if (wave_rows)
-      tile_update<D, KVT, NR>(
-          sacc,
-          [&](int nb, bool) { return *reinterpret_cast<const uint4*>(&sv[buf][(nb * 16 + col) * VS + q4 * 8]); },
-          tb, rg, sl2, q4);
-  };
-
-  // Tile m's loads go to ring slot m % (PD + 1) PD tiles ahead; at step m
-  // (one barrier) tile m+1 is written to LDS buffer (m+1) % 2 while tile m
-  // is computed from buffer m % 2. The steady-state loop issues only tiles
-  // that exist, so its loads are unconditional and the compiler's wait
-  // counts stay exact; the last tiles drain in an unrolled tail.
-  if (ntiles > 0) {
-    Tile ring[PD + 1];
-    fetch_ids();
-#pragma unroll
-    for (int k = 0; k < PD; ++k)
-      if (k < ntiles) issue(ring[k]);
-    stage(ring[0], 0, tile_first * KT);
-    int n = 0;
-    while (n + 2 * PD + 1 < ntiles) {
-#pragma unroll
-      for (int j = 0; j <= PD; ++j) {
-        const int m = n + j;
-        issue(ring[(j + PD) % (PD + 1)]);  // tile m + PD
-        lds_barrier();
-        scores(m & 1);
-        stage(ring[(j + 1) % (PD + 1)], (m + 1) & 1, (tile_first + m + 1) * KT);
-        finish(m & 1, (tile_first + m) * KT);
-      }
-      n += PD + 1;
-    }
-    // Here ntiles - n <= 2 * PD + 1 and n % (PD + 1) == 0.
-#pragma unroll
-    for (int j = 0; j <= 2 * PD + 1; ++j) {
-      const int m = n + j;
-      if (m < ntiles) {
-        if (m + PD < ntiles) issue(ring[(j + PD) % (PD + 1)]);
-        lds_barrier();
-        scores(m & 1);
-        if (m + 1 < ntiles) stage(ring[(j + 1) % (PD + 1)], (m + 1) & 1, (tile_first + m + 1) * KT);
-        finish(m & 1, (tile_first + m) * KT);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int g = 0; g < NR; ++g) finish_rows(a, rg[g], nsplit, s, q4);
-}
-
-
 // ---------------------------------------------------------------------------
 // Row-block kernel with direct global -> LDS staging (head_dim 64 and 128).
 //
@@ -647,12 +437,17 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t* p) {
 
 // Stages in the LDS ring (NS - 1 tiles in flight). 2 and 3 measured the
 // same on the 128- and 512-token suffixes; 3 leaves more slack for latency.
-constexpr int kLdsStages = 3;
+// At head_dim 256 a stage holds 32 KiB; two stages keep two work-groups per
+// compute unit.
+template <int D>
+constexpr int lds_stages() {
+  return D >= 256 ? 2 : 3;
+}
 
 template <int D, int KVT, int NS, int NR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? (NR == 1 ? 4 : 3) : (NR == 1 ? 3 : 2)))) void
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? (NR == 1 ? 4 : 3) : (D == 128 && NR == 1 ? 3 : 2)))) void
 multi_dma_kernel(const KernelArgs a) {
-  static_assert(D == 64 || D == 128, "row layout and slot permutation of the LDS ring");
+  static_assert(D == 64 || D == 128 || D == 256, "row layout and slot permutation of the LDS ring");
   constexpr int QB = 64 * NR;      // query rows per work-group (4 waves x NR groups of 16)
   constexpr int ROWB = D * 2;      // bytes per K/V row
   constexpr int TILE = KT * D;     // 16-bit elements per K (or V) tile
@@ -871,7 +666,6 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int ROWV = D / 8;
   constexpr int NVW = KT * ROWV / 64;   // vectors per lane per tensor per tile
-  constexpr int KS = D + KPAD;
   constexpr int VS = KT + VPAD;
   constexpr int NKS = D / 32;
   constexpr int NDB = D / 16;
@@ -889,7 +683,7 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int q4 = lane >> 4;
-  const int T = a.query_len, G = a.group, P = a.page_size, W = a.window;
+  const int T = a.query_len, G = a.group, P = a.page_size;
   const int L = a.seq_lens[b];
 
   const RowBlock blk = row_block(a, rb, 16, L);
@@ -1040,13 +834,10 @@ __global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
   if (rows == 64) {
-    if constexpr (D <= 128)
-      hipLaunchKernelGGL((multi_dma_kernel<D, KVT, kLdsStages, 1>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((multi_kernel<D, KVT, 4, 1>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 1>), grid, dim3(256), 0, st, a);
   } else if (rows == 128) {
     if constexpr (D <= 128)
-      hipLaunchKernelGGL((multi_dma_kernel<D, KVT, kLdsStages, 2>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 2>), grid, dim3(256), 0, st, a);
     else
       return hipErrorInvalidValue;
   } else if (rows == 16) {

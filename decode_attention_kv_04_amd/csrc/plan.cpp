@@ -32,13 +32,13 @@ constexpr int64_t kTargetGroupsPerCu = 9;
 // sequence 684 us with the last round half empty, and the decode target of
 // 9 work-groups per CU 626 us). Resident work-groups per compute unit, by
 // registers and LDS: the key-split kernel (16 rows) 4 at head_dim 64, 2 at
-// 128; the LDS-ring row kernel 5 / 3 (64- / 128-row blocks) at head_dim 64
-// and 3 / 2 at 128; the register-staged row kernel at head_dim 256 1.
+// 128; the LDS-ring row kernel 5 / 3 (64- / 128-row blocks) at head_dim 64,
+// 3 / 2 at 128, and 2 at 256 (64-row blocks only).
 int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
   if (rows == 16) return head_dim <= 64 ? 4 : 2;
   if (head_dim == 64) return rows == 128 ? 3 : 5;
   if (head_dim == 128) return rows == 128 ? 2 : 3;
-  return 1;
+  return 2;
 }
 // Rows per block of the LDS-ring row kernel (head_dim 64 and 128): 128 (two
 // 16-row groups per wave sharing every K/V operand read) measured 15 %

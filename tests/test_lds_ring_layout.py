@@ -1,4 +1,4 @@
-"""Host model of the multi-token LDS-ring layout (head_dim 64 and 128): the
+"""Host model of the multi-token LDS-ring layout (head_dim 64, 128, 256): the
 1 KiB global->LDS copies, the K operand reads and the 16-bit transposing V^T
 reads, with the slot permutation of decode_multi.hip restated here. Checks
 that every lane receives exactly the K and V^T operand elements of the MFMA
@@ -44,7 +44,7 @@ def build_stage(D):
     return lds
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_k_operand_reads(D):
     lds = build_stage(D)
     for lane in range(64):
@@ -59,7 +59,7 @@ def test_k_operand_reads(D):
             assert len(units) == 16
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_transposing_v_reads(D):
     lds = build_stage(D)
     for nb in range(D // 16):
