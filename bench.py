@@ -424,7 +424,7 @@ def main():
             "bound": "hbm",
             "kernel": {0: "split pass, vector q.K (da::split_kernel)",
                        1: "split pass, q.K on the matrix cores (da::split_kernel_mfma)",
-                       2: "multi-token split pass (da::multi_kernel / da::multi_keys_kernel)"}[plan.info.split_kernel],
+                       2: "multi-token split pass (da::multi_dma_kernel)"}[plan.info.split_kernel],
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

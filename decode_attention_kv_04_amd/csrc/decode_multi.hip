@@ -9,11 +9,11 @@
 // (all keys up to itself, or the last W of them with a window).
 //
 // Query rows. The T*G (token, head) pairs that share KV head j form the rows
-// r = t*G + g of one contraction. multi_dma_kernel: a work-group takes 64
-// or 128 consecutive rows (4 wave64s, one or two groups of 16 rows each) and
-// one split of the keys those rows see, K/V staged through a ring of LDS
-// buffers filled by direct global -> LDS loads. multi_keys_kernel (at most
-// 16 rows, head_dim <= 128): the 4 waves share the rows and split the keys.
+// r = t*G + g of one contraction. A work-group takes 64 or 128 consecutive
+// rows (4 wave64s, one or two groups of 16 rows each; a block of 16 rows or
+// fewer, a few drafted tokens, runs on 64-row blocks with the waves past its
+// rows computing on zero q) and one split of the keys those rows see, K/V
+// staged through a ring of LDS buffers filled by direct global -> LDS loads.
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
 //   S^T = K Q^T    A = 16 keys x 32 dims of K,  B = 32 dims x 16 rows of q
 //   O^T += V^T P^T A = 16 dims x 32 keys of V,  B = 32 keys x 16 rows of P
@@ -24,13 +24,9 @@
 // the order that lets each lane pass its own eight probabilities as its B
 // operand: contraction index 8*q + j is key 4q + j (j < 4) or 16 + 4q + j - 4.
 //
-// Staging: multi_dma_kernel's is described at its definition.
-// multi_keys_kernel loads K straight into operand registers and stages only
-// V, transposed (dims as rows, keys in contraction order) so that its MFMA
-// operand is one 16-byte LDS read, through each wave's own LDS region. V
-// rows outside the split's attended keys are zeroed (they may hold NaN and
-// would poison 0 * V); scores outside a row's own keys become -inf by
-// select.
+// Staging is described at the kernel's definition. V rows outside the
+// split's attended keys (possibly NaN) are cleared in the operand; scores
+// outside a row's own keys become -inf by select.
 //
 // Softmax precision: P enters the P.V product as f16 for f16 K/V and as a
 // bf16 hi + lo pair (two products) for bf16 K/V, since one bf16 rounding of P
@@ -51,7 +47,6 @@ namespace {
 
 constexpr int KT = 32;          // keys per tile
 constexpr float kSlack = 8.0f;  // rescale slack of the reference max, see tile_update
-constexpr int VPAD = 8;         // LDS padding per transposed V row
 
 typedef _Float16 mq_half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 mq_bf168 __attribute__((ext_vector_type(8)));
@@ -68,42 +63,6 @@ __device__ __forceinline__ mq_float4 mfma(const uint4& a, const uint4& b, mq_flo
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf168, a), __builtin_bit_cast(mq_bf168, b),
                                                    c, 0, 0, 0);
-}
-
-// Contraction position of key k (0..31) of a tile in the P.V product.
-__device__ __forceinline__ int kpos(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
-
-// K/V loads of the multi-token kernels go through the caches normally: a
-// thread's segments of one row arrive over several instructions, and a
-// streaming (non-temporal) hint lets the line leave the cache between them
-// (measured: 1.7x the time on the long-context verify workload).
-__device__ __forceinline__ uint4 ldg16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// Transposed V write of one 16-byte segment (dims 8*sg .. 8*sg+7 of key kk,
-// zeroed unless `live`) together with the neighbouring lane, which holds key
-// kk ^ 1: the pair swaps half their data (DPP) so that each lane writes four
-// dwords, each the (even key, odd key) pair of one dim at contraction
-// positions kpos(kk & ~1), +1. The even lane writes dims 0..3 of the
-// segment, the odd lane dims 4..7; the 64 dword writes of a wave fall in 64
-// different LDS banks.
-template <int VS>
-__device__ __forceinline__ void stage_v_pair(uint16_t* sv, int kk, int sg, const uint4& v, bool live) {
-  const uint32_t w0 = live ? v.x : 0u, w1 = live ? v.y : 0u, w2 = live ? v.z : 0u, w3 = live ? v.w : 0u;
-  const bool odd = kk & 1;
-  // quad_perm [1,0,3,2]: exchange with the neighbouring lane
-  const uint32_t r0 =
-      static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? w0 : w2), 0xB1, 0xF, 0xF, false));
-  const uint32_t r1 =
-      static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? w1 : w3), 0xB1, 0xF, 0xF, false));
-  const uint32_t ev0 = odd ? r0 : w0, ev1 = odd ? r1 : w1;  // even key, this lane's 4 dims
-  const uint32_t od0 = odd ? w2 : r0, od1 = odd ? w3 : r1;  // odd key
-  const int d0 = 8 * sg + (odd ? 4 : 0);
-  uint32_t* base = reinterpret_cast<uint32_t*>(sv + d0 * VS + kpos(kk & ~1));
-  constexpr int RS = VS / 2;  // dwords per transposed row
-  base[0] = (ev0 & 0xFFFFu) | (od0 << 16);
-  base[RS] = (ev0 >> 16) | (od0 & 0xFFFF0000u);
-  base[2 * RS] = (ev1 & 0xFFFFu) | (od1 << 16);
-  base[3 * RS] = (ev1 >> 16) | (od1 & 0xFFFF0000u);
 }
 
 // LDS barrier that does not wait for outstanding global loads: the next
@@ -336,30 +295,6 @@ __device__ __forceinline__ void finish_rows(const KernelArgs& a, RowGroup<D>& g,
   }
 }
 
-// Block of query rows [r_first, r_last] of one KV head and its key range:
-// the keys any of its tokens sees, [lo, hi), and the split's part of them.
-struct RowBlock {
-  int r_first, r_last, lo, hi, pf, pe, nsplit;
-};
-
-__device__ __forceinline__ RowBlock row_block(const KernelArgs& a, int rb, int qb_rows, int L) {
-  RowBlock k;
-  const int T = a.query_len, G = a.group, R = T * G, P = a.page_size;
-  k.r_first = rb * qb_rows;
-  k.r_last = (k.r_first + qb_rows < R ? k.r_first + qb_rows : R) - 1;
-  int hi = L - T + k.r_last / G + 1;
-  hi = hi < 0 ? 0 : hi;
-  int lo = a.window > 0 ? L - T + k.r_first / G + 1 - a.window : 0;
-  lo = lo < 0 ? 0 : (lo > hi ? hi : lo);
-  k.lo = lo;
-  k.hi = hi;
-  k.pf = lo / P;
-  k.pe = (hi + P - 1) / P;
-  int ns = (k.pe - k.pf + a.pages_per_split - 1) / a.pages_per_split;
-  k.nsplit = ns < 1 ? 1 : (ns > a.max_splits ? a.max_splits : ns);
-  return k;
-}
-
 // ---------------------------------------------------------------------------
 // Row-block kernel with direct global -> LDS staging (head_dim 64 and 128).
 //
@@ -407,6 +342,10 @@ __device__ __forceinline__ int swz(int k) {
 
 // One wave's 1 KiB global -> LDS copy: lane i's 16 bytes from `src` land at
 // LDS byte address lds_base + 16 i (lds_base wave-uniform, passed in m0).
+// The copy carries the non-temporal hint: its 1 KiB covers whole cache lines,
+// each consumed by this one instruction (4-token check over the long batch,
+// 64-row blocks: 582 -> 531 us; 128-token suffix unchanged, although there
+// the other row blocks of a KV head re-read each tile).
 // Written as inline assembly: through the compiler's builtin, its wait
 // analysis (which cannot tell which LDS bytes a pending copy writes) puts a
 // wait for every copy in flight before each LDS read, which would empty the
@@ -414,7 +353,7 @@ __device__ __forceinline__ int swz(int k) {
 // compiler's own waits stay correct: copies it does not know of only make
 // its counts conservative, as loads complete in order.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
 
 // Wait until at most N of this wave's global loads (the copies above among
@@ -654,183 +593,6 @@ multi_dma_kernel(const KernelArgs a) {
   for (int g = 0; g < NR; ++g) finish_rows(a, rg[g], nsplit, s, q4);
 }
 
-// At most 16 query rows per KV head (a few drafted tokens): the four waves
-// share the rows and split the keys. Wave w computes tiles w, w+4, w+8, ...
-// of the split, each staged through the wave's own LDS region (no barrier in
-// the key loop; one tile of loads in flight while the previous one is
-// computed), and the four per-wave states are merged through LDS at the end
-// in wave order.
-template <int D, int KVT>
-__global__ __launch_bounds__(256) void multi_keys_kernel(const KernelArgs a) {
-  constexpr int KW = 4;                 // waves, each on its own tiles
-  constexpr int ROWB = D * 2;
-  constexpr int ROWV = D / 8;
-  constexpr int NVW = KT * ROWV / 64;   // vectors per lane per tensor per tile
-  constexpr int VS = KT + VPAD;
-  constexpr int NKS = D / 32;
-  constexpr int NDB = D / 16;
-  constexpr int WAVE_LDS = D * VS;  // 16-bit elements per wave: its transposed V tile
-  static_assert(NVW >= 1 && NVW * 2 == ROWV, "staging split");
-  __shared__ __align__(16) uint16_t lds[KW * WAVE_LDS];
-
-  const int kvh = blockIdx.x;
-  const int b = blockIdx.z;
-  const int S = a.max_splits;
-  const int rb = blockIdx.y / S;
-  const int s = blockIdx.y - rb * S;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15;
-  const int q4 = lane >> 4;
-  const int T = a.query_len, G = a.group, P = a.page_size;
-  const int L = a.seq_lens[b];
-
-  const RowBlock blk = row_block(a, rb, 16, L);
-  if (s >= blk.nsplit) return;  // whole work-group, uniform
-  const int plo = blk.pf + s * a.pages_per_split;
-  const int phi = plo + a.pages_per_split < blk.pe ? plo + a.pages_per_split : blk.pe;
-  const int t_lo = blk.lo > plo * P ? blk.lo : plo * P;
-  const int t_hi = blk.hi < phi * P ? blk.hi : phi * P;
-
-  RowGroup<D> rg[1];
-  init_rows(rg[0], a, blk.r_first + col, blk.r_last, b, kvh, L, t_lo, t_hi, q4);
-
-  uint16_t* sv = lds + wave * WAVE_LDS;
-  const int tile_first = t_lo / KT;
-  const int tile_end = t_hi > t_lo ? (t_hi + KT - 1) / KT : tile_first;
-  const int my_first = tile_first + wave;
-  const int ntiles = my_first < tile_end ? (tile_end - my_first + KW - 1) / KW : 0;
-
-  // Staging map as in the row-block kernel, within the wave: lane l takes
-  // key l % 32 of the tile and the 16-byte segments l/32 + 2i of its row.
-  const int kk = lane % KT;
-  const int sg0 = lane / KT;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-  const int64_t block_bytes = static_cast<int64_t>(P) * ROWB;
-  const int64_t page_bytes = block_bytes * a.num_kv_heads;
-  const int64_t head_bytes = block_bytes * kvh + sg0 * 16;
-  const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-  const int pi_last = phi > plo ? phi - 1 : plo;
-  // Page cursor of this lane's key, advanced by KW tiles a step; the page id
-  // is fetched one step ahead.
-  int cpi = (my_first * KT + kk) / P;
-  int coff = my_first * KT + kk - cpi * P;
-  int cphys = 0;
-  auto fetch_id = [&]() {
-    int pi = cpi < plo ? plo : (cpi > pi_last ? pi_last : cpi);
-    pi = pi < a.max_pages ? pi : a.max_pages - 1;
-    cphys = table_row[pi];
-  };
-  // K goes straight from HBM into registers in MFMA operand layout (lane
-  // (col, q4) holds keys col and 16 + col, dims 32*ks + 8*q4 .. +8); only V
-  // is staged through LDS. The next tile's K loads are issued as soon as
-  // this tile's scores are computed and its V loads once its V is staged, so
-  // a wave keeps loads in flight while it waits and computes.
-  uint4 kreg[2 * NKS], rv[NVW];
-  int64_t noff = 0;  // byte offset of this lane's row segment in the tile being loaded
-  auto next_tile = [&]() {
-    noff = static_cast<int64_t>(cphys) * page_bytes + head_bytes + static_cast<int64_t>(coff) * ROWB;
-    coff += KW * KT;
-    while (coff >= P) {
-      coff -= P;
-      ++cpi;
-    }
-    fetch_id();
-  };
-  auto issue_k = [&]() {
-    // Row offsets of keys col and 16 + col, from the lanes that hold them
-    // (lanes 0..31 hold keys 0..31 at segment 0).
-    const int64_t off0 = __shfl(noff, col, 64);
-    const int64_t off1 = __shfl(noff, 16 + col, 64);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kreg[ks] = ldg16(kbase + off0 + ks * 64 + q4 * 16);
-      kreg[NKS + ks] = ldg16(kbase + off1 + ks * 64 + q4 * 16);
-    }
-  };
-  auto issue_v = [&]() {
-#pragma unroll
-    for (int i = 0; i < NVW; ++i) rv[i] = ldg16(vbase + noff + i * 2 * 16);
-  };
-  auto stage_v = [&](int tb) {
-    const int pos = tb + kk;
-    const bool live = pos >= t_lo && pos < t_hi;
-#pragma unroll
-    for (int i = 0; i < NVW; ++i) stage_v_pair<VS>(sv, kk, sg0 + 2 * i, rv[i], live);
-  };
-
-  const float sl2 = a.scale_log2;
-  if (ntiles > 0) {
-    fetch_id();
-    next_tile();
-    issue_k();
-    issue_v();
-    for (int n = 0; n < ntiles; ++n) {
-      const int tb = (my_first + n * KW) * KT;
-      const bool more = n + 1 < ntiles;
-      mq_float4 sacc[1][2];
-      tile_scores<D, KVT, 1>([&](int kb, int ks) { return kreg[kb * NKS + ks]; }, rg, sacc);
-      if (more) {
-        next_tile();
-        issue_k();
-      }
-      stage_v(tb);  // this wave's region only; LDS operations of a wave stay in order
-      if (more) issue_v();
-      tile_update<D, KVT, 1>(
-          sacc, [&](int nb, bool) { return *reinterpret_cast<const uint4*>(&sv[(nb * 16 + col) * VS + q4 * 8]); }, tb,
-          rg, sl2, q4);
-    }
-  }
-
-  // Merge the four waves' states (same rows) in wave order.
-  const float l = row_sum(rg[0]);
-  __syncthreads();  // every wave is done with its staging region
-  float* mo = reinterpret_cast<float*>(lds);             // [KW][16][D] O of each wave
-  float* mm = mo + KW * 16 * D;                          // [KW][16] m
-  float* ml = mm + KW * 16;                              // [KW][16] l
-  static_assert((KW * 16 * D + 2 * KW * 16) * 4 <= KW * WAVE_LDS * 2, "merge fits the staging LDS");
-#pragma unroll
-  for (int nb = 0; nb < NDB; ++nb)
-    *reinterpret_cast<mq_float4*>(&mo[(wave * 16 + col) * D + nb * 16 + q4 * 4]) = rg[0].o[nb];
-  if (q4 == 0) {
-    mm[wave * 16 + col] = rg[0].m;
-    ml[wave * 16 + col] = l;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < 16 * D; idx += 256) {
-    const int rr = idx / D;
-    const int d = idx - rr * D;
-    const int row = blk.r_first + rr;
-    if (row > blk.r_last) break;  // rows are in order: every later idx is past too
-    float M = mm[rr];
-#pragma unroll
-    for (int w = 1; w < KW; ++w) M = fmaxf(M, mm[w * 16 + rr]);
-    const float Mu = M == -INFINITY ? 0.0f : M;
-    float lsum = 0.0f, osum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < KW; ++w) {
-      const float aw = exp2_fast(mm[w * 16 + rr] - Mu);
-      lsum += aw * ml[w * 16 + rr];
-      osum += aw * mo[(w * 16 + rr) * D + d];
-    }
-    const int tt = row / G;
-    const int gg = row - tt * G;
-    const int64_t orow = (static_cast<int64_t>(b) * T + tt) * a.num_q_heads + kvh * G + gg;
-    if (blk.nsplit == 1) {
-      store_elem(a.out, orow * D + d, a.out_dtype, lsum > 0.0f ? osum / lsum : 0.0f);
-    } else {
-      const int64_t srow = orow * S + s;
-      a.ws_o[srow * D + d] = osum;
-      if (d == 0) {
-        a.ws_ml[srow * 2] = M;
-        a.ws_ml[srow * 2 + 1] = lsum;
-      }
-    }
-  }
-}
-
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
   if (rows == 64) {
@@ -838,11 +600,6 @@ hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
   } else if (rows == 128) {
     if constexpr (D <= 128)
       hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 2>), grid, dim3(256), 0, st, a);
-    else
-      return hipErrorInvalidValue;
-  } else if (rows == 16) {
-    if constexpr (D <= 128)
-      hipLaunchKernelGGL((multi_keys_kernel<D, KVT>), grid, dim3(256), 0, st, a);
     else
       return hipErrorInvalidValue;
   } else {

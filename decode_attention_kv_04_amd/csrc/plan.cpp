@@ -24,32 +24,31 @@ namespace {
 // Splits per KV head are sized so the split pass has about this many
 // work-groups per compute unit in total.
 constexpr int64_t kTargetGroupsPerCu = 9;
-// The multi-token kernels are fastest with one round of resident
-// work-groups, so each row block's keys are split only as far as needed to
-// fill that round, sized by the longest sequence (a sweep of split counts on
-// 16..512-token suffixes over 0.5-8k-token contexts; and on the 4-token check
-// over the long batch: 2 splits per sequence, one round, 586 us, 3 per
-// sequence 684 us with the last round half empty, and the decode target of
-// 9 work-groups per CU 626 us). Resident work-groups per compute unit, by
-// registers and LDS: the key-split kernel (16 rows) 4 at head_dim 64, 2 at
-// 128; the LDS-ring row kernel 5 / 3 (64- / 128-row blocks) at head_dim 64,
-// 3 / 2 at 128, and 2 at 256 (64-row blocks only).
+// The multi-token kernel is fastest with one round of resident work-groups,
+// so each row block's keys are split only as far as needed to fill that
+// round, sized by the longest sequence (a sweep of split counts on 16..512-
+// token suffixes over 0.5-8k-token contexts; and on the 4-token check over
+// the long batch: 2 splits per sequence, one round of 64-row blocks, 535 us;
+// 3 per sequence 591 us, the last round partly empty; 4 per sequence 548 us).
+// Resident work-groups per compute unit, from those sweeps: 64-row blocks
+// 4 at head_dim 64 and 2 at 128 (the 4-token checks: 4 and 2 splits per
+// sequence best, 5 and 3 lose 11 %); 128-row blocks 3 at head_dim 64 and 2
+// at 128; 2 at 256 (64-row blocks only).
 int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
-  if (rows == 16) return head_dim <= 64 ? 4 : 2;
-  if (head_dim == 64) return rows == 128 ? 3 : 5;
-  if (head_dim == 128) return rows == 128 ? 2 : 3;
+  if (head_dim == 64) return rows == 128 ? 3 : 4;
   return 2;
 }
-// Rows per block of the LDS-ring row kernel (head_dim 64 and 128): 128 (two
-// 16-row groups per wave sharing every K/V operand read) measured 15 %
-// faster than 64 at head_dim 128 on 128- and 512-token suffixes, 5 % on
-// 24..32 and even on 8..16 (where half of a 128-row block is empty);
-// DECODE_ATTN_MQ_ROWS=64 or 128 overrides it.
-int64_t mq_rows() {
+// Rows per block at head_dim 64 and 128: 128 (two 16-row groups per wave
+// sharing every K/V operand read) measured 15 % faster than 64 at head_dim
+// 128 on 128- and 512-token suffixes and 5 % on 8..32-token suffixes (GQA 4:
+// 32..128 rows); blocks of 16 rows or fewer (a few drafted tokens) take 64, where a 128-row
+// block would compute on 112 empty rows. DECODE_ATTN_MQ_ROWS=64 or 128
+// overrides both.
+int64_t mq_rows(int64_t rows) {
   const char* s = std::getenv("DECODE_ATTN_MQ_ROWS");
   if (s && std::strcmp(s, "64") == 0) return 64;
   if (s && std::strcmp(s, "128") == 0) return 128;
-  return 128;
+  return rows <= 16 ? 64 : 128;
 }
 // A split never holds fewer attended tokens than this (the pages' 256-token
 // switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
@@ -66,15 +65,13 @@ int64_t min_split_tokens() {
 }
 
 // DECODE_ATTN_KERNEL=vector|matrix forces the single-query split kernel
-// (when the matrix one supports the parameters); DECODE_ATTN_KERNEL=rows
-// makes the multi-token pass use 64-row blocks even for 16 rows or fewer;
-// unset or anything else = automatic.
+// (when the matrix one supports the parameters); unset or anything else =
+// automatic.
 int32_t forced_kernel() {
   const char* s = std::getenv("DECODE_ATTN_KERNEL");
   if (!s) return -1;
   if (std::strcmp(s, "vector") == 0) return 0;
   if (std::strcmp(s, "matrix") == 0) return 1;
-  if (std::strcmp(s, "rows") == 0) return 2;
   return -1;
 }
 
@@ -199,10 +196,8 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   const int64_t T = plan->query_len;
   const int64_t G = plan->group;
   const int64_t R = T * G;
-  // Up to 16 rows (D <= 128): four waves share the rows and split the keys;
-  // otherwise four waves of 16 rows share each key tile.
-  const int64_t QB = (R <= 16 && p.head_dim <= 128 && forced_kernel() != 2) ? 16
-                     : (p.head_dim <= 128 ? mq_rows() : 64);
+  // Four waves of 16 rows (or two groups of 16) share each key tile.
+  const int64_t QB = p.head_dim <= 128 ? mq_rows(R) : 64;
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);

@@ -138,10 +138,9 @@ typedef struct {
                                 DECODE_ATTN_KERNEL=vector forces 0. 2 = the
                                 multi-token kernels (query_len > 1; q.K and P.V
                                 on the matrix cores): the T*G rows of a KV head
-                                in blocks of 16 (keys split over the waves) or,
-                                beyond 16 rows or with DECODE_ATTN_KERNEL=rows,
-                                of 64 (head_dim 64, 256) or 128 (head_dim 128;
-                                DECODE_ATTN_MQ_ROWS=64 selects 64). A
+                                in blocks of 64 (16 rows or fewer, and head_dim
+                                256) or 128 (more rows at head_dim 64 and 128;
+                                DECODE_ATTN_MQ_ROWS=64 or 128 forces one). A
                                 query_len > 1 plan with 0 runs the vector kernel
                                 once per token.                                  */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each

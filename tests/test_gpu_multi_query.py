@@ -34,6 +34,10 @@ GRID = [
     (40, 4, 128, "f16", "f32", 64, (40, 700, 5000), 0),
     (20, 2, 128, "bf16", "bf16", 1024, (20, 3000), 500),
     (130, 1, 128, "f16", "f16", 8, (130, 131, 2000), 0),
+    # exactly 16 rows (four drafted tokens, GQA 4): one 64-row block with
+    # three waves past the rows
+    (4, 4, 128, "f16", "f16", 16, (4, 1000, 5000), 0),
+    (4, 4, 64, "bf16", "f32", 32, (4, 2000), 300),
 ]
 
 
@@ -49,15 +53,19 @@ def test_matches_oracle(gpu, T, G, D, kv, out, P, lens, W, splits):
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
 
 
-# Forced block shape: 64-row blocks even for 16 rows or fewer.
-@pytest.mark.parametrize("kernel", ["rows"])
-@pytest.mark.parametrize("T,G,D,kv,out,P,lens,W", [GRID[0], GRID[2], GRID[3], GRID[5], GRID[7], GRID[8]])
-def test_forced_block_shapes_match_oracle(gpu, kernel, T, G, D, kv, out, P, lens, W):
+# Forced block sizes at head_dim 64 and 128, whatever the row count: 128-row
+# blocks for 16 rows or fewer (112 or more rows of the block empty) and
+# 64-row blocks for more.
+@pytest.mark.parametrize("rows", ["64", "128"])
+@pytest.mark.parametrize("T,G,D,kv,out,P,lens,W", [GRID[0], GRID[1], GRID[3], GRID[4], GRID[13], GRID[14]])
+def test_forced_block_shapes_match_oracle(gpu, rows, T, G, D, kv, out, P, lens, W):
     spec = spec_of(T, G, D, kv, out, P, lens, W)
-    say(f"[multi] {spec.name} kernel={kernel}")
+    say(f"[multi] {spec.name} rows={rows}")
     w = wl.make_workload(spec, gpu)
-    got, plan = run_lib(w, num_splits=2, kernel=kernel)
-    err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} {kernel}")
+    with mq_rows(rows):
+        got, plan = run_lib(w, num_splits=2)
+    assert plan.info.split_kernel == 2
+    err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} rows {rows}")
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
 
 
@@ -71,7 +79,7 @@ def test_row_block_sizes_match_oracle(gpu, rows, T, G, D, kv, out, P, lens, W):
     say(f"[multi] {spec.name} rows={rows}")
     w = wl.make_workload(spec, gpu)
     with mq_rows(rows):
-        got, plan = run_lib(w, num_splits=3, kernel="rows")
+        got, plan = run_lib(w, num_splits=3)
     assert plan.info.split_kernel == 2
     err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} rows {rows}")
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
