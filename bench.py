@@ -15,8 +15,10 @@ cpu_baseline: the f64 CPU oracle on a bounded sample of the same batch.
 Also reported, each timed the same way: the fixed-order mode on the same
 batch (fixed_order), several new tokens per sequence on their own workloads
 (multi_token: a 4-token check over the long-context batch and a 128-token
-suffix prefill, each against its HBM or matrix-core roofline) and the K/V
-append of 1 and 256 tokens per sequence (append_kv).
+suffix prefill, each against its HBM or matrix-core roofline), one whole
+decode step (32 layers, 32 KV pools) of the Llama-3.1-8B shape at 3060 tokens
+issued eagerly and as a replayed HIP graph (layer_step), and the K/V append
+of 1 and 256 tokens per sequence (append_kv).
 """
 import argparse
 import ctypes
@@ -251,6 +253,53 @@ def measure_multi_token(binding, workloads, lib, dev, stream, iters):
     return res
 
 
+LAYERS = 32
+
+
+def measure_layer_step(binding, workloads, dev, stream, iters, layers=LAYERS):
+    """Attention of one whole decode step of the Llama-3.1-8B shape at 3060
+    tokens: `layers` independent KV pools (one per layer, 401 MB for 32, more
+    than the last-level cache holds), one decode_attn_run each, back to back,
+    issued eagerly and replayed from a captured HIP graph (the replay must
+    equal the eager outputs bitwise). {layers, eager_us, graph_us, GB_s}."""
+    import torch
+    spec = workloads.LLAMA8B_3060
+    ws_ = [workloads.make_workload(spec.replace(seed=spec.seed * 1000 + i), dev) for i in range(layers)]
+    params = binding.params_for(ws_[0].q, ws_[0].k_pool, ws_[0].page_table, window=ws_[0].window,
+                                scale=ws_[0].scale, out_dtype=spec.out_dtype)
+    plan = binding.decode_attn_plan(params, ws_[0].seq_lens_host, device=dev.index or 0)
+    scratch = binding.alloc_workspace(plan, dev)
+    outs = [torch.empty(w.q.shape, dtype=workloads.DTYPES[spec.out_dtype], device=dev) for w in ws_]
+
+    def step(s=None):
+        for w, o in zip(ws_, outs):
+            binding.decode_attn_run(plan, w.q, w.k_pool, w.v_pool, w.page_table, w.seq_lens, o, scratch, stream=s)
+
+    for _ in range(3):
+        step()
+    eager_ms = time_on_stream(step, iters, stream)
+    eager_out = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(side)
+    torch.cuda.synchronize()
+    for o in outs:
+        o.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(outs, eager_out)):
+        raise RuntimeError("graph replay of the layer step differs from the eager step")
+    graph_ms = time_on_stream(graph.replay, iters, stream)
+    total = sum(w.kv_bytes() for w in ws_)
+    del graph, ws_, outs, eager_out, scratch
+    torch.cuda.empty_cache()
+    return {"workload": f"{spec.name} x {layers} layers", "layers": layers, "eager_us": round(eager_ms * 1e3, 1),
+            "graph_us": round(graph_ms * 1e3, 1), "GB_s": round(total / (graph_ms * 1e-3) / 1e9, 1),
+            "bytes": total}
+
+
 def measure_append(w, lib, params, stream, tokens, iters):
     """Time decode_attn_append_kv writing `tokens` rows per sequence at the
     end of each sequence's context (positions L-T .. L-1), with new rows equal
@@ -381,6 +430,10 @@ def main():
     # Several new tokens per sequence (drafted-token check, suffix prefill).
     multi = [] if args.no_multi_token else measure_multi_token(binding, workloads, lib, dev, stream, args.steps)
 
+    # One whole decode step (32 layers) of the Llama-3.1-8B shape at 3060
+    # tokens, eager and as a replayed HIP graph.
+    layer_step = None if args.no_multi_token else measure_layer_step(binding, workloads, dev, stream, args.steps)
+
     # K/V append (the step before the path): one token per sequence, and a
     # 256-token suffix; written rows equal the resident rows.
     append_stats = [measure_append(w, lib, params, stream, t, args.steps) for t in (1, 256)]
@@ -436,6 +489,7 @@ def main():
         "combine_us": round(combine_ms * 1e3, 2),
         "fixed_order": fixed,
         "multi_token": multi,
+        "layer_step": layer_step,
         "append_kv": append_stats,
         "plan_host_us": round(plan_us, 1),
         "hbm_read_ceiling_GBps": ceilings.get("stream"),
