@@ -222,6 +222,41 @@ def test_multi_token_plans(lib):
     assert pl.info.split_work_groups == 8 and pl.workspace_bytes == 0
 
 
+# Rows per block: 64 for 16 rows or fewer per KV head (and always at head_dim
+# 256), 128 for more at head_dim 64 and 128; the grid is H_kv x (row blocks
+# x max_splits) x B.
+@pytest.mark.parametrize("T,G,D,rows", [(4, 4, 128, 64), (2, 4, 128, 64), (16, 1, 128, 64), (5, 4, 128, 128),
+                                         (4, 4, 64, 64), (33, 1, 64, 128), (4, 4, 256, 64), (64, 2, 256, 64),
+                                         (128, 4, 128, 128)])
+def test_multi_token_rows_per_block(lib, T, G, D, rows):
+    pl = plan(params(batch=2, num_q_heads=8 * G, head_dim=D, query_len=T, num_splits=3), [5000, 300])
+    assert pl.info.split_kernel == 2
+    nrb = math.ceil(T * G / rows)
+    assert pl.info.split_work_groups == 8 * nrb * pl.max_splits * 2
+
+
+@pytest.mark.parametrize("rows", ["64", "128"])
+def test_multi_token_rows_env_override(lib, monkeypatch, rows):
+    monkeypatch.setenv("DECODE_ATTN_MQ_ROWS", rows)
+    pl = plan(params(batch=1, query_len=40, num_splits=1), [5000])    # 160 rows at head_dim 128
+    assert pl.info.split_work_groups == 8 * math.ceil(160 / int(rows))
+
+
+# A few drafted tokens over long contexts: the keys of each (sequence, KV
+# head) are split only as far as one round of 2 resident 64-row work-groups
+# per compute unit (head_dim 128), sized by the longest sequence.
+def test_multi_token_few_rows_fill_one_round(lib):
+    lens = [16384 + 512 * i for i in range(32)]                   # 1024 .. 2016 pages
+    pl = plan(params(batch=32, query_len=4), lens)
+    assert pl.max_splits == 2
+    assert pl.pages_per_split == math.ceil(math.ceil(max(lens) / 16) / 2)
+    assert pl.info.split_work_groups == 8 * 1 * 2 * 32              # = 2 x 256 compute units
+    assert all(pl.splits(b) == math.ceil(math.ceil(L / 16) / pl.pages_per_split) for b, L in enumerate(lens))
+    # head_dim 64: 4 resident per compute unit
+    pl = plan(params(batch=32, head_dim=64, query_len=4), lens)
+    assert pl.max_splits == 4
+
+
 def test_multi_token_window_keys(lib):
     T, W = 8, 100
     pl = plan(params(batch=1, query_len=T, window=W), [5000])
