@@ -12,9 +12,10 @@
 // count depends only on the sequence, so the merge is the same whatever the
 // number of split work-groups.
 //
-// One wave64 per (query head, sequence), four waves per work-group; lane i
-// owns elements i, i+64, ... of the row, so every load of O_s is one
-// contiguous 256-byte-per-64-lane read.
+// Decode: one wave64 per (query head, sequence), four waves per work-group;
+// lane i owns elements i, i+64, ... of the row, so every load of O_s is one
+// contiguous 256-byte-per-64-lane read. Several new tokens per sequence (many
+// more rows, few splits each): 32 lanes per row, two rows per wave.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -51,17 +52,93 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const Kerne
   merge_head_wave<D>(a, static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h, static_cast<int>(nsplit), lane);
 }
 
-// Several new tokens per sequence: one wave per (query head, token, sequence).
-// The split count of a row is that of its row block (rows_per_group
-// consecutive (token, head) rows of one KV head), whose keys run from the
-// window start of its first token to its last token.
+// Merge of one row by 32 lanes (half a wave): lane j owns elements E j ..
+// E j + E - 1 of the row (E = D / 32), so each split's O row is one
+// contiguous read of 4 E bytes per lane, and every lane reads the (m, l)
+// pairs itself (the 32 lanes share each address), so nothing crosses lanes.
+// Splits are taken BATCH at a time, every load of a batch in flight
+// together; across batches the running state is rescaled to the new maximum:
+//     M = max_s m_s,  w_s = 2^(m_s - M),  out = sum_s w_s O_s / sum_s w_s l_s
+// with the sums in split order (identical results run to run). A state with
+// m_s = -inf (no attended key) gets weight 0.
 template <int D>
-__global__ __launch_bounds__(64 * kRowsPerGroup) void combine_multi_kernel(const KernelArgs a) {
-  const int h = blockIdx.x * kRowsPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void merge_row_halfwave(const KernelArgs& a, int64_t qrow, int nsplit, int hl) {
+  constexpr int E = D / 32;
+  constexpr int BATCH = 8;
+  static_assert(E == 2 || E % 4 == 0, "vector width of the O loads");
+  const float* ml = a.ws_ml + qrow * a.max_splits * 2;
+  const float* os = a.ws_o + qrow * a.max_splits * D + hl * E;
+  float M = -INFINITY, lsum = 0.0f;
+  float acc[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += BATCH) {
+    float ov[BATCH][E], mv[BATCH], lv[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      mv[j] = -INFINITY;
+      lv[j] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) ov[j][i] = 0.0f;
+      if (s0 + j < nsplit) {
+        const float* o = os + static_cast<int64_t>(s0 + j) * D;
+        if constexpr (E == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(o);
+          ov[j][0] = x.x;
+          ov[j][1] = x.y;
+        } else {
+#pragma unroll
+          for (int i = 0; i < E; i += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(o + i);
+            ov[j][i] = x.x;
+            ov[j][i + 1] = x.y;
+            ov[j][i + 2] = x.z;
+            ov[j][i + 3] = x.w;
+          }
+        }
+        const float2 st = *reinterpret_cast<const float2*>(ml + 2 * (s0 + j));
+        mv[j] = st.x;
+        lv[j] = st.y;
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) Mn = fmaxf(Mn, mv[j]);
+    const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
+    const float alpha = exp2_fast(M - Mu);  // 0 before the first state
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      if (s0 + j < nsplit) {
+        const float w = exp2_fast(mv[j] - Mu);
+        lsum += w * lv[j];
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] = fmaf(w, ov[j][i], acc[i]);
+      }
+    }
+    M = Mn;
+  }
+  const int64_t row = qrow * D + hl * E;
+#pragma unroll
+  for (int i = 0; i < E; ++i) store_elem(a.out, row + i, a.out_dtype, lsum > 0.0f ? acc[i] / lsum : 0.0f);
+}
+
+// Several new tokens per sequence: two (query head, token, sequence) rows per
+// wave, 32 lanes each, eight rows per work-group. The split count of a row is
+// that of its row block (rows_per_group consecutive (token, head) rows of one
+// KV head), whose keys run from the window start of its first token to its
+// last token.
+constexpr int kMultiRowsPerGroup = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_multi_kernel(const KernelArgs a) {
+  const int h = blockIdx.x * kMultiRowsPerGroup + static_cast<int>(threadIdx.x >> 5);
   const int t = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  if (h >= a.num_q_heads) return;  // whole wave
+  const int hl = threadIdx.x & 31;
+  if (h >= a.num_q_heads) return;  // whole half-wave
   const int T = a.query_len;
   const int G = a.group;
   const int R = T * G;
@@ -79,15 +156,15 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_multi_kernel(const
   int nsplit = (pe - pf + a.pages_per_split - 1) / a.pages_per_split;
   if (nsplit > a.max_splits) nsplit = a.max_splits;
   if (nsplit <= 1) return;  // the split pass wrote this row
-  merge_head_wave<D>(a, (static_cast<int64_t>(b) * T + t) * a.num_q_heads + h, nsplit, lane);
+  merge_row_halfwave<D>(a, (static_cast<int64_t>(b) * T + t) * a.num_q_heads + h, nsplit, hl);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream) {
   if (a.query_len > 1) {
-    const dim3 grid((a.num_q_heads + kRowsPerGroup - 1) / kRowsPerGroup, a.query_len, a.batch);
-    const dim3 block(64 * kRowsPerGroup);
+    const dim3 grid((a.num_q_heads + kMultiRowsPerGroup - 1) / kMultiRowsPerGroup, a.query_len, a.batch);
+    const dim3 block(256);
     switch (head_dim) {
       case 64: hipLaunchKernelGGL(combine_multi_kernel<64>, grid, block, 0, stream, a); break;
       case 128: hipLaunchKernelGGL(combine_multi_kernel<128>, grid, block, 0, stream, a); break;
