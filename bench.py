@@ -253,6 +253,43 @@ def measure_multi_token(binding, workloads, lib, dev, stream, iters):
     return res
 
 
+COLD_BYTES = 1 << 30
+LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+
+
+def measure_cold(w, plan, lib, out, ws, stream, cycles=3):
+    """The step over inputs the last-level cache cannot hold: k copies of the
+    K/V pool side by side (k * KV bytes >= 1 GiB), copy c addressed through
+    the page table offset by c * num_pages, the steps cycling through the
+    copies in order so every step reads pages that ~1 GiB of other steps
+    has touched since. {sets, us, GB_s} per step (mean over whole cycles)."""
+    import torch
+    kvb = w.kv_bytes()
+    k = max(2, -(-COLD_BYTES // max(1, kvb)))
+    n = w.num_pages
+    kp = w.k_pool.repeat(k, 1, 1, 1)
+    vp = w.v_pool.repeat(k, 1, 1, 1)
+    tables = torch.stack([w.page_table + c * n for c in range(k)]).contiguous()
+    row = tables[0].numel() * tables.element_size()
+    sptr = stream.cuda_stream
+    base = [w.q.data_ptr(), kp.data_ptr(), vp.data_ptr()]
+    tail = [w.seq_lens.data_ptr(), out.data_ptr(), ws.data_ptr() if ws is not None else None, plan.workspace_bytes,
+            sptr]
+    args = [base + [tables.data_ptr() + c * row] + tail for c in range(k)]
+
+    def cycle():
+        for a in args:
+            st = lib.decode_attn_run(plan.handle, *a)
+            if st != 0:
+                raise RuntimeError(f"decode_attn_run (cold): status {st}")
+
+    cycle()
+    ms = time_on_stream(cycle, cycles, stream) / k
+    del kp, vp, tables
+    torch.cuda.empty_cache()
+    return {"sets": k, "us": round(ms * 1e3, 2), "GB_s": round(kvb / (ms * 1e-3) / 1e9, 1)}
+
+
 LAYERS = 32
 
 
@@ -438,6 +475,9 @@ def main():
     # 256-token suffix; written rows equal the resident rows.
     append_stats = [measure_append(w, lib, params, stream, t, args.steps) for t in (1, 256)]
 
+    # Workloads the last-level cache could hold are also timed cold.
+    cold = measure_cold(w, plan, lib, out, ws, stream) if kv_bytes < 2 * LLC_BYTES else None
+
     ceilings = {}
     if not args.no_ceiling:
         ceilings = measure_ceilings(dev, sptr, stream)
@@ -486,6 +526,7 @@ def main():
             "algorithmic_bytes_per_launch": kv_bytes,
             "avg_launch_us": round(split_ms * 1e3, 2),
         },
+        "cold": cold,
         "combine_us": round(combine_ms * 1e3, 2),
         "fixed_order": fixed,
         "multi_token": multi,
