@@ -50,6 +50,10 @@ int64_t mq_rows(int64_t rows) {
   if (s && std::strcmp(s, "128") == 0) return 128;
   return rows <= 16 ? 64 : 128;
 }
+// Groups of one or two query heads use the vector split kernel when the
+// launch streams at least this many attended (key, KV head) pairs per
+// compute unit.
+constexpr int64_t kVectorKeyHeadsPerCu = 4096;
 // A split never holds fewer attended tokens than this (the pages' 256-token
 // switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
 constexpr int64_t kDefaultMinSplitTokens = 256;
@@ -316,10 +320,6 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   plan->group = G;
   plan->group_tile = gt;
   plan->num_cus = num_cus;
-  // q.K as a 16 x 32 x 16 matrix-core product per 16-key tile whenever the
-  // parameters allow it: with G query heads sharing the keys it is a dense
-  // contraction, and it takes the dot products and lane sums off the VALU.
-  plan->split_kernel = matrix_kernel_supported(*p) && forced_kernel() != 0 ? 1 : 0;
 
   // Attended pages per sequence.
   std::vector<int64_t> npages(p->batch);
@@ -341,6 +341,24 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     max_np = std::max(max_np, npages[b]);
     total_np += npages[b];
     plan->attended_keys += r.t1 - r.t0;
+  }
+
+  // q.K as a 16 x 32 x 16 matrix-core product per 16-key tile where the
+  // parameters allow it: with G query heads sharing the keys it is a dense
+  // contraction, and it takes the dot products and lane sums off the VALU.
+  // With one or two heads per group (1 or 2 of the product's 16 columns) the
+  // vector kernel streams faster once the launch is bandwidth-bound; measured
+  // (vector / matrix step time, f16 and bf16): G 1 0.95-0.96 over 6.2 M
+  // attended key-heads, 0.97 over 1.5 M, 0.99-1.0 at 0.26-0.79 M; G 2
+  // 0.93-0.95 over 6.2 M, 0.99-1.0 over 1.5 M, 1.00-1.02 at 0.79 M and
+  // 1.06-1.09 at 0.26-0.39 M. The switch depends on lengths, window and head
+  // counts only (never on num_splits), so the fixed-order mode keeps its
+  // split-count invariance.
+  {
+    const int64_t key_heads = total_np * P * p->num_kv_heads;
+    const bool wide_enough = G >= 3 || key_heads < kVectorKeyHeadsPerCu * num_cus;
+    const int32_t fk = forced_kernel();
+    plan->split_kernel = matrix_kernel_supported(*p) && fk != 0 && (fk == 1 || wide_enough) ? 1 : 0;
   }
 
   if (plan->query_len > 1 && !per_token) {
