@@ -1,7 +1,8 @@
 """Seeded random configurations through the C-ABI against the oracle: head
 counts, head_dim, dtypes, page size, lengths (including 0 and page
 boundaries), windows, forced split counts, new-token counts and the
-fixed-order mode, drawn from one generator so a failure names its case."""
+fixed-order mode, drawn from one generator so a failure names its case; and
+a set weighted to a few new tokens per sequence on the multi-token kernels."""
 import numpy as np
 import pytest
 
@@ -46,7 +47,7 @@ def draw_case(i):
     return dict(G=G, Hkv=Hkv, D=D, P=P, kv=kv, q=q, out=out, T=T, lens=lens, W=W, splits=splits, fixed=fixed)
 
 
-@pytest.mark.parametrize("i", range(160))
+@pytest.mark.parametrize("i", range(600))
 def test_random_config_matches_oracle(gpu, i):
     c = draw_case(i)
     say(f"[random {i}] {c}")
@@ -56,3 +57,33 @@ def test_random_config_matches_oracle(gpu, i):
     got, plan = run_lib(w, num_splits=c["splits"], fixed_chunk=c["fixed"])
     err, worst = check(got, oracle_for(w), c["kv"], c["out"], f"case {i}")
     say(f"  kernel {plan.info.split_kernel}: rel L2 {err:.2e}, worst sequence {worst:.2e}")
+
+
+def draw_few_rows(i):
+    """A few new tokens per sequence (2..8) on the 16-bit multi-token
+    kernels: the rows of a KV head fit one block of 64, with contexts up to
+    20k keys in 30 % of the cases."""
+    rng = np.random.default_rng(50000 + i)
+    c = draw_case(100000 + i)
+    c["T"] = int(rng.choice([2, 3, 4, 5, 8]))
+    c["G"] = int(rng.choice([1, 2, 3, 4, 8]))
+    c["kv"] = str(rng.choice(["f16", "bf16"]))
+    c["q"] = c["kv"]
+    c["fixed"] = 0
+    c["lens"] = [max(L, c["T"]) for L in c["lens"]]
+    if rng.random() < 0.3:
+        c["lens"] = [int(rng.integers(c["T"], 20000)) for _ in c["lens"]]
+    return c
+
+
+@pytest.mark.parametrize("i", range(200))
+def test_random_few_row_multi_token_matches_oracle(gpu, i):
+    c = draw_few_rows(i)
+    say(f"[few-row {i}] {c}")
+    spec = wl.WorkloadSpec(f"few{i}", len(c["lens"]), c["G"] * c["Hkv"], c["Hkv"], c["D"], c["q"], c["kv"], c["out"],
+                           c["P"], ("list", tuple(c["lens"])), seed=3000 + i, window=c["W"], query_len=c["T"])
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w, num_splits=c["splits"])
+    assert plan.info.split_kernel == 2
+    err, worst = check(got, oracle_for(w), c["kv"], c["out"], f"few-row case {i}")
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
