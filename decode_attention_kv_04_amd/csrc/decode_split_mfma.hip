@@ -18,6 +18,12 @@
 //  * V is read in rows: lane (r, c) holds row 4*i + r (i = 0..3) of the tile,
 //    elements [v*128 + 8c, +8) for v < D/128, so one wave-wide load covers
 //    four whole rows.
+//  * K is read the same way (whole rows, four per load) and rearranged into
+//    the operand layout through a per-wave LDS tile: loaded straight in
+//    operand layout, each instruction would take 64 bytes of each of 16 rows,
+//    and that pattern streams slower (a probe over shuffled 4 KiB blocks with
+//    non-temporal loads: 5.85 TB/s against 6.5-6.6 for whole rows; this
+//    kernel on the long batch: 504.8 -> 494.2 us per launch).
 //  * Hence each lane already holds the scores of exactly the keys whose V rows
 //    it holds; the online-softmax state (m, l) of head g and row slot r lives
 //    in lane (r, g), and P and the rescale factors reach the P.V lanes of the
@@ -139,9 +145,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
   const int64_t page_bytes = block_bytes * a.num_kv_heads;
   const int64_t head_bytes = block_bytes * kvh;
   const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
-  const uint32_t k_lane_off = static_cast<uint32_t>(key_of_lane * RB + 8 * r * ELT);
   const uint32_t v_lane_off = static_cast<uint32_t>(r * RB + c * E * ELT);
 
+  // K of the tile being computed, per wave: 16 rows of 16-byte slots, slot s
+  // of row k stored at s ^ k, so the 16 lanes of a row write and the 16
+  // lanes of an operand read (one slot of each of 16 rows) fall in distinct
+  // banks.
+  constexpr int NSL = D / 8;
+  static_assert(NSL == TR, "slot permutation by row needs as many slots as rows");
+  __shared__ uint4 sh_k[kWaves][TR][NSL];
   __shared__ float sh_o[kWaves][GT][D];
   __shared__ float sh_m[kWaves][GT];
   __shared__ float sh_l[kWaves][GT];
@@ -184,10 +196,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
     };
     auto issue = [&](Tile& t) {
       const int64_t off = static_cast<int64_t>(cur_phys) * page_bytes + head_bytes + static_cast<int64_t>(cur_off) * RB;
-      const char* kp = kbase + off + k_lane_off;
+      const char* kp = kbase + off + v_lane_off;
       const char* vp = vbase + off + v_lane_off;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) t.k[j] = load16(kp + 32 * j * ELT);
+      for (int j = 0; j < NJ; ++j) t.k[j] = load16(kp + 4 * j * RB);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -209,7 +221,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
       const int tb = tile * TR;
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc = mfma_16x16x32<KVT>(t.k[j], qb[j], acc);
+      for (int j = 0; j < NJ; ++j) sh_k[wave][4 * j + r][c ^ (4 * j + r)] = t.k[j];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc = mfma_16x16x32<KVT>(sh_k[wave][key_of_lane][(4 * j + r) ^ key_of_lane], qb[j], acc);
       bool valid[4];
       float x[4];  // scores in base-2 units
 #pragma unroll
