@@ -50,10 +50,6 @@ int64_t mq_rows(int64_t rows) {
   if (s && std::strcmp(s, "128") == 0) return 128;
   return rows <= 16 ? 64 : 128;
 }
-// Groups of one or two query heads use the vector split kernel when the
-// launch streams at least this many attended (key, KV head) pairs per
-// compute unit.
-constexpr int64_t kVectorKeyHeadsPerCu = 4096;
 // A split never holds fewer attended tokens than this (the pages' 256-token
 // switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
 constexpr int64_t kDefaultMinSplitTokens = 256;
@@ -344,21 +340,16 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   }
 
   // q.K as a 16 x 32 x 16 matrix-core product per 16-key tile where the
-  // parameters allow it: with G query heads sharing the keys it is a dense
-  // contraction, and it takes the dot products and lane sums off the VALU.
-  // With one or two heads per group (1 or 2 of the product's 16 columns) the
-  // vector kernel streams faster once the launch is bandwidth-bound; measured
-  // (vector / matrix step time, f16 and bf16): G 1 0.95-0.96 over 6.2 M
-  // attended key-heads, 0.97 over 1.5 M, 0.99-1.0 at 0.26-0.79 M; G 2
-  // 0.93-0.95 over 6.2 M, 0.99-1.0 over 1.5 M, 1.00-1.02 at 0.79 M and
-  // 1.06-1.09 at 0.26-0.39 M. The switch depends on lengths, window and head
-  // counts only (never on num_splits), so the fixed-order mode keeps its
-  // split-count invariance.
+  // parameters allow it and at least two query heads share the keys: then it
+  // is a dense contraction, and it takes the dot products and lane sums off
+  // the VALU. One head per group (a dot product per key) stays on the vector
+  // kernel. Measured, vector / matrix step time, f16 and bf16: G 1 0.998 over
+  // 6.2 M attended key-heads, 0.99-1.01 at 0.8-1.5 M, 1.02-1.03 at 0.26-0.39 M;
+  // G 2 0.997-0.998 over 6.2 M, 1.00-1.01 over 1.5 M, 1.01-1.02 at 0.79 M,
+  // 1.08-1.10 at 0.26-0.39 M.
   {
-    const int64_t key_heads = total_np * P * p->num_kv_heads;
-    const bool wide_enough = G >= 3 || key_heads < kVectorKeyHeadsPerCu * num_cus;
     const int32_t fk = forced_kernel();
-    plan->split_kernel = matrix_kernel_supported(*p) && fk != 0 && (fk == 1 || wide_enough) ? 1 : 0;
+    plan->split_kernel = matrix_kernel_supported(*p) && fk != 0 && (fk == 1 || G >= 2) ? 1 : 0;
   }
 
   if (plan->query_len > 1 && !per_token) {

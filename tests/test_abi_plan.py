@@ -152,31 +152,19 @@ def test_split_kernel_selection(lib, monkeypatch):
     assert plan(params(head_dim=64), [3060]).info.split_kernel == 0             # unsupported: vector
 
 
-# Groups of one or two query heads take the vector kernel once the launch
-# streams at least 4096 attended (key, KV head) pairs per compute unit (the
-# matrix-core product would fill 1 or 2 of its 16 columns); G >= 3 always
-# takes the matrix-core kernel where it is supported. The choice does not
-# depend on num_splits or fixed_chunk.
+# One query head per group (q.K a dot product per key) takes the vector
+# kernel; two or more take the matrix-core kernel where it is supported,
+# whatever the size of the launch, the split count or the fixed-order chunk.
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
-def test_split_kernel_by_group_and_work(lib, monkeypatch, G):
+def test_split_kernel_by_group(lib, monkeypatch, G):
     monkeypatch.delenv("DECODE_ATTN_KERNEL", raising=False)
-    long = [32768] * 32                     # 2048 pages x 8 KV heads x 32 = 8.4 M key-heads
-    short = [3060] * 2                      # 0.1 M key-heads
-    big = plan(params(batch=32, num_q_heads=8 * G), long).info.split_kernel
-    small = plan(params(batch=2, num_q_heads=8 * G), short).info.split_kernel
-    assert small == 1
-    assert big == (0 if G <= 2 else 1)
-    # the threshold: 4096 key-heads per compute unit, counted over whole pages
-    cus = 64
-    at = [4096 * cus // 8]                  # exactly 4096 per CU over 8 KV heads
-    below = [4096 * cus // 8 - 16]
-    assert plan(params(num_q_heads=8 * G), at, cus=cus).info.split_kernel == (0 if G <= 2 else 1)
-    assert plan(params(num_q_heads=8 * G), below, cus=cus).info.split_kernel == 1
-    # independent of the split count and of the fixed-order chunk length
+    want = 0 if G == 1 else 1
+    for lens in ([32768] * 32, [3060] * 2, [1]):
+        assert plan(params(batch=len(lens), num_q_heads=8 * G), lens).info.split_kernel == want
     for kw in (dict(num_splits=1), dict(num_splits=7), dict(fixed_chunk=1024), dict(fixed_chunk=1024, num_splits=3)):
-        assert plan(params(batch=32, num_q_heads=8 * G, **kw), long).info.split_kernel == big
+        assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == want
     monkeypatch.setenv("DECODE_ATTN_KERNEL", "matrix")
-    assert plan(params(batch=32, num_q_heads=8 * G), long).info.split_kernel == 1
+    assert plan(params(batch=32, num_q_heads=8 * G), [32768] * 32).info.split_kernel == 1
 
 
 # ---------------------------------------------------------------------------

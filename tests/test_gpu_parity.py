@@ -125,11 +125,14 @@ def test_group_dim_dtype_grid(gpu, G, D, kv):
                            ("list", (1, 300, 777)), seed=G * 1000 + D + len(kv), spike_frac=0.01)
     w = make(spec, gpu)
     ref = oracle_for(w)
-    kernels = ["auto", "vector"] if (D == 128 and kv != "f32") else ["auto"]
+    matrix_ok = D == 128 and kv != "f32"
+    kernels = ["auto", "vector", "matrix"] if matrix_ok else ["auto"]
     for kernel in kernels:
         for ns in (0, 3):
             out, plan = run_lib(w, num_splits=ns, kernel=kernel)
-            assert plan.info.split_kernel == (1 if (D == 128 and kv != "f32" and kernel == "auto") else 0)
+            # automatic: the matrix-core kernel from two query heads per group on
+            want = 1 if matrix_ok and (kernel == "matrix" or (kernel == "auto" and G >= 2)) else 0
+            assert plan.info.split_kernel == want
             check(out, ref, kv, "f32", f"G{G} D{D} {kv} splits={ns} kernel={kernel}")
 
 
