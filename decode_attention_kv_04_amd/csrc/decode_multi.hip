@@ -10,10 +10,10 @@
 //
 // Query rows. The T*G (token, head) pairs that share KV head j form the rows
 // r = t*G + g of one contraction. A work-group takes 64 or 128 consecutive
-// rows (4 wave64s, one or two groups of 16 rows each; a block of 16 rows or
-// fewer, a few drafted tokens, runs on 64-row blocks with the waves past its
-// rows computing on zero q) and one split of the keys those rows see, K/V
-// staged through a ring of LDS buffers filled by direct global -> LDS loads.
+// rows (4 wave64s, one or two groups of 16 rows each), or 16 rows (a few
+// drafted tokens: wave 0 computes them, the other three waves only copy),
+// and one split of the keys those rows see, K/V staged through a ring of LDS
+// buffers filled by direct global -> LDS loads.
 // Both products run on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}):
 //   S^T = K Q^T    A = 16 keys x 32 dims of K,  B = 32 dims x 16 rows of q
 //   O^T += V^T P^T A = 16 dims x 32 keys of V,  B = 32 keys x 16 rows of P
@@ -383,11 +383,15 @@ constexpr int lds_stages() {
   return D >= 256 ? 2 : 3;
 }
 
-template <int D, int KVT, int NS, int NR>
+// FEW: blocks of 16 rows (a few drafted tokens): wave 0 computes them and
+// waves 1-3 only copy their share of each tile, passing the same barrier once
+// per tile.
+template <int D, int KVT, int NS, int NR, bool FEW = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? (NR == 1 ? 4 : 3) : (D == 128 && NR == 1 ? 3 : 2)))) void
 multi_dma_kernel(const KernelArgs a) {
   static_assert(D == 64 || D == 128 || D == 256, "row layout and slot permutation of the LDS ring");
-  constexpr int QB = 64 * NR;      // query rows per work-group (4 waves x NR groups of 16)
+  static_assert(!FEW || NR == 1, "16-row blocks are one row group");
+  constexpr int QB = FEW ? 16 : 64 * NR;  // query rows per work-group (4 waves x NR groups of 16, or 16)
   constexpr int ROWB = D * 2;      // bytes per K/V row
   constexpr int TILE = KT * D;     // 16-bit elements per K (or V) tile
   constexpr int NSEG = D / 8;      // 16-byte segments per key row
@@ -439,7 +443,7 @@ multi_dma_kernel(const KernelArgs a) {
   RowGroup<D> rg[NR];
 #pragma unroll
   for (int g = 0; g < NR; ++g)
-    init_rows(rg[g], a, r_first + (wave * NR + g) * 16 + col, r_last, b, kvh, L, t_lo, t_hi, q4);
+    init_rows(rg[g], a, r_first + (FEW ? 0 : (wave * NR + g) * 16) + col, r_last, b, kvh, L, t_lo, t_hi, q4);
   // Let the q loads land here, in a wait the compiler sees: its own wait
   // before their first use would otherwise sit inside the key loop and wait
   // for every copy in flight on each tile (vmcnt(0), other counters at
@@ -502,6 +506,30 @@ multi_dma_kernel(const KernelArgs a) {
   const int vh = (col & 1) * 4;
   const float sl2 = a.scale_log2;
 
+  if constexpr (FEW) {
+    if (wave != 0) {
+      // Copies only, with the ring steps of begin_tile below: per tile one
+      // wait for this wave's copies, one barrier, the copy NS - 1 tiles ahead.
+      // The last tiles wait for every copy, so none is left in flight.
+      if (ntiles > 0) {
+        fetch_id();
+#pragma unroll
+        for (int k = 0; k < NS - 1; ++k)
+          if (k < ntiles) issue(k);
+        int stage = 0;
+        for (int m = 0; m < ntiles; ++m) {
+          if (m + NS - 2 < ntiles)
+            wait_loads<(NS - 2) * LOADS>();
+          else
+            wait_loads<0>();
+          lds_barrier();
+          if (m + NS - 1 < ntiles) issue(stage == 0 ? NS - 1 : stage - 1);
+          stage = stage == NS - 1 ? 0 : stage + 1;
+        }
+      }
+      return;
+    }
+  }
   if (ntiles > 0) {
     fetch_id();
 #pragma unroll
@@ -595,7 +623,9 @@ multi_dma_kernel(const KernelArgs a) {
 
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
-  if (rows == 64) {
+  if (rows == 16) {
+    hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 1, true>), grid, dim3(256), 0, st, a);
+  } else if (rows == 64) {
     hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 1>), grid, dim3(256), 0, st, a);
   } else if (rows == 128) {
     if constexpr (D <= 128)

@@ -41,14 +41,20 @@ int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
 // Rows per block at head_dim 64 and 128: 128 (two 16-row groups per wave
 // sharing every K/V operand read) measured 15 % faster than 64 at head_dim
 // 128 on 128- and 512-token suffixes and 5 % on 8..32-token suffixes (GQA 4:
-// 32..128 rows); blocks of 16 rows or fewer (a few drafted tokens) take 64, where a 128-row
-// block would compute on 112 empty rows. DECODE_ATTN_MQ_ROWS=64 or 128
-// overrides both.
-int64_t mq_rows(int64_t rows) {
+// 32..128 rows). Blocks of 16 rows or fewer (a few drafted tokens) take 16
+// rows at every head_dim: wave 0 computes them and the other waves only copy
+// (64-row blocks would compute the empty rows on zero q). DECODE_ATTN_MQ_ROWS
+// = 16, 64 or 128 forces one size at head_dim 64 and 128; at head_dim 256
+// blocks are 64 rows, or 16 for 16 rows or fewer.
+int64_t mq_rows(int64_t rows, int32_t head_dim) {
   const char* s = std::getenv("DECODE_ATTN_MQ_ROWS");
-  if (s && std::strcmp(s, "64") == 0) return 64;
-  if (s && std::strcmp(s, "128") == 0) return 128;
-  return rows <= 16 ? 64 : 128;
+  if (head_dim <= 128 && s) {
+    if (std::strcmp(s, "16") == 0) return 16;
+    if (std::strcmp(s, "64") == 0) return 64;
+    if (std::strcmp(s, "128") == 0) return 128;
+  }
+  if (rows <= 16) return 16;
+  return head_dim <= 128 ? 128 : 64;
 }
 // A split never holds fewer attended tokens than this (the pages' 256-token
 // switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
@@ -197,7 +203,7 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   const int64_t G = plan->group;
   const int64_t R = T * G;
   // Four waves of 16 rows (or two groups of 16) share each key tile.
-  const int64_t QB = p.head_dim <= 128 ? mq_rows(R) : 64;
+  const int64_t QB = mq_rows(R, p.head_dim);
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);

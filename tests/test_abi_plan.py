@@ -221,7 +221,7 @@ def test_multi_token_plans(lib):
     lens = [16, 3000, 700]
     pl = plan(params(batch=3, query_len=16), lens)
     assert pl.info.split_kernel == 2
-    # 16 tokens x G 4 = 64 rows per KV head: one row block of 64
+    # 16 tokens x G 4 = 64 rows per KV head: one row block
     S = pl.max_splits
     assert pl.info.split_work_groups == 1 * S * 8 * 3
     T = 16
@@ -232,17 +232,17 @@ def test_multi_token_plans(lib):
     # forced: the longest row block's pages over num_splits
     pl = plan(params(batch=3, query_len=16, num_splits=5), lens)
     assert pl.max_splits == 5 and pl.pages_per_split == math.ceil(math.ceil(3000 / 16) / 5)
-    # 2 tokens x G 4 = 8 rows: one block of 64 rows
+    # 2 tokens x G 4 = 8 rows: one block of 16 rows
     pl = plan(params(batch=1, query_len=2, num_splits=1), [100])
     assert pl.info.split_work_groups == 8 and pl.workspace_bytes == 0
 
 
-# Rows per block: 64 for 16 rows or fewer per KV head (and always at head_dim
-# 256), 128 for more at head_dim 64 and 128; the grid is H_kv x (row blocks
-# x max_splits) x B.
-@pytest.mark.parametrize("T,G,D,rows", [(4, 4, 128, 64), (2, 4, 128, 64), (16, 1, 128, 64), (5, 4, 128, 128),
-                                         (4, 4, 64, 64), (33, 1, 64, 128), (4, 4, 256, 64), (64, 2, 256, 64),
-                                         (128, 4, 128, 128)])
+# Rows per block: 16 for 16 rows or fewer per KV head (wave 0 computes, the
+# other waves copy), otherwise 128 at head_dim 64 and 128 and 64 at 256; the
+# grid is H_kv x (row blocks x max_splits) x B.
+@pytest.mark.parametrize("T,G,D,rows", [(4, 4, 128, 16), (2, 4, 128, 16), (16, 1, 128, 16), (5, 4, 128, 128),
+                                         (4, 4, 64, 16), (33, 1, 64, 128), (4, 4, 256, 16), (64, 2, 256, 64),
+                                         (128, 4, 128, 128), (17, 1, 256, 64)])
 def test_multi_token_rows_per_block(lib, T, G, D, rows):
     pl = plan(params(batch=2, num_q_heads=8 * G, head_dim=D, query_len=T, num_splits=3), [5000, 300])
     assert pl.info.split_kernel == 2
@@ -250,7 +250,7 @@ def test_multi_token_rows_per_block(lib, T, G, D, rows):
     assert pl.info.split_work_groups == 8 * nrb * pl.max_splits * 2
 
 
-@pytest.mark.parametrize("rows", ["64", "128"])
+@pytest.mark.parametrize("rows", ["16", "64", "128"])
 def test_multi_token_rows_env_override(lib, monkeypatch, rows):
     monkeypatch.setenv("DECODE_ATTN_MQ_ROWS", rows)
     pl = plan(params(batch=1, query_len=40, num_splits=1), [5000])    # 160 rows at head_dim 128
@@ -258,7 +258,7 @@ def test_multi_token_rows_env_override(lib, monkeypatch, rows):
 
 
 # A few drafted tokens over long contexts: the keys of each (sequence, KV
-# head) are split only as far as one round of 2 resident 64-row work-groups
+# head) are split only as far as one round of 2 resident 16-row work-groups
 # per compute unit (head_dim 128), sized by the longest sequence.
 def test_multi_token_few_rows_fill_one_round(lib):
     lens = [16384 + 512 * i for i in range(32)]                   # 1024 .. 2016 pages

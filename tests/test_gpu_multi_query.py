@@ -53,10 +53,10 @@ def test_matches_oracle(gpu, T, G, D, kv, out, P, lens, W, splits):
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
 
 
-# Forced block sizes at head_dim 64 and 128, whatever the row count: 128-row
-# blocks for 16 rows or fewer (112 or more rows of the block empty) and
-# 64-row blocks for more.
-@pytest.mark.parametrize("rows", ["64", "128"])
+# Forced block sizes at head_dim 64 and 128, whatever the row count: 64- and
+# 128-row blocks for 16 rows or fewer (48 or more rows of the block empty),
+# and 16-row blocks (wave 0 computes, waves 1-3 copy) for more rows.
+@pytest.mark.parametrize("rows", ["16", "64", "128"])
 @pytest.mark.parametrize("T,G,D,kv,out,P,lens,W", [GRID[0], GRID[1], GRID[3], GRID[4], GRID[13], GRID[14]])
 def test_forced_block_shapes_match_oracle(gpu, rows, T, G, D, kv, out, P, lens, W):
     spec = spec_of(T, G, D, kv, out, P, lens, W)
