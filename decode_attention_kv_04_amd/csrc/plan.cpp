@@ -57,16 +57,38 @@ int64_t mq_rows(int64_t rows, int32_t head_dim) {
   return head_dim <= 128 ? 128 : 64;
 }
 // A split never holds fewer attended tokens than this (the pages' 256-token
-// switch-over); DECODE_ATTN_SPLIT_MIN overrides it.
+// switch-over: a dispatch whose contexts are all this short is not split);
+// DECODE_ATTN_SPLIT_MIN overrides it.
 constexpr int64_t kDefaultMinSplitTokens = 256;
+// On the matrix-core decode kernel, once the longest attended context is
+// above the switch-over, splits may be this short (3060-token Llama-8B decode
+// shape: 10.8 -> 10.2 us per step with 128-token splits, 10.2 with 192;
+// the vector kernel at head_dim 256 lost with them, 14.2 -> 17.0 us).
+constexpr int64_t kMatrixMinSplitTokens = 128;
 
-int64_t min_split_tokens() {
+bool split_min_env(int64_t* v) {
   const char* s = std::getenv("DECODE_ATTN_SPLIT_MIN");
   if (s && *s) {
     char* end = nullptr;
-    long v = std::strtol(s, &end, 10);
-    if (end && *end == '\0' && v >= 1) return v;
+    long x = std::strtol(s, &end, 10);
+    if (end && *end == '\0' && x >= 1) {
+      *v = x;
+      return true;
+    }
   }
+  return false;
+}
+
+int64_t min_split_tokens() {
+  int64_t v;
+  return split_min_env(&v) ? v : kDefaultMinSplitTokens;
+}
+
+// Minimum split length of a single-query plan (decode or per-token mode).
+int64_t decode_min_split_tokens(bool matrix_kernel, int64_t max_attended_tokens) {
+  int64_t v;
+  if (split_min_env(&v)) return v;
+  if (matrix_kernel && max_attended_tokens > kDefaultMinSplitTokens) return kMatrixMinSplitTokens;
   return kDefaultMinSplitTokens;
 }
 
@@ -123,14 +145,13 @@ int32_t group_tile_for(int32_t G) {
 namespace {
 
 // Pages per split that give the split pass about `per_cu` work-groups per
-// compute unit (kTargetGroupsPerCu by default), at least the minimum split
-// length.
+// compute unit (kTargetGroupsPerCu by default), at least min_tokens.
 int64_t heuristic_split_pages(int64_t total_np, int64_t max_np, int64_t num_kv_heads, int64_t num_cus, int64_t P,
-                              int64_t per_cu = kTargetGroupsPerCu) {
+                              int64_t min_tokens, int64_t per_cu = kTargetGroupsPerCu) {
   const int64_t work = total_np * num_kv_heads;  // page-heads to stream
   const int64_t target = num_cus * per_cu;
   int64_t c = ceil_div(work, target);
-  c = std::max(c, ceil_div(min_split_tokens(), P));
+  c = std::max(c, ceil_div(min_tokens, P));
   return std::min(c, max_np);
 }
 
@@ -172,7 +193,9 @@ da_status finish_fixed_plan(da_plan* plan, const std::vector<int64_t>& npages, i
     cpg = ceil_div(max_chunks, std::min<int64_t>(p.num_splits, max_chunks));
   } else {
     const int64_t c = max_np > 0 ? heuristic_split_pages(total_np, max_np, p.num_kv_heads, plan->num_cus,
-                                                         p.page_size)
+                                                         p.page_size,
+                                                         decode_min_split_tokens(plan->split_kernel == 1,
+                                                                                 max_np * p.page_size))
                                  : 1;
     cpg = std::min(max_chunks, std::max<int64_t>(1, ceil_div(c, cp)));
   }
@@ -375,7 +398,8 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   } else if (p->num_splits > 0) {
     c = ceil_div(max_np, p->num_splits);
   } else {
-    c = heuristic_split_pages(total_np, max_np, p->num_kv_heads, num_cus, P);
+    c = heuristic_split_pages(total_np, max_np, p->num_kv_heads, num_cus, P,
+                              decode_min_split_tokens(plan->split_kernel == 1, max_np * P));
   }
   c = std::max<int64_t>(c, 1);
   // The split index is the grid's y dimension (at most 65535 splits).

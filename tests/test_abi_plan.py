@@ -115,6 +115,24 @@ def test_heuristic_short_contexts_do_not_split(lib):
     assert pl.max_splits == 1
 
 
+def test_matrix_kernel_splits_down_to_128_tokens(lib, monkeypatch):
+    # the matrix-core kernel (f16, head_dim 128, G 4) over one 3060-token
+    # context: splits of 128 tokens (8 pages); the vector kernel keeps 256
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    monkeypatch.delenv("DECODE_ATTN_KERNEL", raising=False)
+    pl = plan(params(), [3060])
+    assert pl.info.split_kernel == 1 and pl.pages_per_split == 8 and pl.max_splits == 24
+    pl = plan(params(head_dim=64), [3060])
+    assert pl.info.split_kernel == 0 and pl.pages_per_split == 16
+    # contexts of at most 256 tokens are not split (the switch-over), one more token is
+    assert plan(params(batch=3), [256, 100, 1]).max_splits == 1
+    pl = plan(params(batch=3), [257, 100, 1])
+    assert pl.pages_per_split == 8 and pl.max_splits == 3
+    # the fixed-order mode groups its chunks by the same split length
+    pl = plan(params(fixed_chunk=128), [3060])
+    assert pl.info.chunks_per_work_group == 1
+
+
 def test_heuristic_long_batch_fills_the_chip(lib):
     lens = [16384 + (i * 523) % 16384 for i in range(32)]
     pl = plan(params(batch=32), lens)
