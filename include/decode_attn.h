@@ -134,15 +134,18 @@ typedef struct {
   size_t workspace_bytes;    /* bytes of device workspace `run` needs (0 if none)   */
   int32_t split_kernel;      /* 0 = vector q.K (any parameters); 1 = q.K on the
                                 matrix cores (q and K/V share f16 or bf16,
-                                head_dim 128, page size a multiple of 16).
-                                DECODE_ATTN_KERNEL=vector forces 0. 2 = the
+                                head_dim 128, page size a multiple of 16, at
+                                least two query heads per KV head).
+                                DECODE_ATTN_KERNEL=vector|matrix forces 0 or 1
+                                where supported. 2 = the
                                 multi-token kernels (query_len > 1; q.K and P.V
                                 on the matrix cores): the T*G rows of a KV head
-                                in blocks of 64 (16 rows or fewer, and head_dim
-                                256) or 128 (more rows at head_dim 64 and 128;
-                                DECODE_ATTN_MQ_ROWS=64 or 128 forces one). A
-                                query_len > 1 plan with 0 runs the vector kernel
-                                once per token.                                  */
+                                in blocks of 16 (16 rows or fewer: one wave
+                                computes, three copy), 128 (more rows at head_dim
+                                64 and 128) or 64 (more rows at head_dim 256);
+                                DECODE_ATTN_MQ_ROWS=16, 64 or 128 forces one at
+                                head_dim 64 and 128. A query_len > 1 plan with
+                                0 runs the vector kernel once per token.       */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in
