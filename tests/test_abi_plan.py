@@ -217,13 +217,18 @@ def test_fixed_order_chunk_count_follows_attended_pages(lib, L, W, P, chunk):
     assert pl.splits(0) == max(1, math.ceil(attended_pages(L, W, P) / (chunk // P)))
 
 
-def test_fixed_order_heuristic_fills_the_chip(lib):
+def test_fixed_order_heuristic_one_chunk_per_work_group(lib, monkeypatch):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
     lens = [16384 + (i * 523) % 16384 for i in range(32)]
-    pl = plan(params(batch=32, fixed_chunk=512), lens)
-    default = plan(params(batch=32), lens)
-    # about as many pages per work-group as the default split, in whole chunks
-    assert pl.info.chunks_per_work_group == math.ceil(default.pages_per_split / 32)
-    assert pl.info.active_units >= 256 * 2
+    # chunks at least as long as the minimum split length: one per work-group
+    for chunk in (128, 512, 1024):
+        pl = plan(params(batch=32, fixed_chunk=chunk), lens)
+        assert pl.info.chunks_per_work_group == 1
+        assert pl.info.split_work_groups == pl.max_splits * 8 * 32
+    # shorter chunks are grouped up to the minimum split length: 128 tokens on
+    # the matrix-core kernel, 256 on the vector kernel
+    assert plan(params(batch=32, fixed_chunk=32), lens).info.chunks_per_work_group == 4
+    assert plan(params(batch=32, head_dim=64, fixed_chunk=32), lens).info.chunks_per_work_group == 8
 
 
 @pytest.mark.parametrize("chunk", [-16, 8, 24, 100])
