@@ -69,6 +69,22 @@ def test_forced_block_shapes_match_oracle(gpu, rows, T, G, D, kv, out, P, lens, 
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
 
 
+# 16 rows or fewer: the 16-row blocks (wave 0 computes, waves 1-3 only copy)
+# do the same arithmetic per row as 64- and 128-row blocks whose other row
+# groups are empty, so the outputs agree bitwise.
+@pytest.mark.parametrize("T,G,D,kv,out,P,lens,W", [GRID[0], GRID[1], GRID[13], GRID[14]])
+def test_few_row_blocks_equal_wider_blocks_bitwise(gpu, T, G, D, kv, out, P, lens, W):
+    spec = spec_of(T, G, D, kv, out, P, lens, W)
+    assert T * G <= 16
+    say(f"[multi] {spec.name} 16-row vs wider blocks")
+    w = wl.make_workload(spec, gpu)
+    base, _ = run_lib(w, num_splits=2)
+    for rows in ("64", "128"):
+        with mq_rows(rows):
+            got, _ = run_lib(w, num_splits=2)
+        assert torch.equal(got, base), f"{rows}-row blocks differ from 16-row blocks"
+
+
 # Both block sizes of the head_dim-128 kernel (one or two 16-row groups per
 # wave), with forced splits so that blocks start and end inside pages and
 # tiles; the two must agree with each other to the f16-P rounding.
