@@ -79,8 +79,8 @@ CALIBRATION_BYTES = 1 << 30
 def _probe():
     lib = ctypes.CDLL(os.path.join(ROOT, "decode_attention_kv_04_amd", "libda_probe.so"))
     vp = ctypes.c_void_p
-    lib.da_probe_read_cfg.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, ctypes.c_int, vp]
-    lib.da_probe_read_blocks.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.da_probe_read_stream.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
+    lib.da_probe_read_blocks.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
     lib.da_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     return lib
 
@@ -98,10 +98,11 @@ def measure_ceilings(dev, sptr, stream):
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     perm = torch.randperm(nblk, generator=g, device=dev).to(torch.int32)
-    sink = torch.empty(nblk * 256, dtype=torch.int32, device=dev)
+    per_wg = 128
+    sink = torch.empty(max(1024, -(-nblk // per_wg)) * 256, dtype=torch.int32, device=dev)
     runs = {
-        "stream": lambda: probe.da_probe_read_cfg(buf.data_ptr(), nbytes, sink.data_ptr(), 1024, 1, sptr),
-        "gather4k": lambda: probe.da_probe_read_blocks(buf.data_ptr(), perm.data_ptr(), nblk, 128, 1,
+        "stream": lambda: probe.da_probe_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), 1024, sptr),
+        "gather4k": lambda: probe.da_probe_read_blocks(buf.data_ptr(), perm.data_ptr(), nblk, per_wg,
                                                        sink.data_ptr(), sptr),
     }
     out = {}
