@@ -72,6 +72,17 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // One lane's share of 16 query rows of a wave: the row in column `col` of
 // the MFMA tiles (its q as the B operand of S^T = K Q^T, its keys within the
 // split, its online-softmax state and output dims 16*nb + 4*q4 + i).
+// The scale applied to raw scores in the exponents below, always positive,
+// so that masked keys (raw score -inf) get probability 0 and the largest raw
+// score of a row is its largest scaled score. A negative scale is folded
+// into q instead: negating a 16-bit value flips its sign bit, so the raw
+// score of -q is exactly minus that of q, and scale * s = |scale| * (-s)
+// exactly. A zero scale makes every scaled score 0: q is zeroed (every raw
+// score 0) and the unit scale gives the same scores.
+__device__ __forceinline__ float positive_scale(float sl2) {
+  return sl2 > 0.0f ? sl2 : (sl2 < 0.0f ? -sl2 : 1.0f);
+}
+
 template <int D>
 struct RowGroup {
   uint4 qb[D / 32];
@@ -96,11 +107,17 @@ __device__ __forceinline__ void init_rows(RowGroup<D>& g, const KernelArgs& a, i
   g.lo = g.lo > t_lo ? g.lo : t_lo;
   if (!g.ok) g.hi = g.lo;
   g.qrow = (static_cast<int64_t>(b) * T + t) * a.num_q_heads + kvh * G + gh;
+  // The sign of the scale is folded into q (see positive_scale).
+  const uint32_t qx = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const uint32_t qa = a.scale_log2 == 0.0f ? 0u : 0xFFFFFFFFu;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
     g.qb[ks] = make_uint4(0, 0, 0, 0);
-    if (g.ok)
-      g.qb[ks] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + (g.qrow * D + ks * 32 + q4 * 8) * 2);
+    if (g.ok) {
+      const uint4 v =
+          *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + (g.qrow * D + ks * 32 + q4 * 8) * 2);
+      g.qb[ks] = make_uint4((v.x ^ qx) & qa, (v.y ^ qx) & qa, (v.z ^ qx) & qa, (v.w ^ qx) & qa);
+    }
   }
   g.m = -INFINITY;
   g.lsum = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -221,7 +238,7 @@ __device__ __forceinline__ void tile_update(mq_float4 (&sacc)[NR][2], VOp&& vop,
     float mt = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
-    mt *= sl2;  // = the largest scaled score (the scale is positive)
+    mt *= sl2;  // = the largest scaled score (sl2 > 0, see positive_scale)
     // The reference max moves only when a score exceeds it by more than
     // kSlack (base-2 units): probabilities stay below 2^kSlack, exactly
     // representable in range for f16/bf16 P and fp32 sums, and the rescale
@@ -504,7 +521,7 @@ multi_dma_kernel(const KernelArgs a) {
   const int fv = swz<D>(vkey);
   const int vbc = (col & 3) >> 1;
   const int vh = (col & 1) * 4;
-  const float sl2 = a.scale_log2;
+  const float sl2 = positive_scale(a.scale_log2);
 
   if constexpr (FEW) {
     if (wave != 0) {
