@@ -222,8 +222,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
       constexpr bool FULL = decltype(full_tag)::value;
       const int tb = tile * TR;
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      // The previous tile's operand reads of sh_k come before these writes,
+      // and the writes (rows of four lanes' loads each) before the operand
+      // reads, which gather one slot of 16 rows written by other lanes.
+      wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < NJ; ++j) sh_k[wave][4 * j + r][c ^ (4 * j + r)] = t.k[j];
+      wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         acc = mfma_16x16x32<KVT>(sh_k[wave][key_of_lane][(4 * j + r) ^ key_of_lane], qb[j], acc);

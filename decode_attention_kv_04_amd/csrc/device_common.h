@@ -52,6 +52,18 @@ __device__ __forceinline__ float row_bcast(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders a wave's LDS accesses across its lanes: the LDS writes before this
+// point happen before the reads after it (a lane reading what another lane
+// of the wave wrote), and reads before it before later overwrites. A
+// wavefront-scope release / acquire pair around a wave barrier: the LDS
+// instructions of one wave execute in order, so it emits no wait and only
+// keeps the compiler from moving those accesses across each other.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
