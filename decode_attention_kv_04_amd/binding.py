@@ -16,6 +16,9 @@ _LIB_NAME = "libdecode_attn.so"
 DA_OK, DA_ERR_INVALID, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE, DA_ERR_HIP = range(5)
 DA_F32, DA_F16, DA_BF16 = 0, 1, 2
 DTYPE_CODES = {"f32": DA_F32, "f16": DA_F16, "bf16": DA_BF16}
+DA_KERNEL_AUTO, DA_KERNEL_VECTOR, DA_KERNEL_MATRIX = range(3)
+KERNEL_CODES = {None: DA_KERNEL_AUTO, "auto": DA_KERNEL_AUTO, "vector": DA_KERNEL_VECTOR,
+                "matrix": DA_KERNEL_MATRIX}
 
 # Every symbol include/decode_attn.h declares.
 EXPORTS = (
@@ -38,6 +41,7 @@ class Params(ctypes.Structure):
         ("window", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q_dtype", ctypes.c_int), ("kv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("num_splits", ctypes.c_int32), ("fixed_chunk", ctypes.c_int32), ("query_len", ctypes.c_int32),
+        ("kernel", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
     ]
 
 
@@ -100,14 +104,16 @@ decode_attn_status_str = status_str
 
 def make_params(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, *, window=0,
                 scale=None, q_dtype="f16", kv_dtype="f16", out_dtype="f16", num_splits=0,
-                fixed_chunk=0, query_len=1) -> Params:
+                fixed_chunk=0, query_len=1, kernel=None, rows_per_block=0) -> Params:
+    """da_params; `kernel` is None / "auto", "vector", "matrix" or a da_kernel code."""
     def code(t):
         return DTYPE_CODES[t] if isinstance(t, str) else int(t)
+    kern = KERNEL_CODES[kernel] if kernel is None or isinstance(kernel, str) else int(kernel)
     return Params(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                   int(max_pages_per_seq), int(window),
                   float(scale if scale is not None else (head_dim ** -0.5 if head_dim > 0 else 1.0)),
                   code(q_dtype), code(kv_dtype), code(out_dtype), int(num_splits), int(fixed_chunk),
-                  int(query_len))
+                  int(query_len), kern, int(rows_per_block))
 
 
 class Plan:
@@ -241,7 +247,7 @@ def decode_attn_append_kv(params: Params, k_new, v_new, page_table, seq_lens, k_
 
 
 def params_for(q, k_pool, page_table, *, window=0, scale=None, out_dtype=None, num_splits=0,
-               fixed_chunk=0) -> Params:
+               fixed_chunk=0, kernel=None, rows_per_block=0) -> Params:
     """da_params from tensor shapes and dtypes; q is [B][H_q][D] (one query
     token per sequence) or [B][T][H_q][D] (T new tokens per sequence)."""
     import torch
@@ -255,7 +261,7 @@ def params_for(q, k_pool, page_table, *, window=0, scale=None, out_dtype=None, n
     return make_params(B, Hq, Hkv, D, P, page_table.shape[1], window=window, scale=scale,
                        q_dtype=names[q.dtype], kv_dtype=names[k_pool.dtype],
                        out_dtype=out_dtype or names[q.dtype], num_splits=num_splits, fixed_chunk=fixed_chunk,
-                       query_len=T)
+                       query_len=T, kernel=kernel, rows_per_block=rows_per_block)
 
 
 def alloc_workspace(plan: Plan, device):

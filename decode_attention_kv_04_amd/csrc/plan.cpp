@@ -14,7 +14,6 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
-#include <cstring>
 #include <new>
 
 namespace da {
@@ -43,16 +42,11 @@ int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
 // 128 on 128- and 512-token suffixes and 5 % on 8..32-token suffixes (GQA 4:
 // 32..128 rows). Blocks of 16 rows or fewer (a few drafted tokens) take 16
 // rows at every head_dim: wave 0 computes them and the other waves only copy
-// (64-row blocks would compute the empty rows on zero q). DECODE_ATTN_MQ_ROWS
-// = 16, 64 or 128 forces one size at head_dim 64 and 128; at head_dim 256
-// blocks are 64 rows, or 16 for 16 rows or fewer.
-int64_t mq_rows(int64_t rows, int32_t head_dim) {
-  const char* s = std::getenv("DECODE_ATTN_MQ_ROWS");
-  if (head_dim <= 128 && s) {
-    if (std::strcmp(s, "16") == 0) return 16;
-    if (std::strcmp(s, "64") == 0) return 64;
-    if (std::strcmp(s, "128") == 0) return 128;
-  }
+// (64-row blocks would compute the empty rows on zero q). At head_dim 256
+// blocks are 64 rows, or 16 for 16 rows or fewer. da_params.rows_per_block
+// (validated by make_plan) forces a size.
+int64_t mq_rows(int64_t rows, int32_t head_dim, int32_t forced) {
+  if (forced > 0) return forced;
   if (rows <= 16) return 16;
   return head_dim <= 128 ? 128 : 64;
 }
@@ -90,17 +84,6 @@ int64_t decode_min_split_tokens(bool matrix_kernel, int64_t max_attended_tokens)
   if (split_min_env(&v)) return v;
   if (matrix_kernel && max_attended_tokens > kDefaultMinSplitTokens) return kMatrixMinSplitTokens;
   return kDefaultMinSplitTokens;
-}
-
-// DECODE_ATTN_KERNEL=vector|matrix forces the single-query split kernel
-// (when the matrix one supports the parameters); unset or anything else =
-// automatic.
-int32_t forced_kernel() {
-  const char* s = std::getenv("DECODE_ATTN_KERNEL");
-  if (!s) return -1;
-  if (std::strcmp(s, "vector") == 0) return 0;
-  if (std::strcmp(s, "matrix") == 0) return 1;
-  return -1;
 }
 
 bool log_enabled() {
@@ -229,7 +212,7 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
   const int64_t G = plan->group;
   const int64_t R = T * G;
   // Four waves of 16 rows (or two groups of 16) share each key tile.
-  const int64_t QB = mq_rows(R, p.head_dim);
+  const int64_t QB = mq_rows(R, p.head_dim, p.rows_per_block);
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);
@@ -308,6 +291,10 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     return DA_ERR_INVALID;
   if (num_cus < 1) return DA_ERR_INVALID;
   if (p->batch > 0 && (!lens || p->max_pages_per_seq < 1)) return DA_ERR_INVALID;
+  if (p->kernel != DA_KERNEL_AUTO && p->kernel != DA_KERNEL_VECTOR && p->kernel != DA_KERNEL_MATRIX)
+    return DA_ERR_INVALID;
+  if (p->rows_per_block != 0 && p->rows_per_block != 16 && p->rows_per_block != 64 && p->rows_per_block != 128)
+    return DA_ERR_INVALID;
 
   const int32_t G = p->num_q_heads / p->num_kv_heads;
   const int32_t gt = group_tile_for(G);
@@ -331,7 +318,10 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // bf16; otherwise (or with DECODE_ATTN_KERNEL=vector) the single-query
   // kernels once per token.
   const bool multi_dtypes = p->q_dtype == p->kv_dtype && (p->kv_dtype == DA_F16 || p->kv_dtype == DA_BF16);
-  const bool per_token = T > 1 && (!multi_dtypes || forced_kernel() == 0);
+  const bool per_token = T > 1 && (!multi_dtypes || p->kernel == DA_KERNEL_VECTOR);
+  if (T > 1 && p->kernel == DA_KERNEL_MATRIX && !multi_dtypes) return DA_ERR_UNSUPPORTED;
+  if (T <= 1 && p->kernel == DA_KERNEL_MATRIX && !matrix_kernel_supported(*p)) return DA_ERR_UNSUPPORTED;
+  if (T > 1 && !per_token && p->rows_per_block == 128 && p->head_dim > 128) return DA_ERR_UNSUPPORTED;
   if (T > 1) {
     if (fixed) return DA_ERR_UNSUPPORTED;
     // T is the combine grid's y extent; T * G rows are counted in int32.
@@ -379,10 +369,10 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // 6.2 M attended key-heads, 0.99-1.01 at 0.8-1.5 M, 1.02-1.03 at 0.26-0.39 M;
   // G 2 0.997-0.998 over 6.2 M, 1.00-1.01 over 1.5 M, 1.01-1.02 at 0.79 M,
   // 1.08-1.10 at 0.26-0.39 M.
-  {
-    const int32_t fk = forced_kernel();
-    plan->split_kernel = matrix_kernel_supported(*p) && fk != 0 && (fk == 1 || G >= 2) ? 1 : 0;
-  }
+  plan->split_kernel = matrix_kernel_supported(*p) && p->kernel != DA_KERNEL_VECTOR &&
+                               (p->kernel == DA_KERNEL_MATRIX || G >= 2)
+                           ? 1
+                           : 0;
 
   if (plan->query_len > 1 && !per_token) {
     const da_status st = finish_multi_plan(plan, lens);

@@ -18,25 +18,29 @@
  * fixed-order mode makes the output bitwise independent of the split count,
  * and decode_attn_append_kv writes new K/V rows into the pages.
  *
- * Passages this follows:
+ * Where the operations come from (each declaration below cites its own
+ * passage as well; pages are cited by title and section):
  *   - TVM pull 20426 "webgpu-decode-attention", commit message of the sharded
- *     nest: paged decode attention whose context is cut into shards, each
- *     producing an online-softmax state that a merge step combines; the host
- *     picks the path from the page count. Its PR description: a sequence-
- *     sharded kernel selected above 256 tokens; sliding windows.
- *   - mlx-runner pull 3, commit message "GQA-shared split attention" and PR
- *     description "Changes": a split kernel in which each group covers all
- *     query heads of its GQA group, so each K/V row is read once per group,
- *     writing per-split partials that a combine kernel merges; the split
- *     threshold is a knob (default 256 tokens).
+ *     nest: decode attention over a paged cache in which the context is cut
+ *     into shards, each shard summarised by an online-softmax state, the
+ *     states then merged; the host chooses between the paths from the page
+ *     count. PR description: the sharded path takes over above 256 tokens,
+ *     and sliding windows are among its tested cases.
+ *   - mlx-runner pull 3, commit "GQA-shared split attention" and PR
+ *     description "Changes": one work-group serves every query head that
+ *     shares a KV head, so K/V is streamed once per GQA group rather than
+ *     once per query head; the split pass writes partial states and a
+ *     separate combine pass merges them in a fixed order; the token count at
+ *     which splitting starts is a tunable (256 by default). Its split decode
+ *     attention test: with one fixed merge order the split and unsplit paths
+ *     give identical bits.
  *   - llm-web pull 8, commits on build-time constants and on pipeline
- *     creation errors: head_dim / dtype / window fixed per pipeline before
- *     launch; errors surface at creation and the caller picks a fallback.
- *     Its commit on the batched suffix prefill: new tokens' K/V scattered
- *     after the resident prefix, attention of several new tokens over the
- *     cache.
- *   - mlx-runner pull 3, split decode attention test: split and unsplit
- *     paths agree bit for bit when the partials merge in one fixed order.
+ *     creation errors: head_dim, dtype and window are fixed per pipeline
+ *     before any launch; a rejected configuration is reported to the caller
+ *     at creation, and the caller chooses the fallback. Its commit on the
+ *     batched suffix prefill: new tokens' K/V are written behind the
+ *     resident prefix and several new tokens attend the cache together. Its
+ *     commit on engine ownership: the owner releases what it created.
  *
  * Conventions
  *   - Pointers are device pointers unless their name starts with host_.
@@ -79,6 +83,13 @@ typedef enum {
 
 typedef enum { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
 
+/* Which single-query split kernel a plan uses (da_params.kernel). */
+typedef enum {
+  DA_KERNEL_AUTO = 0,   /* the planner chooses (matrix cores from 2 query heads per KV head on) */
+  DA_KERNEL_VECTOR = 1, /* vector q.K; with query_len > 1: the single-query kernels per token   */
+  DA_KERNEL_MATRIX = 2  /* q.K on the matrix cores; DA_ERR_UNSUPPORTED where not built           */
+} da_kernel;
+
 typedef struct {
   int32_t batch;             /* B >= 0                                              */
   int32_t num_q_heads;       /* H_q >= 1                                            */
@@ -116,9 +127,26 @@ typedef struct {
                                 and fixed_chunk == 0. q and K/V sharing f16 or
                                 bf16 run the multi-token kernels (both products
                                 on the matrix cores); other dtype combinations
-                                (or DECODE_ATTN_KERNEL=vector) run the
+                                (or kernel = DA_KERNEL_VECTOR) run the
                                 single-query kernels once per token (meant for
                                 a few tokens).                                 */
+  int32_t kernel;            /* da_kernel: DA_KERNEL_AUTO (0) unless a caller
+                                wants one split kernel (benchmarks, tests).
+                                Decode: DA_KERNEL_MATRIX needs q and K/V
+                                sharing f16 or bf16, head_dim 128 and page_size
+                                a multiple of 16. query_len > 1:
+                                DA_KERNEL_MATRIX = the multi-token kernels
+                                (needs q and K/V sharing f16 or bf16),
+                                DA_KERNEL_VECTOR = the single-query kernels
+                                once per token. DA_ERR_UNSUPPORTED where the
+                                choice is not built; other values
+                                DA_ERR_INVALID.                                 */
+  int32_t rows_per_block;    /* query_len > 1 on the multi-token kernels: the
+                                (token, head) rows of a KV head per work-group.
+                                0 = the planner chooses; 16, 64, or 128 (128
+                                only at head_dim 64 and 128, else
+                                DA_ERR_UNSUPPORTED); other values are
+                                DA_ERR_INVALID. Ignored for query_len <= 1.     */
 } da_params;
 
 typedef struct da_plan* da_plan_t;
@@ -135,17 +163,16 @@ typedef struct {
   int32_t split_kernel;      /* 0 = vector q.K (any parameters); 1 = q.K on the
                                 matrix cores (q and K/V share f16 or bf16,
                                 head_dim 128, page size a multiple of 16, at
-                                least two query heads per KV head).
-                                DECODE_ATTN_KERNEL=vector|matrix forces 0 or 1
-                                where supported. 2 = the
+                                least two query heads per KV head);
+                                da_params.kernel forces 0 or 1. 2 = the
                                 multi-token kernels (query_len > 1; q.K and P.V
                                 on the matrix cores): the T*G rows of a KV head
                                 in blocks of 16 (16 rows or fewer: one wave
                                 computes, three copy), 128 (more rows at head_dim
                                 64 and 128) or 64 (more rows at head_dim 256);
-                                DECODE_ATTN_MQ_ROWS=16, 64 or 128 forces one at
-                                head_dim 64 and 128. A query_len > 1 plan with
-                                0 runs the vector kernel once per token.       */
+                                da_params.rows_per_block forces one. A
+                                query_len > 1 plan with 0 runs the vector
+                                kernel once per token.                        */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in
@@ -158,6 +185,14 @@ typedef struct {
  * lengths and the device's compute-unit count), and size the workspace. Host
  * only: no device work, no allocation on the device. `device` is a HIP device
  * ordinal; its compute-unit count is read once and cached.
+ * Follows: TVM pull 20426, commit message of the sharded nest (the host picks
+ * the path from the page count) and PR description (sharding only above 256
+ * tokens); mlx-runner pull 3, commit "GQA-shared split attention" (the split
+ * threshold is a tunable with a 256-token default; here it is the shortest
+ * split, and the environment variable DECODE_ATTN_SPLIT_MIN overrides it);
+ * llm-web pull 8, commits on build-time constants (head_dim, dtype and
+ * window fixed before launch) and on pipeline creation errors (every
+ * rejection is reported here, before any launch).
  *   host_seq_lens  [B] int32 host array (may be NULL when B = 0); values in
  *                  0 .. max_pages_per_seq * P.
  *   plan_out       receives a new plan on DA_OK (unchanged otherwise).
@@ -176,10 +211,14 @@ da_status decode_attn_plan(const da_params* p, const int32_t* host_seq_lens, int
 da_status decode_attn_plan_for_cus(const da_params* p, const int32_t* host_seq_lens, int32_t num_cus,
                                    da_plan_t* plan_out, size_t* workspace_bytes_out);
 
-/* decode_attn_plan_info: copy a plan's decisions into *info. */
+/* decode_attn_plan_info: copy a plan's decisions into *info. Follows: TVM
+ * pull 20426, commit message of the sharded nest (which path the host chose
+ * from the page count) - exposed so callers and benchmarks can see it. */
 da_status decode_attn_plan_info(da_plan_t plan, da_plan_info* info);
 
-/* decode_attn_plan_splits: number of splits of sequence b (1 .. max_splits). */
+/* decode_attn_plan_splits: number of splits of sequence b (1 .. max_splits);
+ * 0 for a NULL plan or b outside 0 .. B-1. Follows: TVM pull 20426, commit
+ * message of the sharded nest (the shards a sequence's context is cut into). */
 int32_t decode_attn_plan_splits(da_plan_t plan, int32_t b);
 
 /*
@@ -187,6 +226,11 @@ int32_t decode_attn_plan_splits(da_plan_t plan, int32_t b);
  * hipStream_t; NULL = the null stream): the split pass, then, if the plan has
  * more than one split, the combine pass. Returns after enqueueing; no host
  * synchronisation and no allocation, so it can be captured in a HIP graph.
+ * Follows: TVM pull 20426, commit message of the sharded nest (shards of the
+ * paged context, one online-softmax state each, merged in a second phase) and
+ * PR description (sliding windows); mlx-runner pull 3, commit "GQA-shared
+ * split attention" (K/V read once per GQA group; split partials merged by a
+ * combine kernel).
  *   q, k_pool, v_pool, page_table, seq_lens   read-only inputs (layouts above).
  *   seq_lens   must hold the same lengths the plan was made from.
  *   out        [B][H_q][D] out_dtype, fully written.
@@ -206,6 +250,9 @@ da_status decode_attn_run(da_plan_t plan, const void* q, const void* k_pool, con
  * every sequence writes its online-softmax state (running max m, sum l,
  * unnormalised O) to the workspace; sequences with a single split write their
  * final output rows directly. Same arguments and checks as decode_attn_run.
+ * Follows: TVM pull 20426, commit message of the sharded nest (the per-shard
+ * online-softmax states); mlx-runner pull 3, commit "GQA-shared split
+ * attention" (the split kernel writing per-split partials).
  */
 da_status decode_attn_split(da_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
                             const int32_t* page_table, const int32_t* seq_lens, void* out,
@@ -215,7 +262,12 @@ da_status decode_attn_split(da_plan_t plan, const void* q, const void* k_pool, c
  * decode_attn_combine: the second pass alone. Merges the split states that a
  * preceding decode_attn_split (same plan, same seq_lens, same workspace) left
  * in the workspace into the output rows of sequences with more than one split.
- * Enqueues nothing when the plan has a single split.
+ * Enqueues nothing when the plan has a single split. Same status codes as
+ * decode_attn_run (seq_lens and out are checked; q and the pools are not
+ * used).
+ * Follows: TVM pull 20426, commit message of the sharded nest (the merge of
+ * the shard states); mlx-runner pull 3, commit "GQA-shared split attention"
+ * (a combine kernel merging the partials in one fixed order).
  */
 da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out, void* workspace,
                               size_t workspace_bytes, void* stream);
@@ -242,10 +294,15 @@ da_status decode_attn_append_kv(const da_params* p, int32_t tokens, const void* 
                                 const int32_t* page_table, const int32_t* seq_lens, void* k_pool, void* v_pool,
                                 void* stream);
 
-/* decode_attn_plan_destroy: free a plan (NULL is ignored). */
+/* decode_attn_plan_destroy: free a plan (NULL is ignored); the plan must not
+ * be used afterwards. Follows: llm-web pull 8, commit on engine ownership
+ * (the owner of an object releases it explicitly, at once). */
 void decode_attn_plan_destroy(da_plan_t plan);
 
-/* decode_attn_status_str: static text for a status code. */
+/* decode_attn_status_str: static text for a status code (never NULL; an
+ * unknown code gets a fixed "unknown" text). Follows: llm-web pull 8, commit
+ * on pipeline creation errors (failures are reported to the caller, which
+ * chooses what to do). */
 const char* decode_attn_status_str(da_status s);
 
 #ifdef __cplusplus

@@ -119,7 +119,6 @@ def test_matrix_kernel_splits_down_to_128_tokens(lib, monkeypatch):
     # the matrix-core kernel (f16, head_dim 128, G 4) over one 3060-token
     # context: splits of 128 tokens (8 pages); the vector kernel keeps 256
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
-    monkeypatch.delenv("DECODE_ATTN_KERNEL", raising=False)
     pl = plan(params(), [3060])
     assert pl.info.split_kernel == 1 and pl.pages_per_split == 8 and pl.max_splits == 24
     pl = plan(params(head_dim=64), [3060])
@@ -152,8 +151,7 @@ def test_split_min_env_override(lib, monkeypatch):
     assert pl.pages_per_split >= 4 and pl.max_splits > 1
 
 
-def test_split_kernel_selection(lib, monkeypatch):
-    monkeypatch.delenv("DECODE_ATTN_KERNEL", raising=False)
+def test_split_kernel_selection(lib):
     assert plan(params(), [3060]).info.split_kernel == 1                       # f16, D 128, P 16
     assert plan(params(q_dtype="bf16", kv_dtype="bf16"), [3060]).info.split_kernel == 1
     assert plan(params(page_size=32, max_pages_per_seq=1024), [3060]).info.split_kernel == 1
@@ -163,26 +161,27 @@ def test_split_kernel_selection(lib, monkeypatch):
     assert plan(params(head_dim=256), [3060]).info.split_kernel == 0
     assert plan(params(page_size=8, max_pages_per_seq=4096), [3060]).info.split_kernel == 0
     assert plan(params(page_size=24, max_pages_per_seq=4096), [3060]).info.split_kernel == 0
-    monkeypatch.setenv("DECODE_ATTN_KERNEL", "vector")
-    assert plan(params(), [3060]).info.split_kernel == 0
-    monkeypatch.setenv("DECODE_ATTN_KERNEL", "matrix")
-    assert plan(params(), [3060]).info.split_kernel == 1
-    assert plan(params(head_dim=64), [3060]).info.split_kernel == 0             # unsupported: vector
+    assert plan(params(kernel="vector"), [3060]).info.split_kernel == 0
+    assert plan(params(kernel="matrix"), [3060]).info.split_kernel == 1
+    assert plan(params(kernel="auto"), [3060]).info.split_kernel == 1
+    # the matrix-core kernel where it is not built: reported, not replaced
+    for kw in (dict(head_dim=64), dict(q_dtype="f32"), dict(page_size=8, max_pages_per_seq=4096)):
+        assert status_of(params(kernel="matrix", **kw), [3060]) == B.DA_ERR_UNSUPPORTED
+    for bad in (3, -1, 99):
+        assert status_of(params(kernel=bad), [3060]) == B.DA_ERR_INVALID
 
 
 # One query head per group (q.K a dot product per key) takes the vector
 # kernel; two or more take the matrix-core kernel where it is supported,
 # whatever the size of the launch, the split count or the fixed-order chunk.
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
-def test_split_kernel_by_group(lib, monkeypatch, G):
-    monkeypatch.delenv("DECODE_ATTN_KERNEL", raising=False)
+def test_split_kernel_by_group(lib, G):
     want = 0 if G == 1 else 1
     for lens in ([32768] * 32, [3060] * 2, [1]):
         assert plan(params(batch=len(lens), num_q_heads=8 * G), lens).info.split_kernel == want
     for kw in (dict(num_splits=1), dict(num_splits=7), dict(fixed_chunk=1024), dict(fixed_chunk=1024, num_splits=3)):
         assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == want
-    monkeypatch.setenv("DECODE_ATTN_KERNEL", "matrix")
-    assert plan(params(batch=32, num_q_heads=8 * G), [32768] * 32).info.split_kernel == 1
+    assert plan(params(batch=32, num_q_heads=8 * G, kernel="matrix"), [32768] * 32).info.split_kernel == 1
 
 
 # ---------------------------------------------------------------------------
@@ -274,10 +273,21 @@ def test_multi_token_rows_per_block(lib, T, G, D, rows):
 
 
 @pytest.mark.parametrize("rows", ["16", "64", "128"])
-def test_multi_token_rows_env_override(lib, monkeypatch, rows):
-    monkeypatch.setenv("DECODE_ATTN_MQ_ROWS", rows)
-    pl = plan(params(batch=1, query_len=40, num_splits=1), [5000])    # 160 rows at head_dim 128
+def test_multi_token_rows_per_block_forced(lib, rows):
+    pl = plan(params(batch=1, query_len=40, num_splits=1, rows_per_block=int(rows)), [5000])  # 160 rows, D 128
     assert pl.info.split_work_groups == 8 * math.ceil(160 / int(rows))
+
+
+def test_multi_token_rows_per_block_rejects(lib):
+    assert status_of(params(batch=1, query_len=40, rows_per_block=32), [5000]) == B.DA_ERR_INVALID
+    assert status_of(params(batch=1, query_len=40, rows_per_block=-16), [5000]) == B.DA_ERR_INVALID
+    # 128-row blocks are built at head_dim 64 and 128 only
+    assert status_of(params(batch=1, query_len=40, head_dim=256, rows_per_block=128), [5000]) == \
+        B.DA_ERR_UNSUPPORTED
+    pl = plan(params(batch=1, query_len=40, head_dim=256, rows_per_block=16, num_splits=1), [5000])
+    assert pl.info.split_work_groups == 8 * 10
+    # ignored by decode plans
+    assert plan(params(rows_per_block=64), [3060]).info.split_kernel == 1
 
 
 # A few drafted tokens over long contexts: the keys of each (sequence, KV
@@ -334,11 +344,13 @@ def test_per_token_splits_cover_every_token(lib, L, T, W, P, ns):
     assert pl.max_splits >= pl.splits(0)
 
 
-def test_forced_vector_runs_multi_token_per_token(lib, monkeypatch):
-    monkeypatch.setenv("DECODE_ATTN_KERNEL", "vector")
-    assert plan(params(batch=1, query_len=4), [100]).info.split_kernel == 0
-    monkeypatch.delenv("DECODE_ATTN_KERNEL")
+def test_forced_kernels_with_several_tokens(lib):
+    assert plan(params(batch=1, query_len=4, kernel="vector"), [100]).info.split_kernel == 0   # per token
     assert plan(params(batch=1, query_len=4), [100]).info.split_kernel == 2
+    assert plan(params(batch=1, query_len=4, kernel="matrix"), [100]).info.split_kernel == 2
+    assert plan(params(batch=1, query_len=4, kernel="matrix", head_dim=64), [100]).info.split_kernel == 2
+    # the multi-token kernels need q and K/V sharing a 16-bit type
+    assert status_of(params(batch=1, query_len=4, kernel="matrix", q_dtype="f32"), [100]) == B.DA_ERR_UNSUPPORTED
 
 
 def test_query_len_zero_and_one_are_decode(lib):
