@@ -243,12 +243,19 @@ def make_workload(spec: WorkloadSpec, device="cpu", lengths: Optional[Sequence[i
                     window=window, num_pages=num_pages, poison_page=poison)
 
 
-def to_numpy_inputs(w: Workload, rows: Optional[Sequence[int]] = None) -> dict:
+def to_numpy_inputs(w: Workload, rows: Optional[Sequence[int]] = None, attended_only: bool = False) -> dict:
     """Host copies of a workload (or of the sequences in ``rows``) as numpy
     arrays holding the stored values exactly (bf16 is widened to float32,
     which is exact). For a subset, only the pages those rows reference are
     copied and the page table is renumbered to the compact pool; the poison
-    page is kept and unused entries point at it."""
+    page is kept and unused entries point at it.
+
+    ``attended_only``: copy only the pages that hold keys some query attends
+    (from each sequence's first attended page on); table entries before
+    them point at the poison page (NaN, like the pages they replace). Only
+    a layout choice: the values of every attended key are the same."""
+    if attended_only and rows is None:
+        rows = range(w.spec.batch)
     import numpy as np
 
     def host(t: torch.Tensor) -> "np.ndarray":
@@ -265,9 +272,14 @@ def to_numpy_inputs(w: Workload, rows: Optional[Sequence[int]] = None) -> dict:
                     page_size=P, scale=w.scale, window=w.window)
     rows = list(rows)
     table = w.page_table.cpu()
+    T = w.spec.query_len
+
+    def first_page(b):
+        return first_attended(lens[b], T, w.window) // P if attended_only and lens[b] > 0 else 0
+
     used = []
     for b in rows:
-        used.extend(table[b, :(lens[b] + P - 1) // P].tolist())
+        used.extend(table[b, first_page(b):(lens[b] + P - 1) // P].tolist())
     used.append(w.poison_page)
     idx = torch.tensor(used, dtype=torch.long, device=w.k_pool.device)
     remap = {p: i for i, p in enumerate(used)}
@@ -275,7 +287,8 @@ def to_numpy_inputs(w: Workload, rows: Optional[Sequence[int]] = None) -> dict:
     new_table = np.full((len(rows), table.shape[1]), poison_new, dtype=np.int64)
     for r, b in enumerate(rows):
         n = (lens[b] + P - 1) // P
-        new_table[r, :n] = [remap[p] for p in table[b, :n].tolist()]
+        f = first_page(b)
+        new_table[r, f:n] = [remap[p] for p in table[b, f:n].tolist()]
     return dict(q=host(w.q[torch.tensor(rows, device=w.q.device)]),
                 k_pool=host(w.k_pool[idx]), v_pool=host(w.v_pool[idx]),
                 page_table=new_table, seq_lens=np.array([lens[b] for b in rows], dtype=np.int64),

@@ -1,7 +1,5 @@
 """Helpers shared by the GPU tests: run the library on a workload and compare
 with the oracle."""
-import contextlib
-import os
 import sys
 
 import numpy as np
@@ -12,52 +10,27 @@ from decode_attention_kv_04_amd import binding, workloads
 
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 KV_TOL = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
+SIXTEEN_BIT = ("f16", "bf16")
 
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-@contextlib.contextmanager
-def split_kernel(kind):
-    """kind: None / "auto" (the planner chooses) or "vector" / "matrix"."""
-    old = os.environ.get("DECODE_ATTN_KERNEL")
-    if kind and kind != "auto":
-        os.environ["DECODE_ATTN_KERNEL"] = kind
-    else:
-        os.environ.pop("DECODE_ATTN_KERNEL", None)
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("DECODE_ATTN_KERNEL", None)
-        else:
-            os.environ["DECODE_ATTN_KERNEL"] = old
-
-
-@contextlib.contextmanager
-def mq_rows(rows):
-    """Rows per block of the head_dim-128 multi-token kernel ("64" / "128"; None = default)."""
-    old = os.environ.get("DECODE_ATTN_MQ_ROWS")
-    if rows:
-        os.environ["DECODE_ATTN_MQ_ROWS"] = str(rows)
-    else:
-        os.environ.pop("DECODE_ATTN_MQ_ROWS", None)
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("DECODE_ATTN_MQ_ROWS", None)
-        else:
-            os.environ["DECODE_ATTN_MQ_ROWS"] = old
-
-
 def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None, page_table=None,
-            window=None, seq_lens=None, seq_lens_host=None, two_phase=False, kernel=None, fixed_chunk=0):
+            window=None, seq_lens=None, seq_lens_host=None, two_phase=False, kernel=None, fixed_chunk=0,
+            rows_per_block=0, twin=True):
     """One decode_attn_run (or split + combine) on the workload's tensors;
     returns (out tensor, plan). The output starts as NaN so unwritten rows show.
-    `kernel` = "vector" forces the vector split kernel; default: automatic.
-    `fixed_chunk` > 0 selects the fixed-order mode with chunks of that many tokens."""
+    `kernel` = "vector" / "matrix" forces a split kernel (da_params.kernel);
+    `fixed_chunk` > 0 selects the fixed-order mode with chunks of that many
+    tokens; `rows_per_block` forces the multi-token block size.
+
+    For a 16-bit output the same step also runs with an fp32 output (the same
+    plan otherwise: the output dtype changes nothing but the final rounding),
+    and that fp32 twin is attached to the returned tensor as `f32_twin`, so
+    that `check` can pin the rounding bitwise and hold the unrounded result
+    to the KV-dtype bound."""
     q = w.q if q is None else q
     k_pool = w.k_pool if k_pool is None else k_pool
     v_pool = w.v_pool if v_pool is None else v_pool
@@ -66,20 +39,31 @@ def run_lib(w, *, num_splits=0, out_dtype=None, q=None, k_pool=None, v_pool=None
     seq_lens_host = w.seq_lens_host if seq_lens_host is None else seq_lens_host
     window = w.window if window is None else window
     out_dtype = out_dtype or w.spec.out_dtype
-    params = binding.params_for(q, k_pool, page_table, window=window, scale=w.scale, out_dtype=out_dtype,
-                                num_splits=num_splits, fixed_chunk=fixed_chunk)
-    with split_kernel(kernel):
+
+    def one(dt):
+        params = binding.params_for(q, k_pool, page_table, window=window, scale=w.scale, out_dtype=dt,
+                                    num_splits=num_splits, fixed_chunk=fixed_chunk, kernel=kernel,
+                                    rows_per_block=rows_per_block)
         plan = binding.decode_attn_plan(params, seq_lens_host, device=q.device.index)
-    out = torch.full(q.shape, float("nan"), dtype=TORCH_DT[out_dtype], device=q.device)
-    ws = binding.alloc_workspace(plan, q.device)
-    if ws is not None:
-        ws.fill_(0xFF)  # NaN bit patterns: stale state would show
-    if two_phase:
-        binding.decode_attn_split(plan, q, k_pool, v_pool, page_table, seq_lens, out, ws)
-        binding.decode_attn_combine(plan, seq_lens, out, ws)
-    else:
-        binding.decode_attn_run(plan, q, k_pool, v_pool, page_table, seq_lens, out, ws)
-    torch.cuda.synchronize()
+        out = torch.full(q.shape, float("nan"), dtype=TORCH_DT[dt], device=q.device)
+        ws = binding.alloc_workspace(plan, q.device)
+        if ws is not None:
+            ws.fill_(0xFF)  # NaN bit patterns: stale state would show
+        if two_phase:
+            binding.decode_attn_split(plan, q, k_pool, v_pool, page_table, seq_lens, out, ws)
+            binding.decode_attn_combine(plan, seq_lens, out, ws)
+        else:
+            binding.decode_attn_run(plan, q, k_pool, v_pool, page_table, seq_lens, out, ws)
+        torch.cuda.synchronize()
+        return out, plan
+
+    out, plan = one(out_dtype)
+    if twin and out_dtype in SIXTEEN_BIT:
+        f32, plan32 = one("f32")
+        for field in ("pages_per_split", "max_splits", "split_kernel", "chunks_per_work_group",
+                      "split_work_groups"):
+            assert getattr(plan.info, field) == getattr(plan32.info, field), f"fp32-output plan differs in {field}"
+        out.f32_twin = f32
     return out, plan
 
 
@@ -87,8 +71,8 @@ def host64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def oracle_for(w, rows=None):
-    a = workloads.to_numpy_inputs(w, rows)
+def oracle_for(w, rows=None, attended_only=False):
+    a = workloads.to_numpy_inputs(w, rows, attended_only=attended_only)
     fn = oracle.prefill_attention if a["q"].ndim == 4 else oracle.decode_attention
     return fn(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"], a["page_size"], a["scale"],
               a["window"])
@@ -97,27 +81,65 @@ def oracle_for(w, rows=None):
 BF16_ROUNDING = 2.0 ** -8  # largest relative error of rounding to bf16 (half a step at 8 significant bits)
 
 
-def check(got, ref, kv_dtype, out_dtype, label=""):
-    """Relative L2 over the whole output and per sequence, within the bound
+def per_head_l2(got, ref):
+    """Relative L2 of every (sequence, [token,] query head) row of D values."""
+    D = ref.shape[-1]
+    g = np.asarray(got, dtype=np.float64).reshape(-1, D)
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, D)
+    num = np.sqrt(np.sum((g - r) ** 2, axis=1))
+    den = np.sqrt(np.sum(r * r, axis=1))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
+    return rel
+
+
+def _accuracy(got, ref, tol, label):
+    err = oracle.relative_l2(got, ref)
+    seqs = oracle.relative_l2_per_row(got, ref)
+    worst_seq = max(seqs) if seqs else 0.0
+    heads = per_head_l2(got, ref)
+    worst_head = float(heads.max()) if heads.size else 0.0
+    assert err <= tol, f"{label}: relative L2 {err:.3e} > {tol:g}"
+    assert worst_seq <= tol, f"{label}: worst per-sequence relative L2 {worst_seq:.3e} > {tol:g}"
+    assert worst_head <= tol, (f"{label}: worst per-head relative L2 {worst_head:.3e} > {tol:g} "
+                               f"(row {int(heads.argmax())} of {heads.size})")
+    return err, worst_seq, worst_head
+
+
+def check(got, ref, kv_dtype, out_dtype, label="", twin=None):
+    """Hold the output to the oracle: relative L2 over the whole output, per
+    sequence and per (sequence, [token,] query head) row, within the bound
     for the KV dtype (1e-5 fp32, 1e-3 fp16/bf16, fp32 accumulation).
 
-    A bf16 output cannot meet that bar (its own rounding is ~1.6e-3 relative
-    L2), and against the bf16-rounded oracle any tiny difference next to a
-    rounding boundary becomes a whole bf16 step (near-zero elements included).
-    It is held to the bound that follows from the arithmetic: the rounding
-    adds at most 2^-8 of each element, so the relative L2 against the exact
-    oracle is at most the KV bound plus 2^-8. (The same computation at fp32
-    output, in the same suites, is held to the KV bound itself.)"""
-    got = host64(got) if isinstance(got, torch.Tensor) else got
+    A 16-bit output is checked through its fp32 twin (the same step with an
+    fp32 output; `twin`, or the `f32_twin` that run_lib attaches): the 16-bit
+    values must equal the twin rounded to nearest even (the oracle's
+    round_to), bit for bit, and the twin is held to the KV bound. The 16-bit
+    values themselves are also held to the bound that follows from one
+    rounding: fp16 rounding adds at most 2^-11 of each element (under the
+    1e-3 bar; fp32 KV with fp16 output is held to 1e-3), bf16 rounding at
+    most 2^-8 (KV bound plus 2^-8). Returns (global, worst sequence, worst
+    head) relative L2 of the output as stored."""
+    if twin is None:
+        twin = getattr(got, "f32_twin", None)
+    got = host64(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
     tol = KV_TOL[kv_dtype]
-    if out_dtype == "f16" and kv_dtype == "f32":
-        tol = 1e-3  # fp16 output rounding alone is ~2e-4
-    if out_dtype == "bf16":
-        tol = tol + BF16_ROUNDING
-    err = oracle.relative_l2(got, ref)
-    rows = oracle.relative_l2_per_row(got, ref)
-    worst = max(rows) if rows else 0.0
-    assert err <= tol, f"{label}: relative L2 {err:.3e} > {tol:g}"
-    assert worst <= tol, f"{label}: worst per-sequence relative L2 {worst:.3e} > {tol:g}"
+    if out_dtype in SIXTEEN_BIT:
+        assert twin is not None, f"{label}: a {out_dtype} output needs its fp32 twin"
+        t64 = host64(twin) if isinstance(twin, torch.Tensor) else np.asarray(twin, dtype=np.float64)
+        assert np.all(np.isfinite(t64)), f"{label}: non-finite fp32 twin"
+        rounded = oracle.round_to(t64, out_dtype)
+        bad = rounded != got
+        assert not bad.any(), (f"{label}: {int(bad.sum())} {out_dtype} outputs differ from the rounded fp32 twin "
+                               f"(first at flat index {int(np.flatnonzero(bad)[0])})")
+        _accuracy(t64, ref, tol, f"{label} (fp32 twin)")
+        stored_tol = tol
+        if out_dtype == "f16" and kv_dtype == "f32":
+            stored_tol = 1e-3
+        if out_dtype == "bf16":
+            stored_tol = tol + BF16_ROUNDING
+        err, worst, head = _accuracy(got, ref, stored_tol, label)
+    else:
+        err, worst, head = _accuracy(got, ref, tol, label)
     return err, worst

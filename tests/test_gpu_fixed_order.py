@@ -38,23 +38,19 @@ def test_named_workloads_bitwise_across_splits(gpu, name, chunk, kernel):
     check(out, oracle_for(w), spec.kv_dtype, spec.out_dtype, f"{name} fixed {chunk}")
 
 
-def test_mixed_window_full_size_bitwise_across_splits(gpu):
-    spec = wl.MIXED_WINDOW
-    say(f"[fixed-order] {spec.name} full size")
-    w = wl.make_workload(spec, gpu)
+def test_mixed_window_full_size_bitwise_across_splits(gpu, mixed_window):
+    w, ref = mixed_window
+    say(f"[fixed-order] {w.spec.name} full size")
     out = all_split_counts_agree(w, 1024, splits=[1, 4, 0, 1_000_000])
-    rows = [0, 5, 17, 40, 63]
-    check(out[rows], oracle_for(w, rows), spec.kv_dtype, spec.out_dtype, "mixed_window fixed")
+    check(out, ref, w.spec.kv_dtype, w.spec.out_dtype, "mixed_window fixed")
 
 
 @pytest.mark.parametrize("kernel", ["auto", "vector"])
-def test_long_batch_full_size_bitwise_across_splits(gpu, kernel):
-    spec = wl.LONG_BATCH
-    say(f"[fixed-order] {spec.name} full size kernel={kernel}")
-    w = wl.make_workload(spec, gpu)
+def test_long_batch_full_size_bitwise_across_splits(gpu, long_batch, kernel):
+    w, ref = long_batch
+    say(f"[fixed-order] {w.spec.name} full size kernel={kernel}")
     out = all_split_counts_agree(w, 1024, splits=[0, 1, 5, 1_000_000], kernel=kernel)
-    rows = [0, 13, 31]
-    check(out[rows], oracle_for(w, rows), spec.kv_dtype, spec.out_dtype, "long_batch fixed")
+    check(out, ref, w.spec.kv_dtype, w.spec.out_dtype, "long_batch fixed")
 
 
 GRID = [

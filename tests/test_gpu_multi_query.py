@@ -7,7 +7,7 @@ import torch
 import oracle
 from decode_attention_kv_04_amd import workloads as wl
 
-from gpu_util import TORCH_DT, check, host64, mq_rows, oracle_for, run_lib, say
+from gpu_util import TORCH_DT, check, host64, oracle_for, run_lib, say
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +62,7 @@ def test_forced_block_shapes_match_oracle(gpu, rows, T, G, D, kv, out, P, lens, 
     spec = spec_of(T, G, D, kv, out, P, lens, W)
     say(f"[multi] {spec.name} rows={rows}")
     w = wl.make_workload(spec, gpu)
-    with mq_rows(rows):
-        got, plan = run_lib(w, num_splits=2)
+    got, plan = run_lib(w, num_splits=2, rows_per_block=int(rows))
     assert plan.info.split_kernel == 2
     err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} rows {rows}")
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
@@ -80,8 +79,7 @@ def test_few_row_blocks_equal_wider_blocks_bitwise(gpu, T, G, D, kv, out, P, len
     w = wl.make_workload(spec, gpu)
     base, _ = run_lib(w, num_splits=2)
     for rows in ("64", "128"):
-        with mq_rows(rows):
-            got, _ = run_lib(w, num_splits=2)
+        got, _ = run_lib(w, num_splits=2, rows_per_block=int(rows))
         assert torch.equal(got, base), f"{rows}-row blocks differ from 16-row blocks"
 
 
@@ -94,8 +92,7 @@ def test_row_block_sizes_match_oracle(gpu, rows, T, G, D, kv, out, P, lens, W):
     spec = spec_of(T, G, D, kv, out, P, lens, W)
     say(f"[multi] {spec.name} rows={rows}")
     w = wl.make_workload(spec, gpu)
-    with mq_rows(rows):
-        got, plan = run_lib(w, num_splits=3)
+    got, plan = run_lib(w, num_splits=3, rows_per_block=int(rows))
     assert plan.info.split_kernel == 2
     err, worst = check(got, oracle_for(w), kv, out, f"{spec.name} rows {rows}")
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
@@ -201,8 +198,9 @@ def test_full_size_workloads_sampled(gpu, name):
     pairs = [(0, 0), (0, T - 1), (1, T // 2), (spec.batch - 1, T - 1), (spec.batch // 2, 1)]
     ref = sampled_decode_oracle(w, pairs)
     g = np.stack([host64(got[b, t]) for b, t in pairs])
+    g32 = np.stack([host64(got.f32_twin[b, t]) for b, t in pairs])
     r = np.stack([ref[p] for p in pairs])
-    check(g[:, None], r[:, None], spec.kv_dtype, spec.out_dtype, name)
+    check(g[:, None], r[:, None], spec.kv_dtype, spec.out_dtype, name, twin=g32[:, None])
     assert torch.isfinite(got).all()
 
 
@@ -243,3 +241,22 @@ def test_per_token_path_matches_oracle(gpu, T, G, D, qd, kv, out, P, lens, W, ke
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
     two, _ = run_lib(w, num_splits=splits, kernel=kernel, two_phase=True)
     assert torch.equal(got, two)
+
+
+# Zero and negative scales on the multi-token kernels: a negative scale is
+# folded into q (a sign flip, exact), a zero scale makes every score 0 (the
+# output is the mean of the attended V rows).
+@pytest.mark.parametrize("scale", [0.0, -0.0625, -1.3])
+@pytest.mark.parametrize("T,G,D,kv,P,W", [(16, 4, 128, "f16", 16, 0), (3, 4, 64, "bf16", 32, 0),
+                                          (4, 4, 256, "f16", 16, 100), (40, 2, 128, "bf16", 16, 0),
+                                          (8, 1, 128, "f16", 8, 7)])
+def test_zero_and_negative_scale(gpu, scale, T, G, D, kv, P, W):
+    spec = spec_of(T, G, D, kv, kv, P, (T, T + 5, 300, 2000), W).replace(scale=scale)
+    say(f"[multi] {spec.name} scale={scale}")
+    w = wl.make_workload(spec, gpu)
+    ref = oracle_for(w)
+    for ns in (0, 3):
+        got, plan = run_lib(w, num_splits=ns)
+        assert plan.info.split_kernel == 2
+        err, worst = check(got, ref, kv, kv, f"{spec.name} scale {scale} splits {ns}")
+        say(f"  splits {ns}: rel L2 {err:.2e}, worst sequence {worst:.2e}")
