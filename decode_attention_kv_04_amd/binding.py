@@ -24,8 +24,9 @@ KERNEL_CODES = {None: DA_KERNEL_AUTO, "auto": DA_KERNEL_AUTO, "vector": DA_KERNE
 EXPORTS = (
     "decode_attn_plan", "decode_attn_plan_for_cus", "decode_attn_plan_info", "decode_attn_plan_splits",
     "decode_attn_run", "decode_attn_split", "decode_attn_combine", "decode_attn_append_kv",
-    "decode_attn_plan_destroy", "decode_attn_status_str",
+    "decode_attn_run_noalloc", "decode_attn_plan_destroy", "decode_attn_status_str",
 )
+SCRATCH_BYTES = 64 * 1024 * 1024  # DECODE_ATTN_SCRATCH_BYTES
 
 
 class DecodeAttnError(RuntimeError):
@@ -84,12 +85,13 @@ def load() -> ctypes.CDLL:
     lib.decode_attn_split.argtypes = run_args
     lib.decode_attn_combine.argtypes = [vp, vp, vp, vp, sz, vp]
     lib.decode_attn_append_kv.argtypes = [ctypes.POINTER(Params), i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.decode_attn_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.decode_attn_plan_destroy.argtypes = [vp]
     lib.decode_attn_plan_destroy.restype = None
     lib.decode_attn_status_str.argtypes = [ctypes.c_int]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
     for name in ("decode_attn_plan", "decode_attn_plan_for_cus", "decode_attn_plan_info", "decode_attn_run",
-                 "decode_attn_split", "decode_attn_combine", "decode_attn_append_kv"):
+                 "decode_attn_split", "decode_attn_combine", "decode_attn_append_kv", "decode_attn_run_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -221,6 +223,14 @@ def decode_attn_run(plan: Plan, q, k_pool, v_pool, page_table, seq_lens, out, wo
                                 _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream))
     if st != DA_OK:
         raise DecodeAttnError(st, "decode_attn_run")
+
+
+def decode_attn_run_noalloc(plan: Plan, q, k_pool, v_pool, page_table, seq_lens, out, stream=None):
+    """decode_attn_run with the split states in the library's static scratch (no workspace)."""
+    st = load().decode_attn_run_noalloc(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                        _ptr(seq_lens), _ptr(out), _stream(stream))
+    if st != DA_OK:
+        raise DecodeAttnError(st, "decode_attn_run_noalloc")
 
 
 def decode_attn_split(plan: Plan, q, k_pool, v_pool, page_table, seq_lens, out, workspace=None, stream=None):

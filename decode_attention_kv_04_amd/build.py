@@ -34,7 +34,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 HOST_SOURCES = ["plan.cpp", "api.cpp"]
 KERNEL_SOURCES = ["decode_split.hip", "decode_split_mfma.hip", "decode_combine.hip", "append_kv.hip",
-                  "decode_multi.hip"]
+                  "decode_multi.hip", "scratch.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 

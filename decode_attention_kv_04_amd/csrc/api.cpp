@@ -260,6 +260,22 @@ da_status decode_attn_append_kv(const da_params* p, int32_t tokens, const void* 
   return DA_OK;
 }
 
+da_status decode_attn_run_noalloc(da_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* page_table, const int32_t* seq_lens, void* out, void* stream) {
+  if (!plan) return DA_ERR_INVALID;
+  if (plan->ws_bytes > DECODE_ATTN_SCRATCH_BYTES) return DA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan->ws_bytes > 0) {
+    hipDevice_t dev = 0;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess ||
+        da::scratch_address(dev, &ws) != hipSuccess) {
+      (void)hipGetLastError();
+      return DA_ERR_HIP;
+    }
+  }
+  return decode_attn_run(plan, q, k_pool, v_pool, page_table, seq_lens, out, ws, plan->ws_bytes, stream);
+}
+
 void decode_attn_plan_destroy(da_plan_t plan) { delete plan; }
 
 const char* decode_attn_status_str(da_status s) {

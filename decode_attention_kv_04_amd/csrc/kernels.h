@@ -75,4 +75,8 @@ hipError_t launch_multi(const KernelArgs& a, int head_dim, int kv_dtype, int row
 // Enqueue the combine pass on `stream`.
 hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream);
 
+// Device address of `device`'s static scratch (DECODE_ATTN_SCRATCH_BYTES,
+// 256-byte aligned); looked up once per device, then cached.
+hipError_t scratch_address(int device, void** ptr);
+
 }  // namespace da

@@ -294,6 +294,28 @@ da_status decode_attn_append_kv(const da_params* p, int32_t tokens, const void* 
                                 const int32_t* page_table, const int32_t* seq_lens, void* k_pool, void* v_pool,
                                 void* stream);
 
+/*
+ * decode_attn_run_noalloc: decode_attn_run for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): it takes no workspace. The split states
+ * go to a static scratch array of DECODE_ATTN_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on, until the process ends. The call
+ * allocates nothing; its first call on a device looks up that device's
+ * scratch address once. The GPU is the stream's (hipStreamGetDevice; the null
+ * stream: the current device).
+ *   Arguments, checks and results as decode_attn_run (the same kernels run).
+ *   Returns DA_ERR_WORKSPACE if the plan's workspace_bytes exceeds
+ *   DECODE_ATTN_SCRATCH_BYTES (plan with fewer splits, or use
+ *   decode_attn_run), DA_ERR_HIP if the scratch cannot be looked up.
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * contents (no call needs it cleared: every state a call reads, that call
+ * wrote). Calls whose work overlaps in time on one GPU (different streams,
+ * or unordered threads) race: order them on one stream.
+ */
+#define DECODE_ATTN_SCRATCH_BYTES (64u * 1024u * 1024u)
+da_status decode_attn_run_noalloc(da_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* page_table, const int32_t* seq_lens, void* out, void* stream);
+
 /* decode_attn_plan_destroy: free a plan (NULL is ignored); the plan must not
  * be used afterwards. Follows: llm-web pull 8, commit on engine ownership
  * (the owner of an object releases it explicitly, at once). */

@@ -491,3 +491,14 @@ def test_append_argument_errors(lib):
 def test_append_nothing_to_write_launches_nothing(lib):
     assert raw_append(params(batch=2), tokens=0, kn=None, vn=None, table=None, lens=None, kp=None, vp=None) == B.DA_OK
     assert raw_append(params(batch=0), tokens=3, kn=None, vn=None, table=None, lens=None, kp=None, vp=None) == B.DA_OK
+
+
+def test_noalloc_rejects_plans_beyond_the_scratch(lib):
+    """decode_attn_run_noalloc refuses a plan whose split states exceed the
+    static scratch, before any HIP call (null tensors: nothing could run)."""
+    big = params(batch=64, num_q_heads=64, head_dim=256, max_pages_per_seq=4096, num_splits=4096)
+    pl = plan(big, [65536] * 64)
+    assert pl.workspace_bytes > B.SCRATCH_BYTES
+    st = lib.decode_attn_run_noalloc(pl.handle, None, None, None, None, None, None, None)
+    assert st == B.DA_ERR_WORKSPACE
+    assert lib.decode_attn_run_noalloc(None, None, None, None, None, None, None, None) == B.DA_ERR_INVALID

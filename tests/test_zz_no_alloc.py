@@ -1,0 +1,67 @@
+"""decode_attn_run_noalloc, the entry point that allocates nothing (its split
+states go to the library's static scratch), against decode_attn_run with a
+caller's workspace, through the C ABI: the same kernels run, so the outputs
+must be identical, bit for bit. Each case makes two calls in a row, the
+second on a smaller input (the scratch then still holds the first call's
+states, which must not leak into the second)."""
+import pytest
+import torch
+
+from decode_attention_kv_04_amd import binding
+from decode_attention_kv_04_amd import workloads as wl
+
+from gpu_util import TORCH_DT, check, oracle_for, run_lib, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_noalloc(w, **kw):
+    params = binding.params_for(w.q, w.k_pool, w.page_table, window=w.window, scale=w.scale,
+                                out_dtype=w.spec.out_dtype, **kw)
+    plan = binding.decode_attn_plan(params, w.seq_lens_host, device=w.q.device.index)
+    out = torch.full(w.q.shape, float("nan"), dtype=TORCH_DT[w.spec.out_dtype], device=w.q.device)
+    binding.decode_attn_run_noalloc(plan, w.q, w.k_pool, w.v_pool, w.page_table, w.seq_lens, out)
+    torch.cuda.synchronize()
+    return out, plan
+
+
+# (larger first call, smaller second call, plan options)
+CASES = [
+    ("decode", wl.LLAMA8B_3060.replace(batch=6, lengths=("list", (20000, 3060, 1, 0, 9000, 257))),
+     wl.LLAMA8B_3060.replace(batch=2, lengths=("list", (3060, 100)), seed=8), {}),
+    ("decode-window-bf16", wl.MIXED_WINDOW.replace(batch=4, lengths=("list", (70000, 12, 5000, 40000))),
+     wl.MIXED_WINDOW.replace(batch=3, lengths=("list", (9000, 1, 300)), seed=9), {}),
+    ("fixed-order", wl.LLAMA8B_3060.replace(batch=3, lengths=("list", (9000, 3060, 17))),
+     wl.LLAMA8B_3060.replace(batch=1, lengths=("list", (2000,)), seed=10), {"fixed_chunk": 256}),
+    ("multi-token", wl.SUFFIX_PREFILL.replace(batch=2, lengths=("list", (5000, 700))),
+     wl.VERIFY_LONG.replace(batch=2, lengths=("list", (3000, 40)), max_pages_per_seq=None), {}),
+    ("per-token", wl.WorkloadSpec("pt_f32", 2, 8, 2, 64, "f32", "f32", "f32", 16, ("list", (4000, 9)), seed=11,
+                                  query_len=3),
+     wl.WorkloadSpec("pt_f32_small", 1, 8, 2, 64, "f32", "f32", "f32", 16, ("list", (600,)), seed=12,
+                     query_len=2), {}),
+]
+
+
+@pytest.mark.parametrize("name,first,second,kw", CASES, ids=[c[0] for c in CASES])
+def test_noalloc_equals_run_on_two_calls(gpu, name, first, second, kw):
+    for i, spec in enumerate((first, second)):
+        say(f"[no-alloc] {name} call {i + 1}: {spec.name} lengths {spec.lengths}")
+        w = wl.make_workload(spec, gpu)
+        ref, plan = run_lib(w, **kw)
+        if i == 0:
+            assert plan.workspace_bytes > 0, "the first call must use the scratch"
+        assert plan.workspace_bytes <= binding.SCRATCH_BYTES
+        got, plan2 = run_noalloc(w, **kw)
+        assert plan2.workspace_bytes == plan.workspace_bytes
+        assert torch.equal(got, ref), f"{name} call {i + 1}: differs from decode_attn_run"
+        check(ref, oracle_for(w), spec.kv_dtype, spec.out_dtype, f"{name} call {i + 1}")
+
+
+def test_noalloc_full_size_long_batch(gpu, long_batch):
+    """The benchmark's batch and launch configuration (6.4 MB of split
+    states in the scratch): identical to decode_attn_run."""
+    w, ref = long_batch
+    a, plan = run_lib(w)
+    b, _ = run_noalloc(w)
+    assert 0 < plan.workspace_bytes <= binding.SCRATCH_BYTES
+    assert torch.equal(a, b)
