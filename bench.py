@@ -12,6 +12,15 @@ value   = algorithmic KV bytes per step / step time (GB/s), where the
 roofline: the split kernel alone, timed with HIP events on the stream it is
           launched on, against the 8 TB/s HBM peak.
 cpu_baseline: the f64 CPU oracle on a bounded sample of the same batch.
+configs: the five named configurations (tiny, the Llama-3.1-8B shape at 3060
+          tokens, wide-head GQA, this batch, the mixed sliding-window batch):
+          step and split-pass µs as median / p10 / p90 over alternating
+          repeats, GB/s, fractions of the peak and of the measured gather
+          ceiling, cold-cache µs where the inputs fit the last-level cache,
+          the oracle's wall time on each, and each output checked against
+          the oracle (the run exits 1 if any check fails).
+--sweep: only a context-length sweep on the Llama shape (L 256..65536,
+          batch 1 and 32).
 Also reported, each timed the same way: the fixed-order mode on the same
 batch (fixed_order), several new tokens per sequence on their own workloads
 (multi_token: a 4-token check over the long-context batch and a 128-token
@@ -375,6 +384,243 @@ def measure_append(w, lib, params, stream, tokens, iters):
             "bytes": moved}
 
 
+# ---------------------------------------------------------------------------
+# The five named configurations, each timed over alternating repeats, and the
+# oracle's wall time on each (the CPU-baseline leg).
+# ---------------------------------------------------------------------------
+
+CONFIGS = (("C1", "tiny"), ("C2", "llama8b_3060"), ("C3", "wide_gqa"), ("C4", "long_batch"),
+           ("C5", "mixed_window"))
+BLOCK_US = 2000.0   # each timed block holds about this much GPU time
+KV_TOL = {"f32": 1e-5, "f16": 1e-3, "bf16": 1e-3}
+
+
+class Runner:
+    """One planned decode_attn_run on a workload's resident inputs."""
+
+    def __init__(self, binding, lib, w, dev, stream, **plan_kw):
+        import torch
+        self.w = w
+        spec = w.spec
+        params = binding.params_for(w.q, w.k_pool, w.page_table, window=w.window, scale=w.scale,
+                                    out_dtype=spec.out_dtype, **plan_kw)
+        self.plan = binding.decode_attn_plan(params, w.seq_lens_host, device=dev.index or 0)
+        from decode_attention_kv_04_amd import workloads
+        self.out = torch.empty(w.q.shape, dtype=workloads.DTYPES[spec.out_dtype], device=dev)
+        self.ws = binding.alloc_workspace(self.plan, dev)
+        self.ptrs = [w.q.data_ptr(), w.k_pool.data_ptr(), w.v_pool.data_ptr(), w.page_table.data_ptr(),
+                     w.seq_lens.data_ptr(), self.out.data_ptr(), self.ws.data_ptr() if self.ws is not None else None,
+                     self.plan.workspace_bytes, stream.cuda_stream]
+        self.lib, self.binding, self.stream = lib, binding, stream
+
+    def run(self):
+        st = self.lib.decode_attn_run(self.plan.handle, *self.ptrs)
+        if st != 0:
+            raise self.binding.DecodeAttnError(st, f"decode_attn_run ({self.w.spec.name})")
+
+    def split(self):
+        st = self.lib.decode_attn_split(self.plan.handle, *self.ptrs)
+        if st != 0:
+            raise self.binding.DecodeAttnError(st, f"decode_attn_split ({self.w.spec.name})")
+
+
+def block_us(fn, n, stream):
+    """Mean µs per launch over one block of n back-to-back launches."""
+    return time_on_stream(fn, n, stream) * 1e3
+
+
+def quantiles(xs):
+    xs = sorted(xs)
+
+    def q(f):
+        i = f * (len(xs) - 1)
+        lo = int(i)
+        hi = min(lo + 1, len(xs) - 1)
+        return xs[lo] + (xs[hi] - xs[lo]) * (i - lo)
+    return {"median": round(q(0.5), 2), "p10": round(q(0.1), 2), "p90": round(q(0.9), 2), "n": len(xs)}
+
+
+def time_alternating(runners, rounds, stream):
+    """Time every runner's step (and split pass) in `rounds` rounds that visit
+    the runners in turn, so drifts of clock or temperature fall on all of them
+    alike; each sample is the mean over a block of about BLOCK_US of launches.
+    Returns {key: {"run": [...], "split": [...], "block": n}} in µs per launch."""
+    res = {}
+    for key, r in runners.items():
+        for _ in range(3):
+            r.run()
+        est = max(1.0, block_us(r.run, 5, stream))
+        res[key] = {"run": [], "split": [], "block": int(min(2000, max(10, BLOCK_US // est)))}
+    for _ in range(rounds):
+        for key, r in runners.items():
+            n = res[key]["block"]
+            res[key]["run"].append(block_us(r.run, n, stream))
+            res[key]["split"].append(block_us(r.split, n, stream))
+    return res
+
+
+def host_cpu():
+    """The host's CPU model and the threads numpy's BLAS uses (the oracle's)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count(), "oracle_threads": int(threads)}
+
+
+def cpu_baseline_configs(runners):
+    """CPU-baseline leg over the named configurations: the f64 oracle's wall
+    time on each whole batch (median of 3 for the three small ones, one run
+    for the two large ones), excluding input copies to the host. Returns
+    {key: (seconds, oracle output)}; the outputs also check the GPU's."""
+    import oracle
+    from decode_attention_kv_04_amd import workloads
+    res = {}
+    for key, r in runners.items():
+        w = r.w
+        a = workloads.to_numpy_inputs(w, attended_only=w.window > 0)
+        fn = oracle.prefill_attention if a["q"].ndim == 4 else oracle.decode_attention
+        times, ref = [], None
+        for _ in range(1 if w.kv_bytes() > (1 << 30) or w.window > 0 else 3):
+            t = time.perf_counter()
+            ref = fn(a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"], a["page_size"], a["scale"],
+                     a["window"])
+            times.append(time.perf_counter() - t)
+        res[key] = (sorted(times)[len(times) // 2], ref)
+        print(f"[bench] oracle {key}: {res[key][0]:.2f} s", file=sys.stderr, flush=True)
+    return res
+
+
+def output_check(r, ref):
+    """Relative L2 of the runner's last output against the oracle's, over the
+    whole output and per (sequence, query head) row, against the bound the
+    tests use: the KV-dtype bound, 1e-3 for an fp16 output of fp32 K/V, plus
+    2^-8 for a bf16 output (its own rounding)."""
+    import numpy as np
+    got = r.out.float().cpu().numpy().astype(np.float64)
+    spec = r.w.spec
+    finite = bool(np.isfinite(got).all())
+    res = {"finite": finite}
+    if ref is None:
+        res["ok"] = finite
+        return res
+    tol = KV_TOL[spec.kv_dtype]
+    if spec.out_dtype == "f16" and spec.kv_dtype == "f32":
+        tol = 1e-3
+    if spec.out_dtype == "bf16":
+        tol += 2.0 ** -8
+    D = ref.shape[-1]
+    g, f = got.reshape(-1, D), ref.reshape(-1, D)
+    den = np.sqrt((f * f).sum(axis=1))
+    num = np.sqrt(((g - f) ** 2).sum(axis=1))
+    heads = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
+    whole = float(np.sqrt(((got - ref) ** 2).sum()) / max(np.sqrt((ref * ref).sum()), 1e-300))
+    res.update({"rel_l2": float(f"{whole:.3e}"), "worst_head_rel_l2": float(f"{heads.max():.3e}"),
+                "tol": tol, "rows_checked": int(heads.size)})
+    res["ok"] = finite and whole <= tol and float(heads.max()) <= tol
+    return res
+
+
+def measure_configs(binding, workloads, lib, dev, stream, rounds, headline, ceilings, with_oracle):
+    """Every named configuration: step and split-pass µs (median, p10, p90
+    over `rounds` alternating repeats), GB/s of algorithmic KV bytes,
+    fractions of the 8 TB/s peak and of the measured 4 KiB-gather ceiling,
+    cold-cache µs for inputs the last-level cache could hold, the oracle's
+    wall time and the check of the timed output against it."""
+    import torch
+    runners = {}
+    for key, name in CONFIGS:
+        if headline is not None and workloads.NAMED[name] == headline.w.spec:
+            runners[key] = headline
+        else:
+            w = workloads.make_workload(workloads.NAMED[name], dev)
+            runners[key] = Runner(binding, lib, w, dev, stream)
+    torch.cuda.synchronize()
+    times = time_alternating(runners, rounds, stream)
+    refs = cpu_baseline_configs(runners) if with_oracle else {}
+    gather = ceilings.get("gather4k")
+    out = []
+    for key, name in CONFIGS:
+        r = runners[key]
+        w, spec, t = r.w, r.w.spec, times[key]
+        r.out.fill_(float("nan"))
+        r.run()
+        torch.cuda.synchronize()
+        kvb = w.kv_bytes()
+        run_q, split_q = quantiles(t["run"]), quantiles(t["split"])
+        gbs = kvb / (run_q["median"] * 1e-6) / 1e9
+        split_gbs = kvb / (split_q["median"] * 1e-6) / 1e9
+        check = output_check(r, refs[key][1] if key in refs else None)
+        cold = measure_cold(w, r.plan, lib, r.out, r.ws, stream) if kvb < LLC_BYTES else None
+        entry = {
+            "config": key, "workload": spec.name, "batch": spec.batch, "heads": [spec.num_q_heads, spec.num_kv_heads],
+            "head_dim": spec.head_dim, "dtypes": [spec.q_dtype, spec.kv_dtype, spec.out_dtype],
+            "page_size": spec.page_size, "window": spec.window, "attended_keys": int(r.plan.info.attended_keys),
+            "algorithmic_bytes": kvb, "split_kernel": int(r.plan.info.split_kernel),
+            "max_splits": r.plan.max_splits, "block_launches": t["block"],
+            "us": run_q, "split_us": split_q,
+            "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBPS, 4),
+            "frac_gather4k": round(gbs / gather, 4) if gather else None,
+            "split_GB_s": round(split_gbs, 1), "split_frac_hbm_peak": round(split_gbs / HBM_PEAK_GBPS, 4),
+            "cold": cold,
+        }
+        if key in refs:
+            entry["oracle_s"] = round(refs[key][0], 3)
+        entry["output_check"] = check
+        out.append(entry)
+        print(f"[bench] {key} {spec.name}: {run_q['median']:.1f} us (p10 {run_q['p10']:.1f}, p90 {run_q['p90']:.1f}), "
+              f"{gbs:.0f} GB/s, check {entry['output_check']}", file=sys.stderr, flush=True)
+    for key, r in runners.items():
+        if r is not headline:
+            del r.w, r.out, r.ws
+    torch.cuda.empty_cache()
+    return out
+
+
+SWEEP_LENGTHS = tuple(256 << i for i in range(9))   # 256 .. 65536
+SWEEP_BATCHES = (1, 32)
+
+
+def measure_sweep(binding, workloads, lib, dev, stream, rounds):
+    """Context-length sweep on the Llama-3.1-8B decode shape (32/8 heads, D
+    128, fp16, 16-token pages): every sequence of the batch at context L, for
+    L = 256 .. 65536 and batch 1 and 32; step and split µs (median, p10, p90
+    over alternating repeats within each batch size) and GB/s."""
+    import torch
+    res = []
+    for B in SWEEP_BATCHES:
+        runners = {}
+        for L in SWEEP_LENGTHS:
+            spec = workloads.LLAMA8B_3060.replace(name=f"llama8b_b{B}_l{L}_f16", batch=B, lengths=("fixed", L),
+                                                  seed=100 + L % 97 + B, max_pages_per_seq=L // 16)
+            runners[L] = Runner(binding, lib, workloads.make_workload(spec, dev), dev, stream)
+        torch.cuda.synchronize()
+        times = time_alternating(runners, rounds, stream)
+        for L, r in runners.items():
+            kvb = r.w.kv_bytes()
+            run_q, split_q = quantiles(times[L]["run"]), quantiles(times[L]["split"])
+            gbs = kvb / (run_q["median"] * 1e-6) / 1e9
+            res.append({"batch": B, "context": L, "us": run_q, "split_us": split_q, "GB_s": round(gbs, 1),
+                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBPS, 4), "max_splits": r.plan.max_splits,
+                        "split_kernel": int(r.plan.info.split_kernel), "algorithmic_bytes": kvb})
+            print(f"[bench] sweep B {B} L {L}: {run_q['median']:.1f} us, {gbs:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+        del runners
+        torch.cuda.empty_cache()
+    return res
+
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,9 +629,13 @@ def main():
     ap.add_argument("--workload", default="long_batch", help="one of: long_batch, llama8b_3060, wide_gqa, "
                     "mixed_window, tiny")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the planner decides")
+    ap.add_argument("--rounds", type=int, default=7, help="alternating repeats per configuration")
+    ap.add_argument("--no-configs", action="store_true", help="skip the five named configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-multi-token", action="store_true", help="skip the multi-token workloads")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the context-length sweep (Llama shape, L 256..65536, batch 1 and 32)")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy a buffer of known size once (counter calibration)")
     args = ap.parse_args()
@@ -404,6 +654,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    lib = binding.load()
+    sptr = stream.cuda_stream
+
+    if args.sweep:
+        sweep = measure_sweep(binding, workloads, lib, dev, stream, args.rounds)
+        print(json.dumps({"metric": METRIC, "sweep": sweep, "unit": "GB/s", "n_gpus": 1,
+                          "data": "synthetic", "kernel_source_sha256_16": kernel_hash()}), flush=True)
+        return
+
     spec = workloads.NAMED[args.workload]
     print(f"[bench] generating {spec.name} on {dev}", file=sys.stderr, flush=True)
     w = workloads.make_workload(spec, dev)
@@ -414,7 +674,8 @@ def main():
                                 out_dtype=spec.out_dtype, num_splits=args.num_splits)
     # The first plan also reads the device's CU count; the host cost of a
     # plan is the median of later calls.
-    plan = binding.decode_attn_plan(params, w.seq_lens_host, device=0)
+    head = Runner(binding, lib, w, dev, stream, num_splits=args.num_splits)
+    plan = head.plan
     plan_times = []
     for _ in range(21):
         t = time.perf_counter()
@@ -422,24 +683,7 @@ def main():
         plan_times.append((time.perf_counter() - t) * 1e6)
         del again
     plan_us = sorted(plan_times)[len(plan_times) // 2]
-    out = torch.empty(w.q.shape, dtype=workloads.DTYPES[spec.out_dtype], device=dev)
-    ws = binding.alloc_workspace(plan, dev)
-    stream = torch.cuda.current_stream()
-    lib = binding.load()
-    sptr = stream.cuda_stream
-    ptrs = [w.q.data_ptr(), w.k_pool.data_ptr(), w.v_pool.data_ptr(), w.page_table.data_ptr(),
-            w.seq_lens.data_ptr(), out.data_ptr(), ws.data_ptr() if ws is not None else None,
-            plan.workspace_bytes]
-
-    def step():
-        st = lib.decode_attn_run(plan.handle, *ptrs, sptr)
-        if st != 0:
-            raise binding.DecodeAttnError(st, "decode_attn_run")
-
-    def split_only():
-        st = lib.decode_attn_split(plan.handle, *ptrs, sptr)
-        if st != 0:
-            raise binding.DecodeAttnError(st, "decode_attn_split")
+    out, ws, ptrs = head.out, head.ws, head.ptrs
 
     def combine_only():
         st = lib.decode_attn_combine(plan.handle, ptrs[4], ptrs[5], ptrs[6], ptrs[7], sptr)
@@ -448,18 +692,43 @@ def main():
 
     print(f"[bench] plan: pages/split {plan.pages_per_split}, max splits {plan.max_splits}, "
           f"work-groups {plan.info.split_work_groups}; warmup {args.warmup}", file=sys.stderr, flush=True)
+    out.fill_(float("nan"))
     for _ in range(args.warmup):
-        step()
+        head.run()
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` steps, synchronized on both sides.
     torch.cuda.synchronize()
-    ms_per_step = time_on_stream(step, args.steps, stream)
+    ms_per_step = time_on_stream(head.run, args.steps, stream)
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    timed_out = out.clone()   # the output the timed steps left, checked against the oracle below
 
     # The dominant kernel alone (split pass), then the combine pass alone.
-    split_ms = time_on_stream(split_only, args.steps, stream)
+    split_ms = time_on_stream(head.split, args.steps, stream)
     combine_ms = time_on_stream(combine_only, args.steps, stream) if plan.max_splits > 1 else 0.0
+
+    ceilings = {}
+    if not args.no_ceiling:
+        ceilings = measure_ceilings(dev, sptr, stream)
+
+    # The five named configurations (the headline batch among them, reusing
+    # its inputs), over alternating repeats, with the oracle's time on each.
+    configs = None
+    if not args.no_configs and args.num_splits == 0:
+        configs = measure_configs(binding, workloads, lib, dev, stream, args.rounds,
+                                  head if args.workload in dict(CONFIGS).values() else None, ceilings,
+                                  not args.no_cpu_baseline)
+
+    # The headline's timed output against the oracle: the configuration list
+    # re-ran the same plan on the same inputs and checked that output, which
+    # must be bitwise the timed one (the step is deterministic).
+    head_check = {"finite": bool(torch.isfinite(timed_out.float()).all().item())}
+    for c in configs or []:
+        if c["workload"] == spec.name:
+            same = bool(torch.equal(out, timed_out))
+            head_check = dict(c["output_check"], timed_output_identical=same)
+            head_check["ok"] = head_check["ok"] and same
+    head_check.setdefault("ok", head_check["finite"])
 
     # The fixed-order mode (output bitwise independent of the split count) on
     # the same batch: whole step, chunks of FIXED_CHUNK tokens.
@@ -479,15 +748,14 @@ def main():
     # Workloads the last-level cache could hold are also timed cold.
     cold = measure_cold(w, plan, lib, out, ws, stream) if kv_bytes < 2 * LLC_BYTES else None
 
-    ceilings = {}
-    if not args.no_ceiling:
-        ceilings = measure_ceilings(dev, sptr, stream)
     if args.calibrate:
         calibration_copy(dev, sptr)
 
     achieved = kv_bytes / (split_ms * 1e-3) / 1e9
     traffic = recorded_traffic()
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    if cpu is not None:
+        cpu["host"] = host_cpu()
 
     step_gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -514,6 +782,7 @@ def main():
             "pages_per_split": plan.pages_per_split, "max_splits": plan.max_splits,
             "parallelism": "single GPU",
         },
+        "output_check": head_check,
         "roofline": {
             "bound": "hbm",
             "kernel": {0: "split pass, vector q.K (da::split_kernel)",
@@ -524,9 +793,14 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_source": ("FETCH_SIZE + WRITE_SIZE per launch from the committed counter summary "
+                               "(profiles/split_kernel_long_batch_traffic.md), valid while the kernel sources "
+                               "keep its hash; null otherwise") if traffic is not None else None,
             "algorithmic_bytes_per_launch": kv_bytes,
             "avg_launch_us": round(split_ms * 1e3, 2),
         },
+        "configs": configs,
+        "configs_oracle_host": host_cpu() if configs and not args.no_cpu_baseline else None,
         "cold": cold,
         "combine_us": round(combine_ms * 1e3, 2),
         "fixed_order": fixed,
@@ -543,6 +817,9 @@ def main():
         "kernel_source_sha256_16": kernel_hash(),
     }
     print(json.dumps(result), flush=True)
+    if not head_check["ok"] or any(not c["output_check"]["ok"] for c in configs or []):
+        print("[bench] an output check against the oracle FAILED (see output_check)", file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 if __name__ == "__main__":
