@@ -52,6 +52,7 @@ class PlanInfo(ctypes.Structure):
         ("split_work_groups", ctypes.c_int32), ("active_units", ctypes.c_int64),
         ("attended_keys", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
         ("split_kernel", ctypes.c_int32), ("chunks_per_work_group", ctypes.c_int32),
+        ("balanced", ctypes.c_int32),
     ]
 
 

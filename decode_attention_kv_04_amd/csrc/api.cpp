@@ -65,6 +65,9 @@ da_status prepare(const da_plan* plan, const void* q, const void* k_pool, const 
   const bool has_ws = plan->ws_bytes > 0;
   a->ws_o = has_ws ? reinterpret_cast<float*>(ws + plan->ws_o_offset) : nullptr;
   a->ws_ml = has_ws ? reinterpret_cast<float*>(ws + plan->ws_ml_offset) : nullptr;
+  a->ws_cnt = has_ws && plan->balanced ? reinterpret_cast<int32_t*>(ws + plan->ws_cnt_offset) : nullptr;
+  a->balanced = plan->balanced ? 1 : 0;
+  a->bal_overhead = plan->bal_overhead;
   a->batch = p.batch;
   a->num_q_heads = p.num_q_heads;
   a->num_kv_heads = p.num_kv_heads;
@@ -159,12 +162,14 @@ da_status decode_attn_plan_info(da_plan_t plan, da_plan_info* info) {
   info->pages_per_split = plan->pages_per_split;
   info->max_splits = plan->max_splits;
   info->num_cus = plan->num_cus;
-  info->split_work_groups = plan->split_groups * plan->p.num_kv_heads * plan->p.batch;
+  info->split_work_groups =
+      plan->balanced ? plan->split_groups : plan->split_groups * plan->p.num_kv_heads * plan->p.batch;
   info->active_units = plan->active_units;
   info->attended_keys = plan->attended_keys;
   info->workspace_bytes = plan->ws_bytes;
   info->split_kernel = plan->split_kernel;
   info->chunks_per_work_group = plan->chunks_per_group;
+  info->balanced = plan->balanced ? 1 : 0;
   return DA_OK;
 }
 
@@ -209,6 +214,10 @@ da_status decode_attn_combine(da_plan_t plan, const int32_t* seq_lens, void* out
   a.out = out;
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_o_offset);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->ws_ml_offset);
+  a.ws_cnt = plan->balanced ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan->ws_cnt_offset)
+                            : nullptr;
+  a.balanced = plan->balanced ? 1 : 0;
+  a.bal_overhead = plan->bal_overhead;
   a.batch = p.batch;
   a.num_q_heads = p.num_q_heads;
   a.num_kv_heads = p.num_kv_heads;

@@ -36,12 +36,19 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const Kerne
   const int lane = threadIdx.x & 63;
   if (h >= a.num_q_heads) return;  // whole wave
 
-  const int P = a.page_size;
-  const int64_t L = a.seq_lens[b] - a.len_offset;
-  const int64_t t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
-  const int64_t pf = L > 0 ? t0 / P : 0;
-  const int64_t pe = L > 0 ? (L + P - 1) / P : 0;
-  int64_t nsplit = (pe - pf + a.pages_per_split - 1) / a.pages_per_split;
+  int64_t nsplit;
+  if (a.ws_cnt != nullptr) {
+    // Balanced schedule: the split pass recorded the pieces of each
+    // (sequence, KV head) stream.
+    nsplit = a.ws_cnt[static_cast<int64_t>(b) * a.num_kv_heads + h / a.group];
+  } else {
+    const int P = a.page_size;
+    const int64_t L = a.seq_lens[b] - a.len_offset;
+    const int64_t t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
+    const int64_t pf = L > 0 ? t0 / P : 0;
+    const int64_t pe = L > 0 ? (L + P - 1) / P : 0;
+    nsplit = (pe - pf + a.pages_per_split - 1) / a.pages_per_split;
+  }
   if (nsplit > a.max_splits) nsplit = a.max_splits;
   if (a.chunks_per_group > 0) {
     if (nsplit < 1) nsplit = 1;  // fixed-order mode: every row is merged here

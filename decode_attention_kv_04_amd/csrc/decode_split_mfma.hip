@@ -39,6 +39,7 @@
 #include "decode_attn.h"
 #include "device_common.h"
 #include "kernels.h"
+#include "plan.h"
 
 #ifndef DA_MFMA_PREFETCH_TILES
 #define DA_MFMA_PREFETCH_TILES 1
@@ -83,9 +84,24 @@ __device__ __forceinline__ void row_bcast_all(float x, float* out) {
   }
 }
 
-// FIXED: fixed-order mode (chunks_per_group consecutive chunks per
-// work-group, one state per chunk; a chunk's state depends only on its keys).
-template <int D, int KVT, int GT, bool FIXED>
+// Schedules of the split pass (the MODE template parameter):
+//  kGrid      work-group (KV head, s, sequence) computes split s of that
+//             (sequence, KV head) stream: pages_per_split pages from the
+//             first attended page on;
+//  kFixed     fixed-order mode: chunks_per_group consecutive chunks per
+//             work-group, one state per chunk (a chunk's state depends only
+//             on its keys);
+//  kBalanced  work-group w computes units [w q, (w + 1) q), q =
+//             pages_per_split, of the batch's (sequence, KV head) streams in
+//             order, each weighing bal_overhead units and then one per
+//             attended page (an empty stream one page), one state per piece
+//             of a stream; the work-group holding a stream's first page
+//             records its piece count for the combine.
+constexpr int kGrid = 0;
+constexpr int kFixed = 1;
+constexpr int kBalanced = 2;
+
+template <int D, int KVT, int GT, int MODE>
 __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a) {
   static_assert(KVT == DA_F16 || KVT == DA_BF16, "matrix-core path needs a 16-bit KV type");
   static_assert(D == 128, "head_dim (256 does not fit the register budget in this layout)");
@@ -99,52 +115,32 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
   constexpr int TR = 16;        // keys per tile
   constexpr int RB = D * ELT;   // bytes per row
 
-  // KV head fastest: the H_kv work-groups of one page range are dispatched
-  // together, so their K/V blocks (adjacent in a page) are read at the same
-  // time.
-  const int kvh = blockIdx.x;
-  const int s = blockIdx.y;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;  // row slot / MFMA k-group
   const int c = lane & 15;  // column: head c of the scores, MFMA row of K
   const int key_of_lane = (c & 3) * 4 + (c >> 2);
-
   const int P = a.page_size;
-  const int L = a.seq_lens[b] - a.len_offset;
-  const int t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
-  const int pf = L > 0 ? t0 / P : 0;
-  const int pe = L > 0 ? (L + P - 1) / P : 0;
-  const int cp = a.pages_per_split;
-  int nsplit = (pe - pf + cp - 1) / cp;
-  nsplit = nsplit < 1 ? 1 : (nsplit > a.max_splits ? a.max_splits : nsplit);
-  // Splits (chunks in the fixed-order mode) [k_begin, k_end) of this group.
-  const int k_begin = FIXED ? s * a.chunks_per_group : s;
-  if (k_begin >= nsplit) return;  // whole work-group, uniform
-  const int k_end = FIXED ? (k_begin + a.chunks_per_group < nsplit ? k_begin + a.chunks_per_group : nsplit)
-                          : k_begin + 1;
-
   const int G = a.group;
-  const int h0 = kvh * G;
-  const int64_t qrow0 = static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h0;
 
-  // q of head c as the B operand: dims [32j + 8r, +8) for k-step j.
-  uint4 qb[NJ];
+  // q of head c of the group of KV head kvh in sequence b, as the B operand:
+  // dims [32j + 8r, +8) for k-step j.
+  auto load_q = [&](int b, int kvh, uint4 (&qb)[NJ]) {
+    const int64_t qrow0 = static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + kvh * G;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    qb[j] = make_uint4(0, 0, 0, 0);
-    if (c < G)
-      qb[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + ((qrow0 + c) * D + 32 * j + 8 * r) * ELT);
-  }
+    for (int j = 0; j < NJ; ++j) {
+      qb[j] = make_uint4(0, 0, 0, 0);
+      if (c < G)
+        qb[j] =
+            *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) + ((qrow0 + c) * D + 32 * j + 8 * r) * ELT);
+    }
+  };
 
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   const int64_t block_bytes = static_cast<int64_t>(P) * RB;
   const int64_t page_bytes = block_bytes * a.num_kv_heads;
-  const int64_t head_bytes = block_bytes * kvh;
-  const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
   const uint32_t v_lane_off = static_cast<uint32_t>(r * RB + c * E * ELT);
 
   // K of the tile being computed, per wave: 16 rows of 16-byte slots, slot s
@@ -160,12 +156,15 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
   __shared__ float sh_m[kWaves][GT];
   __shared__ float sh_l[kWaves][GT];
 
-  for (int k = k_begin; k < k_end; ++k) {
-    // Attended tokens of this split (chunk): [t_lo, t_hi).
-    const int plo = pf + k * cp;
-    const int phi = (plo + cp < pe) ? plo + cp : pe;
-    const int t_lo = L > 0 ? (t0 > plo * P ? t0 : plo * P) : 0;
-    const int t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
+  // Keys [t_lo, t_hi) of the stream (sequence b, KV head kvh), held in its
+  // logical pages [plo, phi): the four waves' tile loop, the merge of their
+  // states, then either the output rows (direct: the stream has no other
+  // piece) or the state (m, l, O) of every head in workspace slot `slot`.
+  auto process = [&](int b, int kvh, const uint4 (&qb)[NJ], int plo, int phi, int t_lo, int t_hi, bool direct,
+                     int slot) {
+    const int64_t qrow0 = static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + kvh * G;
+    const int64_t head_bytes = block_bytes * kvh;
+    const int32_t* table_row = a.page_table + static_cast<int64_t>(b) * a.max_pages;
 
     float m = -INFINITY, l = 0.0f;  // head c, row slot r
     float o[GT][DPL];
@@ -390,10 +389,10 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
         osum += aw * sh_o[w][g][d];
       }
       const int64_t row = qrow0 + g;
-      if (!FIXED && nsplit == 1) {
+      if (direct) {
         store_elem(a.out, row * D + d, a.out_dtype, lsum > 0.0f ? osum / lsum : 0.0f);
       } else {
-        const int64_t srow = row * a.max_splits + k;
+        const int64_t srow = row * a.max_splits + slot;
         a.ws_o[srow * D + d] = osum;
         if (d == 0) {
           a.ws_ml[srow * 2] = M;
@@ -401,16 +400,141 @@ __global__ __launch_bounds__(kThreads) void split_kernel_mfma(const KernelArgs a
         }
       }
     }
-    if constexpr (FIXED) __syncthreads();  // the next chunk rewrites the LDS
-  }  // chunks
+  };
+
+  if constexpr (MODE == kBalanced) {
+    // Each (sequence, KV head) stream weighs ov + n units: ov for the cost of
+    // starting a piece (a few dependent memory round trips), then one per
+    // attended page (at least one page, so that an empty stream writes its
+    // zero rows). sh_pref[0 .. B] holds the exclusive prefix sums of H_kv
+    // streams per sequence and sh_len the lengths: thread t sums sequences
+    // [t C, (t + 1) C), then a scan over the threads.
+    __shared__ int32_t sh_pref[kBalancedMaxBatch + 1];
+    __shared__ int32_t sh_len[kBalancedMaxBatch];
+    __shared__ int32_t sh_wsum[kWaves];
+    const int B = a.batch;
+    const int H = a.num_kv_heads;
+    const int ov = a.bal_overhead;
+    auto pages_of = [&](int Lb) {
+      const int t0b = (a.window > 0 && Lb > a.window) ? Lb - a.window : 0;
+      const int n = Lb > 0 ? (Lb + P - 1) / P - t0b / P : 0;
+      return n > 1 ? n : 1;
+    };
+    const int C = (B + kThreads - 1) / kThreads;
+    int local = 0;
+    for (int i = 0; i < C; ++i) {
+      const int bb = tid * C + i;
+      if (bb < B) {
+        const int Lb = a.seq_lens[bb];
+        sh_len[bb] = Lb;
+        local += ov + pages_of(Lb);
+      }
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) sh_wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w2 = 0; w2 < wave; ++w2) run += sh_wsum[w2];
+    for (int i = 0; i < C; ++i) {
+      const int bb = tid * C + i;
+      if (bb < B) {
+        sh_pref[bb] = run * H;
+        run += ov + pages_of(sh_len[bb]);
+      }
+    }
+    if (tid == kThreads - 1) sh_pref[B] = run * H;
+    __syncthreads();
+
+    // This work-group's units [u0, u1); the sequence holding u0 is the last
+    // b with sh_pref[b] <= u0 (prefix sums strictly increase).
+    const int q = a.pages_per_split;
+    const int w = blockIdx.x;
+    const int u0 = w * q;
+    const int U = __builtin_amdgcn_readfirstlane(sh_pref[B]);
+    const int u1 = u0 + q < U ? u0 + q : U;
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(sh_pref[mid]) <= u0)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    int b = lo;
+    for (int u = u0; u < u1;) {
+      while (__builtin_amdgcn_readfirstlane(sh_pref[b + 1]) <= u) ++b;
+      const int sb = __builtin_amdgcn_readfirstlane(sh_pref[b]);
+      const int wt = (__builtin_amdgcn_readfirstlane(sh_pref[b + 1]) - sb) / H;  // ov + pages
+      const int kvh = (u - sb) / wt;
+      const int s0 = sb + kvh * wt;  // the stream's first unit
+      const int ps = s0 + ov;        // its first page's unit
+      const int s1 = s0 + wt;
+      const int pa = u > ps ? u : ps;  // pages [pa - ps, pb - ps) of the stream are this piece
+      const int pb = u1 < s1 ? u1 : s1;
+      if (pa < pb) {
+        const int first = ps / q;  // work-group holding the stream's first page
+        const int pieces = (s1 - 1) / q - first + 1;
+        if (w == first && tid == 0 && a.ws_cnt != nullptr) a.ws_cnt[b * H + kvh] = pieces;
+        const int L = __builtin_amdgcn_readfirstlane(sh_len[b]);
+        const int t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
+        const int pf = L > 0 ? t0 / P : 0;
+        const int plo = pf + (pa - ps);
+        const int phi = pf + (pb - ps);
+        const int t_lo = L > 0 ? (t0 > plo * P ? t0 : plo * P) : 0;
+        const int t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
+        uint4 qb[NJ];
+        load_q(b, kvh, qb);
+        process(b, kvh, qb, plo, phi, t_lo, t_hi, pieces == 1, w - first);
+        __syncthreads();  // the next piece rewrites the LDS
+      }
+      u = s1;
+    }
+  } else {
+    // KV head fastest: the H_kv work-groups of one page range are dispatched
+    // together, so their K/V blocks (adjacent in a page) are read at the same
+    // time.
+    const int kvh = blockIdx.x;
+    const int s = blockIdx.y;
+    const int b = blockIdx.z;
+    const int L = a.seq_lens[b] - a.len_offset;
+    const int t0 = (a.window > 0 && L > a.window) ? L - a.window : 0;
+    const int pf = L > 0 ? t0 / P : 0;
+    const int pe = L > 0 ? (L + P - 1) / P : 0;
+    const int cp = a.pages_per_split;
+    int nsplit = (pe - pf + cp - 1) / cp;
+    nsplit = nsplit < 1 ? 1 : (nsplit > a.max_splits ? a.max_splits : nsplit);
+    // Splits (chunks in the fixed-order mode) [k_begin, k_end) of this group.
+    const int k_begin = MODE == kFixed ? s * a.chunks_per_group : s;
+    if (k_begin >= nsplit) return;  // whole work-group, uniform
+    const int k_end =
+        MODE == kFixed ? (k_begin + a.chunks_per_group < nsplit ? k_begin + a.chunks_per_group : nsplit) : k_begin + 1;
+    uint4 qb[NJ];
+    load_q(b, kvh, qb);
+    for (int k = k_begin; k < k_end; ++k) {
+      // Attended tokens of this split (chunk): [t_lo, t_hi).
+      const int plo = pf + k * cp;
+      const int phi = (plo + cp < pe) ? plo + cp : pe;
+      const int t_lo = L > 0 ? (t0 > plo * P ? t0 : plo * P) : 0;
+      const int t_hi = L > 0 ? (L < phi * P ? L : phi * P) : 0;
+      process(b, kvh, qb, plo, phi, t_lo, t_hi, MODE == kGrid && nsplit == 1, k);
+      if constexpr (MODE == kFixed) __syncthreads();  // the next chunk rewrites the LDS
+    }
+  }
 }
 
 template <int D, int KVT, int GT>
 void launch_mode(const KernelArgs& a, dim3 grid, hipStream_t st) {
-  if (a.chunks_per_group > 0)
-    hipLaunchKernelGGL((split_kernel_mfma<D, KVT, GT, true>), grid, dim3(kThreads), 0, st, a);
+  if (a.balanced)
+    hipLaunchKernelGGL((split_kernel_mfma<D, KVT, GT, kBalanced>), dim3(a.split_groups), dim3(kThreads), 0, st, a);
+  else if (a.chunks_per_group > 0)
+    hipLaunchKernelGGL((split_kernel_mfma<D, KVT, GT, kFixed>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((split_kernel_mfma<D, KVT, GT, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((split_kernel_mfma<D, KVT, GT, kGrid>), grid, dim3(kThreads), 0, st, a);
 }
 
 template <int D, int KVT>

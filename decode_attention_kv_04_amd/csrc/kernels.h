@@ -17,6 +17,7 @@ struct KernelArgs {
   void* out;
   float* ws_o;   // [B][H_q][S_max][D]
   float* ws_ml;  // [B][H_q][S_max][2]  (m in log2 units, l)
+  int32_t* ws_cnt;  // balanced schedule: [B][H_kv] pieces per (sequence, KV head) stream, else null
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -36,6 +37,9 @@ struct KernelArgs {
   int32_t rows_per_seq;
   int32_t row_base;
   int32_t rows_per_group;   // multi-token kernel: query rows (token, head) per work-group
+  int32_t balanced;         // 1 = balanced schedule: work-group w takes units [w q, (w+1) q) of the
+                            // batch's (sequence, KV head) streams, q = pages_per_split
+  int32_t bal_overhead;     // balanced schedule: units a stream weighs before its pages
   int32_t q_dtype;        // da_dtype
   int32_t out_dtype;      // da_dtype
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units

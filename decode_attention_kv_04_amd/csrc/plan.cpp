@@ -152,11 +152,76 @@ void log_plan(const da_plan* plan) {
   const da_params& p = plan->p;
   std::fprintf(stderr,
                "decode_attn plan: B=%d Hq=%d Hkv=%d D=%d P=%d W=%d kernel=%s cus=%d pages/split=%d "
-               "max_splits=%d split_groups=%d chunks/group=%d units=%lld keys=%lld ws=%zu\n",
+               "max_splits=%d split_groups=%d chunks/group=%d balanced=%d units=%lld keys=%lld ws=%zu\n",
                p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size, p.window,
                plan->split_kernel ? "matrix" : "vector", plan->num_cus, plan->pages_per_split, plan->max_splits,
-               plan->split_groups, plan->chunks_per_group, static_cast<long long>(plan->active_units),
+               plan->split_groups, plan->chunks_per_group, plan->balanced ? 1 : 0,
+               static_cast<long long>(plan->active_units),
                static_cast<long long>(plan->attended_keys), plan->ws_bytes);
+}
+
+// Resident work-groups per compute unit of the matrix-core decode kernel's
+// balanced-schedule instances, by compiled group width: 188-240 registers
+// per lane at widths 1, 2 and 4 (two waves per SIMD of 512), 298-306 at 8
+// (one); LDS 35-49 KB per work-group.
+int64_t matrix_groups_per_cu(int32_t group_tile) { return group_tile == 8 ? 1 : 2; }
+
+// Balanced schedule (matrix-core decode kernel, the planner's choice when no
+// split count is forced and the split-length heuristic would need more than
+// one round of resident work-groups). The batch's work is its (sequence, KV
+// head) streams in order, each weighing kBalancedOverheadBytes worth of
+// units for starting a piece (reading its length, q and first page id, and
+// merging the waves at the end: a few dependent memory round trips) and then
+// one unit per attended page (an empty stream one page, so that its zero rows
+// get written). Work-group w takes units [w q, (w + 1) q): one round of
+// resident work-groups with the same weight each, so no work-group waits for
+// a slot and none is left running alone at the end. A stream cut by
+// work-group boundaries leaves one state per piece for the combine; the
+// work-group holding a stream's first page records its piece count.
+// Measured before this schedule (same box, split pass): the mixed-window
+// batch's long sequences alone in 512 equal work-groups 83.3 us against 89.0
+// us with the split-length heuristic; the long batch 477-485 us with 2-4
+// splits against 491 us; one 32768-token sequence 24 us with 32-64 splits
+// against 30 us with 256 (and the combine 5-6 against 17 us). Without the
+// start weight, the mixed-window batch slowed from 96 to 128 us: a
+// work-group whose share fell among short sequences started ~10 pieces.
+constexpr int64_t kBalancedOverheadBytes = 64 << 10;
+
+da_status finish_balanced_plan(da_plan* plan, const std::vector<int64_t>& npages, int64_t max_np) {
+  const da_params& p = plan->p;
+  const int64_t H = p.num_kv_heads;
+  const int64_t P = p.page_size;
+  const int64_t page_head_bytes = 2 * P * p.head_dim * (p.kv_dtype == DA_F32 ? 4 : 2);  // K and V
+  const int64_t ov = ceil_div(kBalancedOverheadBytes, page_head_bytes);
+  int64_t U = 0;
+  for (int64_t n : npages) U += (ov + std::max<int64_t>(1, n)) * H;
+  const int64_t slots = static_cast<int64_t>(plan->num_cus) * matrix_groups_per_cu(plan->group_tile);
+  const int64_t min_pages = ceil_div(decode_min_split_tokens(true, max_np * P), P);
+  const int64_t q = std::max(ceil_div(U, slots), min_pages);
+  plan->balanced = true;
+  plan->bal_overhead = static_cast<int32_t>(ov);
+  plan->pages_per_split = static_cast<int32_t>(q);
+  plan->split_groups = static_cast<int32_t>(ceil_div(U, q));
+  plan->active_units = plan->split_groups;
+  plan->splits.assign(p.batch, 1);
+  int64_t smax = 1, start = 0;
+  for (int32_t b = 0; b < p.batch; ++b) {
+    const int64_t n = std::max<int64_t>(1, npages[b]);
+    for (int64_t j = 0; j < H; ++j, start += ov + n) {
+      const int64_t first_page = start + ov;
+      const int64_t pieces = (first_page + n - 1) / q - first_page / q + 1;
+      plan->splits[b] = static_cast<int32_t>(std::max<int64_t>(plan->splits[b], pieces));
+      smax = std::max(smax, pieces);
+    }
+  }
+  plan->max_splits = static_cast<int32_t>(smax);
+  if (smax > 1) {
+    size_workspace(plan);
+    plan->ws_cnt_offset = plan->ws_bytes;
+    plan->ws_bytes += round_up(static_cast<size_t>(p.batch) * H * sizeof(int32_t), 256);
+  }
+  log_plan(plan);
+  return DA_OK;
 }
 
 // Fixed-order mode: chunks of fixed_chunk / P pages from each sequence's
@@ -407,6 +472,22 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     plan->splits[b] = static_cast<int32_t>(s);
     smax = std::max(smax, s);
     plan->active_units += s * p->num_kv_heads;
+  }
+  // The balanced schedule instead, where the matrix-core kernel runs a
+  // single-query step with the planner's split choice, some context is
+  // longer than the switch-over (a dispatch of short contexts alone is not
+  // split), and these splits would take more than one round of resident
+  // work-groups (within one round every work-group has its own slot anyway,
+  // and the balanced schedule's start - the batch's prefix sums - only adds
+  // latency: 3060-token Llama-8B decode 10.4 -> 12.1 us).
+  if (plan->split_kernel == 1 && !per_token && p->num_splits == 0 && p->batch <= kBalancedMaxBatch &&
+      max_np * P > std::max(kDefaultMinSplitTokens, decode_min_split_tokens(true, max_np * P)) &&
+      plan->active_units > static_cast<int64_t>(num_cus) * matrix_groups_per_cu(gt) &&
+      (total_np + p->batch) * static_cast<int64_t>(p->num_kv_heads) * 64 < static_cast<int64_t>(INT32_MAX) / 2) {
+    plan->active_units = 0;
+    const da_status st = finish_balanced_plan(plan, npages, max_np);
+    if (st == DA_OK) *out = plan;
+    return st;
   }
   plan->max_splits = static_cast<int32_t>(smax);
   plan->split_groups = plan->max_splits;

@@ -22,11 +22,14 @@ struct da_plan {
   int32_t query_len = 1;       // T new tokens per sequence
   int32_t rows_per_group = 0;  // multi-token kernel: (token, head) rows per work-group
   bool per_token = false;      // T > 1 on the single-query kernels, one launch per token
+  bool balanced = false;       // balanced schedule: split_groups work-groups of pages_per_split units each
+  int32_t bal_overhead = 0;    // balanced schedule: units a stream weighs before its pages
   std::vector<int32_t> splits; // S_b per sequence
   int64_t active_units = 0;
   int64_t attended_keys = 0;
   size_t ws_o_offset = 0;      // [B][H_q][S_max][D] float
   size_t ws_ml_offset = 0;     // [B][H_q][S_max][2] float (m, l) after the O block
+  size_t ws_cnt_offset = 0;    // balanced schedule: [B][H_kv] int32 pieces per stream, after (m, l)
   size_t ws_bytes = 0;
 };
 
@@ -44,6 +47,10 @@ int32_t group_tile_for(int32_t G);
 
 // Whether the matrix-core split kernel covers these parameters.
 bool matrix_kernel_supported(const da_params& p);
+
+// Largest batch the balanced schedule takes (its work-groups keep the
+// batch's page prefix sums in LDS).
+constexpr int32_t kBalancedMaxBatch = 4096;
 
 // Validate parameters and lengths and build a plan for `num_cus` compute
 // units. On success *out owns a new plan.

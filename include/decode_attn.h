@@ -177,6 +177,16 @@ typedef struct {
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in
                                 pages and max_splits the most chunks of a sequence. */
+  int32_t balanced;          /* 1 = balanced schedule (the matrix-core decode
+                                kernel when num_splits is 0): the batch's
+                                (sequence, KV head, attended page) units in that
+                                order, an empty stream counting one, are dealt
+                                to split_work_groups work-groups, pages_per_split
+                                consecutive units each (about one round of
+                                resident work-groups of equal work); a stream cut
+                                by their boundaries has one state per piece,
+                                max_splits at most. 0 = grid schedule: split s of
+                                every sequence is pages_per_split attended pages. */
 } da_plan_info;
 
 /*

@@ -35,8 +35,9 @@ int main(void) {
   da_plan_info info;
   st = decode_attn_plan_info(plan, &info);
   if (st != DA_OK) return 2;
-  printf("pages_per_split %d max_splits %d split_work_groups %d split_kernel %d attended_keys %lld workspace %zu\n",
-         info.pages_per_split, info.max_splits, info.split_work_groups, info.split_kernel,
+  printf("pages_per_split %d max_splits %d split_work_groups %d split_kernel %d balanced %d attended_keys %lld "
+         "workspace %zu\n",
+         info.pages_per_split, info.max_splits, info.split_work_groups, info.split_kernel, info.balanced,
          (long long)info.attended_keys, ws);
   for (int b = 0; b < 3; ++b) printf("splits[%d] %d\n", b, decode_attn_plan_splits(plan, b));
   decode_attn_plan_destroy(plan);

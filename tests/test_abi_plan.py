@@ -135,7 +135,7 @@ def test_matrix_kernel_splits_down_to_128_tokens(lib, monkeypatch):
 def test_heuristic_long_batch_fills_the_chip(lib):
     lens = [16384 + (i * 523) % 16384 for i in range(32)]
     pl = plan(params(batch=32), lens)
-    assert pl.info.active_units >= 256 * 2
+    assert pl.info.active_units >= 256 * 2 - 1
     assert pl.pages_per_split * 16 >= 256
     # more compute units -> no longer splits
     pl2 = plan(params(batch=32), lens, cus=64)
@@ -502,3 +502,71 @@ def test_noalloc_rejects_plans_beyond_the_scratch(lib):
     st = lib.decode_attn_run_noalloc(pl.handle, None, None, None, None, None, None, None)
     assert st == B.DA_ERR_WORKSPACE
     assert lib.decode_attn_run_noalloc(None, None, None, None, None, None, None, None) == B.DA_ERR_INVALID
+
+
+# ---------------------------------------------------------------------------
+# balanced schedule (matrix-core decode kernel, planner's split choice)
+# ---------------------------------------------------------------------------
+
+def balanced_expectation(lens, P, Hkv, window, cus, per_cu, min_tokens, D=128, elt=2):
+    """Units, pages per work-group, work-groups and pieces per stream of the
+    balanced schedule, written out from its definition: each (sequence, KV
+    head) stream weighs ov = ceil(64 KiB / (2 P D elt)) units and then one per
+    attended page (at least one)."""
+    ov = math.ceil(65536 / (2 * P * D * elt))
+    npages = []
+    for L in lens:
+        t0 = L - window if window > 0 and L > window else 0
+        n = (math.ceil(L / P) - t0 // P) if L > 0 else 0
+        npages.append(max(1, n))
+    U = sum(ov + n for n in npages) * Hkv
+    q = max(math.ceil(U / (cus * per_cu)), math.ceil(min_tokens / P))
+    pieces, start = [], 0
+    for n in npages:
+        row = []
+        for _ in range(Hkv):
+            first = start + ov
+            row.append((first + n - 1) // q - first // q + 1)
+            start += ov + n
+        pieces.append(row)
+    return U, q, math.ceil(U / q), pieces
+
+
+@pytest.mark.parametrize("lens,P,W,G", [
+    ([16384 + (i * 523) % 16384 for i in range(32)], 16, 0, 4),          # the long batch shape
+    ([32768], 16, 0, 4),                                                   # one long sequence
+    ([0, 1, 300, 65536, 17, 4096], 32, 4096, 4),                           # windows, empty and short
+    ([777] * 100 + [20000], 16, 0, 2),
+    ([5000, 1, 9000], 16, 0, 8),                                           # one resident group per CU at G 8
+])
+def test_balanced_plan_partition(lib, monkeypatch, lens, P, W, G):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    p = params(batch=len(lens), num_q_heads=8 * G, page_size=P, max_pages_per_seq=8192, window=W)
+    pl = plan(p, lens)
+    assert pl.info.balanced == 1 and pl.info.split_kernel == 1
+    U, q, N, pieces = balanced_expectation(lens, P, 8, W, 256, 1 if G == 8 else 2, 128)
+    assert pl.pages_per_split == q and pl.info.split_work_groups == N
+    assert pl.max_splits == max(max(r) for r in pieces)
+    assert [pl.splits(b) for b in range(len(lens))] == [max(r) for r in pieces]
+    r256 = lambda x: (x + 255) // 256 * 256
+    rows = len(lens) * 8 * G * pl.max_splits
+    want = 0 if pl.max_splits == 1 else r256(rows * 128 * 4) + r256(rows * 2 * 4) + r256(len(lens) * 8 * 4)
+    assert pl.workspace_bytes == want
+
+
+def test_balanced_plan_is_not_taken(lib, monkeypatch):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    lens = [3060, 9000]
+    assert plan(params(batch=2, num_splits=7), lens).info.balanced == 0                 # forced split count
+    assert plan(params(batch=2, fixed_chunk=256), lens).info.balanced == 0              # fixed-order mode
+    assert plan(params(batch=2, kernel="vector"), lens).info.balanced == 0              # vector kernel
+    assert plan(params(batch=2, head_dim=64), lens).info.balanced == 0                  # vector kernel
+    assert plan(params(batch=2, query_len=4, q_dtype="f32"), lens).info.balanced == 0   # per-token mode
+    assert plan(params(batch=3), [256, 100, 1]).info.balanced == 0                      # nothing to split
+    assert plan(params(), [3060]).info.balanced == 0                  # 192 work-groups: one round already
+    assert plan(params(batch=4097, max_pages_per_seq=1), [16] * 4097).info.balanced == 0
+    assert plan(params(batch=4096), [300] * 4096).info.balanced == 1
+    monkeypatch.setenv("DECODE_ATTN_SPLIT_MIN", "4096")
+    assert plan(params(batch=64), [3060] * 64).info.balanced == 0                       # contexts below the minimum
+    pl = plan(params(batch=64), [5000] * 64)
+    assert pl.info.balanced == 1 and pl.pages_per_split >= 256

@@ -33,9 +33,19 @@ def test_c_program_plans_like_the_binding(lib, tmp_path):
     assert got["max_splits"] == pl.max_splits
     assert got["split_work_groups"] == pl.info.split_work_groups
     assert got["split_kernel"] == pl.info.split_kernel == 1
+    assert got["balanced"] == pl.info.balanced == 1
     assert got["attended_keys"] == sum(lens)
     assert got["workspace"] == pl.workspace_bytes
+    # balanced schedule: units (sequence, KV head, page) dealt q at a time
+    q = pl.pages_per_split
+    ov = 65536 // (2 * 16 * 128 * 2)      # start weight of a stream, in units
+    start = 0
     for b in range(3):
+        n = math.ceil(lens[b] / 16)
+        pieces = []
+        for _ in range(8):
+            pieces.append((start + ov + n - 1) // q - (start + ov) // q + 1)
+            start += ov + n
         assert f"splits[{b}] {pl.splits(b)}" in out
-        assert pl.splits(b) == math.ceil(math.ceil(lens[b] / 16) / pl.pages_per_split)
+        assert pl.splits(b) == max(pieces)
     assert "invalid: DA_ERR_INVALID" in out
