@@ -29,13 +29,9 @@ namespace {
 
 constexpr int kRowsPerGroup = 4;  // one wave per row, four rows per work-group
 
-template <int D>
-__global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const KernelArgs a) {
-  const int h = blockIdx.x * kRowsPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  if (h >= a.num_q_heads) return;  // whole wave
-
+// States to merge for query head h of sequence b; 0 if the split pass wrote
+// the row itself (a single split, outside the fixed-order mode).
+__device__ __forceinline__ int split_count(const KernelArgs& a, int b, int h) {
   int64_t nsplit;
   if (a.ws_cnt != nullptr) {
     // Balanced schedule: the split pass recorded the pieces of each
@@ -50,13 +46,68 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const Kerne
     nsplit = (pe - pf + a.pages_per_split - 1) / a.pages_per_split;
   }
   if (nsplit > a.max_splits) nsplit = a.max_splits;
-  if (a.chunks_per_group > 0) {
-    if (nsplit < 1) nsplit = 1;  // fixed-order mode: every row is merged here
-  } else if (nsplit <= 1) {
-    return;  // the split pass wrote this row
-  }
+  if (a.chunks_per_group > 0) return nsplit < 1 ? 1 : static_cast<int>(nsplit);  // fixed order: every row
+  return nsplit <= 1 ? 0 : static_cast<int>(nsplit);
+}
 
-  merge_head_wave<D>(a, static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h, static_cast<int>(nsplit), lane);
+template <int D>
+__global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const KernelArgs a) {
+  const int h = blockIdx.x * kRowsPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (h >= a.num_q_heads) return;  // whole wave
+  const int nsplit = split_count(a, b, h);
+  if (nsplit <= 0) return;  // the split pass wrote this row
+  merge_head_wave<D>(a, static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h, nsplit, lane);
+}
+
+// Rows with many states (plans with more than kWideSplits states per row):
+// four waves per row, one row per work-group. Wave w merges states [w S / 4,
+// (w + 1) S / 4) (merge_range_wave), then the four partial states are merged
+// through LDS in wave order:
+//     M = max_w M_w,  a_w = 2^(M_w - M),  out = sum_w a_w acc_w / sum_w a_w lsum_w
+// (a_w = 0 for a wave with no state). The wave count depends only on the
+// plan, so results are identical run to run (and, in the fixed-order mode,
+// for every split count: its state count is the chunk count).
+constexpr int kWideSplits = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_wide_kernel(const KernelArgs a) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nsplit = split_count(a, b, h);
+  if (nsplit <= 0) return;  // the split pass wrote this row
+  const int64_t qrow = static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h;
+  constexpr int N = D / 64;
+  __shared__ float sh_acc[4][D];
+  __shared__ float sh_ml[4][2];
+  float M, lsum, acc[N];
+  merge_range_wave<D>(a, qrow, wave * nsplit / 4, (wave + 1) * nsplit / 4, lane, M, lsum, acc);
+#pragma unroll
+  for (int i = 0; i < N; ++i) sh_acc[wave][lane + 64 * i] = acc[i];
+  if (lane == 0) {
+    sh_ml[wave][0] = M;
+    sh_ml[wave][1] = lsum;
+  }
+  __syncthreads();
+  float Mt = sh_ml[0][0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) Mt = fmaxf(Mt, sh_ml[w][0]);
+  const float Mu = (Mt == -INFINITY) ? 0.0f : Mt;
+  float aw[4], lt = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    aw[w] = exp2_fast(sh_ml[w][0] - Mu);
+    lt += aw[w] * sh_ml[w][1];
+  }
+  for (int d = threadIdx.x; d < D; d += 256) {
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o = fmaf(aw[w], sh_acc[w][d], o);
+    store_elem(a.out, qrow * D + d, a.out_dtype, lt > 0.0f ? o / lt : 0.0f);
+  }
 }
 
 // Merge of one row by 32 lanes (half a wave): lane j owns elements E j ..
@@ -176,6 +227,16 @@ hipError_t launch_combine(const KernelArgs& a, int head_dim, hipStream_t stream)
       case 64: hipLaunchKernelGGL(combine_multi_kernel<64>, grid, block, 0, stream, a); break;
       case 128: hipLaunchKernelGGL(combine_multi_kernel<128>, grid, block, 0, stream, a); break;
       case 256: hipLaunchKernelGGL(combine_multi_kernel<256>, grid, block, 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  if (a.max_splits > kWideSplits) {
+    const dim3 grid(a.num_q_heads, a.batch);
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL(combine_wide_kernel<64>, grid, dim3(256), 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(combine_wide_kernel<128>, grid, dim3(256), 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(combine_wide_kernel<256>, grid, dim3(256), 0, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
