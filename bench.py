@@ -634,6 +634,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--no-multi-token", action="store_true", help="skip the multi-token workloads")
+    ap.add_argument("--layer-step-only", action="store_true",
+                    help="only the 32-layer decode step of the Llama-3.1-8B shape at 3060 tokens (for traces)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the context-length sweep (Llama shape, L 256..65536, batch 1 and 32)")
     ap.add_argument("--calibrate", action="store_true",
@@ -657,6 +659,12 @@ def main():
     stream = torch.cuda.current_stream()
     lib = binding.load()
     sptr = stream.cuda_stream
+
+    if args.layer_step_only:
+        ls = measure_layer_step(binding, workloads, dev, stream, args.steps)
+        print(json.dumps({"metric": METRIC, "layer_step": ls, "n_gpus": 1, "data": "synthetic",
+                          "kernel_source_sha256_16": kernel_hash()}), flush=True)
+        return
 
     if args.sweep:
         sweep = measure_sweep(binding, workloads, lib, dev, stream, args.rounds)
