@@ -565,8 +565,29 @@ def test_balanced_plan_is_not_taken(lib, monkeypatch):
     assert plan(params(batch=3), [256, 100, 1]).info.balanced == 0                      # nothing to split
     assert plan(params(), [3060]).info.balanced == 0                  # 192 work-groups: one round already
     assert plan(params(batch=4097, max_pages_per_seq=1), [16] * 4097).info.balanced == 0
-    assert plan(params(batch=4096), [300] * 4096).info.balanced == 1
+    assert plan(params(batch=4096), [300, 2000] * 2048).info.balanced == 1
     monkeypatch.setenv("DECODE_ATTN_SPLIT_MIN", "4096")
-    assert plan(params(batch=64), [3060] * 64).info.balanced == 0                       # contexts below the minimum
-    pl = plan(params(batch=64), [5000] * 64)
+    assert plan(params(batch=64), [3060, 1000] * 32).info.balanced == 0                 # contexts below the minimum
+    pl = plan(params(batch=64), [5000, 1500] * 32)
     assert pl.info.balanced == 1 and pl.pages_per_split >= 256
+
+
+# Whole streams: at least one (sequence, KV head) stream per compute unit and
+# about equal lengths -> no split (one launch, no combine), on either kernel.
+@pytest.mark.parametrize("B,L,kw", [(32, 512, {}), (32, 4096, {}), (128, 512, {}), (64, 1024, {}),
+                                     (48, 3060, {}), (32, 2048, dict(head_dim=64)),
+                                     (32, 2048, dict(window=1000))])
+def test_whole_streams_are_not_split(lib, monkeypatch, B, L, kw):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    pl = plan(params(batch=B, max_pages_per_seq=4096, **kw), [L] * B)
+    assert pl.max_splits == 1 and pl.workspace_bytes == 0 and pl.info.balanced == 0
+    # lengths within 10 % of each other still count as equal
+    lens = [L - (b % 5) * (L // 60) for b in range(B)]
+    assert plan(params(batch=B, max_pages_per_seq=4096, **kw), lens).max_splits == 1
+
+
+@pytest.mark.parametrize("B,lens", [(8, [4096] * 8), (32, [1024 + 224 * b for b in range(32)]),
+                                    (16, [2048] * 16)])
+def test_whole_streams_need_equal_lengths_and_enough_streams(lib, monkeypatch, B, lens):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    assert plan(params(batch=B, max_pages_per_seq=4096), lens).max_splits > 1

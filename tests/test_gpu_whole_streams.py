@@ -1,0 +1,45 @@
+"""Whole streams: a batch with at least one (sequence, KV head) stream per
+compute unit and about equal attended lengths runs unsplit (one work-group per
+stream, no combine, no workspace). Such batches on both split kernels, with
+windows, ragged lengths within the equal-length band and several new tokens
+per sequence, against the oracle, and against a forced split count of the same
+kernel within fp32 rounding."""
+import numpy as np
+import pytest
+
+from decode_attention_kv_04_amd import workloads as wl
+
+from gpu_util import check, host64, oracle_for, run_lib, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, H_q, H_kv, D, q/kv dtype, out, page, lengths, window, query_len
+    (32, 32, 8, 128, "f16", "f16", 16, ("fixed", 2048), 0, 1),
+    (32, 32, 8, 128, "bf16", "f32", 32, ("uniform", 1900, 2050), 1000, 1),
+    (64, 16, 4, 64, "f16", "f32", 16, ("fixed", 777), 0, 1),
+    (32, 8, 8, 128, "f16", "f16", 16, ("fixed", 1500), 0, 1),        # one head per group: vector kernel
+    (32, 32, 8, 128, "f32", "f32", 16, ("fixed", 1024), 0, 1),       # fp32 K/V: vector kernel
+    (256, 32, 8, 128, "f16", "f16", 16, ("uniform", 300, 320), 0, 1),
+    (32, 32, 8, 128, "f32", "f32", 16, ("fixed", 600), 200, 3),      # three new tokens, once per token
+]
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_whole_streams_match_oracle(gpu, i):
+    B, HQ, HKV, D, dt, out, P, lens, W, T = CASES[i]
+    spec = wl.WorkloadSpec(f"whole{i}", B, HQ, HKV, D, dt, dt, out, P, lens, seed=7400 + i, window=W,
+                           spike_frac=0.01, query_len=T)
+    say(f"[whole streams {i}] B={B} H={HQ}/{HKV} D={D} {dt}->{out} P={P} lens={lens} W={W} T={T}")
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w)
+    assert plan.max_splits == 1 and plan.workspace_bytes == 0 and plan.info.balanced == 0
+    say(f"  split kernel {plan.info.split_kernel}, work-groups {plan.info.split_work_groups}")
+    err, worst = check(got, oracle_for(w), dt, out, f"whole streams {i}")
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
+    split, splan = run_lib(w, num_splits=3, twin=False)
+    assert splan.max_splits > 1
+    a = host64(got.f32_twin if hasattr(got, "f32_twin") else got)
+    b = host64(split)
+    if out == "f32":
+        assert np.linalg.norm(a - b) <= 2e-6 * np.linalg.norm(b)
