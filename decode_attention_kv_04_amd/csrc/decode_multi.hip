@@ -119,7 +119,10 @@ __device__ __forceinline__ void init_rows(RowGroup<D>& g, const KernelArgs& a, i
       g.qb[ks] = make_uint4((v.x ^ qx) & qa, (v.y ^ qx) & qa, (v.z ^ qx) & qa, (v.w ^ qx) & qa);
     }
   }
-  g.m = -INFINITY;
+  // A lane of no row gets the reference +inf: every slack test below passes
+  // for it and its probabilities are 0 (or NaN where K holds NaN), which
+  // reach only its own column of S^T and O^T, never written out.
+  g.m = g.ok ? -INFINITY : INFINITY;
   g.lsum = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) g.o[nb] = mq_float4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -174,6 +177,7 @@ __device__ __forceinline__ void make_p(const float (&x)[8], float sl2, float nmu
     pl = make_uint4(wl[0], wl[1], wl[2], wl[3]);
   }
 }
+
 
 // O^T += V^T P^T and the row sums of P for NR row groups. The sums run on
 // the matrix cores (one more product per row group instead of eight
@@ -391,13 +395,21 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// Stages in the LDS ring (NS - 1 tiles in flight). 2 and 3 measured the
-// same on the 128- and 512-token suffixes; 3 leaves more slack for latency.
-// At head_dim 256 a stage holds 32 KiB; two stages keep two work-groups per
-// compute unit.
-template <int D>
+// Stages in the LDS ring. The 16-row blocks and head_dim 256 compute each
+// tile within its own ring step: NS - 1 tiles in flight (2 and 3 stages
+// measured the same; at head_dim 256 a stage holds 32 KiB and two stages keep
+// two work-groups per compute unit). The pipelined row blocks (head_dim 64
+// and 128) hold two tiles at once (tile m's V and tile m + 1's K): NS - 2
+// tiles in flight, 4 stages (64 KiB per work-group at head_dim 128).
+template <int D, bool PIPE>
 constexpr int lds_stages() {
-  return D >= 256 ? 2 : 3;
+  return D >= 256 ? 2 : (PIPE ? 4 : 3);
+}
+
+template <int NS>
+__device__ __forceinline__ int ring(int s, int d) {
+  s += d;
+  return s >= NS ? s - NS : s;
 }
 
 // FEW: blocks of 16 rows (a few drafted tokens): wave 0 computes them and
@@ -415,6 +427,9 @@ multi_dma_kernel(const KernelArgs a) {
   constexpr int KPC = 1024 / ROWB; // key rows per 1 KiB copy
   constexpr int NCP = 8 / KPC;     // copies per wave per tile and tensor
   constexpr int LOADS = 2 * NCP;   // copies per wave per tile (K and V)
+  constexpr bool PIPE = !FEW && D <= 128;  // software-pipelined plain tiles
+  constexpr int LEAD = PIPE ? NS - 2 : NS - 1;  // tiles in flight ahead of the one begun
+  static_assert(NS == lds_stages<D, PIPE>() && LEAD >= 1, "ring");
   static_assert(NS >= 2 && 2 * NS * TILE * 2 <= 65536, "LDS ring");
   __shared__ __align__(1024) uint16_t sk[NS][TILE];
   __shared__ __align__(1024) uint16_t sv[NS][TILE];
@@ -466,6 +481,20 @@ multi_dma_kernel(const KernelArgs a) {
   // for every copy in flight on each tile (vmcnt(0), other counters at
   // their maximum: the gfx9 encoding).
   __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // Keys inside every row of this wave: rows r0 .. r1 (tokens t0 .. t1)
+  // attend [lo(t), hi(t)) with both bounds growing in t, so the common keys
+  // are [lo(t1), hi(t0)); a wave without rows takes the split's keys.
+  int w_lo = t_lo, w_hi = t_hi;
+  {
+    const int r0 = r_first + (FEW ? 0 : wave * NR * 16);
+    const int r1 = r0 + (FEW ? 16 : NR * 16) - 1 < r_last ? r0 + (FEW ? 16 : NR * 16) - 1 : r_last;
+    if (r0 <= r1) {
+      const int t0 = r0 / G, t1 = r1 / G;
+      w_hi = L - T + t0 + 1 < t_hi ? L - T + t0 + 1 : t_hi;
+      if (W > 0) w_lo = L - T + t1 + 1 - W > t_lo ? L - T + t1 + 1 - W : t_lo;
+    }
+  }
 
   const int tile_first = t_lo / KT;
   const int ntiles = t_hi > t_lo ? (t_hi + KT - 1) / KT - tile_first : 0;
@@ -523,25 +552,33 @@ multi_dma_kernel(const KernelArgs a) {
   const int vh = (col & 1) * 4;
   const float sl2 = positive_scale(a.scale_log2);
 
+  // Ring steps, shared by every wave: the begin of tile j waits for this
+  // wave's copies of tile j (at most the LEAD - 1 later tiles' copies stay
+  // outstanding), passes the barrier (every wave's copies of tile j have
+  // landed, and every wave is done with the stage the next copy overwrites),
+  // and sends out the copies of tile j + LEAD. The last tiles wait for every
+  // copy, so none is left in flight.
+  auto begin_copies = [&](int j, int sj) {
+    if (j + LEAD - 1 < ntiles)
+      wait_loads<(LEAD - 1) * LOADS>();
+    else
+      wait_loads<0>();
+    lds_barrier();
+    if (j + LEAD < ntiles) issue(ring<NS>(sj, LEAD));
+  };
+
   if constexpr (FEW) {
     if (wave != 0) {
-      // Copies only, with the ring steps of begin_tile below: per tile one
-      // wait for this wave's copies, one barrier, the copy NS - 1 tiles ahead.
-      // The last tiles wait for every copy, so none is left in flight.
+      // Copies only, the same ring steps as the computing wave.
       if (ntiles > 0) {
         fetch_id();
 #pragma unroll
-        for (int k = 0; k < NS - 1; ++k)
+        for (int k = 0; k < LEAD; ++k)
           if (k < ntiles) issue(k);
         int stage = 0;
         for (int m = 0; m < ntiles; ++m) {
-          if (m + NS - 2 < ntiles)
-            wait_loads<(NS - 2) * LOADS>();
-          else
-            wait_loads<0>();
-          lds_barrier();
-          if (m + NS - 1 < ntiles) issue(stage == 0 ? NS - 1 : stage - 1);
-          stage = stage == NS - 1 ? 0 : stage + 1;
+          begin_copies(m, stage);
+          stage = ring<NS>(stage, 1);
         }
       }
       return;
@@ -550,32 +587,22 @@ multi_dma_kernel(const KernelArgs a) {
   if (ntiles > 0) {
     fetch_id();
 #pragma unroll
-    for (int k = 0; k < NS - 1; ++k)
+    for (int k = 0; k < LEAD; ++k)
       if (k < ntiles) issue(k);
     int stage = 0;
     int m = 0;
     mq_float4 sacc[NR][2];
     uint4 vt[D / 16];
-    // Start of tile m: its copies landed (this wave's: at most the copies of
-    // the later tiles already issued are outstanding; every wave's: the
-    // barrier, which also ends every wave's reads of the stage the next copy
-    // overwrites), the copy NS - 1 tiles ahead goes out, then S^T and all
-    // V^T operands of the tile (read before the softmax so that their
-    // latency hides behind it).
-    auto begin_tile = [&]() {
-      if (m + NS - 2 < ntiles)
-        wait_loads<(NS - 2) * LOADS>();
-      else
-        wait_loads<0>();
-      lds_barrier();
-      if (m + NS - 1 < ntiles) issue(stage == 0 ? NS - 1 : stage - 1);
-      const uint16_t* ks_ = sk[stage];
-      const uint16_t* vs_ = sv[stage];
+    auto scores = [&](int sj, mq_float4(&acc)[NR][2]) {
+      const uint16_t* ks_ = sk[sj];
       tile_scores<D, KVT, NR>(
           [&](int kb, int kstep) {
             return *reinterpret_cast<const uint4*>(&ks_[(kb * 16 + col) * D + (((4 * kstep + q4) ^ fk) * 8)]);
           },
-          rg, sacc);
+          rg, acc);
+    };
+    auto read_v = [&](int sj) {
+      const uint16_t* vs_ = sv[sj];
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) {
         const uint16_t* p = &vs_[vkey * D + (((2 * nb + vbc) ^ fv) * 8) + vh];
@@ -584,34 +611,93 @@ multi_dma_kernel(const KernelArgs a) {
         vt[nb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     };
+    // A tile is plain when it lies inside the split's keys and inside the
+    // keys of every row of this wave (wave-uniform bounds w_lo, w_hi) and no
+    // score of it exceeds its row's reference by more than the slack: then
+    // nothing is masked and no reference moves (tile_update_plain).
+    auto is_plain = [&](int tb, const mq_float4(&sc)[NR][2]) {
+      if (tb < w_lo || tb + KT > w_hi) return false;
+      bool ok = true;
+#pragma unroll
+      for (int g = 0; g < NR; ++g) {
+        float mt = sc[g][0][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sc[g][j >> 2][j & 3]);
+        ok = ok & (mt * sl2 <= rg[g].m + kSlack);
+      }
+      return static_cast<bool>(__all(ok));
+    };
     // Waves whose rows all lie past the block's last row compute too (on
     // zero q; nothing of theirs is written): a branch around the work would
     // put every accumulator through a join, and the compiler then copies
     // them on each tile. Likewise the tiles that need masks or move a
-    // reference leave the inner loop for the general update below, so that
-    // the inner loop carries O only through its matrix products.
+    // reference leave the plain loop for the general update below, so that
+    // the plain loop carries O only through its matrix products.
     while (m < ntiles) {
-      for (; m < ntiles; ++m) {
-        begin_tile();
-        const int tb = (tile_first + m) * KT;
-        if (tb < t_lo || tb + KT > t_hi) break;  // straddles the split's keys
-        bool plain = true;
+      begin_copies(m, stage);
+      scores(stage, sacc);
+      if constexpr (PIPE) {
+        // Software pipeline over plain tiles followed by another tile: tile
+        // m + 1 is begun and its S^T products go out together with tile m's
+        // softmax and P.V products (tile m's V and tile m + 1's K are both
+        // resident: LEAD = NS - 2). Unrolled by two with the score
+        // registers alternating, so that no scores are copied per tile.
+        mq_float4 sb[NR][2];
+        auto step = [&](mq_float4(&cur)[NR][2], mq_float4(&nxt)[NR][2]) {
+          const int sn = ring<NS>(stage, 1);
+          begin_copies(m + 1, sn);
+          read_v(stage);
+          scores(sn, nxt);
+          tile_update_plain<D, KVT, NR>(cur, [&](int nb) { return vt[nb]; }, rg, sl2);
+          // Scheduling groups for this block: the next tile's K operand
+          // reads first, then each S^T product with three vector
+          // instructions and one V^T read, then the P.V products. What the
+          // compiler makes of them (it puts this tile's softmax ahead of the
+          // products) measured 3-4 % faster than its own order and than a
+          // strict one-product-one-exponential interleave (128-token suffix
+          // 84.6 / 81.5 / 83.0 us, 512-token suffix 251 / 251 / 258 us).
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * NR, 0);
 #pragma unroll
-        for (int g = 0; g < NR; ++g) {
-          float mt = sacc[g][0][0];
+          for (int i = 0; i < 8 * NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 9 * NR, 0);
+          stage = sn;
+          ++m;
+        };
+        for (;;) {
+          if (m + 1 >= ntiles || !is_plain((tile_first + m) * KT, sacc)) break;
+          step(sacc, sb);
+          if (m + 1 >= ntiles || !is_plain((tile_first + m) * KT, sb)) {
 #pragma unroll
-          for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sacc[g][j >> 2][j & 3]);
-          plain = plain && (!rg[g].ok || (tb >= rg[g].lo && tb + KT <= rg[g].hi && mt * sl2 <= rg[g].m + kSlack));
+            for (int g = 0; g < NR; ++g) {
+              sacc[g][0] = sb[g][0];
+              sacc[g][1] = sb[g][1];
+            }
+            break;
+          }
+          step(sb, sacc);
         }
-        if (!__all(plain)) break;
-        tile_update_plain<D, KVT, NR>(sacc, [&](int nb) { return vt[nb]; }, rg, sl2);
-        stage = stage == NS - 1 ? 0 : stage + 1;
+      } else {
+        for (;;) {
+          if (!is_plain((tile_first + m) * KT, sacc)) break;
+          read_v(stage);
+          tile_update_plain<D, KVT, NR>(sacc, [&](int nb) { return vt[nb]; }, rg, sl2);
+          stage = ring<NS>(stage, 1);
+          ++m;
+          if (m >= ntiles) break;
+          begin_copies(m, stage);
+          scores(stage, sacc);
+        }
       }
       if (m >= ntiles) break;
-      // Tile m, already begun: V rows of keys outside [t_lo, t_hi) may
+      // Tile m, begun and scored: V rows of keys outside [t_lo, t_hi) may
       // hold anything, so tiles that straddle those keys clear them in the
       // operand (keys 4 q4 + j and 16 + 4 q4 + j, two per dword); then the
       // general update with masks and reference moves.
+      read_v(stage);
       const int tb = (tile_first + m) * KT;
       if (tb < t_lo || tb + KT > t_hi) {
         uint32_t vmask[4];
@@ -630,7 +716,7 @@ multi_dma_kernel(const KernelArgs a) {
         }
       }
       tile_update<D, KVT, NR>(sacc, [&](int nb, bool) { return vt[nb]; }, tb, rg, sl2, q4);
-      stage = stage == NS - 1 ? 0 : stage + 1;
+      stage = ring<NS>(stage, 1);
       ++m;
     }
   }
@@ -641,14 +727,15 @@ multi_dma_kernel(const KernelArgs a) {
 template <int D, int KVT>
 hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
   if (rows == 16) {
-    hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 1, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D, false>(), 1, true>), grid, dim3(256), 0, st, a);
   } else if (rows == 64) {
-    hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 1>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D, D <= 128>(), 1>), grid, dim3(256), 0, st, a);
   } else if (rows == 128) {
     if constexpr (D <= 128)
-      hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D>(), 2>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D, true>(), 2>), grid, dim3(256), 0, st, a);
     else
       return hipErrorInvalidValue;
+
   } else {
     return hipErrorInvalidValue;
   }
