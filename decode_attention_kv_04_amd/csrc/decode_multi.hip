@@ -528,6 +528,8 @@ multi_dma_kernel(const KernelArgs a) {
     pi = pi < a.max_pages ? pi : a.max_pages - 1;
     cphys = table_row[pi];
   };
+  // Copies of the next tile from the page id fetched last (fetch_id after
+  // each issue, before the next).
   auto issue = [&](int stage) {
     const int64_t off = static_cast<int64_t>(cphys) * page_bytes + static_cast<int64_t>(coff) * ROWB;
     const uint32_t lk = lds_address(&sk[stage][8 * wave * D]);
@@ -541,7 +543,6 @@ multi_dma_kernel(const KernelArgs a) {
       coff -= P;
       ++cpi;
     }
-    fetch_id();
   };
 
   // Operand addresses (16-bit elements within a stage).
@@ -558,13 +559,20 @@ multi_dma_kernel(const KernelArgs a) {
   // landed, and every wave is done with the stage the next copy overwrites),
   // and sends out the copies of tile j + LEAD. The last tiles wait for every
   // copy, so none is left in flight.
-  auto begin_copies = [&](int j, int sj) {
+  // The page id for the copy after that is read here, or (defer) by the
+  // caller once its LDS reads are consumed: a scalar load shares the LDS
+  // reads' wait counter and may complete out of order, so while one is
+  // outstanding every wait for an LDS read waits for all of them.
+  auto begin_copies = [&](int j, int sj, bool defer = false) {
     if (j + LEAD - 1 < ntiles)
       wait_loads<(LEAD - 1) * LOADS>();
     else
       wait_loads<0>();
     lds_barrier();
-    if (j + LEAD < ntiles) issue(ring<NS>(sj, LEAD));
+    if (j + LEAD < ntiles) {
+      issue(ring<NS>(sj, LEAD));
+      if (!defer) fetch_id();
+    }
   };
 
   if constexpr (FEW) {
@@ -574,7 +582,10 @@ multi_dma_kernel(const KernelArgs a) {
         fetch_id();
 #pragma unroll
         for (int k = 0; k < LEAD; ++k)
-          if (k < ntiles) issue(k);
+          if (k < ntiles) {
+            issue(k);
+            fetch_id();
+          }
         int stage = 0;
         for (int m = 0; m < ntiles; ++m) {
           begin_copies(m, stage);
@@ -588,7 +599,10 @@ multi_dma_kernel(const KernelArgs a) {
     fetch_id();
 #pragma unroll
     for (int k = 0; k < LEAD; ++k)
-      if (k < ntiles) issue(k);
+      if (k < ntiles) {
+        issue(k);
+        fetch_id();
+      }
     int stage = 0;
     int m = 0;
     mq_float4 sacc[NR][2];
@@ -645,7 +659,7 @@ multi_dma_kernel(const KernelArgs a) {
         mq_float4 sb[NR][2];
         auto step = [&](mq_float4(&cur)[NR][2], mq_float4(&nxt)[NR][2]) {
           const int sn = ring<NS>(stage, 1);
-          begin_copies(m + 1, sn);
+          begin_copies(m + 1, sn, true);
           read_v(stage);
           scores(sn, nxt);
           tile_update_plain<D, KVT, NR>(cur, [&](int nb) { return vt[nb]; }, rg, sl2);
@@ -664,6 +678,8 @@ multi_dma_kernel(const KernelArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 9 * NR, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (m + 1 + LEAD < ntiles) fetch_id();
           stage = sn;
           ++m;
         };
