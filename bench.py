@@ -247,17 +247,32 @@ def measure_multi_token(binding, workloads, lib, dev, stream, iters):
             if st != 0:
                 raise binding.DecodeAttnError(st, f"decode_attn_run ({name})")
 
+        def split():
+            st = lib.decode_attn_split(plan.handle, *ptrs)
+            if st != 0:
+                raise binding.DecodeAttnError(st, f"decode_attn_split ({name})")
+
         for _ in range(3):
             run()
         ms = time_on_stream(run, iters, stream)
+        ms_split = time_on_stream(split, iters, stream)
         by, fl = w.kv_bytes(), attention_flops(w)
-        gbs, tfs = by / (ms * 1e-3) / 1e9, fl / (ms * 1e-3) / 1e12
         hbm = fl / by < ridge
+
+        def frac(t_ms):
+            return round(by / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS if hbm
+                         else fl / (t_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_16BIT, 4)
+
+        gbs, tfs = by / (ms * 1e-3) / 1e9, fl / (ms * 1e-3) / 1e12
+        # "frac" places the dominant kernel (the split pass) against its
+        # roofline, as the headline does; "step_frac" the whole step (with
+        # the combine).
         res.append({"workload": spec.name, "query_len": spec.query_len, "us": round(ms * 1e3, 2),
-                    "GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 1), "bound": "hbm" if hbm else "mfma",
-                    "frac": round(gbs / HBM_PEAK_GBPS if hbm else tfs / MFMA_PEAK_TFLOPS_16BIT, 4),
+                    "split_us": round(ms_split * 1e3, 2), "GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 1),
+                    "split_TFLOP_s": round(fl / (ms_split * 1e-3) / 1e12, 1), "bound": "hbm" if hbm else "mfma",
+                    "frac": frac(ms_split), "step_frac": frac(ms),
                     "algorithmic_bytes": by, "flops": fl, "work_groups": plan.info.split_work_groups})
-        print(f"[bench] {name}: {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        print(f"[bench] {name}: {ms * 1e3:.1f} us (split pass {ms_split * 1e3:.1f} us)", file=sys.stderr, flush=True)
         del w, out, ws
         torch.cuda.empty_cache()
     return res
