@@ -751,7 +751,6 @@ hipError_t launch_nq(const KernelArgs& a, int rows, dim3 grid, hipStream_t st) {
       hipLaunchKernelGGL((multi_dma_kernel<D, KVT, lds_stages<D, true>(), 2>), grid, dim3(256), 0, st, a);
     else
       return hipErrorInvalidValue;
-
   } else {
     return hipErrorInvalidValue;
   }
