@@ -178,7 +178,7 @@ int64_t matrix_groups_per_cu(int32_t group_tile) { return group_tile == 8 ? 1 : 
 // a slot and none is left running alone at the end. A stream cut by
 // work-group boundaries leaves one state per piece for the combine; the
 // work-group holding a stream's first page records its piece count.
-// Measured before this schedule (same box, split pass): the mixed-window
+// Measured before this schedule (same machine, split pass): the mixed-window
 // batch's long sequences alone in 512 equal work-groups 83.3 us against 89.0
 // us with the split-length heuristic; the long batch 477-485 us with 2-4
 // splits against 491 us; one 32768-token sequence 24 us with 32-64 splits
