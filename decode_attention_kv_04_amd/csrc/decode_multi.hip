@@ -322,15 +322,22 @@ __device__ __forceinline__ void finish_rows(const KernelArgs& a, RowGroup<D>& g,
 // The K and V tiles go from HBM into LDS without passing through registers:
 // global_load_lds_dwordx4 writes lane i's 16 bytes at a wave-uniform LDS
 // address + 16 i, so a wave instruction fills 1 KiB (four 256-byte or eight
-// 128-byte key rows). Tiles are kept in a ring of NS LDS stages, NS - 1
-// tiles ahead of the one being computed, and every wave loads its own 8 keys
-// of each tile (one page, as pages hold a multiple of 8 keys), so a tile
-// costs a wave one scalar page lookup and D / 32 load instructions.
+// 128-byte key rows). Tiles are kept in a ring of LDS stages, and every
+// wave copies its own 8 keys of each tile (one page, as pages hold a
+// multiple of 8 keys): one scalar page lookup and D / 32 load instructions.
 //
-// Layout of a stage: K and V both row-major (key rows of 2 D bytes), the
-// 16-byte segment c of tile key k stored in slot c ^ swz(k). A K operand read
-// (16 keys, one segment each) then touches 16 different slots, and V^T is
-// read with the 16-bit transposing LDS read (ds_read_b64_tr_b16): within each
+// Layout of a stage (row blocks; the 16-row blocks keep K like V). K in
+// four blocks, block w holding keys 8 w .. 8 w + 7
+// (the keys wave w copies) by 16-byte segment: segment s of key k at
+// position s ^ (w % 2) of 128 bytes (8 keys x 16 bytes), key k at 16 (k % 8)
+// within it. The 16 lanes of a K operand read (segment 4 ks + q4 of keys
+// 16 kb .. 16 kb + 15) then take two runs of 128 bytes, blocks 2 kb and
+// 2 kb + 1, and the swapped positions put the two runs in opposite halves
+// of the 64 four-byte banks. (K rows with permuted slots, as V below,
+// measured 2-way bank conflicted on those reads.) V row-major (key rows of
+// 2 D bytes), the 16-byte segment c of tile key k stored in slot
+// c ^ swz(k); V^T is read with the 16-bit transposing LDS read
+// (ds_read_b64_tr_b16): within each
 // 16-lane group, lane i receives element i % 4 of the 8-byte rows addressed
 // by lanes (i % 16) / 4 + 4 j, j = 0..3. Lane (col, q4) addresses dims
 // 16 nb + 4 (col % 4) .. +3 of key 4 q4 + col / 4 (and that key + 16), so
@@ -344,11 +351,8 @@ __device__ __forceinline__ void finish_rows(const KernelArgs& a, RowGroup<D>& g,
 // Slot permutation. swz(k) >> 1 = k mod 8 differs across the 8 keys that 32
 // lanes of a transposing V read address, two segments each, so those lanes
 // read 32 different 8-byte units of the 64 four-byte banks: measured free of
-// bank conflicts on gfx950. swz is a bijection on k mod 16 and on k mod 8
-// within each aligned group of 8, so the 16 keys of a K operand read fall
-// in different slots; 16-byte reads in this pattern still measured 2-way
-// conflicted (as did the plain k-times-2 permutation), against none for 16
-// lanes reading 256 contiguous bytes.
+// bank conflicts on gfx950. swz is also a bijection on k mod 8 within each
+// aligned group of 8, so a wave's 8 rows of a copy land in distinct slots.
 // At head_dim 64 (128-byte rows, two per 256 bytes of banks) the same two
 // properties hold for the pair (row parity, slot): swz is a bijection on
 // (k >> 1) mod 8 within each row parity, and its bits 1-2 equal (k >> 1)
@@ -428,6 +432,10 @@ multi_dma_kernel(const KernelArgs a) {
   constexpr int NCP = 8 / KPC;     // copies per wave per tile and tensor
   constexpr int LOADS = 2 * NCP;   // copies per wave per tile (K and V)
   constexpr bool PIPE = !FEW && D <= 128;  // software-pipelined plain tiles
+  // K in blocks (conflict-free operand reads) for the row blocks; the 16-row
+  // blocks, bound by HBM, keep K in whole rows like V (whole-row copies:
+  // 4-token check over the long batch 506.4 -> 512.0 us with blocks).
+  constexpr bool KBLK = !FEW;
   constexpr int LEAD = PIPE ? NS - 2 : NS - 1;  // tiles in flight ahead of the one begun
   static_assert(NS == lds_stages<D, PIPE>() && LEAD >= 1, "ring");
   static_assert(NS >= 2 && 2 * NS * TILE * 2 <= 65536, "LDS ring");
@@ -499,18 +507,24 @@ multi_dma_kernel(const KernelArgs a) {
   const int tile_first = t_lo / KT;
   const int ntiles = t_hi > t_lo ? (t_hi + KT - 1) / KT - tile_first : 0;
 
-  // Copies: this wave's keys 8 w .. 8 w + 7 of a tile; lane i of copy j
-  // takes key 8 w + KPC j + i / NSEG and fills slot i % NSEG of its row.
+  // Copies: this wave's keys 8 w .. 8 w + 7 of a tile, one page (pages hold
+  // a multiple of 8 keys). K in blocks: lane i of copy j takes segment
+  // (8 j + i / 8) ^ (w % 2) of key i % 8, so each copy reads whole 128-byte
+  // lines of 8 rows and fills K block w in the order of the layout above.
+  // V (and K in rows): lane i of copy j takes key KPC j + i / NSEG and fills
+  // slot i % NSEG of its row, whole rows per copy.
   const int64_t block_bytes = static_cast<int64_t>(P) * ROWB;
   const int64_t page_bytes = block_bytes * a.num_kv_heads;
   const char* kbase = static_cast<const char*>(a.k_pool) + block_bytes * kvh;
   const char* vbase = static_cast<const char*>(a.v_pool) + block_bytes * kvh;
   const int krow = lane / NSEG;
   const int slot = lane % NSEG;
-  int loff[NCP];
+  int koff[NCP], voff[NCP];
 #pragma unroll
-  for (int j = 0; j < NCP; ++j)
-    loff[j] = (KPC * j + krow) * ROWB + 16 * (slot ^ swz<D>(8 * wave + KPC * j + krow));
+  for (int j = 0; j < NCP; ++j) {
+    voff[j] = (KPC * j + krow) * ROWB + 16 * (slot ^ swz<D>(8 * wave + KPC * j + krow));
+    koff[j] = KBLK ? (lane & 7) * ROWB + 16 * ((8 * j + (lane >> 3)) ^ (wave & 1)) : voff[j];
+  }
   // The page table is not written while the kernel runs: reading it through
   // the constant address space lets the wave-uniform lookups below be scalar
   // loads (the copies' memory clobbers would otherwise force vector loads,
@@ -535,9 +549,9 @@ multi_dma_kernel(const KernelArgs a) {
     const uint32_t lk = lds_address(&sk[stage][8 * wave * D]);
     const uint32_t lv = lds_address(&sv[stage][8 * wave * D]);
 #pragma unroll
-    for (int j = 0; j < NCP; ++j) dma16(kbase + off + loff[j], lk + 1024 * j);
+    for (int j = 0; j < NCP; ++j) dma16(kbase + off + koff[j], lk + 1024 * j);
 #pragma unroll
-    for (int j = 0; j < NCP; ++j) dma16(vbase + off + loff[j], lv + 1024 * j);
+    for (int j = 0; j < NCP; ++j) dma16(vbase + off + voff[j], lv + 1024 * j);
     coff += KT;
     while (coff >= P) {
       coff -= P;
@@ -545,8 +559,12 @@ multi_dma_kernel(const KernelArgs a) {
     }
   };
 
-  // Operand addresses (16-bit elements within a stage).
-  const int fk = swz<D>(col);
+  // Operand addresses (16-bit elements within a stage). K in blocks: key
+  // col of the half, segment 4 ks + q4, in block 2 kb + col / 8 (see the
+  // layout); K in rows: row kb 16 + col, slot (4 ks + q4) ^ swz(col).
+  const int kgrp = col >> 3;
+  const int klane = KBLK ? kgrp * (NSEG * 64) + ((q4 ^ kgrp) * 64) + (col & 7) * 8 : col * D;
+  const int kswz = swz<D>(col);
   const int vkey = 4 * q4 + (col >> 2);
   const int fv = swz<D>(vkey);
   const int vbc = (col & 3) >> 1;
@@ -611,7 +629,10 @@ multi_dma_kernel(const KernelArgs a) {
       const uint16_t* ks_ = sk[sj];
       tile_scores<D, KVT, NR>(
           [&](int kb, int kstep) {
-            return *reinterpret_cast<const uint4*>(&ks_[(kb * 16 + col) * D + (((4 * kstep + q4) ^ fk) * 8)]);
+            if constexpr (KBLK)
+              return *reinterpret_cast<const uint4*>(&ks_[klane + kb * (2 * NSEG * 64) + kstep * 256]);
+            else
+              return *reinterpret_cast<const uint4*>(&ks_[klane + kb * 16 * D + (((4 * kstep + q4) ^ kswz) * 8)]);
           },
           rg, acc);
     };
