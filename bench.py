@@ -222,59 +222,50 @@ def attention_flops(w):
     return keys * w.spec.num_q_heads * w.spec.head_dim * 4
 
 
-def measure_multi_token(binding, workloads, lib, dev, stream, iters):
-    """Several new tokens per sequence: time decode_attn_run on each
-    multi-token workload and place it against its roofline (HBM when the
-    FLOPs per algorithmic byte are below the 16-bit matrix-core ridge,
-    matrix cores otherwise)."""
+def measure_multi_token(binding, workloads, lib, dev, stream, rounds):
+    """Several new tokens per sequence: time decode_attn_run and the split
+    pass alone on each multi-token workload, and place them against their
+    roofline (HBM when the FLOPs per algorithmic byte are below the 16-bit
+    matrix-core ridge, matrix cores otherwise). The workloads are timed like
+    the named configurations: after ~30 ms of warm-up launches (the clocks
+    rise over the first blocks of a compute-bound kernel: 109 -> 93 us per
+    step over six 50-launch blocks of the 128-token suffix), in `rounds`
+    alternating rounds of ~2 ms blocks; the median is reported with p10 and
+    p90."""
     import torch
     ridge = MFMA_PEAK_TFLOPS_16BIT * 1e12 / (HBM_PEAK_GBPS * 1e9)
-    res = []
+    runners = {}
     for name in MULTI_TOKEN_WORKLOADS:
-        spec = workloads.NAMED[name]
-        w = workloads.make_workload(spec, dev)
-        params = binding.params_for(w.q, w.k_pool, w.page_table, window=w.window, scale=w.scale,
-                                    out_dtype=spec.out_dtype)
-        plan = binding.decode_attn_plan(params, w.seq_lens_host, device=dev.index or 0)
-        out = torch.empty(w.q.shape, dtype=workloads.DTYPES[spec.out_dtype], device=dev)
-        ws = binding.alloc_workspace(plan, dev)
-        ptrs = [w.q.data_ptr(), w.k_pool.data_ptr(), w.v_pool.data_ptr(), w.page_table.data_ptr(),
-                w.seq_lens.data_ptr(), out.data_ptr(), ws.data_ptr() if ws is not None else None,
-                plan.workspace_bytes, stream.cuda_stream]
-
-        def run():
-            st = lib.decode_attn_run(plan.handle, *ptrs)
-            if st != 0:
-                raise binding.DecodeAttnError(st, f"decode_attn_run ({name})")
-
-        def split():
-            st = lib.decode_attn_split(plan.handle, *ptrs)
-            if st != 0:
-                raise binding.DecodeAttnError(st, f"decode_attn_split ({name})")
-
-        for _ in range(3):
-            run()
-        ms = time_on_stream(run, iters, stream)
-        ms_split = time_on_stream(split, iters, stream)
+        w = workloads.make_workload(workloads.NAMED[name], dev)
+        runners[name] = Runner(binding, lib, w, dev, stream)
+    for r in runners.values():
+        n = int(max(10, 30000.0 // max(1.0, block_us(r.run, 5, stream))))
+        block_us(r.run, n, stream)
+    t = time_alternating(runners, rounds, stream)
+    res = []
+    for name, r in runners.items():
+        w, spec = r.w, r.w.spec
+        step, split = quantiles(t[name]["run"]), quantiles(t[name]["split"])
         by, fl = w.kv_bytes(), attention_flops(w)
         hbm = fl / by < ridge
 
-        def frac(t_ms):
-            return round(by / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS if hbm
-                         else fl / (t_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS_16BIT, 4)
+        def frac(t_us):
+            return round(by / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS if hbm
+                         else fl / (t_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS_16BIT, 4)
 
-        gbs, tfs = by / (ms * 1e-3) / 1e9, fl / (ms * 1e-3) / 1e12
+        us, us_split = step["median"], split["median"]
         # "frac" places the dominant kernel (the split pass) against its
         # roofline, as the headline does; "step_frac" the whole step (with
         # the combine).
-        res.append({"workload": spec.name, "query_len": spec.query_len, "us": round(ms * 1e3, 2),
-                    "split_us": round(ms_split * 1e3, 2), "GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 1),
-                    "split_TFLOP_s": round(fl / (ms_split * 1e-3) / 1e12, 1), "bound": "hbm" if hbm else "mfma",
-                    "frac": frac(ms_split), "step_frac": frac(ms),
-                    "algorithmic_bytes": by, "flops": fl, "work_groups": plan.info.split_work_groups})
-        print(f"[bench] {name}: {ms * 1e3:.1f} us (split pass {ms_split * 1e3:.1f} us)", file=sys.stderr, flush=True)
-        del w, out, ws
-        torch.cuda.empty_cache()
+        res.append({"workload": spec.name, "query_len": spec.query_len, "us": us, "us_quantiles": step,
+                    "split_us": us_split, "split_us_quantiles": split,
+                    "GB_s": round(by / (us * 1e-6) / 1e9, 1), "TFLOP_s": round(fl / (us * 1e-6) / 1e12, 1),
+                    "split_TFLOP_s": round(fl / (us_split * 1e-6) / 1e12, 1), "bound": "hbm" if hbm else "mfma",
+                    "frac": frac(us_split), "step_frac": frac(us),
+                    "algorithmic_bytes": by, "flops": fl, "work_groups": r.plan.info.split_work_groups})
+        print(f"[bench] {name}: {us:.1f} us (split pass {us_split:.1f} us)", file=sys.stderr, flush=True)
+    del runners
+    torch.cuda.empty_cache()
     return res
 
 
@@ -758,7 +749,7 @@ def main():
     fixed = measure_fixed_order(w, binding, lib, dev, stream, args.steps) if spec.query_len == 1 else None
 
     # Several new tokens per sequence (drafted-token check, suffix prefill).
-    multi = [] if args.no_multi_token else measure_multi_token(binding, workloads, lib, dev, stream, args.steps)
+    multi = [] if args.no_multi_token else measure_multi_token(binding, workloads, lib, dev, stream, args.rounds)
 
     # One whole decode step (32 layers) of the Llama-3.1-8B shape at 3060
     # tokens, eager and as a replayed HIP graph.
