@@ -14,8 +14,12 @@
 //
 // Decode: one wave64 per (query head, sequence), four waves per work-group;
 // lane i owns elements i, i+64, ... of the row, so every load of O_s is one
-// contiguous 256-byte-per-64-lane read. Several new tokens per sequence (many
-// more rows, few splits each): 32 lanes per row, two rows per wave.
+// contiguous 256-byte-per-64-lane read. A decode step planned on the
+// multi-token split kernel (one token: a single row block per KV head, split
+// s of the attended pages in state slot s of row b H_q + h) has the decode
+// kernels' split ranges and state layout, so it takes this merge too.
+// Several new tokens per sequence (many more rows, few splits each): 32
+// lanes per row, two rows per wave.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

@@ -73,7 +73,7 @@ hipError_t launch_split(const KernelArgs& a, int head_dim, int kv_dtype, int gro
 // 16-bit type, head_dim 128, page size a multiple of 16).
 hipError_t launch_split_mfma(const KernelArgs& a, int head_dim, int kv_dtype, int group_tile, hipStream_t stream);
 
-// Enqueue the multi-token split pass (query_len > 1) on `stream`.
+// Enqueue the multi-token split pass (query_len >= 1) on `stream`.
 hipError_t launch_multi(const KernelArgs& a, int head_dim, int kv_dtype, int rows_per_group, hipStream_t stream);
 
 // Enqueue the combine pass on `stream`.

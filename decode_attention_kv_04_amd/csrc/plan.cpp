@@ -86,6 +86,19 @@ int64_t decode_min_split_tokens(bool matrix_kernel, int64_t max_attended_tokens)
   return kDefaultMinSplitTokens;
 }
 
+// Minimum split length of a decode step on the multi-token kernel: past the
+// switch-over, splits may be 64 tokens (µs per step, 64 / 128 / 256-token
+// minimum: 64 query heads over 8 KV heads at 1 x 3060 tokens 9.9 / 11.0 /
+// 12.1, 4 x 1024 10.1 / 9.8 / 11.5; 32 over 8 at head_dim 256 and 1 x 3060
+// 11.9 / 13.3 / 15.3; longer batches fill the chip with longer splits).
+constexpr int64_t kMultiDecodeMinSplitTokens = 64;
+
+int64_t multi_decode_min_split_tokens(int64_t max_attended_tokens) {
+  int64_t v;
+  if (split_min_env(&v)) return v;
+  return max_attended_tokens > kDefaultMinSplitTokens ? kMultiDecodeMinSplitTokens : kDefaultMinSplitTokens;
+}
+
 bool log_enabled() {
   const char* s = std::getenv("DECODE_ATTN_LOG");
   return s && s[0] == '1';
@@ -315,7 +328,8 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
     const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim, QB),
                                   blocks);
     c = ceil_div(max_np, std::max<int64_t>(1, want));
-    c = std::min(max_np, std::max(c, ceil_div(min_split_tokens(), P)));
+    c = std::min(max_np, std::max(c, ceil_div(T == 1 ? multi_decode_min_split_tokens(max_np * P) : min_split_tokens(),
+                                              P)));
   }
   c = std::max<int64_t>(c, 1);
   c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));  // grid y = row blocks x splits
@@ -439,7 +453,27 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
                            ? 1
                            : 0;
 
-  if (plan->query_len > 1 && !per_token) {
+  // Single-query decode on 16-bit q and K/V runs on the multi-token kernel
+  // as one token (a 16-row block, both products on the matrix cores) with 5
+  // to 8 query heads per KV head, and with 3 or 4 where the matrix-core
+  // decode kernel does not apply (head_dim 64 or 256, pages not a multiple of
+  // 16). The decode kernels keep P.V on the vector ALUs: at 8 heads that is
+  // 8 x 8 accumulators per lane and one wave per SIMD, and the vector
+  // kernel's q.K is a lane sum per key. Measured, µs per step (decode
+  // kernels -> this): 64 query heads over 8 KV heads, f16, head_dim 128:
+  // the long batch 580 -> 498, 48 heads 578 -> 498, 32 x 1-8k tokens 142 ->
+  // 115, the mixed-window batch 155 -> 97, 8 x 8-24k 120 -> 97, 1 x 32k 38.4
+  // -> 25.5, 1 x 3060 13.4 -> 9.9; at head_dim 64 and 256 over 32 x 1-8k
+  // tokens 168 -> 66 and 489 -> 216; 32 query heads over 8, head_dim 64 and
+  // 256: 32 x 1-8k 74 -> 63 and 245 -> 215, 1 x 3060 10.8 -> 8.5 and 20.0 ->
+  // 11.4; page size 8 at head_dim 128 129 -> 116. With 2 heads per KV head
+  // (2 of 16 rows used) it lost: 4 x 1-4k tokens at head_dim 256 14.5 ->
+  // 16.3. An empty context stays on the decode kernels (the multi-token
+  // kernel needs the new token's own key).
+  bool mq_decode = T == 1 && (gt == 8 || (gt == 4 && !matrix_kernel_supported(*p))) && multi_dtypes &&
+                   p->kernel == DA_KERNEL_AUTO && !fixed;
+  for (int32_t b = 0; mq_decode && b < p->batch; ++b) mq_decode = lens[b] >= 1;
+  if ((plan->query_len > 1 && !per_token) || mq_decode) {
     const da_status st = finish_multi_plan(plan, lens);
     if (st == DA_OK) *out = plan;
     return st;

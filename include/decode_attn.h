@@ -85,7 +85,10 @@ typedef enum { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
 
 /* Which single-query split kernel a plan uses (da_params.kernel). */
 typedef enum {
-  DA_KERNEL_AUTO = 0,   /* the planner chooses (matrix cores from 2 query heads per KV head on) */
+  DA_KERNEL_AUTO = 0,   /* the planner chooses (matrix cores from 2 query heads per KV head on;
+                           a decode step with 5-8 of them, or 3-4 where the
+                           decode matrix-core kernel is not built, on the
+                           multi-token kernel as one token)                     */
   DA_KERNEL_VECTOR = 1, /* vector q.K; with query_len > 1: the single-query kernels per token   */
   DA_KERNEL_MATRIX = 2  /* q.K on the matrix cores; DA_ERR_UNSUPPORTED where not built           */
 } da_kernel;
@@ -140,7 +143,8 @@ typedef struct {
                                 DA_KERNEL_VECTOR = the single-query kernels
                                 once per token. DA_ERR_UNSUPPORTED where the
                                 choice is not built; other values
-                                DA_ERR_INVALID.                                 */
+                                DA_ERR_INVALID. Only DA_KERNEL_AUTO takes a
+                                decode step to the multi-token kernel.          */
   int32_t rows_per_block;    /* query_len > 1 on the multi-token kernels: the
                                 (token, head) rows of a KV head per work-group.
                                 0 = the planner chooses; 16, 64, or 128 (128
@@ -165,14 +169,18 @@ typedef struct {
                                 head_dim 128, page size a multiple of 16, at
                                 least two query heads per KV head);
                                 da_params.kernel forces 0 or 1. 2 = the
-                                multi-token kernels (query_len > 1; q.K and P.V
-                                on the matrix cores): the T*G rows of a KV head
-                                in blocks of 16 (16 rows or fewer: one wave
-                                computes, three copy), 128 (more rows at head_dim
-                                64 and 128) or 64 (more rows at head_dim 256);
-                                da_params.rows_per_block forces one. A
-                                query_len > 1 plan with 0 runs the vector
-                                kernel once per token.                        */
+                                multi-token kernels (q.K and P.V on the matrix
+                                cores): the T*G rows of a KV head in blocks of
+                                16 (16 rows or fewer: one wave computes, three
+                                copy), 128 (more rows at head_dim 64 and 128)
+                                or 64 (more rows at head_dim 256);
+                                da_params.rows_per_block forces one. Decode
+                                plans (query_len <= 1) with DA_KERNEL_AUTO
+                                take 2 when q and K/V share f16 or bf16, every
+                                length is at least 1, and G is 5 to 8, or 3 to
+                                4 where 1 is not built; outside the fixed-order
+                                mode. A query_len > 1 plan with 0 runs the
+                                vector kernel once per token.                 */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in

@@ -121,7 +121,7 @@ def test_matrix_kernel_splits_down_to_128_tokens(lib, monkeypatch):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
     pl = plan(params(), [3060])
     assert pl.info.split_kernel == 1 and pl.pages_per_split == 8 and pl.max_splits == 24
-    pl = plan(params(head_dim=64), [3060])
+    pl = plan(params(num_q_heads=16, head_dim=64), [3060])              # G 2: the vector kernel
     assert pl.info.split_kernel == 0 and pl.pages_per_split == 16
     # contexts of at most 256 tokens are not split (the switch-over), one more token is
     assert plan(params(batch=3), [256, 100, 1]).max_splits == 1
@@ -157,10 +157,11 @@ def test_split_kernel_selection(lib):
     assert plan(params(page_size=32, max_pages_per_seq=1024), [3060]).info.split_kernel == 1
     assert plan(params(q_dtype="f32"), [3060]).info.split_kernel == 0           # q and KV differ
     assert plan(params(q_dtype="f32", kv_dtype="f32"), [3060]).info.split_kernel == 0
-    assert plan(params(head_dim=64), [3060]).info.split_kernel == 0
-    assert plan(params(head_dim=256), [3060]).info.split_kernel == 0
-    assert plan(params(page_size=8, max_pages_per_seq=4096), [3060]).info.split_kernel == 0
-    assert plan(params(page_size=24, max_pages_per_seq=4096), [3060]).info.split_kernel == 0
+    # no matrix-core decode kernel: G 4 takes the multi-token kernel (one token), G 2 the vector kernel
+    for kw in (dict(head_dim=64), dict(head_dim=256), dict(page_size=8, max_pages_per_seq=4096),
+               dict(page_size=24, max_pages_per_seq=4096)):
+        assert plan(params(**kw), [3060]).info.split_kernel == 2
+        assert plan(params(num_q_heads=16, **kw), [3060]).info.split_kernel == 0
     assert plan(params(kernel="vector"), [3060]).info.split_kernel == 0
     assert plan(params(kernel="matrix"), [3060]).info.split_kernel == 1
     assert plan(params(kernel="auto"), [3060]).info.split_kernel == 1
@@ -172,15 +173,19 @@ def test_split_kernel_selection(lib):
 
 
 # One query head per group (q.K a dot product per key) takes the vector
-# kernel; two or more take the matrix-core kernel where it is supported,
-# whatever the size of the launch, the split count or the fixed-order chunk.
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+# kernel; two to four take the matrix-core decode kernel where it is
+# supported, five to eight the multi-token kernel (one token), whatever the
+# size of the launch or the split count; the fixed-order mode stays on the
+# decode kernels.
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_split_kernel_by_group(lib, G):
-    want = 0 if G == 1 else 1
+    want = 0 if G == 1 else (1 if G <= 4 else 2)
     for lens in ([32768] * 32, [3060] * 2, [1]):
         assert plan(params(batch=len(lens), num_q_heads=8 * G), lens).info.split_kernel == want
-    for kw in (dict(num_splits=1), dict(num_splits=7), dict(fixed_chunk=1024), dict(fixed_chunk=1024, num_splits=3)):
+    for kw in (dict(num_splits=1), dict(num_splits=7)):
         assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == want
+    for kw in (dict(fixed_chunk=1024), dict(fixed_chunk=1024, num_splits=3)):
+        assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == min(want, 1)
     assert plan(params(batch=32, num_q_heads=8 * G, kernel="matrix"), [32768] * 32).info.split_kernel == 1
 
 
@@ -357,6 +362,64 @@ def test_query_len_zero_and_one_are_decode(lib):
     for T in (0, 1):
         pl = plan(params(query_len=T), [3060])
         assert pl.info.split_kernel in (0, 1)
+
+
+# A decode step (one new token) runs on the multi-token kernel, as one
+# 16-row block per KV head, with 5 to 8 query heads per KV head on 16-bit q
+# and K/V, and with 3 or 4 where the matrix-core decode kernel is not built
+# (head_dim 64 or 256, pages not a multiple of 16); not with an empty context
+# (the kernel needs the new token's own key), a forced kernel or the
+# fixed-order mode.
+@pytest.mark.parametrize("G,kw,want", [
+    (5, {}, 2), (6, {}, 2), (8, {}, 2), (8, dict(q_dtype="bf16", kv_dtype="bf16", out_dtype="f32"), 2),
+    (8, dict(head_dim=64), 2), (8, dict(head_dim=256), 2), (7, dict(page_size=24, max_pages_per_seq=4096), 2),
+    (3, dict(head_dim=64), 2), (4, dict(head_dim=256), 2), (4, dict(page_size=8, max_pages_per_seq=4096), 2),
+    (3, {}, 1), (4, {}, 1), (2, dict(head_dim=64), 0), (2, dict(head_dim=256), 0), (1, dict(head_dim=256), 0),
+    (8, dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), 0), (8, dict(q_dtype="f32"), 0),
+    (8, dict(kernel="vector"), 0), (8, dict(kernel="matrix"), 1), (8, dict(fixed_chunk=256), 1),
+    (4, dict(head_dim=64, fixed_chunk=256), 0),
+])
+def test_decode_on_the_multi_token_kernel(lib, G, kw, want):
+    lens = [3060, 1, 700]
+    kw = dict(kw)
+    P = kw.get("page_size", 16)
+    D = kw.get("head_dim", 128)
+    pl = plan(params(batch=3, num_q_heads=8 * G, **kw), lens)
+    assert pl.info.split_kernel == want
+    if want != 2:
+        return
+    S = pl.max_splits
+    assert pl.info.split_work_groups == 8 * S * 3                 # one row block per KV head
+    assert [pl.splits(b) for b in range(3)] == [max(1, math.ceil(math.ceil(L / P) / pl.pages_per_split))
+                                                for L in lens]
+    assert pl.info.attended_keys == sum(lens)
+    rows = 3 * 8 * G * S
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert pl.workspace_bytes == (r256(rows * D * 4) + r256(rows * 2 * 4) if S > 1 else 0)
+    # an empty context keeps the decode kernels
+    assert plan(params(batch=4, num_q_heads=8 * G, **kw), lens + [0]).info.split_kernel in (0, 1)
+
+
+# Split length of a decode step on the multi-token kernel: one round of
+# resident 16-row blocks (2 per compute unit at head_dim 128), splits no
+# shorter than 64 tokens once some context is past the 256-token switch-over.
+def test_decode_on_the_multi_token_kernel_splits(lib, monkeypatch):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    pl = plan(params(num_q_heads=64), [3060])      # 192 pages; one round would cut 3 pages, below 4
+    assert pl.pages_per_split == 4 and pl.max_splits == 48
+    assert plan(params(batch=3, num_q_heads=64), [256, 100, 1]).max_splits == 1
+    pl = plan(params(num_q_heads=64), [257])
+    assert pl.pages_per_split == 4 and pl.max_splits == 5
+    pl = plan(params(num_q_heads=64, window=1000), [5000])   # pages 250 .. 312
+    assert pl.pages_per_split == 4 and pl.max_splits == 16 and pl.info.attended_keys == 1000
+    lens = [16384 + (i * 523) % 16384 for i in range(32)]
+    pl = plan(params(batch=32, num_q_heads=64), lens)
+    assert pl.max_splits == 2 and pl.info.split_work_groups == 2 * 8 * 32
+    assert pl.pages_per_split == math.ceil(math.ceil(max(lens) / 16) / 2)
+    pl = plan(params(batch=3, num_q_heads=64, num_splits=5), [3060, 1, 700])
+    assert pl.max_splits == 5 and pl.pages_per_split == math.ceil(192 / 5)
+    monkeypatch.setenv("DECODE_ATTN_SPLIT_MIN", "4096")
+    assert plan(params(num_q_heads=64), [3060]).max_splits == 1
 
 
 def test_empty_batch_plans(lib):
@@ -541,7 +604,9 @@ def balanced_expectation(lens, P, Hkv, window, cus, per_cu, min_tokens, D=128, e
 ])
 def test_balanced_plan_partition(lib, monkeypatch, lens, P, W, G):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
-    p = params(batch=len(lens), num_q_heads=8 * G, page_size=P, max_pages_per_seq=8192, window=W)
+    # G 8 runs on the multi-token kernel unless the matrix-core decode kernel is asked for
+    p = params(batch=len(lens), num_q_heads=8 * G, page_size=P, max_pages_per_seq=8192, window=W,
+               kernel="matrix" if G == 8 else None)
     pl = plan(p, lens)
     assert pl.info.balanced == 1 and pl.info.split_kernel == 1
     U, q, N, pieces = balanced_expectation(lens, P, 8, W, 256, 1 if G == 8 else 2, 128)
@@ -560,7 +625,9 @@ def test_balanced_plan_is_not_taken(lib, monkeypatch):
     assert plan(params(batch=2, num_splits=7), lens).info.balanced == 0                 # forced split count
     assert plan(params(batch=2, fixed_chunk=256), lens).info.balanced == 0              # fixed-order mode
     assert plan(params(batch=2, kernel="vector"), lens).info.balanced == 0              # vector kernel
-    assert plan(params(batch=2, head_dim=64), lens).info.balanced == 0                  # vector kernel
+    assert plan(params(batch=2, num_q_heads=16, head_dim=64), lens).info.balanced == 0  # vector kernel
+    assert plan(params(batch=2, head_dim=64), lens).info.balanced == 0                  # multi-token kernel
+    assert plan(params(batch=2, num_q_heads=64), lens).info.balanced == 0               # multi-token kernel
     assert plan(params(batch=2, query_len=4, q_dtype="f32"), lens).info.balanced == 0   # per-token mode
     assert plan(params(batch=3), [256, 100, 1]).info.balanced == 0                      # nothing to split
     assert plan(params(), [3060]).info.balanced == 0                  # 192 work-groups: one round already
@@ -575,7 +642,7 @@ def test_balanced_plan_is_not_taken(lib, monkeypatch):
 # Whole streams: at least one (sequence, KV head) stream per compute unit and
 # about equal lengths -> no split (one launch, no combine), on either kernel.
 @pytest.mark.parametrize("B,L,kw", [(32, 512, {}), (32, 4096, {}), (128, 512, {}), (64, 1024, {}),
-                                     (48, 3060, {}), (32, 2048, dict(head_dim=64)),
+                                     (48, 3060, {}), (32, 2048, dict(num_q_heads=16, head_dim=64)),
                                      (32, 2048, dict(window=1000))])
 def test_whole_streams_are_not_split(lib, monkeypatch, B, L, kw):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)

@@ -35,7 +35,7 @@ CASES = [
     (96, 4, 16, "f16", "f16", 0, 0.5, 9000),
     (64, 4, 32, "bf16", "f32", 1000, 0.5, 20000),
     (200, 2, 16, "bf16", "bf16", 0, 0.3, 6000),
-    (48, 8, 64, "f16", "f32", 0, 0.7, 12000),
+    (48, 8, 64, "f16", "f32", 0, 0.7, 12000),     # G 8 on the forced matrix-core kernel
     (128, 1, 16, "f16", "f16", 300, 0.6, 8000),    # G 1 on the forced matrix-core kernel
     (40, 3, 16, "f16", "f32", 0, 1.0, 16000),
     (700, 4, 16, "f16", "f16", 0, 0.05, 30000),
@@ -51,7 +51,8 @@ def test_balanced_schedule_matches_oracle(gpu, i):
                            window=W, spike_frac=0.01)
     say(f"[balanced {i}] B={B} G={G} P={P} {dt}->{out} W={W} keys={sum(lens)}")
     w = wl.make_workload(spec, gpu)
-    kernel = "matrix" if G == 1 else None
+    # G 1 and G 5-8 reach the matrix-core decode kernel only when it is asked for
+    kernel = "matrix" if G == 1 or G >= 5 else None
     got, plan = run_lib(w, kernel=kernel)
     assert plan.info.balanced == 1 and plan.info.split_kernel == 1
     say(f"  work-groups {plan.info.split_work_groups}, pages each {plan.pages_per_split}, "
