@@ -110,6 +110,61 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool valid_dtype(da_dtype t) { return t == DA_F32 || t == DA_F16 || t == DA_BF16; }
 
+// A decode step on the multi-token kernel is taken only if its longest
+// work-group streams at most 1/kMultiDecodeShare of the batch's page-heads:
+// one work-group alone streams about 31 GB/s (four 32768-token contexts
+// among 60 short ones, 64/8 heads: 32 work-groups of 16 MB in 537 us), the
+// chip about 6.4 TB/s, so beyond that share the longest work-groups, not
+// HBM, set the time (that batch: 537 us against 160 on the decode kernel's
+// balanced schedule; 15 short contexts and one of 65536 tokens: 268 against
+// 85 with a split count per stream).
+constexpr int64_t kMultiDecodeShare = 170;
+
+// Split length (pages) of a decode step on the multi-token kernel for the
+// attended page counts `npages`, or 0 where that kernel would leave the
+// batch unbalanced (the decode kernels then run). First the largest split
+// count per stream that keeps every stream's work-groups within one round of
+// resident work-groups (a round and a fraction measured worst: 24 x 4096
+// tokens at 32/8 heads, 2 / 3 / 4 splits per stream 67.7 / 74.5 / 65.8 us,
+// 12 x 2048 5 / 6 splits 20.5 / 23.7 us). With `fit`, where that leaves the
+// longest work-groups too long, the shortest split whose working
+// work-groups, ceil(pages / c) per stream, fit the round (the 65536-token
+// context among 15 short ones: 67 us against 85 on the decode kernel; on
+// batches of 1-8k tokens it ran 4-7 % slower than the count per stream, so
+// it is only the second choice).
+int64_t multi_decode_split_pages(const std::vector<int64_t>& npages, int64_t num_kv_heads, int64_t num_cus,
+                                 int32_t head_dim, int64_t P, bool fit) {
+  int64_t max_np = 0, total = 0;
+  for (int64_t n : npages) {
+    max_np = std::max(max_np, n);
+    total += n;
+  }
+  if (max_np == 0) return 1;
+  const int64_t slots = num_cus * resident_row_groups_per_cu(head_dim, 16);
+  const int64_t blocks = static_cast<int64_t>(npages.size()) * num_kv_heads;
+  const int64_t cmin = std::min(max_np, ceil_div(multi_decode_min_split_tokens(max_np * P), P));
+  const int64_t limit = std::max(cmin, ceil_div(total * num_kv_heads, kMultiDecodeShare));
+  const int64_t per_stream = std::max<int64_t>(1, slots / blocks);
+  const int64_t c = std::min(max_np, std::max(cmin, ceil_div(max_np, per_stream)));
+  if (c <= limit) return c;
+  if (!fit) return 0;
+  auto groups = [&](int64_t cc) {
+    int64_t n = 0;
+    for (int64_t np : npages) n += std::max<int64_t>(1, ceil_div(np, cc));
+    return n * num_kv_heads;
+  };
+  // groups() never grows with c; with no c in range fitting, lo ends at max_np.
+  int64_t lo = cmin, hi = max_np;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (groups(mid) <= slots)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo <= limit ? lo : 0;
+}
+
 }  // namespace
 
 SeqRange seq_range(int64_t L, int64_t window, int64_t P) {
@@ -283,14 +338,14 @@ da_status finish_fixed_plan(da_plan* plan, const std::vector<int64_t>& npages, i
 // into blocks of rows_per_group; a block sees keys from the window start of
 // its first token to its last token, and those pages are split with one split
 // length for the whole batch.
-da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
+da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_pages) {
   const da_params& p = plan->p;
   const int64_t P = p.page_size;
   const int64_t T = plan->query_len;
   const int64_t G = plan->group;
   const int64_t R = T * G;
   // Four waves of 16 rows (or two groups of 16) share each key tile.
-  const int64_t QB = mq_rows(R, p.head_dim, p.rows_per_block);
+  const int64_t QB = mq_rows(R, p.head_dim, T == 1 ? 0 : p.rows_per_block);
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);
@@ -323,13 +378,14 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens) {
     c = 1;
   } else if (p.num_splits > 0) {
     c = ceil_div(max_np, p.num_splits);
+  } else if (decode_pages > 0) {
+    c = decode_pages;
   } else {
     const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * nrb;
     const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim, QB),
                                   blocks);
     c = ceil_div(max_np, std::max<int64_t>(1, want));
-    c = std::min(max_np, std::max(c, ceil_div(T == 1 ? multi_decode_min_split_tokens(max_np * P) : min_split_tokens(),
-                                              P)));
+    c = std::min(max_np, std::max(c, ceil_div(min_split_tokens(), P)));
   }
   c = std::max<int64_t>(c, 1);
   c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));  // grid y = row blocks x splits
@@ -394,7 +450,7 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
 
   const int32_t T = p->query_len > 1 ? p->query_len : 1;
   // Several new tokens: the multi-token kernels when q and K/V share f16 or
-  // bf16; otherwise (or with DECODE_ATTN_KERNEL=vector) the single-query
+  // bf16; otherwise (or with kernel = DA_KERNEL_VECTOR) the single-query
   // kernels once per token.
   const bool multi_dtypes = p->q_dtype == p->kv_dtype && (p->kv_dtype == DA_F16 || p->kv_dtype == DA_BF16);
   const bool per_token = T > 1 && (!multi_dtypes || p->kernel == DA_KERNEL_VECTOR);
@@ -457,24 +513,38 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // as one token (a 16-row block, both products on the matrix cores) with 5
   // to 8 query heads per KV head, and with 3 or 4 where the matrix-core
   // decode kernel does not apply (head_dim 64 or 256, pages not a multiple of
-  // 16). The decode kernels keep P.V on the vector ALUs: at 8 heads that is
-  // 8 x 8 accumulators per lane and one wave per SIMD, and the vector
-  // kernel's q.K is a lane sum per key. Measured, µs per step (decode
-  // kernels -> this): 64 query heads over 8 KV heads, f16, head_dim 128:
-  // the long batch 580 -> 498, 48 heads 578 -> 498, 32 x 1-8k tokens 142 ->
-  // 115, the mixed-window batch 155 -> 97, 8 x 8-24k 120 -> 97, 1 x 32k 38.4
-  // -> 25.5, 1 x 3060 13.4 -> 9.9; at head_dim 64 and 256 over 32 x 1-8k
-  // tokens 168 -> 66 and 489 -> 216; 32 query heads over 8, head_dim 64 and
-  // 256: 32 x 1-8k 74 -> 63 and 245 -> 215, 1 x 3060 10.8 -> 8.5 and 20.0 ->
-  // 11.4; page size 8 at head_dim 128 129 -> 116. With 2 heads per KV head
-  // (2 of 16 rows used) it lost: 4 x 1-4k tokens at head_dim 256 14.5 ->
-  // 16.3. An empty context stays on the decode kernels (the multi-token
-  // kernel needs the new token's own key).
-  bool mq_decode = T == 1 && (gt == 8 || (gt == 4 && !matrix_kernel_supported(*p))) && multi_dtypes &&
+  // 16) or the batch has fewer (sequence, KV head) streams than compute
+  // units; in each case only if its plan is balanced (see
+  // multi_decode_split_pages). The decode kernels keep P.V on the vector
+  // ALUs: at 8 heads that is 8 x 8 accumulators per lane and one wave per
+  // SIMD, and the vector kernel's q.K is a lane sum per key. Measured, us per
+  // step (decode kernels -> this): 64 query heads over 8 KV heads, f16,
+  // head_dim 128: the long batch 580 -> 498, 48 heads 578 -> 498, 32 x 1-8k
+  // tokens 142 -> 115, the mixed-window batch 155 -> 97, 8 x 8-24k 120 -> 97,
+  // 1 x 32k 38.4 -> 25.5, 1 x 3060 13.4 -> 9.9; at head_dim 64 and 256 over
+  // 32 x 1-8k tokens 168 -> 66 and 489 -> 216; 32 query heads over 8,
+  // head_dim 64 and 256: 32 x 1-8k 74 -> 63 and 245 -> 215, 1 x 3060 10.8
+  // -> 8.5 and 20.0 -> 11.4; page size 8 at head_dim 128 129 -> 116; 32 over
+  // 8 at head_dim 128 with few streams: 1 x 3060 10.4 -> 9.5, 4 x 3060 18.1
+  // -> 13.9, 1 x 32k 30.9 -> 26.8, 16 x 8192 90.1 -> 84.8, 24 x 4096 71.8 ->
+  // 68.1. From one stream per compute unit on, the matrix-core decode kernel
+  // wins at 3 or 4 heads per KV head (the long batch 482 against 490, the
+  // mixed-window batch 95 against 99, 32 x 2048 42.5 against 45.0). With 2
+  // heads per KV head (2 of 16 rows used) it lost: 4 x 1-4k tokens at
+  // head_dim 256 14.5 -> 16.3. An empty context stays on the decode kernels
+  // (the multi-token kernel needs the new token's own key).
+  const bool few_streams = static_cast<int64_t>(p->batch) * p->num_kv_heads < num_cus;
+  const bool weak_decode = gt == 8 || !matrix_kernel_supported(*p);
+  bool mq_decode = T == 1 && (gt == 8 || (gt == 4 && (weak_decode || few_streams))) && multi_dtypes &&
                    p->kernel == DA_KERNEL_AUTO && !fixed;
   for (int32_t b = 0; mq_decode && b < p->batch; ++b) mq_decode = lens[b] >= 1;
+  int64_t mq_pages = 0;
+  if (mq_decode && p->num_splits == 0) {
+    mq_pages = multi_decode_split_pages(npages, p->num_kv_heads, num_cus, p->head_dim, P, weak_decode);
+    mq_decode = mq_pages > 0;
+  }
   if ((plan->query_len > 1 && !per_token) || mq_decode) {
-    const da_status st = finish_multi_plan(plan, lens);
+    const da_status st = finish_multi_plan(plan, lens, mq_pages);
     if (st == DA_OK) *out = plan;
     return st;
   }

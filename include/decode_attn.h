@@ -87,8 +87,10 @@ typedef enum { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
 typedef enum {
   DA_KERNEL_AUTO = 0,   /* the planner chooses (matrix cores from 2 query heads per KV head on;
                            a decode step with 5-8 of them, or 3-4 where the
-                           decode matrix-core kernel is not built, on the
-                           multi-token kernel as one token)                     */
+                           decode matrix-core kernel is not built or the batch
+                           has fewer (sequence, KV head) streams than compute
+                           units, on the multi-token kernel as one token when
+                           its plan is balanced)                               */
   DA_KERNEL_VECTOR = 1, /* vector q.K; with query_len > 1: the single-query kernels per token   */
   DA_KERNEL_MATRIX = 2  /* q.K on the matrix cores; DA_ERR_UNSUPPORTED where not built           */
 } da_kernel;
@@ -178,9 +180,14 @@ typedef struct {
                                 plans (query_len <= 1) with DA_KERNEL_AUTO
                                 take 2 when q and K/V share f16 or bf16, every
                                 length is at least 1, and G is 5 to 8, or 3 to
-                                4 where 1 is not built; outside the fixed-order
-                                mode. A query_len > 1 plan with 0 runs the
-                                vector kernel once per token.                 */
+                                4 where 1 is not built or B * H_kv is below
+                                num_cus; outside the fixed-order mode; and
+                                (num_splits 0) only if no work-group of that
+                                plan holds more than about 1/170 of the
+                                batch's attended page-heads (else the decode
+                                kernels and their balanced schedule run). A
+                                query_len > 1 plan with 0 runs the vector
+                                kernel once per token.                        */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
                                 work-group computes (0 in the default mode). In
                                 that mode pages_per_split is the chunk length in

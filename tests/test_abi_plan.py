@@ -116,16 +116,17 @@ def test_heuristic_short_contexts_do_not_split(lib):
 
 
 def test_matrix_kernel_splits_down_to_128_tokens(lib, monkeypatch):
-    # the matrix-core kernel (f16, head_dim 128, G 4) over one 3060-token
-    # context: splits of 128 tokens (8 pages); the vector kernel keeps 256
+    # the matrix-core decode kernel (f16, head_dim 128, G 4) over one
+    # 3060-token context: splits of 128 tokens (8 pages); the vector kernel
+    # keeps 256
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
-    pl = plan(params(), [3060])
+    pl = plan(params(kernel="matrix"), [3060])
     assert pl.info.split_kernel == 1 and pl.pages_per_split == 8 and pl.max_splits == 24
     pl = plan(params(num_q_heads=16, head_dim=64), [3060])              # G 2: the vector kernel
     assert pl.info.split_kernel == 0 and pl.pages_per_split == 16
     # contexts of at most 256 tokens are not split (the switch-over), one more token is
-    assert plan(params(batch=3), [256, 100, 1]).max_splits == 1
-    pl = plan(params(batch=3), [257, 100, 1])
+    assert plan(params(batch=3, kernel="matrix"), [256, 100, 1]).max_splits == 1
+    pl = plan(params(batch=3, kernel="matrix"), [257, 100, 1])
     assert pl.pages_per_split == 8 and pl.max_splits == 3
     # the fixed-order mode groups its chunks by the same split length
     pl = plan(params(fixed_chunk=128), [3060])
@@ -152,19 +153,24 @@ def test_split_min_env_override(lib, monkeypatch):
 
 
 def test_split_kernel_selection(lib):
-    assert plan(params(), [3060]).info.split_kernel == 1                       # f16, D 128, P 16
-    assert plan(params(q_dtype="bf16", kv_dtype="bf16"), [3060]).info.split_kernel == 1
-    assert plan(params(page_size=32, max_pages_per_seq=1024), [3060]).info.split_kernel == 1
-    assert plan(params(q_dtype="f32"), [3060]).info.split_kernel == 0           # q and KV differ
-    assert plan(params(q_dtype="f32", kv_dtype="f32"), [3060]).info.split_kernel == 0
+    # 32 sequences x 8 KV heads: as many streams as compute units
+    NB, L = 32, [3060] * 32
+    assert plan(params(batch=NB), L).info.split_kernel == 1                      # f16, D 128, P 16
+    assert plan(params(batch=NB, q_dtype="bf16", kv_dtype="bf16"), L).info.split_kernel == 1
+    assert plan(params(batch=NB, page_size=32, max_pages_per_seq=1024), L).info.split_kernel == 1
+    assert plan(params(batch=NB, q_dtype="f32"), L).info.split_kernel == 0       # q and KV differ
+    assert plan(params(batch=NB, q_dtype="f32", kv_dtype="f32"), L).info.split_kernel == 0
     # no matrix-core decode kernel: G 4 takes the multi-token kernel (one token), G 2 the vector kernel
     for kw in (dict(head_dim=64), dict(head_dim=256), dict(page_size=8, max_pages_per_seq=4096),
                dict(page_size=24, max_pages_per_seq=4096)):
-        assert plan(params(**kw), [3060]).info.split_kernel == 2
-        assert plan(params(num_q_heads=16, **kw), [3060]).info.split_kernel == 0
-    assert plan(params(kernel="vector"), [3060]).info.split_kernel == 0
+        assert plan(params(batch=NB, **kw), L).info.split_kernel == 2
+        assert plan(params(batch=NB, num_q_heads=16, **kw), L).info.split_kernel == 0
+    assert plan(params(batch=NB, kernel="vector"), L).info.split_kernel == 0
+    assert plan(params(batch=NB, kernel="matrix"), L).info.split_kernel == 1
+    assert plan(params(batch=NB, kernel="auto"), L).info.split_kernel == 1
+    # fewer streams than compute units: G 4 at head_dim 128 on the multi-token kernel too
+    assert plan(params(), [3060]).info.split_kernel == 2
     assert plan(params(kernel="matrix"), [3060]).info.split_kernel == 1
-    assert plan(params(kernel="auto"), [3060]).info.split_kernel == 1
     # the matrix-core kernel where it is not built: reported, not replaced
     for kw in (dict(head_dim=64), dict(q_dtype="f32"), dict(page_size=8, max_pages_per_seq=4096)):
         assert status_of(params(kernel="matrix", **kw), [3060]) == B.DA_ERR_UNSUPPORTED
@@ -174,14 +180,17 @@ def test_split_kernel_selection(lib):
 
 # One query head per group (q.K a dot product per key) takes the vector
 # kernel; two to four take the matrix-core decode kernel where it is
-# supported, five to eight the multi-token kernel (one token), whatever the
-# size of the launch or the split count; the fixed-order mode stays on the
-# decode kernels.
+# supported (three and four the multi-token kernel when the batch has fewer
+# (sequence, KV head) streams than compute units), five to eight the
+# multi-token kernel (one token), whatever the split count; the fixed-order
+# mode stays on the decode kernels.
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_split_kernel_by_group(lib, G):
     want = 0 if G == 1 else (1 if G <= 4 else 2)
     for lens in ([32768] * 32, [3060] * 2, [1]):
-        assert plan(params(batch=len(lens), num_q_heads=8 * G), lens).info.split_kernel == want
+        few = len(lens) * 8 < 256
+        w = 2 if (few and G in (3, 4)) else want
+        assert plan(params(batch=len(lens), num_q_heads=8 * G), lens).info.split_kernel == w
     for kw in (dict(num_splits=1), dict(num_splits=7)):
         assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == want
     for kw in (dict(fixed_chunk=1024), dict(fixed_chunk=1024, num_splits=3)):
@@ -291,8 +300,10 @@ def test_multi_token_rows_per_block_rejects(lib):
         B.DA_ERR_UNSUPPORTED
     pl = plan(params(batch=1, query_len=40, head_dim=256, rows_per_block=16, num_splits=1), [5000])
     assert pl.info.split_work_groups == 8 * 10
-    # ignored by decode plans
-    assert plan(params(rows_per_block=64), [3060]).info.split_kernel == 1
+    # ignored by decode plans (one token: 16-row blocks)
+    pl = plan(params(rows_per_block=64), [3060])
+    assert pl.info.split_kernel == 2 and pl.info.split_work_groups == 8 * pl.max_splits
+    assert plan(params(rows_per_block=64, kernel="matrix"), [3060]).info.split_kernel == 1
 
 
 # A few drafted tokens over long contexts: the keys of each (sequence, KV
@@ -359,22 +370,26 @@ def test_forced_kernels_with_several_tokens(lib):
 
 
 def test_query_len_zero_and_one_are_decode(lib):
-    for T in (0, 1):
-        pl = plan(params(query_len=T), [3060])
-        assert pl.info.split_kernel in (0, 1)
+    for lens, kw in (([3060], {}), ([3060] * 32, dict(batch=32)), ([3060], dict(q_dtype="f32"))):
+        a = plan(params(query_len=0, **kw), lens)
+        b = plan(params(query_len=1, **kw), lens)
+        assert (a.info.split_kernel, a.pages_per_split, a.max_splits, a.workspace_bytes) == \
+            (b.info.split_kernel, b.pages_per_split, b.max_splits, b.workspace_bytes)
+        assert a.info.attended_keys == sum(lens)
 
 
 # A decode step (one new token) runs on the multi-token kernel, as one
 # 16-row block per KV head, with 5 to 8 query heads per KV head on 16-bit q
 # and K/V, and with 3 or 4 where the matrix-core decode kernel is not built
-# (head_dim 64 or 256, pages not a multiple of 16); not with an empty context
-# (the kernel needs the new token's own key), a forced kernel or the
-# fixed-order mode.
+# (head_dim 64 or 256, pages not a multiple of 16) or the batch has fewer
+# (sequence, KV head) streams than compute units (as here: 3 x 8); not with an
+# empty context (the kernel needs the new token's own key), a forced kernel or
+# the fixed-order mode.
 @pytest.mark.parametrize("G,kw,want", [
     (5, {}, 2), (6, {}, 2), (8, {}, 2), (8, dict(q_dtype="bf16", kv_dtype="bf16", out_dtype="f32"), 2),
     (8, dict(head_dim=64), 2), (8, dict(head_dim=256), 2), (7, dict(page_size=24, max_pages_per_seq=4096), 2),
     (3, dict(head_dim=64), 2), (4, dict(head_dim=256), 2), (4, dict(page_size=8, max_pages_per_seq=4096), 2),
-    (3, {}, 1), (4, {}, 1), (2, dict(head_dim=64), 0), (2, dict(head_dim=256), 0), (1, dict(head_dim=256), 0),
+    (3, {}, 2), (4, {}, 2), (2, dict(head_dim=64), 0), (2, dict(head_dim=256), 0), (1, dict(head_dim=256), 0),
     (8, dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), 0), (8, dict(q_dtype="f32"), 0),
     (8, dict(kernel="vector"), 0), (8, dict(kernel="matrix"), 1), (8, dict(fixed_chunk=256), 1),
     (4, dict(head_dim=64, fixed_chunk=256), 0),
@@ -420,6 +435,60 @@ def test_decode_on_the_multi_token_kernel_splits(lib, monkeypatch):
     assert pl.max_splits == 5 and pl.pages_per_split == math.ceil(192 / 5)
     monkeypatch.setenv("DECODE_ATTN_SPLIT_MIN", "4096")
     assert plan(params(num_q_heads=64), [3060]).max_splits == 1
+
+
+def test_decode_on_the_multi_token_kernel_below_one_stream_per_cu(lib):
+    # 32/8 heads, head_dim 128: 31 sequences are 248 streams, 32 are 256
+    assert plan(params(batch=31), [4096] * 31).info.split_kernel == 2
+    assert plan(params(batch=32), [4096] * 32).info.split_kernel == 1
+    assert plan(params(batch=31), [4096] * 31, cus=248).info.split_kernel == 1
+    assert plan(params(batch=31, num_q_heads=24), [4096] * 31).info.split_kernel == 2   # G 3
+
+
+# The multi-token plan of a decode step keeps every stream's work-groups
+# within one round of resident work-groups (2 per compute unit at head_dim
+# 128 and 256, 4 at 64): the largest equal split count per stream, which
+# drops the fraction of a round the per-stream count would round up to.
+@pytest.mark.parametrize("B,L,S", [(24, 4096, 2), (12, 2048, 5), (16, 8192, 4), (4, 3060, 16), (1, 32768, 64),
+                                   (48, 3060, 1)])
+def test_decode_on_the_multi_token_kernel_one_round(lib, monkeypatch, B, L, S):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    pl = plan(params(batch=B, num_q_heads=64), [L] * B)
+    assert pl.info.split_kernel == 2 and pl.max_splits == S
+    assert pl.info.active_units == B * 8 * S <= 512
+    assert pl.pages_per_split == math.ceil(math.ceil(L / 16) / S)
+
+
+# Balance: the longest work-group of the multi-token plan may stream at most
+# 1/170 of the batch's page-heads (or the minimum split). A long context
+# among short ones first gets the shortest split whose work-groups fit the
+# round (G 5-8 and where no matrix-core decode kernel is built); where that
+# still leaves it too long, or at G 3-4 on head_dim 128, the decode kernels
+# (balanced schedule) run.
+def test_decode_on_the_multi_token_kernel_balance(lib, monkeypatch):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    lens = [200] * 15 + [65536]                       # 13 pages each and 4096
+    total = (15 * 13 + 4096) * 8
+    pl = plan(params(batch=16, num_q_heads=64, max_pages_per_seq=4096), lens)
+    assert pl.info.split_kernel == 2
+    c = pl.pages_per_split
+    assert c <= math.ceil(total / 170)
+    groups = lambda cc: 8 * sum(max(1, math.ceil(math.ceil(L / 16) / cc)) for L in lens)
+    assert groups(c) <= 512 < groups(c - 1)           # the shortest split that fits the round
+    assert pl.max_splits == math.ceil(4096 / c) and pl.info.active_units == groups(c)
+    # head_dim 64: 4 resident per compute unit
+    pl = plan(params(batch=16, head_dim=64, max_pages_per_seq=4096), lens)
+    assert pl.info.split_kernel == 2 and pl.info.active_units <= 1024
+    # G 4 at head_dim 128: the decode kernel's balanced schedule
+    pl = plan(params(batch=16, max_pages_per_seq=4096), lens)
+    assert pl.info.split_kernel == 1 and pl.info.balanced == 1
+    # four 32768-token contexts among 60 short ones: 512 streams fill the round
+    # with one work-group each, so the long ones cannot be split: decode kernel
+    pl = plan(params(batch=64, num_q_heads=64), [500] * 60 + [32768] * 4)
+    assert pl.info.split_kernel == 1 and pl.info.balanced == 1
+    # a forced split count skips the check
+    pl = plan(params(batch=64, num_q_heads=64, num_splits=4), [500] * 60 + [32768] * 4)
+    assert pl.info.split_kernel == 2 and pl.max_splits == 4
 
 
 def test_empty_batch_plans(lib):
@@ -604,9 +673,10 @@ def balanced_expectation(lens, P, Hkv, window, cus, per_cu, min_tokens, D=128, e
 ])
 def test_balanced_plan_partition(lib, monkeypatch, lens, P, W, G):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
-    # G 8 runs on the multi-token kernel unless the matrix-core decode kernel is asked for
+    # the balanced schedule belongs to the matrix-core decode kernel; G 8 and
+    # short batches at G 4 run on the multi-token kernel unless it is asked for
     p = params(batch=len(lens), num_q_heads=8 * G, page_size=P, max_pages_per_seq=8192, window=W,
-               kernel="matrix" if G == 8 else None)
+               kernel="matrix")
     pl = plan(p, lens)
     assert pl.info.balanced == 1 and pl.info.split_kernel == 1
     U, q, N, pieces = balanced_expectation(lens, P, 8, W, 256, 1 if G == 8 else 2, 128)
@@ -630,7 +700,7 @@ def test_balanced_plan_is_not_taken(lib, monkeypatch):
     assert plan(params(batch=2, num_q_heads=64), lens).info.balanced == 0               # multi-token kernel
     assert plan(params(batch=2, query_len=4, q_dtype="f32"), lens).info.balanced == 0   # per-token mode
     assert plan(params(batch=3), [256, 100, 1]).info.balanced == 0                      # nothing to split
-    assert plan(params(), [3060]).info.balanced == 0                  # 192 work-groups: one round already
+    assert plan(params(kernel="matrix"), [3060]).info.balanced == 0   # 192 work-groups: one round already
     assert plan(params(batch=4097, max_pages_per_seq=1), [16] * 4097).info.balanced == 0
     assert plan(params(batch=4096), [300, 2000] * 2048).info.balanced == 1
     monkeypatch.setenv("DECODE_ATTN_SPLIT_MIN", "4096")

@@ -1,8 +1,10 @@
 """Decode steps on the multi-token kernel: one new token per sequence, with 5
-to 8 query heads per KV head (and 3 or 4 at head_dim 64 and 256 or pages not a
-multiple of 16) on 16-bit q and K/V, run as one 16-row block per KV head with
-both products on the matrix cores, merged by the decode combine. Against the
-oracle at several head dims, page sizes, windows and split counts, ragged and
+to 8 query heads per KV head (and 3 or 4 at head_dim 64 and 256, pages not a
+multiple of 16, or fewer (sequence, KV head) streams than compute units) on
+16-bit q and K/V, run as one 16-row block per KV head with both products on
+the matrix cores, merged by the decode combine. Against the oracle at several
+head dims, page sizes, windows and split counts, ragged, bimodal (one long
+context among short ones: the split that fits one round of work-groups) and
 single-key contexts; an empty context in the batch keeps the decode kernels;
 the full long-context batch at 64 query heads in the planner's launch
 configuration, sampled sequences against the oracle."""
@@ -27,6 +29,10 @@ CASES = [
     (3, 16, 4, 128, "f16", "f32", 8, (7, 1500, 260), 0),                    # G 4, 8-token pages
     (6, 16, 2, 128, "f16", "f32", 16, (1, 1, 1, 1, 1, 1), 0),               # one key each: the output is v
     (2, 64, 8, 128, "f16", "f32", 16, (257, 256), 1),                       # window 1: the new token's own v
+    (16, 64, 8, 128, "f16", "f16", 16, (200,) * 15 + (20000,), 0),          # bimodal: 49 splits of 26 pages
+    (16, 32, 8, 64, "bf16", "f32", 32, (300,) * 15 + (30000,), 0),         # bimodal at head_dim 64
+    (3, 32, 8, 128, "bf16", "f32", 16, (3060, 100, 2049), 0),              # G 4, head_dim 128, 24 streams
+    (3, 24, 8, 128, "f16", "f16", 16, (4097, 1, 640), 2000),               # G 3, head_dim 128, window
 ]
 
 

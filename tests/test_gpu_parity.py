@@ -106,9 +106,9 @@ def test_group_dim_dtype_grid(gpu, G, D, kv):
         for ns in (0, 3):
             out, plan = run_lib(w, num_splits=ns, kernel=kernel)
             # automatic: the matrix-core kernel from two query heads per group on;
-            # the multi-token kernel (one token) from five on, or from three on
-            # where the matrix-core decode kernel is not built
-            multi = kernel == "auto" and kv != "f32" and (G >= 5 or (G >= 3 and not matrix_ok))
+            # the multi-token kernel (one token) from three on here (6 streams,
+            # fewer than compute units)
+            multi = kernel == "auto" and kv != "f32" and G >= 3
             want = 2 if multi else (1 if matrix_ok and (kernel == "matrix" or (kernel == "auto" and G >= 2)) else 0)
             assert plan.info.split_kernel == want
             check(out, ref, kv, "f32", f"G{G} D{D} {kv} splits={ns} kernel={kernel}")
@@ -217,7 +217,7 @@ def test_vector_and_matrix_kernels_agree(gpu):
     """The two split kernels on the same inputs: within fp32 rounding."""
     spec = wl.LLAMA8B_3060.replace(batch=4, lengths=("list", (3060, 5000, 17, 999)), out_dtype="f32")
     w = make(spec, gpu)
-    a, pa = run_lib(w, kernel="auto")
+    a, pa = run_lib(w, kernel="matrix")
     b, pb = run_lib(w, kernel="vector")
     assert pa.info.split_kernel == 1 and pb.info.split_kernel == 0
     rel = ((a - b).norm() / a.norm()).item()
