@@ -533,14 +533,22 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // heads per KV head (2 of 16 rows used) it lost: 4 x 1-4k tokens at
   // head_dim 256 14.5 -> 16.3. An empty context stays on the decode kernels
   // (the multi-token kernel needs the new token's own key).
+  // At 3 or 4 heads on head_dim 128 (the matrix-core decode kernel built)
+  // only the planner's own split choice, and only a plan that splits: an
+  // unsplit stream's tiles run through one computing wave there, against
+  // four waves on the decode kernel (1 x 100 tokens 5.9 against 8.4 us, 8 x
+  // 256 7.3 against 10.2; at 8 heads or head_dim 64 and 256 the two are even
+  // or this is faster: 64 heads over 8, 64 x 200 tokens 20.7 -> 11.7).
   const bool few_streams = static_cast<int64_t>(p->batch) * p->num_kv_heads < num_cus;
   const bool weak_decode = gt == 8 || !matrix_kernel_supported(*p);
-  bool mq_decode = T == 1 && (gt == 8 || (gt == 4 && (weak_decode || few_streams))) && multi_dtypes &&
-                   p->kernel == DA_KERNEL_AUTO && !fixed;
+  bool mq_decode = T == 1 &&
+                   (gt == 8 || (gt == 4 && (weak_decode || (few_streams && p->num_splits == 0)))) &&
+                   multi_dtypes && p->kernel == DA_KERNEL_AUTO && !fixed;
   for (int32_t b = 0; mq_decode && b < p->batch; ++b) mq_decode = lens[b] >= 1;
   int64_t mq_pages = 0;
   if (mq_decode && p->num_splits == 0) {
     mq_pages = multi_decode_split_pages(npages, p->num_kv_heads, num_cus, p->head_dim, P, weak_decode);
+    if (!weak_decode && mq_pages >= max_np) mq_pages = 0;
     mq_decode = mq_pages > 0;
   }
   if ((plan->query_len > 1 && !per_token) || mq_decode) {

@@ -188,9 +188,13 @@ def test_split_kernel_selection(lib):
 def test_split_kernel_by_group(lib, G):
     want = 0 if G == 1 else (1 if G <= 4 else 2)
     for lens in ([32768] * 32, [3060] * 2, [1]):
-        few = len(lens) * 8 < 256
-        w = 2 if (few and G in (3, 4)) else want
+        # G 3-4 with fewer streams than compute units, when the plan splits
+        few_split = len(lens) * 8 < 256 and max(lens) > 256
+        w = 2 if (few_split and G in (3, 4)) else want
         assert plan(params(batch=len(lens), num_q_heads=8 * G), lens).info.split_kernel == w
+    # a forced split count keeps G 3-4 on the decode kernel
+    for kw in (dict(num_splits=1), dict(num_splits=7)):
+        assert plan(params(batch=2, num_q_heads=8 * G, **kw), [3060] * 2).info.split_kernel == want
     for kw in (dict(num_splits=1), dict(num_splits=7)):
         assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == want
     for kw in (dict(fixed_chunk=1024), dict(fixed_chunk=1024, num_splits=3)):
@@ -443,6 +447,15 @@ def test_decode_on_the_multi_token_kernel_below_one_stream_per_cu(lib):
     assert plan(params(batch=32), [4096] * 32).info.split_kernel == 1
     assert plan(params(batch=31), [4096] * 31, cus=248).info.split_kernel == 1
     assert plan(params(batch=31, num_q_heads=24), [4096] * 31).info.split_kernel == 2   # G 3
+    # only a plan that splits (contexts up to the 256-token switch-over are not split)
+    assert plan(params(batch=8), [256] * 8).info.split_kernel == 1
+    pl = plan(params(batch=8), [257] * 8)
+    assert pl.info.split_kernel == 2 and pl.max_splits > 1
+    # not with a forced split count
+    assert plan(params(batch=31, num_splits=4), [4096] * 31).info.split_kernel == 1
+    # G 8 and head_dim 64 run unsplit streams on the multi-token kernel too
+    assert plan(params(batch=8, num_q_heads=64), [256] * 8).info.split_kernel == 2
+    assert plan(params(batch=8, head_dim=64), [256] * 8).info.split_kernel == 2
 
 
 # The multi-token plan of a decode step keeps every stream's work-groups

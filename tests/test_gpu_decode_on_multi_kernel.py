@@ -44,9 +44,11 @@ def test_decode_on_multi_kernel_matches_oracle(gpu, i):
     say(f"[decode on multi {i}] B={B} H={HQ}/{HKV} D={D} {dt}->{out} P={P} lens={lens} W={W}")
     w = wl.make_workload(spec, gpu)
     ref = oracle_for(w)
+    # G 3-4 at head_dim 128 take it only with the planner's own split choice
+    g34_d128 = HQ // HKV <= 4 and D == 128 and P % 16 == 0
     for ns in (0, 1, 3):
         got, plan = run_lib(w, num_splits=ns)
-        assert plan.info.split_kernel == 2
+        assert plan.info.split_kernel == (1 if (g34_d128 and ns > 0) else 2)
         err, worst = check(got, ref, dt, out, f"decode on multi {i} splits={ns}")
         say(f"  splits {ns} -> {plan.max_splits} x {plan.pages_per_split} pages: rel L2 {err:.2e}, "
             f"worst sequence {worst:.2e}")
