@@ -180,8 +180,9 @@ typedef struct {
                                 plans (query_len <= 1) with DA_KERNEL_AUTO
                                 take 2 when q and K/V share f16 or bf16, every
                                 length is at least 1, and G is 5 to 8, or 3 to
-                                4 where 1 is not built or B * H_kv is below
-                                num_cus; outside the fixed-order mode; and
+                                4 where 1 is not built or (num_splits 0, and
+                                the plan splits) B * H_kv is below num_cus;
+                                outside the fixed-order mode; and
                                 (num_splits 0) only if no work-group of that
                                 plan holds more than about 1/170 of the
                                 batch's attended page-heads (else the decode
