@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     # (workload, overrides, fixed_chunk)
-    ("llama8b_3060", {}, 0),
+    ("llama8b_3060", {}, 0),                                                          # one token, multi-token kernel
+    ("long_batch", {"batch": 4, "num_q_heads": 64, "lengths": ("list", (20000, 3060, 100, 9000))}, 0),  # GQA 8
     ("mixed_window", {"batch": 4, "lengths": ("list", (100, 40000, 7, 33000))}, 0),
     ("llama8b_3060", {"batch": 3, "lengths": ("list", (3060, 9000, 1))}, 256),      # fixed-order mode
     ("verify_long", {"batch": 3, "lengths": ("list", (20000, 4, 900))}, 0),          # multi-token kernel
