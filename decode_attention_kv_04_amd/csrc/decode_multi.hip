@@ -668,6 +668,32 @@ multi_dma_kernel(const KernelArgs a) {
     // them on each tile. Likewise the tiles that need masks or move a
     // reference leave the plain loop for the general update below, so that
     // the plain loop carries O only through its matrix products.
+    // Wave priority by progress: 3 for the first quarter of this wave's
+    // tiles, down to 0 for the last. The two work-groups sharing a compute
+    // unit start together with about equal work; the issue arbiter favours
+    // the older waves, so without this the second one falls behind and then
+    // runs alone at one wave per SIMD (its end 12 us after its partner's on
+    // the 128-token suffix). A wave that lags keeps the higher priority.
+    // Measured (split pass, us): 32-token suffix 34.0 -> 32.5, head_dim 64
+    // suffix 51.4 -> 49.2, 512-token suffix 255.4 -> 248.7, the 4-token check
+    // 506.3 -> 496.6, 64 query heads over the long batch 492.6 -> 484.5; the
+    // 128-token suffix 81.4 -> 82.3 (its step 92.8 -> 91.8). Priorities by
+    // the remaining tiles of a full split measured the same or slower.
+    int plev = 3;
+    int pnext = ntiles >> 2;
+    __builtin_amdgcn_s_setprio(3);
+    auto lower_prio = [&]() {
+      if (m >= pnext) {
+        --plev;
+        pnext = plev == 2 ? (ntiles >> 1) : (plev == 1 ? 3 * (ntiles >> 2) : 0x7FFFFFFF);
+        if (plev == 2)
+          __builtin_amdgcn_s_setprio(2);
+        else if (plev == 1)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
+      }
+    };
     while (m < ntiles) {
       begin_copies(m, stage);
       scores(stage, sacc);
@@ -703,6 +729,7 @@ multi_dma_kernel(const KernelArgs a) {
           if (m + 1 + LEAD < ntiles) fetch_id();
           stage = sn;
           ++m;
+          lower_prio();
         };
         for (;;) {
           if (m + 1 >= ntiles || !is_plain((tile_first + m) * KT, sacc)) break;
@@ -724,6 +751,7 @@ multi_dma_kernel(const KernelArgs a) {
           tile_update_plain<D, KVT, NR>(sacc, [&](int nb) { return vt[nb]; }, rg, sl2);
           stage = ring<NS>(stage, 1);
           ++m;
+          lower_prio();
           if (m >= ntiles) break;
           begin_copies(m, stage);
           scores(stage, sacc);
