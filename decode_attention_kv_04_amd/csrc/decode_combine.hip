@@ -33,6 +33,107 @@ namespace {
 
 constexpr int kRowsPerGroup = 4;  // one wave per row, four rows per work-group
 
+__device__ __forceinline__ float ldf(const float* p) { return *p; }
+
+// States loaded together by the single-row merges.
+constexpr int kMergeBatch = 16;
+
+// The first batch of the states [s_lo, s_lo + avail) of query row `qrow`:
+// the O rows of the first min(avail, kMergeBatch) states (lane i takes
+// elements i, i + 64, ...) and the (m, l) of state s_lo + lane for lanes below
+// avail. `avail` may exceed the range later merged (every slot below
+// max_splits lies inside the workspace): entries past the range are never
+// used.
+template <int D>
+__device__ __forceinline__ void load_first(const KernelArgs& a, int64_t qrow, int s_lo, int avail, int lane,
+                                           float (&ov)[kMergeBatch][D / 64], float& m0, float& l0) {
+  constexpr int N = D / 64;
+  const int64_t base = qrow * a.max_splits + s_lo;
+  const float* ml = a.ws_ml + base * 2;
+  const float* os = a.ws_o + base * D;
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j)
+    if (j < avail)
+#pragma unroll
+      for (int i = 0; i < N; ++i) ov[j][i] = ldf(os + static_cast<int64_t>(j) * D + lane + 64 * i);
+  m0 = -INFINITY;
+  l0 = 0.0f;
+  if (lane < avail) {
+    m0 = ldf(ml + 2 * lane);
+    l0 = ldf(ml + 2 * lane + 1);
+  }
+}
+
+// Merge states [s_lo, s_hi) of query row `qrow` (the flat index of
+// (sequence, query head), or of (sequence, new token, query head)) in one
+// wave; lane i owns elements i, i + 64, ... of the row:
+//     M = max_s m_s,  w_s = 2^(m_s - M),  acc = sum_s w_s O_s,  lsum = sum_s w_s l_s
+// A state with m_s = -inf gets weight 0; an empty range gives M = -inf and
+// zeros. `ov`, `m0`, `l0` hold the range's first batch (load_first); lane j
+// holds (m, l) of state s_lo + j of each chunk of 64, later O rows are loaded
+// kMergeBatch at a time, and the weights are broadcast with readlane. The
+// order of every sum is fixed, so results are identical run to run.
+template <int D>
+__device__ __forceinline__ void merge_range_wave(const KernelArgs& a, int64_t qrow, int s_lo, int s_hi, int lane,
+                                                 float& M_out, float& lsum_out, float (&acc)[D / 64],
+                                                 float (&ov)[kMergeBatch][D / 64], float m0, float l0) {
+  constexpr int N = D / 64;
+  constexpr int BATCH = kMergeBatch;
+  const int cnt_all = s_hi > s_lo ? s_hi - s_lo : 0;
+  const int64_t base = qrow * a.max_splits + s_lo;
+  const float* ml = a.ws_ml + base * 2;
+  const float* os = a.ws_o + base * D;
+  auto load_rows = [&](int first, int cnt) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j)
+      if (j < cnt)
+#pragma unroll
+        for (int i = 0; i < N; ++i) ov[j][i] = ldf(os + static_cast<int64_t>(first + j) * D + lane + 64 * i);
+  };
+
+  // state `lane` of the first chunk; a slot past the range is replaced here
+  m0 = lane < cnt_all ? m0 : -INFINITY;
+  l0 = lane < cnt_all ? l0 : 0.0f;
+  float M = m0;
+  for (int s = 64 + lane; s < cnt_all; s += 64) M = fmaxf(M, ldf(ml + 2 * s));
+  M = wave_max(M);
+  const float Mu = (M == -INFINITY) ? 0.0f : M;
+
+  float lsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+  for (int s0 = 0; s0 < cnt_all; s0 += 64) {
+    float mk = m0, lk = l0;
+    if (s0 > 0) {
+      mk = -INFINITY;
+      lk = 0.0f;
+      if (s0 + lane < cnt_all) {
+        mk = ldf(ml + 2 * (s0 + lane));
+        lk = ldf(ml + 2 * (s0 + lane) + 1);
+      }
+    }
+    float w = 0.0f;
+    if (s0 + lane < cnt_all) {
+      w = exp2_fast(mk - Mu);
+      lsum += w * lk;
+    }
+    const int cnt = cnt_all - s0 < 64 ? cnt_all - s0 : 64;
+    for (int j0 = 0; j0 < cnt; j0 += BATCH) {
+      if (s0 + j0 > 0) load_rows(s0 + j0, cnt - j0);
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        if (j0 + j < cnt) {
+          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + j));
+#pragma unroll
+          for (int i = 0; i < N; ++i) acc[i] = fmaf(wj, ov[j][i], acc[i]);
+        }
+      }
+    }
+  }
+  lsum_out = wave_sum(lsum);
+  M_out = M;
+}
+
 // States to merge for query head h of sequence b; 0 if the split pass wrote
 // the row itself (a single split, outside the fixed-order mode).
 __device__ __forceinline__ int split_count(const KernelArgs& a, int b, int h) {
@@ -60,9 +161,19 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void combine_kernel(const Kerne
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   if (h >= a.num_q_heads) return;  // whole wave
+  const int64_t qrow = static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h;
+  // The first states' loads go out before the row's state count is known:
+  // a dependent memory round trip less.
+  constexpr int N = D / 64;
+  float ov[kMergeBatch][N], m0, l0;
+  load_first<D>(a, qrow, 0, a.max_splits, lane, ov, m0, l0);
   const int nsplit = split_count(a, b, h);
   if (nsplit <= 0) return;  // the split pass wrote this row
-  merge_head_wave<D>(a, static_cast<int64_t>(b) * a.rows_per_seq + a.row_base + h, nsplit, lane);
+  float M, lsum, acc[N];
+  merge_range_wave<D>(a, qrow, 0, nsplit, lane, M, lsum, acc, ov, m0, l0);
+  const int64_t row = qrow * D;
+#pragma unroll
+  for (int i = 0; i < N; ++i) store_elem(a.out, row + lane + 64 * i, a.out_dtype, lsum > 0.0f ? acc[i] / lsum : 0.0f);
 }
 
 // Rows with many states (plans with more than kWideSplits states per row):
@@ -88,7 +199,11 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(const KernelArgs a) {
   __shared__ float sh_acc[4][D];
   __shared__ float sh_ml[4][2];
   float M, lsum, acc[N];
-  merge_range_wave<D>(a, qrow, wave * nsplit / 4, (wave + 1) * nsplit / 4, lane, M, lsum, acc);
+  const int s_lo = wave * nsplit / 4;
+  const int s_hi = (wave + 1) * nsplit / 4;
+  float ov[kMergeBatch][N], m0, l0;
+  load_first<D>(a, qrow, s_lo, s_hi - s_lo, lane, ov, m0, l0);
+  merge_range_wave<D>(a, qrow, s_lo, s_hi, lane, M, lsum, acc, ov, m0, l0);
 #pragma unroll
   for (int i = 0; i < N; ++i) sh_acc[wave][lane + 64 * i] = acc[i];
   if (lane == 0) {
@@ -202,6 +317,43 @@ __global__ __launch_bounds__(256) void combine_multi_kernel(const KernelArgs a) 
   const int hl = threadIdx.x & 31;
   if (h >= a.num_q_heads) return;  // whole half-wave
   const int T = a.query_len;
+  constexpr int E = D / 32;
+  constexpr int BATCH = 8;
+  const int64_t qrow = (static_cast<int64_t>(b) * T + t) * a.num_q_heads + h;
+  const float* ml = a.ws_ml + qrow * a.max_splits * 2;
+  const float* os = a.ws_o + qrow * a.max_splits * D + hl * E;
+  // The first BATCH states' loads go out before the split count is known
+  // (their slots lie inside the workspace); slots past the count are
+  // replaced below by select, so whatever they hold is never used.
+  const int first = a.max_splits < BATCH ? a.max_splits : BATCH;
+  float ov[BATCH][E], mv[BATCH], lv[BATCH];
+#pragma unroll
+  for (int j = 0; j < BATCH; ++j) {
+    mv[j] = -INFINITY;
+    lv[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) ov[j][i] = 0.0f;
+    if (j < first) {
+      const float* o = os + static_cast<int64_t>(j) * D;
+      if constexpr (E == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(o);
+        ov[j][0] = x.x;
+        ov[j][1] = x.y;
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; i += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(o + i);
+          ov[j][i] = x.x;
+          ov[j][i + 1] = x.y;
+          ov[j][i + 2] = x.z;
+          ov[j][i + 3] = x.w;
+        }
+      }
+      const float2 st = *reinterpret_cast<const float2*>(ml + 2 * j);
+      mv[j] = st.x;
+      lv[j] = st.y;
+    }
+  }
   const int G = a.group;
   const int R = T * G;
   const int P = a.page_size;
@@ -218,7 +370,83 @@ __global__ __launch_bounds__(256) void combine_multi_kernel(const KernelArgs a) 
   int nsplit = (pe - pf + a.pages_per_split - 1) / a.pages_per_split;
   if (nsplit > a.max_splits) nsplit = a.max_splits;
   if (nsplit <= 1) return;  // the split pass wrote this row
-  merge_row_halfwave<D>(a, (static_cast<int64_t>(b) * T + t) * a.num_q_heads + h, nsplit, hl);
+#pragma unroll
+  for (int j = 0; j < BATCH; ++j) {
+    const bool use = j < nsplit;
+    mv[j] = use ? mv[j] : -INFINITY;
+    lv[j] = use ? lv[j] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) ov[j][i] = use ? ov[j][i] : 0.0f;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < BATCH; ++j) M = fmaxf(M, mv[j]);
+  const float Mu0 = (M == -INFINITY) ? 0.0f : M;
+  float lsum = 0.0f;
+  float acc[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < BATCH; ++j) {
+    if (j < nsplit) {
+      const float w = exp2_fast(mv[j] - Mu0);
+      lsum += w * lv[j];
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[i] = fmaf(w, ov[j][i], acc[i]);
+    }
+  }
+  // Further states (more than BATCH splits), BATCH at a time as in the
+  // single-row merge.
+  for (int s0 = BATCH; s0 < nsplit; s0 += BATCH) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      mv[j] = -INFINITY;
+      lv[j] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) ov[j][i] = 0.0f;
+      if (s0 + j < nsplit) {
+        const float* o = os + static_cast<int64_t>(s0 + j) * D;
+        if constexpr (E == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(o);
+          ov[j][0] = x.x;
+          ov[j][1] = x.y;
+        } else {
+#pragma unroll
+          for (int i = 0; i < E; i += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(o + i);
+            ov[j][i] = x.x;
+            ov[j][i + 1] = x.y;
+            ov[j][i + 2] = x.z;
+            ov[j][i + 3] = x.w;
+          }
+        }
+        const float2 st = *reinterpret_cast<const float2*>(ml + 2 * (s0 + j));
+        mv[j] = st.x;
+        lv[j] = st.y;
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) Mn = fmaxf(Mn, mv[j]);
+    const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
+    const float alpha = exp2_fast(M - Mu);  // 0 while no state had a key
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      if (s0 + j < nsplit) {
+        const float w = exp2_fast(mv[j] - Mu);
+        lsum += w * lv[j];
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] = fmaf(w, ov[j][i], acc[i]);
+      }
+    }
+    M = Mn;
+  }
+  const int64_t row = qrow * D + hl * E;
+#pragma unroll
+  for (int i = 0; i < E; ++i) store_elem(a.out, row + i, a.out_dtype, lsum > 0.0f ? acc[i] / lsum : 0.0f);
 }
 
 }  // namespace

@@ -202,93 +202,5 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float ldf(const float* p) { return *p; }
-
-// Merge states [s_lo, s_hi) of query row `qrow` (the flat index of
-// (sequence, query head), or of (sequence, new token, query head)) in one
-// wave; lane i owns elements i, i + 64, ... of the row:
-//     M = max_s m_s,  w_s = 2^(m_s - M),  acc = sum_s w_s O_s,  lsum = sum_s w_s l_s
-// A state with m_s = -inf gets weight 0; an empty range gives M = -inf and
-// zeros. Lane j holds (m, l) of state s_lo + j of each chunk of 64; the O rows
-// of the first BATCH states are loaded together with them (one memory round
-// trip when the range holds at most BATCH), later rows BATCH at a time; the
-// weights are broadcast with readlane. The order of every sum is fixed, so
-// results are identical run to run.
-template <int D>
-__device__ void merge_range_wave(const KernelArgs& a, int64_t qrow, int s_lo, int s_hi, int lane, float& M_out,
-                                 float& lsum_out, float (&acc)[D / 64]) {
-  constexpr int N = D / 64;
-  constexpr int BATCH = 16;
-  const int cnt_all = s_hi > s_lo ? s_hi - s_lo : 0;
-  const int64_t base = qrow * a.max_splits + s_lo;
-  const float* ml = a.ws_ml + base * 2;
-  const float* os = a.ws_o + base * D;
-  auto load_rows = [&](float (&ov)[BATCH][N], int first, int cnt) {
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j)
-      if (j < cnt)
-#pragma unroll
-        for (int i = 0; i < N; ++i) ov[j][i] = ldf(os + static_cast<int64_t>(first + j) * D + lane + 64 * i);
-  };
-
-  float ov[BATCH][N];
-  load_rows(ov, 0, cnt_all < BATCH ? cnt_all : BATCH);
-  float m0 = -INFINITY, l0 = 0.0f;  // state `lane` of the first chunk
-  if (lane < cnt_all) {
-    m0 = ldf(ml + 2 * lane);
-    l0 = ldf(ml + 2 * lane + 1);
-  }
-  float M = m0;
-  for (int s = 64 + lane; s < cnt_all; s += 64) M = fmaxf(M, ldf(ml + 2 * s));
-  M = wave_max(M);
-  const float Mu = (M == -INFINITY) ? 0.0f : M;
-
-  float lsum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-  for (int s0 = 0; s0 < cnt_all; s0 += 64) {
-    float mk = m0, lk = l0;
-    if (s0 > 0) {
-      mk = -INFINITY;
-      lk = 0.0f;
-      if (s0 + lane < cnt_all) {
-        mk = ldf(ml + 2 * (s0 + lane));
-        lk = ldf(ml + 2 * (s0 + lane) + 1);
-      }
-    }
-    float w = 0.0f;
-    if (s0 + lane < cnt_all) {
-      w = exp2_fast(mk - Mu);
-      lsum += w * lk;
-    }
-    const int cnt = cnt_all - s0 < 64 ? cnt_all - s0 : 64;
-    for (int j0 = 0; j0 < cnt; j0 += BATCH) {
-      if (s0 + j0 > 0) load_rows(ov, s0 + j0, cnt - j0);
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j) {
-        if (j0 + j < cnt) {
-          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + j));
-#pragma unroll
-          for (int i = 0; i < N; ++i) acc[i] = fmaf(wj, ov[j][i], acc[i]);
-        }
-      }
-    }
-  }
-  lsum_out = wave_sum(lsum);
-  M_out = M;
-}
-
-// Merge the nsplit states of query row `qrow` into its output row (one
-// wave):  out = sum_s w_s O_s / sum_s w_s l_s  (see merge_range_wave).
-template <int D>
-__device__ void merge_head_wave(const KernelArgs& a, int64_t qrow, int nsplit, int lane) {
-  constexpr int N = D / 64;
-  float M, lsum, acc[N];
-  merge_range_wave<D>(a, qrow, 0, nsplit, lane, M, lsum, acc);
-  const int64_t row = qrow * D;
-#pragma unroll
-  for (int i = 0; i < N; ++i) store_elem(a.out, row + lane + 64 * i, a.out_dtype, lsum > 0.0f ? acc[i] / lsum : 0.0f);
-}
-
 }  // namespace
 }  // namespace da
