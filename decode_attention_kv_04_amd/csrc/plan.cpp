@@ -120,6 +120,35 @@ bool valid_dtype(da_dtype t) { return t == DA_F32 || t == DA_F16 || t == DA_BF16
 // 85 with a split count per stream).
 constexpr int64_t kMultiDecodeShare = 170;
 
+// Shortest split (at least cmin pages) whose working work-groups, ceil(pages
+// / c) for every block of `npages` on each of H KV heads, fit `slots`; the
+// longest block's page count when no split fits. The count of work-groups
+// never grows with c, so a bisection finds it.
+int64_t fit_split_pages(const std::vector<int64_t>& npages, int64_t H, int64_t slots, int64_t cmin, int64_t max_np) {
+  auto groups = [&](int64_t cc) {
+    int64_t n = 0;
+    for (int64_t np : npages) n += std::max<int64_t>(1, ceil_div(np, cc));
+    return n * H;
+  };
+  int64_t lo = std::min(cmin, max_np), hi = max_np;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (groups(mid) <= slots)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
+// Largest split (pages) a balanced multi-token plan gives one work-group:
+// 1/kMultiDecodeShare of the blocks' page-heads, or the minimum split.
+int64_t balance_limit(const std::vector<int64_t>& npages, int64_t H, int64_t cmin) {
+  int64_t total = 0;
+  for (int64_t n : npages) total += n;
+  return std::max(cmin, ceil_div(total * H, kMultiDecodeShare));
+}
+
 // Split length (pages) of a decode step on the multi-token kernel for the
 // attended page counts `npages`, or 0 where that kernel would leave the
 // batch unbalanced (the decode kernels then run). First the largest split
@@ -134,35 +163,19 @@ constexpr int64_t kMultiDecodeShare = 170;
 // it is only the second choice).
 int64_t multi_decode_split_pages(const std::vector<int64_t>& npages, int64_t num_kv_heads, int64_t num_cus,
                                  int32_t head_dim, int64_t P, bool fit) {
-  int64_t max_np = 0, total = 0;
-  for (int64_t n : npages) {
-    max_np = std::max(max_np, n);
-    total += n;
-  }
+  int64_t max_np = 0;
+  for (int64_t n : npages) max_np = std::max(max_np, n);
   if (max_np == 0) return 1;
   const int64_t slots = num_cus * resident_row_groups_per_cu(head_dim, 16);
   const int64_t blocks = static_cast<int64_t>(npages.size()) * num_kv_heads;
   const int64_t cmin = std::min(max_np, ceil_div(multi_decode_min_split_tokens(max_np * P), P));
-  const int64_t limit = std::max(cmin, ceil_div(total * num_kv_heads, kMultiDecodeShare));
+  const int64_t limit = balance_limit(npages, num_kv_heads, cmin);
   const int64_t per_stream = std::max<int64_t>(1, slots / blocks);
   const int64_t c = std::min(max_np, std::max(cmin, ceil_div(max_np, per_stream)));
   if (c <= limit) return c;
   if (!fit) return 0;
-  auto groups = [&](int64_t cc) {
-    int64_t n = 0;
-    for (int64_t np : npages) n += std::max<int64_t>(1, ceil_div(np, cc));
-    return n * num_kv_heads;
-  };
-  // groups() never grows with c; with no c in range fitting, lo ends at max_np.
-  int64_t lo = cmin, hi = max_np;
-  while (lo < hi) {
-    const int64_t mid = lo + (hi - lo) / 2;
-    if (groups(mid) <= slots)
-      hi = mid;
-    else
-      lo = mid + 1;
-  }
-  return lo <= limit ? lo : 0;
+  const int64_t f = fit_split_pages(npages, num_kv_heads, slots, cmin, max_np);
+  return f <= limit ? f : 0;
 }
 
 }  // namespace
@@ -385,7 +398,19 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_p
     const int64_t want = ceil_div(static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim, QB),
                                   blocks);
     c = ceil_div(max_np, std::max<int64_t>(1, want));
-    c = std::min(max_np, std::max(c, ceil_div(min_split_tokens(), P)));
+    const int64_t cmin = std::min(max_np, ceil_div(min_split_tokens(), P));
+    c = std::min(max_np, std::max(c, cmin));
+    // A few long contexts among short ones: the split from the longest block
+    // leaves the long blocks on a few work-groups, each streaming at most
+    // about 31 GB/s. Past the balance limit the shortest split that fits the
+    // round, or else the limit itself (more than one round of work-groups:
+    // there is no other kernel for several tokens).
+    const int64_t limit = balance_limit(blk_pages, p.num_kv_heads, cmin);
+    if (c > limit) {
+      const int64_t slots = static_cast<int64_t>(plan->num_cus) * resident_row_groups_per_cu(p.head_dim, QB);
+      const int64_t f = fit_split_pages(blk_pages, p.num_kv_heads, slots, cmin, max_np);
+      c = f <= limit ? f : limit;
+    }
   }
   c = std::max<int64_t>(c, 1);
   c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));  // grid y = row blocks x splits

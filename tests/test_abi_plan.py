@@ -325,6 +325,30 @@ def test_multi_token_few_rows_fill_one_round(lib):
     assert pl.max_splits == 4
 
 
+# A few long contexts among short ones: the split from the longest row block
+# is capped at the balance limit (1/170 of the blocks' page-heads): first the
+# shortest split whose work-groups fit one round, else the limit itself.
+def test_multi_token_plan_balance(lib, monkeypatch):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    groups = lambda lens, c: 8 * sum(max(1, math.ceil(math.ceil(L / 16) / c)) for L in lens)
+    # 4 drafted tokens x G 4 = 16 rows: one block per (sequence, KV head), pages ceil(L / 16)
+    lens = [200] * 15 + [65536]
+    total = 8 * sum(math.ceil(L / 16) for L in lens)
+    pl = plan(params(batch=16, query_len=4, max_pages_per_seq=4096), lens)
+    c = pl.pages_per_split
+    assert c <= math.ceil(total / 170) and groups(lens, c) <= 512 < groups(lens, c - 1)
+    # 512 blocks fill the round alone: the limit itself, more than one round
+    lens = [500] * 60 + [32768] * 4
+    total = 8 * sum(math.ceil(L / 16) for L in lens)
+    pl = plan(params(batch=64, query_len=4), lens)
+    assert pl.pages_per_split == math.ceil(total / 170)
+    assert pl.info.active_units == groups(lens, pl.pages_per_split) > 512
+    # about equal lengths keep the split of the longest block
+    lens = [16384 + 512 * i for i in range(32)]
+    pl = plan(params(batch=32, query_len=4), lens)
+    assert pl.max_splits == 2 and pl.pages_per_split == math.ceil(math.ceil(max(lens) / 16) / 2)
+
+
 def test_multi_token_window_keys(lib):
     T, W = 8, 100
     pl = plan(params(batch=1, query_len=T, window=W), [5000])

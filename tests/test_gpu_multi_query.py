@@ -186,6 +186,30 @@ def sampled_decode_oracle(w, pairs):
     return out
 
 
+# A few long contexts among short ones: the split length capped at the
+# balance limit (the fit-the-round split, or the limit itself with more than
+# one round of work-groups); every sequence against the oracle.
+BIMODAL = [
+    # T, G, Hkv, D, kv, out, P, lens
+    (4, 4, 2, 128, "f16", "f16", 16, (200,) * 15 + (20000,)),        # fit: 79 splits of 16 pages
+    (128, 4, 2, 128, "f16", "f32", 16, (300,) * 7 + (9000,)),       # 128-row blocks, fit
+    (2, 8, 8, 128, "bf16", "f32", 16, (100,) * 62 + (30000,) * 2),   # 512 blocks: the limit itself
+    (4, 4, 2, 64, "bf16", "bf16", 32, (64,) * 20 + (40000,)),        # head_dim 64
+]
+
+
+@pytest.mark.parametrize("T,G,Hkv,D,kv,out,P,lens", BIMODAL)
+def test_bimodal_batches_match_oracle(gpu, T, G, Hkv, D, kv, out, P, lens):
+    spec = spec_of(T, G, D, kv, out, P, lens, 0, Hkv=Hkv, seed=77)
+    say(f"[multi bimodal] {spec.name} B={len(lens)} longest {max(lens)}")
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w)
+    assert plan.info.split_kernel == 2 and plan.max_splits > 2
+    say(f"  pages/split {plan.pages_per_split}, max splits {plan.max_splits}, active {plan.info.active_units}")
+    err, worst = check(got, oracle_for(w), kv, out, spec.name)
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
+
+
 @pytest.mark.parametrize("name", ["suffix_prefill", "verify_long"])
 def test_full_size_workloads_sampled(gpu, name):
     spec = wl.NAMED[name]
