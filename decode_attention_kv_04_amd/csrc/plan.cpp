@@ -110,15 +110,16 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool valid_dtype(da_dtype t) { return t == DA_F32 || t == DA_F16 || t == DA_BF16; }
 
-// A decode step on the multi-token kernel is taken only if its longest
-// work-group streams at most 1/kMultiDecodeShare of the batch's page-heads:
-// one work-group alone streams about 31 GB/s (four 32768-token contexts
-// among 60 short ones, 64/8 heads: 32 work-groups of 16 MB in 537 us), the
-// chip about 6.4 TB/s, so beyond that share the longest work-groups, not
-// HBM, set the time (that batch: 537 us against 160 on the decode kernel's
-// balanced schedule; 15 short contexts and one of 65536 tokens: 268 against
-// 85 with a split count per stream).
-constexpr int64_t kMultiDecodeShare = 170;
+// Balance of a multi-token plan: its longest work-group should stream at
+// most 1/kMultiBalanceShare of the batch's page-heads. One work-group alone
+// streams about 31 GB/s (four 32768-token contexts among 60 short ones,
+// 64/8 heads: 32 work-groups of 16 MB in 537 us), the chip about 6.4 TB/s,
+// so beyond that share the longest work-groups, not HBM, set the time (that
+// batch: 537 us against 160 on the decode kernel's balanced schedule; 15
+// short contexts and one of 65536 tokens: 268 against 85 with a split count
+// per stream). A decode step that cannot be balanced runs on the decode
+// kernels; several tokens take the limit itself as their split.
+constexpr int64_t kMultiBalanceShare = 170;
 
 // Shortest split (at least cmin pages) whose working work-groups, ceil(pages
 // / c) for every block of `npages` on each of H KV heads, fit `slots`; the
@@ -142,11 +143,11 @@ int64_t fit_split_pages(const std::vector<int64_t>& npages, int64_t H, int64_t s
 }
 
 // Largest split (pages) a balanced multi-token plan gives one work-group:
-// 1/kMultiDecodeShare of the blocks' page-heads, or the minimum split.
+// 1/kMultiBalanceShare of the blocks' page-heads, or the minimum split.
 int64_t balance_limit(const std::vector<int64_t>& npages, int64_t H, int64_t cmin) {
   int64_t total = 0;
   for (int64_t n : npages) total += n;
-  return std::max(cmin, ceil_div(total * H, kMultiDecodeShare));
+  return std::max(cmin, ceil_div(total * H, kMultiBalanceShare));
 }
 
 // Split length (pages) of a decode step on the multi-token kernel for the
