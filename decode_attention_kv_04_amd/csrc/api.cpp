@@ -168,7 +168,7 @@ da_status decode_attn_plan_info(da_plan_t plan, da_plan_info* info) {
   info->attended_keys = plan->attended_keys;
   info->workspace_bytes = plan->ws_bytes;
   info->split_kernel = plan->split_kernel;
-  info->chunks_per_work_group = plan->chunks_per_group;
+  info->chunks_per_work_group = plan->fixed_multi ? 1 : plan->chunks_per_group;
   info->balanced = plan->balanced ? 1 : 0;
   return DA_OK;
 }

@@ -353,6 +353,8 @@ da_status finish_fixed_plan(da_plan* plan, const std::vector<int64_t>& npages, i
 // its first token to its last token, and those pages are split with one split
 // length for the whole batch.
 da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_pages) {
+  // decode_pages > 0: a decode step's split length, or (fixed_multi) the
+  // fixed-order chunk in pages, which num_splits does not change.
   const da_params& p = plan->p;
   const int64_t P = p.page_size;
   const int64_t T = plan->query_len;
@@ -390,6 +392,8 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_p
   int64_t c;
   if (max_np == 0) {
     c = 1;
+  } else if (plan->fixed_multi) {
+    c = decode_pages;
   } else if (p.num_splits > 0) {
     c = ceil_div(max_np, p.num_splits);
   } else if (decode_pages > 0) {
@@ -576,6 +580,25 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     mq_pages = multi_decode_split_pages(npages, p->num_kv_heads, num_cus, p->head_dim, P, weak_decode);
     if (!weak_decode && mq_pages >= max_np) mq_pages = 0;
     mq_decode = mq_pages > 0;
+  }
+  // The fixed-order mode where the decode kernels are weak (group width 8,
+  // or 3-4 query heads without the matrix-core decode kernel) runs on the
+  // multi-token kernel too: its splits of `fixed_chunk` tokens from each
+  // sequence's first attended page are the mode's chunks, one per
+  // work-group, each state computed from its own keys alone; num_splits
+  // does not enter the plan, so the output is the same bits for every
+  // value. Rows of one chunk are written by the split pass; the combine
+  // merges the others in chunk order. 1024-token chunks, us per step,
+  // decode kernels -> this: 64 query heads over 8 KV heads, the long batch
+  // 608 -> 539, at head_dim 64 over 32 x 1-8k tokens 156 -> 64; 32 over 8 at
+  // head_dim 256, 32 x 1-8k 246 -> 229.
+  bool mq_fixed = fixed && T == 1 && weak_decode && gt >= 4 && multi_dtypes && p->kernel == DA_KERNEL_AUTO;
+  for (int32_t b = 0; mq_fixed && b < p->batch; ++b) mq_fixed = lens[b] >= 1;
+  if (mq_fixed) mq_fixed = ceil_div(max_np, p->fixed_chunk / P) <= 65535;  // the grid's y extent
+  if (mq_fixed) {
+    plan->fixed_multi = true;
+    mq_decode = true;
+    mq_pages = p->fixed_chunk / P;
   }
   if ((plan->query_len > 1 && !per_token) || mq_decode) {
     const da_status st = finish_multi_plan(plan, lens, mq_pages);

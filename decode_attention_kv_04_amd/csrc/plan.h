@@ -23,6 +23,7 @@ struct da_plan {
   int32_t rows_per_group = 0;  // multi-token kernel: (token, head) rows per work-group
   bool per_token = false;      // T > 1 on the single-query kernels, one launch per token
   bool balanced = false;       // balanced schedule: split_groups work-groups of pages_per_split units each
+  bool fixed_multi = false;    // fixed-order mode on the multi-token kernel: one chunk (split) per work-group
   int32_t bal_overhead = 0;    // balanced schedule: units a stream weighs before its pages
   std::vector<int32_t> splits; // S_b per sequence
   int64_t active_units = 0;

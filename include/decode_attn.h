@@ -119,7 +119,12 @@ typedef struct {
                                 agree bit for bit because the partials are merged
                                 in one fixed order). num_splits then counts
                                 work-groups per sequence and KV head, each taking
-                                consecutive chunks.                              */
+                                consecutive chunks; on the multi-token kernel
+                                (DA_KERNEL_AUTO with G 5-8, or 3-4 where the
+                                decode matrix-core kernel is not built, every
+                                length at least 1, q and K/V sharing f16 or
+                                bf16) every chunk has its own work-group and
+                                num_splits does not apply.                       */
   int32_t query_len;         /* T, new tokens per sequence; 0 or 1 = one query
                                 token (decode). T > 1 (llm-web pull 8, commit on
                                 the batched suffix prefill: several new tokens
@@ -182,15 +187,17 @@ typedef struct {
                                 length is at least 1, and G is 5 to 8, or 3 to
                                 4 where 1 is not built or (num_splits 0, and
                                 the plan splits) B * H_kv is below num_cus;
-                                outside the fixed-order mode; and
-                                (num_splits 0) only if no work-group of that
-                                plan holds more than about 1/170 of the
+                                and (num_splits 0) only if no work-group of
+                                that plan holds more than about 1/170 of the
                                 batch's attended page-heads (else the decode
-                                kernels and their balanced schedule run). A
-                                query_len > 1 plan with 0 runs the vector
-                                kernel once per token.                        */
+                                kernels and their balanced schedule run). In
+                                the fixed-order mode they take 2 for G 5 to 8,
+                                or 3 to 4 where 1 is not built. A query_len > 1
+                                plan with 0 runs the vector kernel once per
+                                token.                                        */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each
-                                work-group computes (0 in the default mode). In
+                                work-group computes (1 on the multi-token
+                                kernel; 0 in the default mode). In
                                 that mode pages_per_split is the chunk length in
                                 pages and max_splits the most chunks of a sequence. */
   int32_t balanced;          /* 1 = balanced schedule (the matrix-core decode

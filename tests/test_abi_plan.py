@@ -198,7 +198,7 @@ def test_split_kernel_by_group(lib, G):
     for kw in (dict(num_splits=1), dict(num_splits=7)):
         assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == want
     for kw in (dict(fixed_chunk=1024), dict(fixed_chunk=1024, num_splits=3)):
-        assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == min(want, 1)
+        assert plan(params(batch=32, num_q_heads=8 * G, **kw), [32768] * 32).info.split_kernel == want
     assert plan(params(batch=32, num_q_heads=8 * G, kernel="matrix"), [32768] * 32).info.split_kernel == 1
 
 
@@ -245,7 +245,30 @@ def test_fixed_order_heuristic_one_chunk_per_work_group(lib, monkeypatch):
     # shorter chunks are grouped up to the minimum split length: 128 tokens on
     # the matrix-core kernel, 256 on the vector kernel
     assert plan(params(batch=32, fixed_chunk=32), lens).info.chunks_per_work_group == 4
-    assert plan(params(batch=32, head_dim=64, fixed_chunk=32), lens).info.chunks_per_work_group == 8
+    assert plan(params(batch=32, num_q_heads=16, head_dim=64, fixed_chunk=32), lens).info.chunks_per_work_group == 8
+
+
+# The fixed-order mode where the decode kernels are weak (group width 8, or 3-4
+# query heads at head_dim 64 / 256 or pages off the 16-token grid) runs on
+# the multi-token kernel: one chunk (split) per work-group, the same plan for
+# every num_splits; rows of one chunk need no combine.
+@pytest.mark.parametrize("kw", [dict(num_q_heads=64), dict(head_dim=64), dict(head_dim=256, num_q_heads=24),
+                                dict(page_size=8, max_pages_per_seq=4096)])
+def test_fixed_order_on_the_multi_token_kernel(lib, kw):
+    lens = [3060, 100, 9000, 1]
+    P = kw.get("page_size", 16)
+    plans = [plan(params(batch=4, fixed_chunk=256, num_splits=ns, **kw), lens) for ns in (0, 1, 3, 10_000)]
+    for pl in plans:
+        assert pl.info.split_kernel == 2 and pl.info.chunks_per_work_group == 1
+        assert pl.pages_per_split == 256 // P
+        assert pl.max_splits == math.ceil(math.ceil(9000 / P) / (256 // P))
+        assert [pl.splits(b) for b in range(4)] == [max(1, math.ceil(math.ceil(L / P) / (256 // P))) for L in lens]
+        assert (pl.info.split_work_groups, pl.workspace_bytes) == \
+            (plans[0].info.split_work_groups, plans[0].workspace_bytes)
+    # an empty context, a forced kernel, or G 4 at head_dim 128: the decode kernels' fixed-order mode
+    assert plan(params(batch=5, fixed_chunk=256, **kw), lens + [0]).info.split_kernel in (0, 1)
+    assert plan(params(batch=4, fixed_chunk=256, kernel="vector", **kw), lens).info.split_kernel == 0
+    assert plan(params(batch=4, fixed_chunk=256), lens).info.split_kernel == 1
 
 
 @pytest.mark.parametrize("chunk", [-16, 8, 24, 100])
@@ -411,16 +434,16 @@ def test_query_len_zero_and_one_are_decode(lib):
 # and K/V, and with 3 or 4 where the matrix-core decode kernel is not built
 # (head_dim 64 or 256, pages not a multiple of 16) or the batch has fewer
 # (sequence, KV head) streams than compute units (as here: 3 x 8); not with an
-# empty context (the kernel needs the new token's own key), a forced kernel or
-# the fixed-order mode.
+# empty context (the kernel needs the new token's own key) or a forced kernel.
+# The fixed-order mode takes it where the decode kernels are weak.
 @pytest.mark.parametrize("G,kw,want", [
     (5, {}, 2), (6, {}, 2), (8, {}, 2), (8, dict(q_dtype="bf16", kv_dtype="bf16", out_dtype="f32"), 2),
     (8, dict(head_dim=64), 2), (8, dict(head_dim=256), 2), (7, dict(page_size=24, max_pages_per_seq=4096), 2),
     (3, dict(head_dim=64), 2), (4, dict(head_dim=256), 2), (4, dict(page_size=8, max_pages_per_seq=4096), 2),
     (3, {}, 2), (4, {}, 2), (2, dict(head_dim=64), 0), (2, dict(head_dim=256), 0), (1, dict(head_dim=256), 0),
     (8, dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), 0), (8, dict(q_dtype="f32"), 0),
-    (8, dict(kernel="vector"), 0), (8, dict(kernel="matrix"), 1), (8, dict(fixed_chunk=256), 1),
-    (4, dict(head_dim=64, fixed_chunk=256), 0),
+    (8, dict(kernel="vector"), 0), (8, dict(kernel="matrix"), 1), (8, dict(fixed_chunk=256), 2),
+    (4, dict(head_dim=64, fixed_chunk=256), 2), (4, dict(fixed_chunk=256), 1),
 ])
 def test_decode_on_the_multi_token_kernel(lib, G, kw, want):
     lens = [3060, 1, 700]
@@ -429,7 +452,7 @@ def test_decode_on_the_multi_token_kernel(lib, G, kw, want):
     D = kw.get("head_dim", 128)
     pl = plan(params(batch=3, num_q_heads=8 * G, **kw), lens)
     assert pl.info.split_kernel == want
-    if want != 2:
+    if want != 2 or "fixed_chunk" in kw:
         return
     S = pl.max_splits
     assert pl.info.split_work_groups == 8 * S * 3                 # one row block per KV head

@@ -38,6 +38,35 @@ def test_named_workloads_bitwise_across_splits(gpu, name, chunk, kernel):
     check(out, oracle_for(w), spec.kv_dtype, spec.out_dtype, f"{name} fixed {chunk}")
 
 
+# Where the decode kernels are weak (group width 8, or 3-4 query heads at
+# head_dim 64 / 256 or 8-token pages) the mode runs on the multi-token kernel:
+# one chunk per work-group, rows of one chunk written by the split pass.
+MULTI_FIXED = [
+    # B, H_q, H_kv, D, dtype, out, P, lengths, window, chunk
+    (4, 64, 8, 128, "f16", "f16", 16, (3060, 100, 9000, 1), 0, 256),
+    (3, 32, 8, 64, "bf16", "f32", 16, (5000, 17, 2049), 0, 1024),
+    (3, 48, 8, 256, "f16", "f32", 16, (40, 3000, 700), 500, 128),
+    (2, 16, 4, 128, "f16", "f32", 8, (6000, 333), 0, 64),
+    (2, 64, 8, 128, "bf16", "bf16", 32, (70000, 12), 4096, 2048),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MULTI_FIXED)))
+def test_multi_token_kernel_bitwise_across_splits(gpu, i):
+    B, HQ, HKV, D, dt, out, P, lens, W, chunk = MULTI_FIXED[i]
+    spec = wl.WorkloadSpec(f"mqfixed{i}", B, HQ, HKV, D, dt, dt, out, P, ("list", lens), seed=7800 + i, window=W,
+                           spike_frac=0.01)
+    say(f"[fixed-order, multi-token kernel {i}] B={B} H={HQ}/{HKV} D={D} {dt} P={P} lens={lens} W={W} chunk={chunk}")
+    w = wl.make_workload(spec, gpu)
+    _, plan = run_lib(w, fixed_chunk=chunk, twin=False)
+    assert plan.info.split_kernel == 2 and plan.info.chunks_per_work_group == 1
+    got = all_split_counts_agree(w, chunk)
+    check(got, oracle_for(w), dt, out, f"multi fixed {i}")
+    # two-phase (split, then combine) equals run
+    b, _ = run_lib(w, fixed_chunk=chunk, two_phase=True)
+    assert torch.equal(b, got)
+
+
 def test_mixed_window_full_size_bitwise_across_splits(gpu, mixed_window):
     w, ref = mixed_window
     say(f"[fixed-order] {w.spec.name} full size")
