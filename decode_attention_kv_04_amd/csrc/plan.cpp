@@ -569,11 +569,16 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // four waves on the decode kernel (1 x 100 tokens 5.9 against 8.4 us, 8 x
   // 256 7.3 against 10.2; at 8 heads or head_dim 64 and 256 the two are even
   // or this is faster: 64 heads over 8, 64 x 200 tokens 20.7 -> 11.7).
+  // Where the decode kernels are weak: group width 8, 3-4 query heads
+  // without the matrix-core decode kernel, and 2 at head_dim 64 (16/8 heads,
+  // 32 x 1-8k tokens: 43.4 -> 34.1 us; at head_dim 256 and with 8-token
+  // pages it was even on batches and lost on the 4 x 1-4k wide-head batch,
+  // 15.5 -> 16.3).
   const bool few_streams = static_cast<int64_t>(p->batch) * p->num_kv_heads < num_cus;
-  const bool weak_decode = gt == 8 || !matrix_kernel_supported(*p);
-  bool mq_decode = T == 1 &&
-                   (gt == 8 || (gt == 4 && (weak_decode || (few_streams && p->num_splits == 0)))) &&
-                   multi_dtypes && p->kernel == DA_KERNEL_AUTO && !fixed;
+  const bool weak_decode =
+      gt == 8 || (gt == 4 && !matrix_kernel_supported(*p)) || (gt == 2 && p->head_dim == 64);
+  bool mq_decode = T == 1 && (weak_decode || (gt == 4 && few_streams && p->num_splits == 0)) && multi_dtypes &&
+                   p->kernel == DA_KERNEL_AUTO && !fixed;
   for (int32_t b = 0; mq_decode && b < p->batch; ++b) mq_decode = lens[b] >= 1;
   int64_t mq_pages = 0;
   if (mq_decode && p->num_splits == 0) {
@@ -581,10 +586,9 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     if (!weak_decode && mq_pages >= max_np) mq_pages = 0;
     mq_decode = mq_pages > 0;
   }
-  // The fixed-order mode where the decode kernels are weak (group width 8,
-  // or 3-4 query heads without the matrix-core decode kernel) runs on the
-  // multi-token kernel too: its splits of `fixed_chunk` tokens from each
-  // sequence's first attended page are the mode's chunks, one per
+  // The fixed-order mode where the decode kernels are weak (see above) runs
+  // on the multi-token kernel too: its splits of `fixed_chunk` tokens from
+  // each sequence's first attended page are the mode's chunks, one per
   // work-group, each state computed from its own keys alone; num_splits
   // does not enter the plan, so the output is the same bits for every
   // value. Rows of one chunk are written by the split pass; the combine
@@ -592,7 +596,7 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // decode kernels -> this: 64 query heads over 8 KV heads, the long batch
   // 608 -> 539, at head_dim 64 over 32 x 1-8k tokens 156 -> 64; 32 over 8 at
   // head_dim 256, 32 x 1-8k 246 -> 229.
-  bool mq_fixed = fixed && T == 1 && weak_decode && gt >= 4 && multi_dtypes && p->kernel == DA_KERNEL_AUTO;
+  bool mq_fixed = fixed && T == 1 && weak_decode && multi_dtypes && p->kernel == DA_KERNEL_AUTO;
   for (int32_t b = 0; mq_fixed && b < p->batch; ++b) mq_fixed = lens[b] >= 1;
   if (mq_fixed) mq_fixed = ceil_div(max_np, p->fixed_chunk / P) <= 65535;  // the grid's y extent
   if (mq_fixed) {

@@ -86,11 +86,11 @@ typedef enum { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
 /* Which single-query split kernel a plan uses (da_params.kernel). */
 typedef enum {
   DA_KERNEL_AUTO = 0,   /* the planner chooses (matrix cores from 2 query heads per KV head on;
-                           a decode step with 5-8 of them, or 3-4 where the
+                           a decode step with 5-8 of them, 3-4 where the
                            decode matrix-core kernel is not built or the batch
                            has fewer (sequence, KV head) streams than compute
-                           units, on the multi-token kernel as one token when
-                           its plan is balanced)                               */
+                           units, or 2 at head_dim 64, on the multi-token
+                           kernel as one token when its plan is balanced)      */
   DA_KERNEL_VECTOR = 1, /* vector q.K; with query_len > 1: the single-query kernels per token   */
   DA_KERNEL_MATRIX = 2  /* q.K on the matrix cores; DA_ERR_UNSUPPORTED where not built           */
 } da_kernel;
@@ -120,8 +120,9 @@ typedef struct {
                                 in one fixed order). num_splits then counts
                                 work-groups per sequence and KV head, each taking
                                 consecutive chunks; on the multi-token kernel
-                                (DA_KERNEL_AUTO with G 5-8, or 3-4 where the
-                                decode matrix-core kernel is not built, every
+                                (DA_KERNEL_AUTO with G 5-8, 2 at head_dim 64,
+                                or 3-4 where the decode matrix-core kernel is
+                                not built, every
                                 length at least 1, q and K/V sharing f16 or
                                 bf16) every chunk has its own work-group and
                                 num_splits does not apply.                       */
@@ -184,15 +185,17 @@ typedef struct {
                                 da_params.rows_per_block forces one. Decode
                                 plans (query_len <= 1) with DA_KERNEL_AUTO
                                 take 2 when q and K/V share f16 or bf16, every
-                                length is at least 1, and G is 5 to 8, or 3 to
-                                4 where 1 is not built or (num_splits 0, and
-                                the plan splits) B * H_kv is below num_cus;
+                                length is at least 1, and G is 5 to 8, 2 at
+                                head_dim 64, or 3 to 4 where 1 is not built or
+                                (num_splits 0, and the plan splits) B * H_kv is
+                                below num_cus;
                                 and (num_splits 0) only if no work-group of
                                 that plan holds more than about 1/170 of the
                                 batch's attended page-heads (else the decode
                                 kernels and their balanced schedule run). In
                                 the fixed-order mode they take 2 for G 5 to 8,
-                                or 3 to 4 where 1 is not built. A query_len > 1
+                                2 at head_dim 64, or 3 to 4 where 1 is not
+                                built. A query_len > 1
                                 plan with 0 runs the vector kernel once per
                                 token.                                        */
   int32_t chunks_per_work_group; /* fixed-order mode: consecutive chunks each

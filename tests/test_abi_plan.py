@@ -122,7 +122,7 @@ def test_matrix_kernel_splits_down_to_128_tokens(lib, monkeypatch):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
     pl = plan(params(kernel="matrix"), [3060])
     assert pl.info.split_kernel == 1 and pl.pages_per_split == 8 and pl.max_splits == 24
-    pl = plan(params(num_q_heads=16, head_dim=64), [3060])              # G 2: the vector kernel
+    pl = plan(params(num_q_heads=16, head_dim=256), [3060])             # G 2: the vector kernel
     assert pl.info.split_kernel == 0 and pl.pages_per_split == 16
     # contexts of at most 256 tokens are not split (the switch-over), one more token is
     assert plan(params(batch=3, kernel="matrix"), [256, 100, 1]).max_splits == 1
@@ -164,7 +164,8 @@ def test_split_kernel_selection(lib):
     for kw in (dict(head_dim=64), dict(head_dim=256), dict(page_size=8, max_pages_per_seq=4096),
                dict(page_size=24, max_pages_per_seq=4096)):
         assert plan(params(batch=NB, **kw), L).info.split_kernel == 2
-        assert plan(params(batch=NB, num_q_heads=16, **kw), L).info.split_kernel == 0
+        # G 2: the multi-token kernel at head_dim 64 only
+        assert plan(params(batch=NB, num_q_heads=16, **kw), L).info.split_kernel == (2 if kw.get("head_dim") == 64 else 0)
     assert plan(params(batch=NB, kernel="vector"), L).info.split_kernel == 0
     assert plan(params(batch=NB, kernel="matrix"), L).info.split_kernel == 1
     assert plan(params(batch=NB, kernel="auto"), L).info.split_kernel == 1
@@ -245,7 +246,7 @@ def test_fixed_order_heuristic_one_chunk_per_work_group(lib, monkeypatch):
     # shorter chunks are grouped up to the minimum split length: 128 tokens on
     # the matrix-core kernel, 256 on the vector kernel
     assert plan(params(batch=32, fixed_chunk=32), lens).info.chunks_per_work_group == 4
-    assert plan(params(batch=32, num_q_heads=16, head_dim=64, fixed_chunk=32), lens).info.chunks_per_work_group == 8
+    assert plan(params(batch=32, num_q_heads=16, head_dim=256, fixed_chunk=32), lens).info.chunks_per_work_group == 8
 
 
 # The fixed-order mode where the decode kernels are weak (group width 8, or 3-4
@@ -431,8 +432,9 @@ def test_query_len_zero_and_one_are_decode(lib):
 
 # A decode step (one new token) runs on the multi-token kernel, as one
 # 16-row block per KV head, with 5 to 8 query heads per KV head on 16-bit q
-# and K/V, and with 3 or 4 where the matrix-core decode kernel is not built
-# (head_dim 64 or 256, pages not a multiple of 16) or the batch has fewer
+# and K/V, with 2 at head_dim 64, and with 3 or 4 where the matrix-core
+# decode kernel is not built (head_dim 64 or 256, pages not a multiple of 16)
+# or the batch has fewer
 # (sequence, KV head) streams than compute units (as here: 3 x 8); not with an
 # empty context (the kernel needs the new token's own key) or a forced kernel.
 # The fixed-order mode takes it where the decode kernels are weak.
@@ -440,7 +442,8 @@ def test_query_len_zero_and_one_are_decode(lib):
     (5, {}, 2), (6, {}, 2), (8, {}, 2), (8, dict(q_dtype="bf16", kv_dtype="bf16", out_dtype="f32"), 2),
     (8, dict(head_dim=64), 2), (8, dict(head_dim=256), 2), (7, dict(page_size=24, max_pages_per_seq=4096), 2),
     (3, dict(head_dim=64), 2), (4, dict(head_dim=256), 2), (4, dict(page_size=8, max_pages_per_seq=4096), 2),
-    (3, {}, 2), (4, {}, 2), (2, dict(head_dim=64), 0), (2, dict(head_dim=256), 0), (1, dict(head_dim=256), 0),
+    (3, {}, 2), (4, {}, 2), (2, dict(head_dim=64), 2), (2, dict(head_dim=256), 0), (1, dict(head_dim=256), 0),
+    (2, dict(page_size=8, max_pages_per_seq=4096), 0), (1, dict(head_dim=64), 0), (2, dict(head_dim=64, fixed_chunk=256), 2),
     (8, dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), 0), (8, dict(q_dtype="f32"), 0),
     (8, dict(kernel="vector"), 0), (8, dict(kernel="matrix"), 1), (8, dict(fixed_chunk=256), 2),
     (4, dict(head_dim=64, fixed_chunk=256), 2), (4, dict(fixed_chunk=256), 1),
@@ -755,7 +758,7 @@ def test_balanced_plan_is_not_taken(lib, monkeypatch):
     assert plan(params(batch=2, num_splits=7), lens).info.balanced == 0                 # forced split count
     assert plan(params(batch=2, fixed_chunk=256), lens).info.balanced == 0              # fixed-order mode
     assert plan(params(batch=2, kernel="vector"), lens).info.balanced == 0              # vector kernel
-    assert plan(params(batch=2, num_q_heads=16, head_dim=64), lens).info.balanced == 0  # vector kernel
+    assert plan(params(batch=2, num_q_heads=16, head_dim=256), lens).info.balanced == 0  # vector kernel
     assert plan(params(batch=2, head_dim=64), lens).info.balanced == 0                  # multi-token kernel
     assert plan(params(batch=2, num_q_heads=64), lens).info.balanced == 0               # multi-token kernel
     assert plan(params(batch=2, query_len=4, q_dtype="f32"), lens).info.balanced == 0   # per-token mode
@@ -772,7 +775,7 @@ def test_balanced_plan_is_not_taken(lib, monkeypatch):
 # Whole streams: at least one (sequence, KV head) stream per compute unit and
 # about equal lengths -> no split (one launch, no combine), on either kernel.
 @pytest.mark.parametrize("B,L,kw", [(32, 512, {}), (32, 4096, {}), (128, 512, {}), (64, 1024, {}),
-                                     (48, 3060, {}), (32, 2048, dict(num_q_heads=16, head_dim=64)),
+                                     (48, 3060, {}), (32, 2048, dict(num_q_heads=16, head_dim=256)),
                                      (32, 2048, dict(window=1000))])
 def test_whole_streams_are_not_split(lib, monkeypatch, B, L, kw):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)

@@ -1,6 +1,7 @@
 """Decode steps on the multi-token kernel: one new token per sequence, with 5
-to 8 query heads per KV head (and 3 or 4 at head_dim 64 and 256, pages not a
-multiple of 16, or fewer (sequence, KV head) streams than compute units) on
+to 8 query heads per KV head (3 or 4 at head_dim 64 and 256, pages not a
+multiple of 16, or fewer (sequence, KV head) streams than compute units; 2 at
+head_dim 64) on
 16-bit q and K/V, run as one 16-row block per KV head with both products on
 the matrix cores, merged by the decode combine. Against the oracle at several
 head dims, page sizes, windows and split counts, ragged, bimodal (one long
@@ -33,6 +34,7 @@ CASES = [
     (16, 32, 8, 64, "bf16", "f32", 32, (300,) * 15 + (30000,), 0),         # bimodal at head_dim 64
     (3, 32, 8, 128, "bf16", "f32", 16, (3060, 100, 2049), 0),              # G 4, head_dim 128, 24 streams
     (3, 24, 8, 128, "f16", "f16", 16, (4097, 1, 640), 2000),               # G 3, head_dim 128, window
+    (4, 16, 8, 64, "bf16", "f32", 16, (3000, 1, 257, 9000), 0),             # G 2, head_dim 64
 ]
 
 

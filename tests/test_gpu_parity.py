@@ -106,10 +106,12 @@ def test_group_dim_dtype_grid(gpu, G, D, kv):
         for ns in (0, 3):
             out, plan = run_lib(w, num_splits=ns, kernel=kernel)
             # automatic: the matrix-core kernel from two query heads per group on;
-            # the multi-token kernel (one token) from five on, or from three on
+            # the multi-token kernel (one token) from five on, from three on
             # where the matrix-core decode kernel is not built or (the
-            # planner's split choice) with fewer streams than compute units (6)
-            multi = kernel == "auto" and kv != "f32" and (G >= 5 or (G >= 3 and (not matrix_ok or ns == 0)))
+            # planner's split choice) with fewer streams than compute units (6),
+            # and with two at head_dim 64
+            multi = kernel == "auto" and kv != "f32" and (G >= 5 or (G >= 3 and (not matrix_ok or ns == 0))
+                                                          or (G == 2 and D == 64))
             want = 2 if multi else (1 if matrix_ok and (kernel == "matrix" or (kernel == "auto" and G >= 2)) else 0)
             assert plan.info.split_kernel == want
             check(out, ref, kv, "f32", f"G{G} D{D} {kv} splits={ns} kernel={kernel}")

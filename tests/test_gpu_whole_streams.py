@@ -17,7 +17,7 @@ CASES = [
     # B, H_q, H_kv, D, q/kv dtype, out, page, lengths, window, query_len
     (32, 32, 8, 128, "f16", "f16", 16, ("fixed", 2048), 0, 1),
     (32, 32, 8, 128, "bf16", "f32", 32, ("uniform", 1900, 2050), 1000, 1),
-    (64, 8, 4, 64, "f16", "f32", 16, ("fixed", 777), 0, 1),          # G 2, head_dim 64: vector kernel
+    (64, 8, 4, 256, "f16", "f32", 16, ("fixed", 777), 0, 1),         # G 2, head_dim 256: vector kernel
     (32, 8, 8, 128, "f16", "f16", 16, ("fixed", 1500), 0, 1),        # one head per group: vector kernel
     (32, 32, 8, 128, "f32", "f32", 16, ("fixed", 1024), 0, 1),       # fp32 K/V: vector kernel
     (256, 32, 8, 128, "f16", "f16", 16, ("uniform", 300, 320), 0, 1),
