@@ -569,14 +569,30 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // four waves on the decode kernel (1 x 100 tokens 5.9 against 8.4 us, 8 x
   // 256 7.3 against 10.2; at 8 heads or head_dim 64 and 256 the two are even
   // or this is faster: 64 heads over 8, 64 x 200 tokens 20.7 -> 11.7).
+  // Whole streams: with at least one (sequence, KV head) stream per compute
+  // unit and about equal attended lengths (the longest within 10 % of the
+  // mean), one unsplit work-group per stream already fills the chip evenly,
+  // and splitting only adds the combine launch and the piece starts.
+  // Measured on the Llama shape, µs per step, unsplit vs the split choice:
+  // 32 x 512 tokens 13.9 vs 20.5, 32 x 1024 24.7 vs 30.3, 32 x 2048 43.6 vs
+  // 50.1, 32 x 4096 82.4 vs 88.9, 64 x 1024 43.3 vs 45.3, 128 x 512 43.9 vs
+  // 47.1, 48 x 3060 103.3 vs 104.8; with unequal lengths it loses (the long
+  // batch 512.9 vs 483.7, 32 x 1-8k tokens 123.2 vs 117.2, the mixed-window
+  // batch 106.7 vs 96.6) and so does a batch of fewer streams than compute
+  // units (8 x 4096 tokens 47.4 vs 29.7).
+  const bool whole_streams = p->num_splits == 0 && max_np > 0 &&
+                             static_cast<int64_t>(p->batch) * p->num_kv_heads >= num_cus &&
+                             max_np * p->batch * 10 <= total_np * 11;
   // Where the decode kernels are weak: group width 8, 3-4 query heads
-  // without the matrix-core decode kernel, and 2 at head_dim 64 (16/8 heads,
-  // 32 x 1-8k tokens: 43.4 -> 34.1 us; at head_dim 256 and with 8-token
-  // pages it was even on batches and lost on the 4 x 1-4k wide-head batch,
-  // 15.5 -> 16.3).
+  // without the matrix-core decode kernel, and 2 at head_dim 64 unless the
+  // batch runs as whole streams (16/8 heads, 32 x 1-8k tokens: 43.4 -> 34.1
+  // us; whole streams of 64 x 2048 and 64 x 8192 tokens stay faster on the
+  // vector kernel, 23.2 against 25.1 and 82.3 against 83.7 us; at head_dim
+  // 256 and with 8-token pages G 2 was even on batches and lost on the 4 x
+  // 1-4k wide-head batch, 15.5 -> 16.3).
   const bool few_streams = static_cast<int64_t>(p->batch) * p->num_kv_heads < num_cus;
-  const bool weak_decode =
-      gt == 8 || (gt == 4 && !matrix_kernel_supported(*p)) || (gt == 2 && p->head_dim == 64);
+  const bool weak_decode = gt == 8 || (gt == 4 && !matrix_kernel_supported(*p)) ||
+                           (gt == 2 && p->head_dim == 64 && !whole_streams);
   bool mq_decode = T == 1 && (weak_decode || (gt == 4 && few_streams && p->num_splits == 0)) && multi_dtypes &&
                    p->kernel == DA_KERNEL_AUTO && !fixed;
   for (int32_t b = 0; mq_decode && b < p->batch; ++b) mq_decode = lens[b] >= 1;
@@ -615,20 +631,6 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     return st;
   }
 
-  // Whole streams: with at least one (sequence, KV head) stream per compute
-  // unit and about equal attended lengths (the longest within 10 % of the
-  // mean), one unsplit work-group per stream already fills the chip evenly,
-  // and splitting only adds the combine launch and the piece starts.
-  // Measured on the Llama shape, µs per step, unsplit vs the split choice:
-  // 32 x 512 tokens 13.9 vs 20.5, 32 x 1024 24.7 vs 30.3, 32 x 2048 43.6 vs
-  // 50.1, 32 x 4096 82.4 vs 88.9, 64 x 1024 43.3 vs 45.3, 128 x 512 43.9 vs
-  // 47.1, 48 x 3060 103.3 vs 104.8; with unequal lengths it loses (the long
-  // batch 512.9 vs 483.7, 32 x 1-8k tokens 123.2 vs 117.2, the mixed-window
-  // batch 106.7 vs 96.6) and so does a batch of fewer streams than compute
-  // units (8 x 4096 tokens 47.4 vs 29.7).
-  const bool whole_streams = p->num_splits == 0 && max_np > 0 &&
-                             static_cast<int64_t>(p->batch) * p->num_kv_heads >= num_cus &&
-                             max_np * p->batch * 10 <= total_np * 11;
   int64_t c;
   if (max_np == 0) {
     c = 1;

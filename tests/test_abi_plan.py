@@ -164,8 +164,12 @@ def test_split_kernel_selection(lib):
     for kw in (dict(head_dim=64), dict(head_dim=256), dict(page_size=8, max_pages_per_seq=4096),
                dict(page_size=24, max_pages_per_seq=4096)):
         assert plan(params(batch=NB, **kw), L).info.split_kernel == 2
-        # G 2: the multi-token kernel at head_dim 64 only
-        assert plan(params(batch=NB, num_q_heads=16, **kw), L).info.split_kernel == (2 if kw.get("head_dim") == 64 else 0)
+        # G 2: the vector kernel (this batch runs as whole streams; see below for head_dim 64)
+        assert plan(params(batch=NB, num_q_heads=16, **kw), L).info.split_kernel == 0
+    # G 2 at head_dim 64 takes the multi-token kernel unless the batch runs as whole streams
+    ragged = [1024 + 224 * b for b in range(32)]
+    assert plan(params(batch=NB, num_q_heads=16, head_dim=64), ragged).info.split_kernel == 2
+    assert plan(params(batch=NB, num_q_heads=16, head_dim=64), L).info.split_kernel == 0
     assert plan(params(batch=NB, kernel="vector"), L).info.split_kernel == 0
     assert plan(params(batch=NB, kernel="matrix"), L).info.split_kernel == 1
     assert plan(params(batch=NB, kernel="auto"), L).info.split_kernel == 1
