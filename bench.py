@@ -20,7 +20,8 @@ configs: the five named configurations (tiny, the Llama-3.1-8B shape at 3060
           the oracle's wall time on each, and each output checked against
           the oracle (the run exits 1 if any check fails).
 --sweep: only a context-length sweep on the Llama shape (L 256..65536,
-          batch 1 and 32).
+          batch 1 and 32), and the same shape at 3060 tokens with head_dim
+          64, 128 and 256.
 Also reported, each timed the same way: the fixed-order mode on the same
 batch (fixed_order), several new tokens per sequence on their own workloads
 (multi_token: a 4-token check over the long-context batch and a 128-token
@@ -626,6 +627,35 @@ def measure_sweep(binding, workloads, lib, dev, stream, rounds):
     return res
 
 
+def measure_head_dims(binding, workloads, lib, dev, stream, rounds):
+    """The Llama-3.1-8B decode shape at 3060 tokens with head_dim 64, 128 and
+    256 (32/8 heads, fp16, 16-token pages), batch 1 and 32: step and split
+    µs over alternating repeats, GB/s, and the split kernel the plan picks."""
+    import torch
+    res = []
+    for B in SWEEP_BATCHES:
+        runners = {}
+        for D in (64, 128, 256):
+            spec = workloads.LLAMA8B_3060.replace(name=f"llama8b_b{B}_l3060_d{D}_f16", batch=B, head_dim=D,
+                                                  seed=300 + D + B)
+            runners[D] = Runner(binding, lib, workloads.make_workload(spec, dev), dev, stream)
+        torch.cuda.synchronize()
+        times = time_alternating(runners, rounds, stream)
+        for D, r in runners.items():
+            kvb = r.w.kv_bytes()
+            run_q, split_q = quantiles(times[D]["run"]), quantiles(times[D]["split"])
+            gbs = kvb / (run_q["median"] * 1e-6) / 1e9
+            res.append({"batch": B, "context": 3060, "head_dim": D, "us": run_q, "split_us": split_q,
+                        "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBPS, 4),
+                        "max_splits": r.plan.max_splits, "split_kernel": int(r.plan.info.split_kernel),
+                        "algorithmic_bytes": kvb})
+            print(f"[bench] head_dim {D} B {B} L 3060: {run_q['median']:.1f} us, {gbs:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+        del runners
+        torch.cuda.empty_cache()
+    return res
+
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -643,7 +673,8 @@ def main():
     ap.add_argument("--layer-step-only", action="store_true",
                     help="only the 32-layer decode step of the Llama-3.1-8B shape at 3060 tokens (for traces)")
     ap.add_argument("--sweep", action="store_true",
-                    help="only the context-length sweep (Llama shape, L 256..65536, batch 1 and 32)")
+                    help="only the context-length sweep (Llama shape, L 256..65536, batch 1 and 32) and "
+                    "the head_dim sweep at 3060 tokens")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy a buffer of known size once (counter calibration)")
     args = ap.parse_args()
@@ -674,7 +705,8 @@ def main():
 
     if args.sweep:
         sweep = measure_sweep(binding, workloads, lib, dev, stream, args.rounds)
-        print(json.dumps({"metric": METRIC, "sweep": sweep, "unit": "GB/s", "n_gpus": 1,
+        head_dims = measure_head_dims(binding, workloads, lib, dev, stream, args.rounds)
+        print(json.dumps({"metric": METRIC, "sweep": sweep, "head_dims": head_dims, "unit": "GB/s", "n_gpus": 1,
                           "data": "synthetic", "kernel_source_sha256_16": kernel_hash()}), flush=True)
         return
 
