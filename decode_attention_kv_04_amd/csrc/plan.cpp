@@ -43,11 +43,16 @@ int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
 // 32..128 rows). Blocks of 16 rows or fewer (a few drafted tokens) take 16
 // rows at every head_dim: wave 0 computes them and the other waves only copy
 // (64-row blocks would compute the empty rows on zero q). At head_dim 256
-// blocks are 64 rows, or 16 for 16 rows or fewer. da_params.rows_per_block
-// (validated by make_plan) forces a size.
-int64_t mq_rows(int64_t rows, int32_t head_dim, int32_t forced) {
+// blocks are 64 rows, or 16 for 16 rows or fewer. A decode step (one token)
+// with 17 to 64 rows (32 or 48 query heads per KV head) takes 64-row blocks:
+// at head_dim 128 they ran 8-12 % faster than 128-row blocks (32 x 1-8k
+// tokens at 48 over one KV head 24.4 -> 21.4 us, 32 over 2 heads 38.6 ->
+// 34.1) and twice as fast as 16-row blocks re-reading the keys for each.
+// da_params.rows_per_block (validated by make_plan) forces a size.
+int64_t mq_rows(int64_t rows, int32_t head_dim, int32_t forced, bool decode) {
   if (forced > 0) return forced;
   if (rows <= 16) return 16;
+  if (decode && rows <= 64) return 64;
   return head_dim <= 128 ? 128 : 64;
 }
 // A split never holds fewer attended tokens than this (the pages' 256-token
@@ -161,9 +166,10 @@ int64_t balance_limit(const std::vector<int64_t>& npages, int64_t H, int64_t cmi
 // work-groups, ceil(pages / c) per stream, fit the round (the 65536-token
 // context among 15 short ones: 67 us against 85 on the decode kernel; on
 // batches of 1-8k tokens it ran 4-7 % slower than the count per stream, so
-// it is only the second choice).
+// it is only the second choice). Without `decode_kernels` (a group width
+// they are not built for) an unbalanced plan takes the limit itself.
 int64_t multi_decode_split_pages(const std::vector<int64_t>& npages, int64_t num_kv_heads, int64_t num_cus,
-                                 int32_t head_dim, int64_t P, bool fit) {
+                                 int32_t head_dim, int64_t P, bool fit, bool decode_kernels = true) {
   int64_t max_np = 0;
   for (int64_t n : npages) max_np = std::max(max_np, n);
   if (max_np == 0) return 1;
@@ -176,7 +182,10 @@ int64_t multi_decode_split_pages(const std::vector<int64_t>& npages, int64_t num
   if (c <= limit) return c;
   if (!fit) return 0;
   const int64_t f = fit_split_pages(npages, num_kv_heads, slots, cmin, max_np);
-  return f <= limit ? f : 0;
+  if (f <= limit) return f;
+  // No decode kernel for this group width: the limit itself, as for several
+  // tokens (more than one round of work-groups).
+  return decode_kernels ? 0 : limit;
 }
 
 }  // namespace
@@ -361,7 +370,7 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_p
   const int64_t G = plan->group;
   const int64_t R = T * G;
   // Four waves of 16 rows (or two groups of 16) share each key tile.
-  const int64_t QB = mq_rows(R, p.head_dim, T == 1 ? 0 : p.rows_per_block);
+  const int64_t QB = mq_rows(R, p.head_dim, p.rows_per_block, T == 1);
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);
@@ -462,8 +471,9 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     return DA_ERR_INVALID;
 
   const int32_t G = p->num_q_heads / p->num_kv_heads;
+  // Group width compiled in the decode kernels; 0 for G > 8, which only the
+  // multi-token kernel serves (checked below).
   const int32_t gt = group_tile_for(G);
-  if (gt == 0) return DA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return DA_ERR_UNSUPPORTED;
   if (p->page_size % 8 != 0 || p->page_size > 1024) return DA_ERR_UNSUPPORTED;
   if (p->batch > 65535 || p->num_kv_heads > 65535) return DA_ERR_UNSUPPORTED;
@@ -485,8 +495,12 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   const bool multi_dtypes = p->q_dtype == p->kv_dtype && (p->kv_dtype == DA_F16 || p->kv_dtype == DA_BF16);
   const bool per_token = T > 1 && (!multi_dtypes || p->kernel == DA_KERNEL_VECTOR);
   if (T > 1 && p->kernel == DA_KERNEL_MATRIX && !multi_dtypes) return DA_ERR_UNSUPPORTED;
+  // More than 8 query heads per KV head (e.g. 128 over 8): the multi-token
+  // kernel only, so 16-bit q and K/V of one type, and no decode kernel forced.
+  if (gt == 0 && (!multi_dtypes || per_token || (T <= 1 && p->kernel != DA_KERNEL_AUTO)))
+    return DA_ERR_UNSUPPORTED;
   if (T <= 1 && p->kernel == DA_KERNEL_MATRIX && !matrix_kernel_supported(*p)) return DA_ERR_UNSUPPORTED;
-  if (T > 1 && !per_token && p->rows_per_block == 128 && p->head_dim > 128) return DA_ERR_UNSUPPORTED;
+  if (!per_token && p->rows_per_block == 128 && p->head_dim > 128) return DA_ERR_UNSUPPORTED;
   if (T > 1) {
     if (fixed) return DA_ERR_UNSUPPORTED;
     // T is the combine grid's y extent; T * G rows are counted in int32.
@@ -561,8 +575,9 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // wins at 3 or 4 heads per KV head (the long batch 482 against 490, the
   // mixed-window batch 95 against 99, 32 x 2048 42.5 against 45.0). With 2
   // heads per KV head (2 of 16 rows used) it lost: 4 x 1-4k tokens at
-  // head_dim 256 14.5 -> 16.3. An empty context stays on the decode kernels
-  // (the multi-token kernel needs the new token's own key).
+  // head_dim 256 14.5 -> 16.3. An empty context there has no tiles and its
+  // row is written as zeros, as on the decode kernels. More than 8 heads per
+  // KV head have no decode kernel and always take this one.
   // At 3 or 4 heads on head_dim 128 (the matrix-core decode kernel built)
   // only the planner's own split choice, and only a plan that splits: an
   // unsplit stream's tiles run through one computing wave there, against
@@ -591,14 +606,13 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // 256 and with 8-token pages G 2 was even on batches and lost on the 4 x
   // 1-4k wide-head batch, 15.5 -> 16.3).
   const bool few_streams = static_cast<int64_t>(p->batch) * p->num_kv_heads < num_cus;
-  const bool weak_decode = gt == 8 || (gt == 4 && !matrix_kernel_supported(*p)) ||
+  const bool weak_decode = gt == 0 || gt == 8 || (gt == 4 && !matrix_kernel_supported(*p)) ||
                            (gt == 2 && p->head_dim == 64 && !whole_streams);
   bool mq_decode = T == 1 && (weak_decode || (gt == 4 && few_streams && p->num_splits == 0)) && multi_dtypes &&
                    p->kernel == DA_KERNEL_AUTO && !fixed;
-  for (int32_t b = 0; mq_decode && b < p->batch; ++b) mq_decode = lens[b] >= 1;
   int64_t mq_pages = 0;
   if (mq_decode && p->num_splits == 0) {
-    mq_pages = multi_decode_split_pages(npages, p->num_kv_heads, num_cus, p->head_dim, P, weak_decode);
+    mq_pages = multi_decode_split_pages(npages, p->num_kv_heads, num_cus, p->head_dim, P, weak_decode, gt != 0);
     if (!weak_decode && mq_pages >= max_np) mq_pages = 0;
     mq_decode = mq_pages > 0;
   }
@@ -613,8 +627,11 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // 608 -> 539, at head_dim 64 over 32 x 1-8k tokens 156 -> 64; 32 over 8 at
   // head_dim 256, 32 x 1-8k 246 -> 229.
   bool mq_fixed = fixed && T == 1 && weak_decode && multi_dtypes && p->kernel == DA_KERNEL_AUTO;
-  for (int32_t b = 0; mq_fixed && b < p->batch; ++b) mq_fixed = lens[b] >= 1;
   if (mq_fixed) mq_fixed = ceil_div(max_np, p->fixed_chunk / P) <= 65535;  // the grid's y extent
+  if (fixed && gt == 0 && !mq_fixed) {
+    delete plan;
+    return DA_ERR_UNSUPPORTED;
+  }
   if (mq_fixed) {
     plan->fixed_multi = true;
     mq_decode = true;

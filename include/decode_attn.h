@@ -98,7 +98,14 @@ typedef enum {
 typedef struct {
   int32_t batch;             /* B >= 0                                              */
   int32_t num_q_heads;       /* H_q >= 1                                            */
-  int32_t num_kv_heads;      /* H_kv >= 1, divides H_q; G = H_q / H_kv in 1..8       */
+  int32_t num_kv_heads;      /* H_kv >= 1, divides H_q; G = H_q / H_kv. G 1..8 on
+                                every kernel; G > 8 (e.g. 128 query heads over 8,
+                                or many over one KV head) only on the multi-token
+                                kernel: q and K/V sharing f16 or bf16, kernel
+                                DA_KERNEL_AUTO for decode (DA_KERNEL_VECTOR for
+                                query_len > 1 is the per-token path), and in the
+                                fixed-order mode at most 65535 chunks per
+                                sequence; else DA_ERR_UNSUPPORTED              */
   int32_t head_dim;          /* D in {64, 128, 256}                                 */
   int32_t page_size;         /* P: a multiple of 8, 8..1024                         */
   int32_t max_pages_per_seq; /* row stride of page_table; >= ceil(L_b / P)          */
@@ -120,11 +127,10 @@ typedef struct {
                                 in one fixed order). num_splits then counts
                                 work-groups per sequence and KV head, each taking
                                 consecutive chunks; on the multi-token kernel
-                                (DA_KERNEL_AUTO with G 5-8, 2 at head_dim 64,
-                                or 3-4 where the decode matrix-core kernel is
-                                not built, every
-                                length at least 1, q and K/V sharing f16 or
-                                bf16) every chunk has its own work-group and
+                                (DA_KERNEL_AUTO with G 5 or more, 2 at head_dim
+                                64, or 3-4 where the decode matrix-core kernel
+                                is not built; q and K/V sharing f16 or bf16)
+                                every chunk has its own work-group and
                                 num_splits does not apply.                       */
   int32_t query_len;         /* T, new tokens per sequence; 0 or 1 = one query
                                 token (decode). T > 1 (llm-web pull 8, commit on
@@ -153,12 +159,13 @@ typedef struct {
                                 choice is not built; other values
                                 DA_ERR_INVALID. Only DA_KERNEL_AUTO takes a
                                 decode step to the multi-token kernel.          */
-  int32_t rows_per_block;    /* query_len > 1 on the multi-token kernels: the
-                                (token, head) rows of a KV head per work-group.
-                                0 = the planner chooses; 16, 64, or 128 (128
-                                only at head_dim 64 and 128, else
-                                DA_ERR_UNSUPPORTED); other values are
-                                DA_ERR_INVALID. Ignored for query_len <= 1.     */
+  int32_t rows_per_block;    /* On the multi-token kernels (also a decode plan
+                                that takes them): the (token, head) rows of a
+                                KV head per work-group. 0 = the planner
+                                chooses; 16, 64, or 128 (128 only at head_dim
+                                64 and 128, else DA_ERR_UNSUPPORTED for every
+                                plan); other values are DA_ERR_INVALID. The
+                                decode kernels ignore it.                       */
 } da_params;
 
 typedef struct da_plan* da_plan_t;
@@ -181,19 +188,21 @@ typedef struct {
                                 cores): the T*G rows of a KV head in blocks of
                                 16 (16 rows or fewer: one wave computes, three
                                 copy), 128 (more rows at head_dim 64 and 128)
-                                or 64 (more rows at head_dim 256);
+                                or 64 (more rows at head_dim 256; and 17 to
+                                64 rows of a decode step);
                                 da_params.rows_per_block forces one. Decode
                                 plans (query_len <= 1) with DA_KERNEL_AUTO
-                                take 2 when q and K/V share f16 or bf16, every
-                                length is at least 1, and G is 5 to 8, 2 at
-                                head_dim 64, or 3 to 4 where 1 is not built or
-                                (num_splits 0, and the plan splits) B * H_kv is
-                                below num_cus;
+                                take 2 when q and K/V share f16 or bf16 and G
+                                is above 8 (always), 5 to 8, 2 at head_dim 64,
+                                or 3 to 4 where 1 is not built or (num_splits
+                                0, and the plan splits) B * H_kv is below
+                                num_cus;
                                 and (num_splits 0) only if no work-group of
                                 that plan holds more than about 1/170 of the
                                 batch's attended page-heads (else the decode
-                                kernels and their balanced schedule run). In
-                                the fixed-order mode they take 2 for G 5 to 8,
+                                kernels and their balanced schedule run; G
+                                above 8 then takes that limit). In the
+                                fixed-order mode they take 2 for G 5 or more,
                                 2 at head_dim 64, or 3 to 4 where 1 is not
                                 built. A query_len > 1
                                 plan with 0 runs the vector kernel once per

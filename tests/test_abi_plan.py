@@ -270,8 +270,9 @@ def test_fixed_order_on_the_multi_token_kernel(lib, kw):
         assert [pl.splits(b) for b in range(4)] == [max(1, math.ceil(math.ceil(L / P) / (256 // P))) for L in lens]
         assert (pl.info.split_work_groups, pl.workspace_bytes) == \
             (plans[0].info.split_work_groups, plans[0].workspace_bytes)
-    # an empty context, a forced kernel, or G 4 at head_dim 128: the decode kernels' fixed-order mode
-    assert plan(params(batch=5, fixed_chunk=256, **kw), lens + [0]).info.split_kernel in (0, 1)
+    # an empty context (no chunk: a zero row) stays on it; a forced kernel, or G 4 at head_dim 128:
+    # the decode kernels' fixed-order mode
+    assert plan(params(batch=5, fixed_chunk=256, **kw), lens + [0]).info.split_kernel == 2
     assert plan(params(batch=4, fixed_chunk=256, kernel="vector", **kw), lens).info.split_kernel == 0
     assert plan(params(batch=4, fixed_chunk=256), lens).info.split_kernel == 1
 
@@ -332,10 +333,14 @@ def test_multi_token_rows_per_block_rejects(lib):
         B.DA_ERR_UNSUPPORTED
     pl = plan(params(batch=1, query_len=40, head_dim=256, rows_per_block=16, num_splits=1), [5000])
     assert pl.info.split_work_groups == 8 * 10
-    # ignored by decode plans (one token: 16-row blocks)
+    # decode plans on the multi-token kernel take it too (4 rows: one block of
+    # any size); the decode kernels ignore it, but 128 at head_dim 256 is
+    # rejected for every plan
     pl = plan(params(rows_per_block=64), [3060])
     assert pl.info.split_kernel == 2 and pl.info.split_work_groups == 8 * pl.max_splits
     assert plan(params(rows_per_block=64, kernel="matrix"), [3060]).info.split_kernel == 1
+    assert status_of(params(head_dim=256, rows_per_block=128), [3060]) == B.DA_ERR_UNSUPPORTED
+    assert status_of(params(head_dim=256, rows_per_block=128, kernel="vector"), [3060]) == B.DA_ERR_UNSUPPORTED
 
 
 # A few drafted tokens over long contexts: the keys of each (sequence, KV
@@ -439,9 +444,10 @@ def test_query_len_zero_and_one_are_decode(lib):
 # and K/V, with 2 at head_dim 64, and with 3 or 4 where the matrix-core
 # decode kernel is not built (head_dim 64 or 256, pages not a multiple of 16)
 # or the batch has fewer
-# (sequence, KV head) streams than compute units (as here: 3 x 8); not with an
-# empty context (the kernel needs the new token's own key) or a forced kernel.
-# The fixed-order mode takes it where the decode kernels are weak.
+# (sequence, KV head) streams than compute units (as here: 3 x 8); not with
+# a forced kernel. More than 8 query heads per KV head always take it (one
+# block of 16, 64 or 128 rows per KV head). The fixed-order mode takes it
+# where the decode kernels are weak.
 @pytest.mark.parametrize("G,kw,want", [
     (5, {}, 2), (6, {}, 2), (8, {}, 2), (8, dict(q_dtype="bf16", kv_dtype="bf16", out_dtype="f32"), 2),
     (8, dict(head_dim=64), 2), (8, dict(head_dim=256), 2), (7, dict(page_size=24, max_pages_per_seq=4096), 2),
@@ -451,6 +457,9 @@ def test_query_len_zero_and_one_are_decode(lib):
     (8, dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), 0), (8, dict(q_dtype="f32"), 0),
     (8, dict(kernel="vector"), 0), (8, dict(kernel="matrix"), 1), (8, dict(fixed_chunk=256), 2),
     (4, dict(head_dim=64, fixed_chunk=256), 2), (4, dict(fixed_chunk=256), 1),
+    (12, {}, 2), (16, {}, 2), (16, dict(head_dim=64), 2), (16, dict(head_dim=256), 2), (32, {}, 2),
+    (32, dict(head_dim=256), 2), (16, dict(q_dtype="bf16", kv_dtype="bf16", out_dtype="f32"), 2),
+    (16, dict(page_size=8, max_pages_per_seq=4096), 2), (16, dict(fixed_chunk=256), 2),
 ])
 def test_decode_on_the_multi_token_kernel(lib, G, kw, want):
     lens = [3060, 1, 700]
@@ -469,13 +478,46 @@ def test_decode_on_the_multi_token_kernel(lib, G, kw, want):
     rows = 3 * 8 * G * S
     r256 = lambda x: (x + 255) // 256 * 256
     assert pl.workspace_bytes == (r256(rows * D * 4) + r256(rows * 2 * 4) if S > 1 else 0)
-    # an empty context keeps the decode kernels
-    assert plan(params(batch=4, num_q_heads=8 * G, **kw), lens + [0]).info.split_kernel in (0, 1)
+    # an empty context changes nothing (its row has no keys and is written as zeros)
+    assert plan(params(batch=4, num_q_heads=8 * G, **kw), lens + [0]).info.split_kernel == 2
 
 
 # Split length of a decode step on the multi-token kernel: one round of
 # resident 16-row blocks (2 per compute unit at head_dim 128), splits no
 # shorter than 64 tokens once some context is past the 256-token switch-over.
+# More than 8 query heads per KV head (128 over 8, as in the largest Llama
+# models; 48 over one KV head): only the multi-token kernel serves them, so
+# decode steps, the fixed order and several tokens all take it, blocks of
+# 16 rows up to 16 rows, else 128 (64 at head_dim 256), or the forced size.
+@pytest.mark.parametrize("HQ,HKV,D,T,rows,nrb", [
+    (128, 8, 128, 1, 0, 1), (48, 1, 128, 1, 0, 1), (48, 1, 128, 1, 16, 3), (48, 1, 256, 1, 0, 1),
+    (128, 1, 64, 1, 0, 1), (128, 1, 256, 1, 0, 2), (128, 1, 256, 1, 16, 8), (128, 8, 128, 4, 0, 1),
+    (128, 8, 128, 9, 0, 2), (128, 8, 256, 4, 16, 4), (96, 8, 128, 1, 0, 1), (72, 8, 64, 1, 64, 1),
+])
+def test_wide_groups_on_the_multi_token_kernel(lib, HQ, HKV, D, T, rows, nrb):
+    lens = [3060, 9000, 700]
+    pl = plan(params(batch=3, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, query_len=T, rows_per_block=rows,
+                     max_pages_per_seq=1024), lens)
+    assert pl.info.split_kernel == 2
+    assert pl.info.split_work_groups == 3 * HKV * nrb * pl.max_splits
+    fx = plan(params(batch=3, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D, rows_per_block=rows, fixed_chunk=512,
+                     max_pages_per_seq=1024), lens)
+    assert fx.info.split_kernel == 2 and fx.info.chunks_per_work_group == 1
+    assert fx.max_splits == math.ceil(9000 / 512)
+
+
+def test_wide_groups_limits(lib):
+    for G in (9, 12, 16, 32, 64, 128):
+        assert status_of(params(num_q_heads=G * 2, num_kv_heads=2), [10]) == B.DA_OK
+        assert status_of(params(num_q_heads=G * 2, num_kv_heads=2), [0]) == B.DA_OK
+    # the fixed order on the multi-token kernel: a grid of at most 65535 chunks
+    # per sequence, with no decode kernel to fall back to
+    big = dict(num_q_heads=128, fixed_chunk=16, max_pages_per_seq=70000)
+    assert status_of(params(**big), [16 * 65535]) == B.DA_OK
+    assert status_of(params(**big), [16 * 65536]) == B.DA_ERR_UNSUPPORTED
+    assert plan(params(**dict(big, num_q_heads=64)), [16 * 65536]).info.split_kernel in (0, 1)
+
+
 def test_decode_on_the_multi_token_kernel_splits(lib, monkeypatch):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
     pl = plan(params(num_q_heads=64), [3060])      # 192 pages; one round would cut 3 pages, below 4
@@ -585,7 +627,13 @@ def test_empty_batch_plans(lib):
     (dict(q_dtype=7), [10], B.DA_ERR_INVALID),
     (dict(kv_dtype=3), [10], B.DA_ERR_INVALID),
     (dict(out_dtype=-1), [10], B.DA_ERR_INVALID),
-    (dict(num_q_heads=32, num_kv_heads=2), [10], B.DA_ERR_UNSUPPORTED),   # G = 16
+    (dict(num_q_heads=32, num_kv_heads=2, q_dtype="f32", kv_dtype="f32"), [10], B.DA_ERR_UNSUPPORTED),  # G 16, f32
+    (dict(num_q_heads=32, num_kv_heads=2, kernel="matrix"), [10], B.DA_ERR_UNSUPPORTED),  # G 16: no decode kernel
+    (dict(num_q_heads=32, num_kv_heads=2, kernel="vector"), [10], B.DA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=32, num_kv_heads=2, q_dtype="f32"), [10], B.DA_ERR_UNSUPPORTED),   # q and K/V differ
+    (dict(num_q_heads=32, num_kv_heads=2, query_len=4, q_dtype="f32", kv_dtype="f32", out_dtype="f32"), [10],
+     B.DA_ERR_UNSUPPORTED),                                                # per-token path
+    (dict(head_dim=256, rows_per_block=128), [10], B.DA_ERR_UNSUPPORTED),
     (dict(max_pages_per_seq=0), [10], B.DA_ERR_INVALID),
     (dict(max_pages_per_seq=(1 << 31) // 16), [10], B.DA_ERR_UNSUPPORTED),  # token index would overflow int32
     (dict(max_pages_per_seq=4), [65], B.DA_ERR_INVALID),                  # 65 > 4 * 16

@@ -1,13 +1,14 @@
 """Decode steps on the multi-token kernel: one new token per sequence, with 5
 to 8 query heads per KV head (3 or 4 at head_dim 64 and 256, pages not a
 multiple of 16, or fewer (sequence, KV head) streams than compute units; 2 at
-head_dim 64) on
-16-bit q and K/V, run as one 16-row block per KV head with both products on
-the matrix cores, merged by the decode combine. Against the oracle at several
-head dims, page sizes, windows and split counts, ragged, bimodal (one long
-context among short ones: the split that fits one round of work-groups) and
-single-key contexts; an empty context in the batch keeps the decode kernels;
-the full long-context batch at 64 query heads in the planner's launch
+head_dim 64), and every group wider than 8 (16 query heads per KV head as in
+a 128-over-8 model, 32 to 64 over one KV head), on 16-bit q and K/V: one
+16-row block per KV head (more rows: blocks of 64 or 128) with both products
+on the matrix cores, merged by the decode combine. Against the oracle at
+several head dims, page sizes, windows, split counts and forced block sizes,
+ragged, bimodal (one long context among short ones: the split that fits one
+round of work-groups), single-key and empty contexts (rows of zeros); the
+full long-context batch at 64 and 128 query heads in the planner's launch
 configuration, sampled sequences against the oracle."""
 import numpy as np
 import pytest
@@ -35,6 +36,12 @@ CASES = [
     (3, 32, 8, 128, "bf16", "f32", 16, (3060, 100, 2049), 0),              # G 4, head_dim 128, 24 streams
     (3, 24, 8, 128, "f16", "f16", 16, (4097, 1, 640), 2000),               # G 3, head_dim 128, window
     (4, 16, 8, 64, "bf16", "f32", 16, (3000, 1, 257, 9000), 0),             # G 2, head_dim 64
+    (3, 128, 8, 128, "f16", "f16", 16, (3060, 1, 9000), 0),                # G 16
+    (2, 96, 8, 128, "bf16", "f32", 32, (5000, 700), 1000),                 # G 12, window
+    (2, 48, 1, 128, "f16", "f32", 16, (4097, 300), 0),                     # G 48, one KV head
+    (2, 64, 2, 64, "bf16", "bf16", 8, (2, 6000), 0),                       # G 32, head_dim 64
+    (2, 32, 2, 256, "f16", "f32", 16, (1500, 333), 200),                   # G 16, head_dim 256
+    (2, 64, 1, 256, "bf16", "f32", 16, (2500, 17), 0),                     # G 64 at head_dim 256: 64-row block
 ]
 
 
@@ -76,13 +83,17 @@ def test_single_key_returns_v(gpu):
         np.testing.assert_array_equal(host64(got)[b], want.astype(np.float64))
 
 
-def test_empty_context_keeps_the_decode_kernels(gpu):
-    lens = (0, 3060, 1, 0)
-    spec = wl.WorkloadSpec("mqdec_empty", len(lens), 64, 8, 128, "f16", "f16", "f16", 16, ("list", lens),
-                           seed=7660)
+@pytest.mark.parametrize("HQ,chunk", [(64, 0), (64, 256), (128, 0), (128, 512)])
+def test_empty_context_rows_are_zero(gpu, HQ, chunk):
+    """An empty context has no keys: its block reads no page and its rows are
+    written as zeros, also in a batch that splits and in the fixed order."""
+    lens = (0, 3060, 1, 0, 20000)
+    spec = wl.WorkloadSpec(f"mqdec_empty{HQ}", len(lens), HQ, 8, 128, "f16", "f16", "f16", 16, ("list", lens),
+                           seed=7660 + HQ + chunk)
     w = wl.make_workload(spec, gpu)
-    got, plan = run_lib(w)
-    assert plan.info.split_kernel == 1
+    say(f"[empty contexts on the multi-token kernel] H={HQ}/8 lens={lens} chunk={chunk}")
+    got, plan = run_lib(w, fixed_chunk=chunk)
+    assert plan.info.split_kernel == 2 and plan.max_splits > 1
     g = host64(got)
     for b, L in enumerate(lens):
         if L == 0:
@@ -90,12 +101,33 @@ def test_empty_context_keeps_the_decode_kernels(gpu):
     check(got, oracle_for(w), "f16", "f16", "empty context")
 
 
-def test_long_batch_64_query_heads_full_size(gpu):
-    """Batch 32, 64/8 heads, head_dim 128, fp16, 16k-32k tokens with spiky
-    keys: the whole batch in the planner's launch configuration (one round of
-    16-row work-groups), five sequences checked against the oracle; and
-    against the matrix-core decode kernel on every sequence."""
-    spec = wl.LONG_BATCH.replace(name="long_batch_g8", num_q_heads=64)
+@pytest.mark.parametrize("rows", [16, 64, 128])
+def test_wide_group_block_sizes_agree(gpu, rows):
+    """48 query heads over one KV head in 16-, 64- and 128-row blocks (three
+    blocks reading the same keys, one with 16 empty rows, one with 80): each
+    against the oracle, and all within fp32 rounding of the planner's own."""
+    spec = wl.WorkloadSpec("mqdec_rows", 3, 48, 1, 128, "bf16", "bf16", "f32", 16, ("list", (3000, 40, 12000)),
+                           seed=7670, spike_frac=0.01)
+    w = wl.make_workload(spec, gpu)
+    say(f"[wide group, {rows}-row blocks]")
+    ref = oracle_for(w)
+    got, plan = run_lib(w, rows_per_block=rows)
+    assert plan.info.split_kernel == 2
+    assert plan.info.split_work_groups == 3 * -(-48 // rows) * plan.max_splits  # B x row blocks x splits
+    check(got, ref, "bf16", "f32", f"{rows}-row blocks")
+    auto, _ = run_lib(w)
+    a, b = host64(got), host64(auto)
+    assert np.linalg.norm(a - b) <= 2e-6 * np.linalg.norm(b)
+
+
+@pytest.mark.parametrize("HQ", [64, 128])
+def test_long_batch_wide_groups_full_size(gpu, HQ):
+    """Batch 32, 64/8 and 128/8 heads, head_dim 128, fp16, 16k-32k tokens with
+    spiky keys: the whole batch in the planner's launch configuration (one
+    round of 16-row work-groups), five sequences checked against the oracle;
+    at 64 heads also against the matrix-core decode kernel on every
+    sequence."""
+    spec = wl.LONG_BATCH.replace(name=f"long_batch_h{HQ}", num_q_heads=HQ)
     w = wl.make_workload(spec, gpu)
     got, plan = run_lib(w)
     assert plan.info.split_kernel == 2
@@ -107,6 +139,8 @@ def test_long_batch_64_query_heads_full_size(gpu):
     sub.f32_twin = got.f32_twin[idx]
     err, worst = check(sub, oracle_for(w, rows), "f16", "f16", "long batch, 64 query heads")
     say(f"  sampled sequences: rel L2 {err:.2e}, worst {worst:.2e}")
+    if HQ != 64:
+        return
     other, oplan = run_lib(w, kernel="matrix")
     assert oplan.info.split_kernel == 1
     a, b = got.f32_twin.double(), other.f32_twin.double()

@@ -48,6 +48,8 @@ MULTI_FIXED = [
     (3, 48, 8, 256, "f16", "f32", 16, (40, 3000, 700), 500, 128),
     (2, 16, 4, 128, "f16", "f32", 8, (6000, 333), 0, 64),
     (2, 64, 8, 128, "bf16", "bf16", 32, (70000, 12), 4096, 2048),
+    (3, 128, 8, 128, "f16", "f16", 16, (3060, 0, 9000), 0, 512),            # G 16, an empty context
+    (2, 48, 1, 64, "bf16", "f32", 16, (4000, 260), 1000, 256),            # G 48 (one KV head)
 ]
 
 

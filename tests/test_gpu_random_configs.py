@@ -87,3 +87,34 @@ def test_random_few_row_multi_token_matches_oracle(gpu, i):
     assert plan.info.split_kernel == 2
     err, worst = check(got, oracle_for(w), c["kv"], c["out"], f"few-row case {i}")
     say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
+
+
+def draw_wide_group(i):
+    """More than 8 query heads per KV head (only the multi-token kernel
+    serves them): 16-bit q and K/V, one to a few new tokens, empty contexts
+    in decode batches, forced block sizes and the fixed order."""
+    rng = np.random.default_rng(70000 + i)
+    c = draw_case(200000 + i)
+    c["G"] = int(rng.choice([9, 12, 16, 24, 32, 48, 64]))
+    c["Hkv"] = int(rng.choice([1, 1, 2, 8]))
+    c["kv"] = str(rng.choice(["f16", "bf16"]))
+    c["q"] = c["kv"]
+    c["T"] = int(rng.choice([1, 1, 1, 2, 4]))
+    c["rows"] = int(rng.choice([0, 0, 16, 64] + ([128] if c["D"] <= 128 else [])))
+    if c["T"] > 1:
+        c["fixed"] = 0
+        c["lens"] = [max(L, c["T"]) for L in c["lens"]]
+    return c
+
+
+@pytest.mark.parametrize("i", range(120))
+def test_random_wide_group_matches_oracle(gpu, i):
+    c = draw_wide_group(i)
+    say(f"[wide-group {i}] {c}")
+    spec = wl.WorkloadSpec(f"wide{i}", len(c["lens"]), c["G"] * c["Hkv"], c["Hkv"], c["D"], c["q"], c["kv"], c["out"],
+                           c["P"], ("list", tuple(c["lens"])), seed=4000 + i, window=c["W"], query_len=c["T"])
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w, num_splits=c["splits"], fixed_chunk=c["fixed"], rows_per_block=c["rows"])
+    assert plan.info.split_kernel == 2
+    err, worst = check(got, oracle_for(w), c["kv"], c["out"], f"wide-group case {i}")
+    say(f"  rel L2 {err:.2e}, worst sequence {worst:.2e}")
