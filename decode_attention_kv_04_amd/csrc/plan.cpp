@@ -427,7 +427,13 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_p
     }
   }
   c = std::max<int64_t>(c, 1);
-  c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));  // grid y = row blocks x splits
+  // Grid y = row blocks x splits. The fixed order cannot lengthen its chunk
+  // to fit (G 8 or fewer is one row block, checked before it got here).
+  if (plan->fixed_multi && ceil_div(max_np, c) > 65535 / nrb) {
+    delete plan;
+    return DA_ERR_UNSUPPORTED;
+  }
+  c = std::max<int64_t>(c, ceil_div(max_np, 65535 / nrb));
   if (c > INT32_MAX) c = INT32_MAX;
   plan->pages_per_split = static_cast<int32_t>(c);
   plan->splits.assign(p.batch, 1);
