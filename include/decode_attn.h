@@ -104,8 +104,8 @@ typedef struct {
                                 kernel: q and K/V sharing f16 or bf16, kernel
                                 DA_KERNEL_AUTO for decode (DA_KERNEL_VECTOR for
                                 query_len > 1 is the per-token path), and in the
-                                fixed-order mode at most 65535 chunks per
-                                sequence; else DA_ERR_UNSUPPORTED              */
+                                fixed-order mode at most 65535 row blocks x
+                                chunks per sequence; else DA_ERR_UNSUPPORTED   */
   int32_t head_dim;          /* D in {64, 128, 256}                                 */
   int32_t page_size;         /* P: a multiple of 8, 8..1024                         */
   int32_t max_pages_per_seq; /* row stride of page_table; >= ceil(L_b / P)          */
