@@ -20,8 +20,9 @@ configs: the five named configurations (tiny, the Llama-3.1-8B shape at 3060
           the oracle's wall time on each, and each output checked against
           the oracle (the run exits 1 if any check fails).
 --sweep: only a context-length sweep on the Llama shape (L 256..65536,
-          batch 1 and 32), and the same shape at 3060 tokens with head_dim
-          64, 128 and 256.
+          batch 1 and 32), the same shape at 3060 tokens with head_dim
+          64, 128 and 256, and with 1, 2, 4, 8 and 16 query heads per KV
+          head (batch 1 x 3060 and 32 x 4096 tokens).
 Also reported, each timed the same way: the fixed-order mode on the same
 batch (fixed_order), several new tokens per sequence on their own workloads
 (multi_token: a 4-token check over the long-context batch and a 128-token
@@ -656,6 +657,35 @@ def measure_head_dims(binding, workloads, lib, dev, stream, rounds):
     return res
 
 
+def measure_groups(binding, workloads, lib, dev, stream, rounds):
+    """Query heads per KV head 1, 2, 4, 8 and 16 (8 KV heads, head_dim 128,
+    fp16, 16-token pages) at batch 1 x 3060 and batch 32 x 4096 tokens: step
+    and split µs over alternating repeats, GB/s of K/V, and the split kernel
+    the plan picks (G 16 has only the multi-token kernel)."""
+    import torch
+    res = []
+    for B, L in ((1, 3060), (32, 4096)):
+        runners = {}
+        for G in (1, 2, 4, 8, 16):
+            spec = workloads.LLAMA8B_3060.replace(name=f"g{G}_b{B}_l{L}_f16", batch=B, num_q_heads=8 * G,
+                                                  lengths=("fixed", L), seed=500 + G + B)
+            runners[G] = Runner(binding, lib, workloads.make_workload(spec, dev), dev, stream)
+        torch.cuda.synchronize()
+        times = time_alternating(runners, rounds, stream)
+        for G, r in runners.items():
+            kvb = r.w.kv_bytes()
+            run_q, split_q = quantiles(times[G]["run"]), quantiles(times[G]["split"])
+            gbs = kvb / (run_q["median"] * 1e-6) / 1e9
+            res.append({"batch": B, "context": L, "group": G, "heads": [8 * G, 8], "us": run_q, "split_us": split_q,
+                        "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBPS, 4),
+                        "max_splits": r.plan.max_splits, "split_kernel": int(r.plan.info.split_kernel),
+                        "algorithmic_bytes": kvb})
+            print(f"[bench] G {G} B {B} L {L}: {run_q['median']:.1f} us, {gbs:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+        del runners
+        torch.cuda.empty_cache()
+    return res
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -674,7 +704,7 @@ def main():
                     help="only the 32-layer decode step of the Llama-3.1-8B shape at 3060 tokens (for traces)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the context-length sweep (Llama shape, L 256..65536, batch 1 and 32) and "
-                    "the head_dim sweep at 3060 tokens")
+                    "the head_dim sweep at 3060 tokens, and query heads per KV head 1..16")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, copy a buffer of known size once (counter calibration)")
     args = ap.parse_args()
@@ -706,7 +736,9 @@ def main():
     if args.sweep:
         sweep = measure_sweep(binding, workloads, lib, dev, stream, args.rounds)
         head_dims = measure_head_dims(binding, workloads, lib, dev, stream, args.rounds)
-        print(json.dumps({"metric": METRIC, "sweep": sweep, "head_dims": head_dims, "unit": "GB/s", "n_gpus": 1,
+        groups = measure_groups(binding, workloads, lib, dev, stream, args.rounds)
+        print(json.dumps({"metric": METRIC, "sweep": sweep, "head_dims": head_dims, "groups": groups,
+                          "unit": "GB/s", "n_gpus": 1,
                           "data": "synthetic", "kernel_source_sha256_16": kernel_hash()}), flush=True)
         return
 
