@@ -617,7 +617,15 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   bool mq_decode = T == 1 && (weak_decode || (gt == 4 && few_streams && p->num_splits == 0)) && multi_dtypes &&
                    p->kernel == DA_KERNEL_AUTO && !fixed;
   int64_t mq_pages = 0;
-  if (mq_decode && p->num_splits == 0) {
+  if (mq_decode && whole_streams && p->head_dim == 128 && G >= 5) {
+    // Whole streams on this kernel too, at head_dim 128 from 5 query heads
+    // per KV head: one unsplit work-group per stream (64 over 8 KV heads,
+    // 32 x 4096 tokens 84.1 -> 81.2 us, 32 x 2048 45.4 -> 42.8; 128 over 8,
+    // 32 x 4096 86.0 -> 80.9; 32 x 512 even). Not at head_dim 64 or 256,
+    // where one work-group streams too slowly to fill the chip (32 over 8,
+    // 32 x 2048 tokens: 25.7 -> 34.5 and 84.9 -> 91.4).
+    mq_pages = max_np;
+  } else if (mq_decode && p->num_splits == 0) {
     mq_pages = multi_decode_split_pages(npages, p->num_kv_heads, num_cus, p->head_dim, P, weak_decode, gt != 0);
     if (!weak_decode && mq_pages >= max_np) mq_pages = 0;
     mq_decode = mq_pages > 0;

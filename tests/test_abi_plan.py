@@ -843,3 +843,27 @@ def test_whole_streams_are_not_split(lib, monkeypatch, B, L, kw):
 def test_whole_streams_need_equal_lengths_and_enough_streams(lib, monkeypatch, B, lens):
     monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
     assert plan(params(batch=B, max_pages_per_seq=4096), lens).max_splits > 1
+
+
+# Whole streams on the multi-token kernel: at head_dim 128 with 5 or more
+# query heads per KV head, a batch of at least one stream per compute unit
+# with about equal lengths runs unsplit (no combine); at head_dim 64 and 256
+# it keeps the split that fills the round.
+@pytest.mark.parametrize("HQ,D,P,lens,unsplit", [
+    (64, 128, 16, [4096] * 32, True), (128, 128, 16, [4096] * 32, True), (48, 128, 16, [2048] * 32, True),
+    (64, 128, 24, [2048] * 32, True), (64, 128, 16, [1900 + 6 * b for b in range(32)], True),
+    (64, 128, 16, [1024 + 224 * b for b in range(32)], False), (64, 128, 16, [4096] * 16, False),
+    (32, 64, 16, [2048] * 32, False), (32, 256, 16, [2048] * 32, False), (64, 256, 16, [2048] * 32, False),
+])
+def test_whole_streams_on_the_multi_token_kernel(lib, monkeypatch, HQ, D, P, lens, unsplit):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    pl = plan(params(batch=len(lens), num_q_heads=HQ, head_dim=D, page_size=P, max_pages_per_seq=512), lens)
+    assert pl.info.split_kernel == 2
+    if unsplit:
+        assert pl.max_splits == 1 and pl.workspace_bytes == 0
+        assert pl.info.split_work_groups == 8 * len(lens)
+    else:
+        assert pl.max_splits > 1
+    # a forced split count still splits
+    assert plan(params(batch=len(lens), num_q_heads=HQ, head_dim=D, page_size=P, max_pages_per_seq=512,
+                       num_splits=3), lens).max_splits == 3

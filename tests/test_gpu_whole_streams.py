@@ -1,6 +1,7 @@
 """Whole streams: a batch with at least one (sequence, KV head) stream per
 compute unit and about equal attended lengths runs unsplit (one work-group per
-stream, no combine, no workspace). Such batches on both split kernels, with
+stream, no combine, no workspace). Such batches on both decode kernels and on
+the multi-token kernel (head_dim 128, 8 and 16 query heads per KV head), with
 windows, ragged lengths within the equal-length band and several new tokens
 per sequence, against the oracle, and against a forced split count of the same
 kernel within fp32 rounding."""
@@ -22,6 +23,8 @@ CASES = [
     (32, 32, 8, 128, "f32", "f32", 16, ("fixed", 1024), 0, 1),       # fp32 K/V: vector kernel
     (256, 32, 8, 128, "f16", "f16", 16, ("uniform", 300, 320), 0, 1),
     (32, 32, 8, 128, "f32", "f32", 16, ("fixed", 600), 200, 3),      # three new tokens, once per token
+    (32, 64, 8, 128, "f16", "f32", 16, ("fixed", 2048), 0, 1),       # G 8: the multi-token kernel, unsplit
+    (32, 128, 8, 128, "bf16", "f32", 24, ("uniform", 1900, 2050), 500, 1),  # G 16, 24-token pages, window
 ]
 
 
@@ -42,4 +45,9 @@ def test_whole_streams_match_oracle(gpu, i):
     a = host64(got.f32_twin if hasattr(got, "f32_twin") else got)
     b = host64(split)
     if out == "f32":
-        assert np.linalg.norm(a - b) <= 2e-6 * np.linalg.norm(b)
+        # The decode kernels keep P in fp32: the split changes only the fp32
+        # summation order. The multi-token kernel rounds P to f16 (or a bf16
+        # pair) relative to each split's running maximum, so a split changes
+        # that rounding: bounded by the f16 unit roundoff 2^-11.
+        tol = 2.0 ** -11 if plan.info.split_kernel == 2 else 2e-6
+        assert np.linalg.norm(a - b) <= tol * np.linalg.norm(b)
