@@ -361,9 +361,10 @@ da_status finish_fixed_plan(da_plan* plan, const std::vector<int64_t>& npages, i
 // into blocks of rows_per_group; a block sees keys from the window start of
 // its first token to its last token, and those pages are split with one split
 // length for the whole batch.
-da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_pages) {
+da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_pages, bool unsplit) {
   // decode_pages > 0: a decode step's split length, or (fixed_multi) the
-  // fixed-order chunk in pages, which num_splits does not change.
+  // fixed-order chunk in pages, which num_splits does not change. unsplit:
+  // whole streams, one split per row block.
   const da_params& p = plan->p;
   const int64_t P = p.page_size;
   const int64_t T = plan->query_len;
@@ -405,6 +406,8 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_p
     c = decode_pages;
   } else if (p.num_splits > 0) {
     c = ceil_div(max_np, p.num_splits);
+  } else if (unsplit) {
+    c = max_np;
   } else if (decode_pages > 0) {
     c = decode_pages;
   } else {
@@ -617,13 +620,18 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   bool mq_decode = T == 1 && (weak_decode || (gt == 4 && few_streams && p->num_splits == 0)) && multi_dtypes &&
                    p->kernel == DA_KERNEL_AUTO && !fixed;
   int64_t mq_pages = 0;
-  if (mq_decode && whole_streams && p->head_dim == 128 && G >= 5) {
-    // Whole streams on this kernel too, at head_dim 128 from 5 query heads
-    // per KV head: one unsplit work-group per stream (64 over 8 KV heads,
-    // 32 x 4096 tokens 84.1 -> 81.2 us, 32 x 2048 45.4 -> 42.8; 128 over 8,
-    // 32 x 4096 86.0 -> 80.9; 32 x 512 even). Not at head_dim 64 or 256,
-    // where one work-group streams too slowly to fill the chip (32 over 8,
-    // 32 x 2048 tokens: 25.7 -> 34.5 and 84.9 -> 91.4).
+  // Whole streams on this kernel too, at head_dim 128 where the rows of a KV
+  // head fit one 16-row block (5 to 16 query heads per KV head, or a few
+  // tokens: T x G <= 16): one unsplit work-group per stream. 64 over 8 KV
+  // heads, 32 x 4096 tokens 84.1 -> 81.2 us, 32 x 2048 45.4 -> 42.8; 128
+  // over 8, 32 x 4096 86.0 -> 80.9; 32 x 512 even; a 4-token check over
+  // 32 x 4096 85.8 -> 81.4, over 32 x 2048 46.8 -> 43.5. Not at head_dim 64
+  // or 256, where one work-group streams too slowly to fill the chip (32
+  // over 8, 32 x 2048 tokens: 25.7 -> 34.5 and 84.9 -> 91.4), nor with more
+  // rows (a 4-token check at 64 over 8: 91.5 -> 127.5).
+  const bool mq_whole = whole_streams && p->head_dim == 128 && static_cast<int64_t>(T) * G <= 16 &&
+                        (p->rows_per_block == 0 || p->rows_per_block == 16);
+  if (mq_decode && mq_whole && G >= 5) {
     mq_pages = max_np;
   } else if (mq_decode && p->num_splits == 0) {
     mq_pages = multi_decode_split_pages(npages, p->num_kv_heads, num_cus, p->head_dim, P, weak_decode, gt != 0);
@@ -652,7 +660,7 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
     mq_pages = p->fixed_chunk / P;
   }
   if ((plan->query_len > 1 && !per_token) || mq_decode) {
-    const da_status st = finish_multi_plan(plan, lens, mq_pages);
+    const da_status st = finish_multi_plan(plan, lens, mq_pages, mq_whole && !plan->fixed_multi);
     if (st == DA_OK) *out = plan;
     return st;
   }

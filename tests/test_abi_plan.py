@@ -867,3 +867,24 @@ def test_whole_streams_on_the_multi_token_kernel(lib, monkeypatch, HQ, D, P, len
     # a forced split count still splits
     assert plan(params(batch=len(lens), num_q_heads=HQ, head_dim=D, page_size=P, max_pages_per_seq=512,
                        num_splits=3), lens).max_splits == 3
+
+
+# Several tokens whose rows of a KV head fit one 16-row block (T x G <= 16)
+# at head_dim 128: a whole-streams batch runs unsplit as well; with more rows
+# (128-row blocks) it keeps the split that fills the round.
+@pytest.mark.parametrize("T,HQ,D,lens,unsplit", [
+    (4, 32, 128, [4096] * 32, True), (2, 32, 128, [4096] * 32, True), (4, 32, 128, [1900 + 6 * b for b in range(32)], True),
+    (16, 8, 128, [2048] * 32, True), (4, 64, 128, [4096] * 32, False), (4, 32, 64, [2048] * 32, False),
+    (4, 32, 256, [2048] * 32, False), (4, 32, 128, [1024 + 224 * b for b in range(32)], False),
+    (4, 32, 128, [4096] * 16, False),
+])
+def test_whole_streams_of_a_few_tokens(lib, monkeypatch, T, HQ, D, lens, unsplit):
+    monkeypatch.delenv("DECODE_ATTN_SPLIT_MIN", raising=False)
+    kw = dict(batch=len(lens), num_q_heads=HQ, head_dim=D, query_len=T, max_pages_per_seq=512)
+    pl = plan(params(**kw), lens)
+    assert pl.info.split_kernel == 2
+    assert (pl.max_splits == 1) == unsplit
+    if unsplit:
+        assert pl.workspace_bytes == 0
+        # a forced block size other than 16 rows keeps the split rule
+        assert plan(params(rows_per_block=64, **kw), lens).max_splits > 1

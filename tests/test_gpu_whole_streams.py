@@ -1,7 +1,8 @@
 """Whole streams: a batch with at least one (sequence, KV head) stream per
 compute unit and about equal attended lengths runs unsplit (one work-group per
 stream, no combine, no workspace). Such batches on both decode kernels and on
-the multi-token kernel (head_dim 128, 8 and 16 query heads per KV head), with
+the multi-token kernel (head_dim 128, 8 and 16 query heads per KV head, and
+4 tokens x 4 heads in one 16-row block), with
 windows, ragged lengths within the equal-length band and several new tokens
 per sequence, against the oracle, and against a forced split count of the same
 kernel within fp32 rounding."""
@@ -25,6 +26,7 @@ CASES = [
     (32, 32, 8, 128, "f32", "f32", 16, ("fixed", 600), 200, 3),      # three new tokens, once per token
     (32, 64, 8, 128, "f16", "f32", 16, ("fixed", 2048), 0, 1),       # G 8: the multi-token kernel, unsplit
     (32, 128, 8, 128, "bf16", "f32", 24, ("uniform", 1900, 2050), 500, 1),  # G 16, 24-token pages, window
+    (32, 32, 8, 128, "f16", "f32", 16, ("fixed", 2048), 0, 4),       # a 4-token check: one 16-row block
 ]
 
 
