@@ -128,12 +128,13 @@ constexpr int64_t kMultiBalanceShare = 170;
 
 // Shortest split (at least cmin pages) whose working work-groups, ceil(pages
 // / c) for every block of `npages` on each of H KV heads, fit `slots`; the
-// longest block's page count when no split fits. The count of work-groups
-// never grows with c, so a bisection finds it.
+// longest block's page count when no split fits. An empty block's work-group
+// exits at once and holds no slot. The count of work-groups never grows with
+// c, so a bisection finds it.
 int64_t fit_split_pages(const std::vector<int64_t>& npages, int64_t H, int64_t slots, int64_t cmin, int64_t max_np) {
   auto groups = [&](int64_t cc) {
     int64_t n = 0;
-    for (int64_t np : npages) n += std::max<int64_t>(1, ceil_div(np, cc));
+    for (int64_t np : npages) n += ceil_div(np, cc);
     return n * H;
   };
   int64_t lo = std::min(cmin, max_np), hi = max_np;
@@ -174,7 +175,10 @@ int64_t multi_decode_split_pages(const std::vector<int64_t>& npages, int64_t num
   for (int64_t n : npages) max_np = std::max(max_np, n);
   if (max_np == 0) return 1;
   const int64_t slots = num_cus * resident_row_groups_per_cu(head_dim, 16);
-  const int64_t blocks = static_cast<int64_t>(npages.size()) * num_kv_heads;
+  // Streams with keys: an empty one's work-group exits at once.
+  int64_t nonempty = 0;
+  for (int64_t n : npages) nonempty += n > 0 ? 1 : 0;
+  const int64_t blocks = nonempty * num_kv_heads;
   const int64_t cmin = std::min(max_np, ceil_div(multi_decode_min_split_tokens(max_np * P), P));
   const int64_t limit = balance_limit(npages, num_kv_heads, cmin);
   const int64_t per_stream = std::max<int64_t>(1, slots / blocks);
@@ -613,11 +617,16 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // us; whole streams of 64 x 2048 and 64 x 8192 tokens stay faster on the
   // vector kernel, 23.2 against 25.1 and 82.3 against 83.7 us; at head_dim
   // 256 and with 8-token pages G 2 was even on batches and lost on the 4 x
-  // 1-4k wide-head batch, 15.5 -> 16.3).
+  // 1-4k wide-head batch, 15.5 -> 16.3). With fewer streams than compute
+  // units at head_dim 128 (the planner's split choice, a plan that splits)
+  // 1 to 4 query heads per KV head take it too: 16/8 heads, 4 x 3060 tokens
+  // 16.1 -> 13.2 us, 1 x 32768 28.3 -> 25.0; 8/8, 4 x 3060 14.3 -> 12.5;
+  // 1 x 3060 even. Not at head_dim 64 or 256: the 4 x 1-4k wide-head batch
+  // 14.1 -> 15.7, 8/8 heads at head_dim 64, 4 x 3060 9.9 -> 11.0.
   const bool few_streams = static_cast<int64_t>(p->batch) * p->num_kv_heads < num_cus;
   const bool weak_decode = gt == 0 || gt == 8 || (gt == 4 && !matrix_kernel_supported(*p)) ||
                            (gt == 2 && p->head_dim == 64 && !whole_streams);
-  bool mq_decode = T == 1 && (weak_decode || (gt == 4 && few_streams && p->num_splits == 0)) && multi_dtypes &&
+  bool mq_decode = T == 1 && (weak_decode || (gt <= 4 && p->head_dim == 128 && few_streams && p->num_splits == 0)) && multi_dtypes &&
                    p->kernel == DA_KERNEL_AUTO && !fixed;
   int64_t mq_pages = 0;
   // Whole streams on this kernel too, at head_dim 128 where the rows of a KV

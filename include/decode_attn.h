@@ -86,10 +86,11 @@ typedef enum { DA_F32 = 0, DA_F16 = 1, DA_BF16 = 2 } da_dtype;
 /* Which single-query split kernel a plan uses (da_params.kernel). */
 typedef enum {
   DA_KERNEL_AUTO = 0,   /* the planner chooses (matrix cores from 2 query heads per KV head on;
-                           a decode step with 5-8 of them, 3-4 where the
-                           decode matrix-core kernel is not built or the batch
-                           has fewer (sequence, KV head) streams than compute
-                           units, or 2 at head_dim 64, on the multi-token
+                           a decode step with 5 or more of them, 3-4 where the
+                           decode matrix-core kernel is not built, 1-4 at
+                           head_dim 128 when the batch has fewer (sequence, KV
+                           head) streams than compute units, or 2 at head_dim
+                           64, on the multi-token
                            kernel as one token when its plan is balanced)      */
   DA_KERNEL_VECTOR = 1, /* vector q.K; with query_len > 1: the single-query kernels per token   */
   DA_KERNEL_MATRIX = 2  /* q.K on the matrix cores; DA_ERR_UNSUPPORTED where not built           */
@@ -194,9 +195,9 @@ typedef struct {
                                 plans (query_len <= 1) with DA_KERNEL_AUTO
                                 take 2 when q and K/V share f16 or bf16 and G
                                 is above 8 (always), 5 to 8, 2 at head_dim 64,
-                                or 3 to 4 where 1 is not built or (num_splits
-                                0, and the plan splits) B * H_kv is below
-                                num_cus;
+                                3 to 4 where 1 is not built, or 1 to 4 at
+                                head_dim 128 when (num_splits 0, and the plan
+                                splits) B * H_kv is below num_cus;
                                 and (num_splits 0) only if no work-group of
                                 that plan holds more than about 1/170 of the
                                 batch's attended page-heads (else the decode

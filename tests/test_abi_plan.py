@@ -193,11 +193,16 @@ def test_split_kernel_selection(lib):
 def test_split_kernel_by_group(lib, G):
     want = 0 if G == 1 else (1 if G <= 4 else 2)
     for lens in ([32768] * 32, [3060] * 2, [1]):
-        # G 3-4 with fewer streams than compute units, when the plan splits
+        # G 1-4 at head_dim 128 with fewer streams than compute units, when the
+        # plan splits: the multi-token kernel
         few_split = len(lens) * 8 < 256 and max(lens) > 256
-        w = 2 if (few_split and G in (3, 4)) else want
+        w = 2 if (few_split and G <= 4) else want
         assert plan(params(batch=len(lens), num_q_heads=8 * G), lens).info.split_kernel == w
-    # a forced split count keeps G 3-4 on the decode kernel
+        # not at head_dim 64 or 256 for G 1 (G 2 at head_dim 64 is weak on the decode kernels)
+        if G == 1:
+            for D in (64, 256):
+                assert plan(params(batch=len(lens), num_q_heads=8, head_dim=D), lens).info.split_kernel == 0
+    # a forced split count keeps G 1-4 on the decode kernels
     for kw in (dict(num_splits=1), dict(num_splits=7)):
         assert plan(params(batch=2, num_q_heads=8 * G, **kw), [3060] * 2).info.split_kernel == want
     for kw in (dict(num_splits=1), dict(num_splits=7)):
@@ -442,10 +447,9 @@ def test_query_len_zero_and_one_are_decode(lib):
 # A decode step (one new token) runs on the multi-token kernel, as one
 # 16-row block per KV head, with 5 to 8 query heads per KV head on 16-bit q
 # and K/V, with 2 at head_dim 64, and with 3 or 4 where the matrix-core
-# decode kernel is not built (head_dim 64 or 256, pages not a multiple of 16)
-# or the batch has fewer
-# (sequence, KV head) streams than compute units (as here: 3 x 8); not with
-# a forced kernel. More than 8 query heads per KV head always take it (one
+# decode kernel is not built (head_dim 64 or 256, pages not a multiple of 16);
+# at head_dim 128 with 1 to 4 when the batch has fewer (sequence, KV head)
+# streams than compute units (as here: 3 x 8); not with a forced kernel. More than 8 query heads per KV head always take it (one
 # block of 16, 64 or 128 rows per KV head). The fixed-order mode takes it
 # where the decode kernels are weak.
 @pytest.mark.parametrize("G,kw,want", [
@@ -453,7 +457,8 @@ def test_query_len_zero_and_one_are_decode(lib):
     (8, dict(head_dim=64), 2), (8, dict(head_dim=256), 2), (7, dict(page_size=24, max_pages_per_seq=4096), 2),
     (3, dict(head_dim=64), 2), (4, dict(head_dim=256), 2), (4, dict(page_size=8, max_pages_per_seq=4096), 2),
     (3, {}, 2), (4, {}, 2), (2, dict(head_dim=64), 2), (2, dict(head_dim=256), 0), (1, dict(head_dim=256), 0),
-    (2, dict(page_size=8, max_pages_per_seq=4096), 0), (1, dict(head_dim=64), 0), (2, dict(head_dim=64, fixed_chunk=256), 2),
+    (2, dict(page_size=8, max_pages_per_seq=4096), 2), (1, dict(head_dim=64), 0), (2, dict(head_dim=64, fixed_chunk=256), 2),
+    (1, {}, 2), (2, {}, 2), (1, dict(fixed_chunk=256), 0), (2, dict(fixed_chunk=256), 1),
     (8, dict(q_dtype="f32", kv_dtype="f32", out_dtype="f32"), 0), (8, dict(q_dtype="f32"), 0),
     (8, dict(kernel="vector"), 0), (8, dict(kernel="matrix"), 1), (8, dict(fixed_chunk=256), 2),
     (4, dict(head_dim=64, fixed_chunk=256), 2), (4, dict(fixed_chunk=256), 1),

@@ -107,11 +107,11 @@ def test_group_dim_dtype_grid(gpu, G, D, kv):
             out, plan = run_lib(w, num_splits=ns, kernel=kernel)
             # automatic: the matrix-core kernel from two query heads per group on;
             # the multi-token kernel (one token) from five on, from three on
-            # where the matrix-core decode kernel is not built or (the
-            # planner's split choice) with fewer streams than compute units (6),
-            # and with two at head_dim 64
+            # where the matrix-core decode kernel is not built, with two at
+            # head_dim 64, and from one on at head_dim 128 (the planner's split
+            # choice) with fewer streams than compute units (6)
             multi = kernel == "auto" and kv != "f32" and (G >= 5 or (G >= 3 and (not matrix_ok or ns == 0))
-                                                          or (G == 2 and D == 64))
+                                                          or (G == 2 and D == 64) or (matrix_ok and ns == 0))
             want = 2 if multi else (1 if matrix_ok and (kernel == "matrix" or (kernel == "auto" and G >= 2)) else 0)
             assert plan.info.split_kernel == want
             check(out, ref, kv, "f32", f"G{G} D{D} {kv} splits={ns} kernel={kernel}")
@@ -127,7 +127,10 @@ def test_page_sizes(gpu, P, kernel):
     ref = oracle_for(w)
     for ns in (0, 1, 4):
         out, plan = run_lib(w, num_splits=ns, kernel=kernel)
-        assert plan.info.split_kernel == (1 if (P % 16 == 0 and kernel == "auto") else 0)
+        # automatic with the planner's split choice: 12 streams, fewer than
+        # the compute units, on the multi-token kernel
+        want = 2 if (kernel == "auto" and ns == 0) else (1 if (P % 16 == 0 and kernel == "auto") else 0)
+        assert plan.info.split_kernel == want
         check(out, ref, "bf16", "f32", f"P={P} splits={ns}")
 
 
