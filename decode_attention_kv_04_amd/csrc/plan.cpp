@@ -621,12 +621,16 @@ da_status make_plan(const da_params* p, const int32_t* lens, int32_t num_cus, da
   // units at head_dim 128 (the planner's split choice, a plan that splits)
   // 1 to 4 query heads per KV head take it too: 16/8 heads, 4 x 3060 tokens
   // 16.1 -> 13.2 us, 1 x 32768 28.3 -> 25.0; 8/8, 4 x 3060 14.3 -> 12.5;
-  // 1 x 3060 even. Not at head_dim 64 or 256: the 4 x 1-4k wide-head batch
-  // 14.1 -> 15.7, 8/8 heads at head_dim 64, 4 x 3060 9.9 -> 11.0.
+  // 1 x 3060 even. At head_dim 256 only from 8192 attended tokens: 16/8
+  // heads, 1 x 8192 17.6 -> 16.0, 4 x 16384 90.4 -> 85.7, 1 x 32768 47.4 ->
+  // 45.3; the 4 x 1-4k wide-head batch lost, 14.1 -> 15.7. Not at head_dim
+  // 64: 8/8 heads, 4 x 3060 9.9 -> 11.0, 1 x 8192 8.5 -> 9.6, 1 x 16384
+  // 10.5 -> 11.5 (a gain only at 32768, 16.8 -> 14.9).
   const bool few_streams = static_cast<int64_t>(p->batch) * p->num_kv_heads < num_cus;
   const bool weak_decode = gt == 0 || gt == 8 || (gt == 4 && !matrix_kernel_supported(*p)) ||
                            (gt == 2 && p->head_dim == 64 && !whole_streams);
-  bool mq_decode = T == 1 && (weak_decode || (gt <= 4 && p->head_dim == 128 && few_streams && p->num_splits == 0)) && multi_dtypes &&
+  bool mq_decode = T == 1 && (weak_decode || (gt <= 4 && few_streams && p->num_splits == 0 &&
+                    (p->head_dim == 128 || (p->head_dim == 256 && max_np * P >= 8192)))) && multi_dtypes &&
                    p->kernel == DA_KERNEL_AUTO && !fixed;
   int64_t mq_pages = 0;
   // Whole streams on this kernel too, at head_dim 128 where the rows of a KV

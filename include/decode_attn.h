@@ -88,9 +88,10 @@ typedef enum {
   DA_KERNEL_AUTO = 0,   /* the planner chooses (matrix cores from 2 query heads per KV head on;
                            a decode step with 5 or more of them, 3-4 where the
                            decode matrix-core kernel is not built, 1-4 at
-                           head_dim 128 when the batch has fewer (sequence, KV
-                           head) streams than compute units, or 2 at head_dim
-                           64, on the multi-token
+                           head_dim 128 (at 256 from 8192 attended tokens)
+                           when the batch has fewer (sequence, KV head)
+                           streams than compute units, or 2 at head_dim 64,
+                           on the multi-token
                            kernel as one token when its plan is balanced)      */
   DA_KERNEL_VECTOR = 1, /* vector q.K; with query_len > 1: the single-query kernels per token   */
   DA_KERNEL_MATRIX = 2  /* q.K on the matrix cores; DA_ERR_UNSUPPORTED where not built           */
@@ -196,8 +197,9 @@ typedef struct {
                                 take 2 when q and K/V share f16 or bf16 and G
                                 is above 8 (always), 5 to 8, 2 at head_dim 64,
                                 3 to 4 where 1 is not built, or 1 to 4 at
-                                head_dim 128 when (num_splits 0, and the plan
-                                splits) B * H_kv is below num_cus;
+                                head_dim 128 (256 with a context of at least
+                                8192 attended tokens) when (num_splits 0, and
+                                the plan splits) B * H_kv is below num_cus;
                                 and (num_splits 0) only if no work-group of
                                 that plan holds more than about 1/170 of the
                                 batch's attended page-heads (else the decode

@@ -893,3 +893,19 @@ def test_whole_streams_of_a_few_tokens(lib, monkeypatch, T, HQ, D, lens, unsplit
         assert pl.workspace_bytes == 0
         # a forced block size other than 16 rows keeps the split rule
         assert plan(params(rows_per_block=64, **kw), lens).max_splits > 1
+
+
+# Few streams with 1 or 2 query heads per KV head: the multi-token kernel at
+# head_dim 128, at head_dim 256 only from 8192 attended tokens, never at 64.
+@pytest.mark.parametrize("G,D,lens,want", [
+    (1, 128, [3060], 2), (2, 128, [3060] * 4, 2), (2, 256, [8192], 2), (1, 256, [16384], 2),
+    (2, 256, [16384] * 4, 2), (2, 256, [8176], 0), (2, 256, [4096, 100, 3000, 1], 0), (1, 256, [3060] * 4, 0),
+    (1, 64, [16384], 0), (1, 64, [32768], 0), (2, 256, [100], 0),
+])
+def test_few_streams_small_groups(lib, G, D, lens, want):
+    pl = plan(params(batch=len(lens), num_q_heads=8 * G, head_dim=D, max_pages_per_seq=4096), lens)
+    assert pl.info.split_kernel == want
+    # a window caps the attended tokens
+    if D == 256 and want == 2:
+        assert plan(params(batch=len(lens), num_q_heads=8 * G, head_dim=D, max_pages_per_seq=4096, window=4096),
+                    lens).info.split_kernel == 0
