@@ -147,3 +147,34 @@ def test_long_batch_wide_groups_full_size(gpu, HQ):
     per_seq = ((a - b).flatten(1).norm(dim=1) / b.flatten(1).norm(dim=1)).max().item()
     say(f"  against the decode kernel: worst per-sequence relative L2 {per_seq:.2e}")
     assert per_seq <= 1e-3
+
+
+SMALL_GROUPS = [
+    # B, H_q, H_kv, D, q/kv dtype, out, page, lengths, window, kernel with the planner's split, forced 3 splits
+    (4, 8, 8, 128, "f16", "f16", 16, (3060, 1, 700, 0), 0, 2, 0),           # G 1, head_dim 128
+    (2, 16, 8, 128, "bf16", "f32", 8, (5000, 17), 0, 2, 0),                 # G 2, 8-token pages
+    (3, 16, 8, 128, "f16", "f32", 16, (2049, 300, 4096), 1000, 2, 1),       # G 2, window
+    (2, 16, 8, 256, "bf16", "f32", 16, (9000, 300), 0, 2, 0),               # G 2, head_dim 256, 9000 tokens
+    (1, 8, 8, 256, "f16", "f32", 32, (12000,), 0, 2, 0),                    # G 1, head_dim 256
+    (2, 16, 8, 256, "f16", "f32", 16, (4000, 100), 0, 0, 0),                # G 2, head_dim 256, short: vector
+    (2, 8, 8, 64, "bf16", "f32", 16, (20000, 5), 0, 0, 0),                  # G 1, head_dim 64: vector
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL_GROUPS)))
+def test_small_groups_few_streams_match_oracle(gpu, i):
+    """One or two query heads per KV head in batches of fewer streams than
+    compute units: the multi-token kernel at head_dim 128, and at head_dim
+    256 from 8192 attended tokens, with the planner's split choice; the
+    decode kernels otherwise and with a forced split count."""
+    B, HQ, HKV, D, dt, out, P, lens, W, want_auto, want_forced = SMALL_GROUPS[i]
+    spec = wl.WorkloadSpec(f"smallg{i}", B, HQ, HKV, D, dt, dt, out, P, ("list", lens), seed=7700 + i, window=W,
+                           spike_frac=0.01)
+    say(f"[small groups {i}] B={B} H={HQ}/{HKV} D={D} {dt}->{out} P={P} lens={lens} W={W}")
+    w = wl.make_workload(spec, gpu)
+    ref = oracle_for(w)
+    for ns, want in ((0, want_auto), (3, want_forced)):
+        got, plan = run_lib(w, num_splits=ns)
+        assert plan.info.split_kernel == want
+        err, worst = check(got, ref, dt, out, f"small groups {i} splits={ns}")
+        say(f"  splits {ns}: kernel {plan.info.split_kernel}, rel L2 {err:.2e}, worst sequence {worst:.2e}")
