@@ -37,22 +37,24 @@ int64_t resident_row_groups_per_cu(int32_t head_dim, int64_t rows) {
   if (head_dim == 64) return rows == 128 ? 3 : 4;
   return 2;
 }
-// Rows per block at head_dim 64 and 128: 128 (two 16-row groups per wave
-// sharing every K/V operand read) measured 15 % faster than 64 at head_dim
-// 128 on 128- and 512-token suffixes and 5 % on 8..32-token suffixes (GQA 4:
-// 32..128 rows). Blocks of 16 rows or fewer (a few drafted tokens) take 16
-// rows at every head_dim: wave 0 computes them and the other waves only copy
-// (64-row blocks would compute the empty rows on zero q). At head_dim 256
-// blocks are 64 rows, or 16 for 16 rows or fewer. A decode step (one token)
-// with 17 to 64 rows (32 or 48 query heads per KV head) takes 64-row blocks:
-// at head_dim 128 they ran 8-12 % faster than 128-row blocks (32 x 1-8k
-// tokens at 48 over one KV head 24.4 -> 21.4 us, 32 over 2 heads 38.6 ->
-// 34.1) and twice as fast as 16-row blocks re-reading the keys for each.
+// Rows per block at head_dim 64 and 128 above 64 rows: 128 (two 16-row
+// groups per wave sharing every K/V operand read) measured 15 % faster than
+// 64 at head_dim 128 on 128- and 512-token suffixes (GQA 4: 512 and 2048
+// rows), and on the 32-token suffix (128 rows) 33.9 against 39.8 us. Blocks
+// of 16 rows or fewer (a few drafted tokens) take 16 rows at every head_dim:
+// wave 0 computes them and the other waves only copy (64-row blocks would
+// compute the empty rows on zero q). 17 to 64 rows take 64-row blocks, at
+// every head_dim: against 128-row blocks at head_dim 128, a decode step at
+// 48 query heads over one KV head, 32 x 1-8k tokens 24.4 -> 21.4 us, 32 over
+// 2 heads 38.6 -> 34.1; a 4-token check at 64 over 8 heads over the long
+// batch 570.9 -> 526.0, 8 tokens at 32 over 8, 32 x 1-8k 131.3 -> 118.3, a
+// 16-token suffix 36.3 -> 33.8; and twice as fast as 16-row blocks
+// re-reading the keys for each. At head_dim 256 blocks are 64 rows, or 16.
 // da_params.rows_per_block (validated by make_plan) forces a size.
-int64_t mq_rows(int64_t rows, int32_t head_dim, int32_t forced, bool decode) {
+int64_t mq_rows(int64_t rows, int32_t head_dim, int32_t forced) {
   if (forced > 0) return forced;
   if (rows <= 16) return 16;
-  if (decode && rows <= 64) return 64;
+  if (rows <= 64) return 64;
   return head_dim <= 128 ? 128 : 64;
 }
 // A split never holds fewer attended tokens than this (the pages' 256-token
@@ -375,7 +377,7 @@ da_status finish_multi_plan(da_plan* plan, const int32_t* lens, int64_t decode_p
   const int64_t G = plan->group;
   const int64_t R = T * G;
   // Four waves of 16 rows (or two groups of 16) share each key tile.
-  const int64_t QB = mq_rows(R, p.head_dim, p.rows_per_block, T == 1);
+  const int64_t QB = mq_rows(R, p.head_dim, p.rows_per_block);
   const int64_t nrb = ceil_div(R, QB);
   plan->split_kernel = 2;
   plan->rows_per_group = static_cast<int32_t>(QB);

@@ -189,9 +189,9 @@ typedef struct {
                                 multi-token kernels (q.K and P.V on the matrix
                                 cores): the T*G rows of a KV head in blocks of
                                 16 (16 rows or fewer: one wave computes, three
-                                copy), 128 (more rows at head_dim 64 and 128)
-                                or 64 (more rows at head_dim 256; and 17 to
-                                64 rows of a decode step);
+                                copy), 64 (17 to 64 rows; more rows at
+                                head_dim 256) or 128 (more than 64 rows at
+                                head_dim 64 and 128);
                                 da_params.rows_per_block forces one. Decode
                                 plans (query_len <= 1) with DA_KERNEL_AUTO
                                 take 2 when q and K/V share f16 or bf16 and G
