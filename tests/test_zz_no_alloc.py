@@ -31,6 +31,8 @@ CASES = [
      wl.LLAMA8B_3060.replace(batch=2, lengths=("list", (3060, 100)), seed=8), {}),
     ("decode-gqa8", wl.LONG_BATCH.replace(batch=4, num_q_heads=64, lengths=("list", (20000, 3060, 1, 9000))),
      wl.LONG_BATCH.replace(batch=2, num_q_heads=64, lengths=("list", (700, 5)), seed=13), {}),
+    ("decode-gqa16", wl.LONG_BATCH.replace(batch=3, num_q_heads=128, lengths=("list", (12000, 0, 3060))),
+     wl.LONG_BATCH.replace(batch=2, num_q_heads=128, lengths=("list", (900, 2)), seed=14), {}),
     ("decode-window-bf16", wl.MIXED_WINDOW.replace(batch=4, lengths=("list", (70000, 12, 5000, 40000))),
      wl.MIXED_WINDOW.replace(batch=3, lengths=("list", (9000, 1, 300)), seed=9), {}),
     ("fixed-order", wl.LLAMA8B_3060.replace(batch=3, lengths=("list", (9000, 3060, 17))),
