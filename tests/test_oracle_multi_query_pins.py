@@ -88,6 +88,8 @@ SHAPES = [
     (2, 5, 4, 1, 3, 4, [13, 6], 3),
     (3, 2, 2, 2, 4, 4, [2, 11, 17], 1),
     (1, 6, 4, 4, 2, 2, [20], 4),
+    (2, 3, 32, 2, 4, 4, [7, 3], 0),        # 16 query heads per KV head
+    (1, 2, 24, 1, 3, 2, [9], 3),           # 24 over one KV head, window
 ]
 
 

@@ -132,6 +132,8 @@ def run_oracle(case, P, scale, window):
     (1, 2, 1, 4, 8, [15], 15),
     (1, 2, 1, 4, 8, [15], 16),
     (2, 3, 1, 5, 2, [6, 3], 1),
+    (1, 32, 2, 4, 4, [9], 0),           # 16 query heads per KV head
+    (2, 48, 1, 4, 2, [5, 3], 2),        # 48 over one KV head, window
 ])
 def test_oracle_matches_brute_force(B, Hq, Hkv, D, P, lens, window):
     rng = np.random.default_rng(B * 100 + D * 10 + P + window)
@@ -153,6 +155,7 @@ def test_oracle_matches_brute_force(B, Hq, Hkv, D, P, lens, window):
     (2, 8, 4, 256, 16, [513, 96], 0),
     (2, 8, 8, 64, 32, [700, 33], 100),
     (1, 6, 2, 32, 8, [257], 256),
+    (2, 128, 8, 64, 16, [300, 5], 0),   # 16 query heads per KV head
 ])
 def test_oracle_matches_sdpa_f64(B, Hq, Hkv, D, P, lens, window):
     rng = np.random.default_rng(7 + D + P)
@@ -310,10 +313,10 @@ def test_window_at_least_length_is_no_window():
     assert np.array_equal(oracle.decode_attention(*case, 4, 0.4, 5)[1], a[1])
 
 
-def test_gqa_equals_mha_with_repeated_kv():
-    rng = np.random.default_rng(12)
-    G = 3
-    q, kp, vp, table, lens = rand_case(rng, 2, 6, 2, 8, 4, [14, 21])
+@pytest.mark.parametrize("G", [3, 16])
+def test_gqa_equals_mha_with_repeated_kv(G):
+    rng = np.random.default_rng(12 + G)
+    q, kp, vp, table, lens = rand_case(rng, 2, 2 * G, 2, 8, 4, [14, 21])
     a = oracle.decode_attention(q, kp, vp, table, lens, 4, 0.3, 0)
     kr = np.repeat(kp, G, axis=1)  # KV head j becomes heads jG..jG+G-1
     vr = np.repeat(vp, G, axis=1)
