@@ -178,3 +178,14 @@ def test_small_groups_few_streams_match_oracle(gpu, i):
         assert plan.info.split_kernel == want
         err, worst = check(got, ref, dt, out, f"small groups {i} splits={ns}")
         say(f"  splits {ns}: kernel {plan.info.split_kernel}, rel L2 {err:.2e}, worst sequence {worst:.2e}")
+
+
+def test_all_contexts_empty_wide_group(gpu):
+    """Every context empty at 128/8 heads: one unsplit block per KV head that
+    reads nothing, and every row of the output is zero."""
+    spec = wl.WorkloadSpec("mqdec_all_empty", 3, 128, 8, 128, "bf16", "bf16", "f32", 16, ("list", (0, 0, 0)),
+                           seed=7690)
+    w = wl.make_workload(spec, gpu)
+    got, plan = run_lib(w)
+    assert plan.info.split_kernel == 2 and plan.max_splits == 1 and plan.workspace_bytes == 0
+    assert torch.count_nonzero(got).item() == 0
